@@ -1,0 +1,179 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet record / replay / GQA-expand library
+ * for AMD Instinct MI355X (gfx950).  Link with libgdn.so.
+ *
+ * Plain C: callers need neither HIP nor PyTorch headers.  Device pointers are
+ * HIP device allocations; `stream` is a hipStream_t passed as void* (NULL is
+ * the default stream).
+ *
+ * Common conventions
+ * ------------------
+ * - Layouts are dense and row-major with no strides (the index arithmetic of
+ *   the record and replay kernels on the metaltile-std 0.1.0 page
+ *   src/ffai/gated_delta_replay.rs, and its "Tape layout" paragraph):
+ *       q, k            [B, T, Hk, Dk]      I/O dtype
+ *       v, y, delta_log [B, T, Hv, Dv]      I/O dtype
+ *       g, beta         [B, T, Hv]          I/O dtype
+ *       k_log           [B, T, Hv, Dk]      I/O dtype (keys expanded to value heads)
+ *       g_log           [B, T, Hv]          I/O dtype
+ *       state           [B, Hv, Dv, Dk]     float32 always (row dv, column dk)
+ *       mask            [B, T]              uint32; step active iff entry > 0
+ * - Arithmetic is float32 throughout; every I/O element is widened to float32
+ *   on load and rounded to nearest even on store.
+ * - Ownership: the caller owns every buffer.  The library allocates nothing,
+ *   keeps no state between calls and never synchronises; each call enqueues
+ *   its kernel on `stream` and returns.  Ordering between calls is stream
+ *   order.  Errors a kernel meets at run time (e.g. a fault) surface at the
+ *   caller's next synchronisation, as usual in HIP.
+ * - Validation happens on the host before any HIP call; a rejected call
+ *   enqueues nothing and returns a negative gdn_status.  gdn_last_error()
+ *   then holds a human-readable reason (per calling thread).
+ * - Pointers to tensors other than mask, g, beta and g_log must be 16-byte
+ *   aligned (mask 4-byte, the others element-aligned).
+ * - Raw pointers carry no length: the caller guarantees each buffer holds the
+ *   elements its shape implies.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_dtype {
+    GDN_F32 = 0,
+    GDN_F16 = 1,
+    GDN_BF16 = 2
+} gdn_dtype;
+
+typedef enum gdn_gqa_map {
+    GDN_GQA_BLOCK = 0,  /* hk = hv / (Hv / Hk): consecutive value heads share a key head */
+    GDN_GQA_TILED = 1   /* hk = hv mod Hk: the key heads repeat as a whole            */
+} gdn_gqa_map;
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL = -1,              /* a required pointer is NULL                          */
+    GDN_ERR_ZERO_DIM = -2,          /* a dimension is zero                                 */
+    GDN_ERR_GQA_RATIO = -3,         /* Hk does not divide Hv (hg does not divide h)        */
+    GDN_ERR_UNSUPPORTED_SHAPE = -4, /* (Dk, Dv) not built: see gdn_record                  */
+    GDN_ERR_OVERFLOW = -5,          /* an element count or the launch grid is too large    */
+    GDN_ERR_ALIAS = -6,             /* an output overlaps an input or another output       */
+    GDN_ERR_BAD_ENUM = -7,          /* unknown dtype or GQA map                            */
+    GDN_ERR_LAUNCH = -8,            /* the HIP runtime refused the launch                  */
+    GDN_ERR_MISALIGNED = -9         /* a pointer lacks the alignment stated above          */
+} gdn_status;
+
+/*
+ * gdn_record -- gated delta-rule forward step with innovation-tape capture.
+ *
+ * Defined by the record kernel (macro `gated_delta_record!`) on the
+ * metaltile-std 0.1.0 page src/ffai/gated_delta_replay.rs.  For every batch
+ * row b, value head hv (key head hk given by `gqa_map`), value row dv and step
+ * t = 0..T-1 whose mask entry is non-zero (all steps when mask == NULL):
+ *     S[dv,:] <- g[b,t,hv] * S[dv,:]
+ *     kv      <- S[dv,:] . k[b,t,hk,:]
+ *     delta   <- (v[b,t,hv,dv] - kv) * beta[b,t,hv]
+ *     delta_log[b,t,hv,dv] <- delta
+ *     S[dv,:] <- S[dv,:] + delta * k[b,t,hk,:]
+ *     y[b,t,hv,dv] <- S[dv,:] . q[b,t,hk,:]
+ * starting from S = state_in[b,hv] and ending with state_out[b,hv] = S.
+ * An inactive step changes nothing and writes nothing: y and delta_log keep
+ * whatever the caller's buffers held at those positions.
+ *
+ * Arguments
+ *   q, k, v, g, beta  inputs, io_dtype, layouts above.
+ *   state_in          float32 [B,Hv,Dv,Dk].
+ *   mask              uint32 [B,T] or NULL (every step active).
+ *   y                 output, io_dtype [B,T,Hv,Dv].
+ *   state_out         output, float32 [B,Hv,Dv,Dk]; may be exactly state_in
+ *                     (in place), but must not overlap it otherwise.
+ *   delta_log         output tape, io_dtype [B,T,Hv,Dv], or NULL for the plain
+ *                     forward step without a tape.
+ *   B, T, Hk, Hv, Dk, Dv  sizes; Hk must divide Hv.  Dk in {32,64,128,192,256};
+ *                     Dv a multiple of 16, at most 1024.
+ *   io_dtype          gdn_dtype of every non-state tensor.
+ *   gqa_map           gdn_gqa_map.
+ *   stream            hipStream_t or NULL.
+ * Returns GDN_OK or a negative gdn_status (nothing is enqueued on error).
+ */
+int gdn_record(const void* q, const void* k, const void* v, const void* g, const void* beta,
+               const float* state_in, const uint32_t* mask,
+               void* y, float* state_out, void* delta_log,
+               uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+               int io_dtype, int gqa_map, void* stream);
+
+/*
+ * gdn_replay -- re-fold the accepted prefix of an innovation tape onto a
+ * pre-record state snapshot (speculative-decode rollback).
+ *
+ * Defined by the replay kernel (macro `state_replay!`) and the module
+ * documentation ("Two kernels", "Tape layout") on the metaltile-std 0.1.0 page
+ * src/ffai/gated_delta_replay.rs.  For every (b, hv, dv), starting from
+ * S = state_in[b,hv], for t = 0..T_log-1 the step is taken iff t < accepted and
+ * mask[b,t] > 0 (mask == NULL: every step passes); a taken step does
+ *     S[dv,:] <- S[dv,:] * g_log[b,t,hv] + k_log[b,t,hv,:] * delta_log[b,t,hv,dv]
+ * and an untaken one leaves S as it was, whatever its tape slot holds (NaN
+ * included).  state_out[b,hv] = S.  accepted > T_log acts as T_log;
+ * accepted == 0 copies the snapshot.
+ *
+ * Arguments
+ *   delta_log   io_dtype [B,T_log,Hv,Dv].
+ *   k_log       io_dtype [B,T_log,Hv,Dk] (keys already expanded to value heads,
+ *               e.g. by gqa_expand).
+ *   g_log       io_dtype [B,T_log,Hv].
+ *   state_in    float32 [B,Hv,Dv,Dk], the snapshot taken before the record.
+ *   mask        uint32 [B,T_log] or NULL.
+ *   state_out   float32 [B,Hv,Dv,Dk]; may be exactly state_in.
+ *   B, T_log, Hv, Dk, Dv, accepted   sizes as for gdn_record.
+ *   io_dtype, stream                 as for gdn_record.
+ * Returns GDN_OK or a negative gdn_status.
+ */
+int gdn_replay(const void* delta_log, const void* k_log, const void* g_log,
+               const float* state_in, const uint32_t* mask, float* state_out,
+               uint32_t B, uint32_t T_log, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+               uint32_t accepted, int io_dtype, void* stream);
+
+/*
+ * gqa_expand -- GQA head broadcast [seq, hg, k] -> [seq, h, k], a bit copy.
+ *
+ * Defined on the mlx-native 0.6.5 page mlx_native/ops/repeat_tiled.rs (module
+ * documentation "Mapping": dst[t,h,k] = src[t, h % hg, k], and the argument
+ * rules of `dispatch_repeat_tiled_f32`), with the block map of the
+ * metaltile-std record kernel as the alternative:
+ *     GDN_GQA_TILED  dst[s,hh,e] = src[s, hh % hg,        e]
+ *     GDN_GQA_BLOCK  dst[s,hh,e] = src[s, hh / (h / hg),  e]
+ * Element bits are copied unchanged (NaN payloads included).  A batched
+ * tensor [B,T,H,K] is expanded with seq = B*T.
+ *
+ * Arguments
+ *   src, dst    device buffers of seq*hg*k and seq*h*k elements; must not
+ *               overlap; element-aligned.
+ *   seq, hg, h, k  sizes, all non-zero, hg dividing h.
+ *   dtype       gdn_dtype (fixes the element size: 4 bytes for GDN_F32,
+ *               2 for GDN_F16 and GDN_BF16).
+ *   gqa_map     gdn_gqa_map.
+ *   stream      hipStream_t or NULL.
+ * Returns GDN_OK or a negative gdn_status.
+ */
+int gqa_expand(const void* src, void* dst, uint32_t seq, uint32_t hg, uint32_t h, uint32_t k,
+               int dtype, int gqa_map, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* gdn_strerror(int status);
+
+/* Reason for the last failed call on this thread ("" if none yet). */
+const char* gdn_last_error(void);
+
+/* GDN_ABI_VERSION of the loaded library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

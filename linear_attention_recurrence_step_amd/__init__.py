@@ -1,0 +1,166 @@
+"""Gated DeltaNet record / replay / GQA-expand for AMD Instinct MI355X (gfx950).
+
+Python binding of libgdn (include/gdn.h).  Each function has the name of its
+C entry point, checks that the torch tensors it is given have the layouts the
+C ABI expects, allocates missing outputs with torch, and calls the library on
+the current torch stream.  Every step of the computation runs in the HIP
+kernels; there is no CPU fallback, and importing this package fails if the
+library has not been built.
+
+Layouts (dense, contiguous):
+    q, k [B,T,Hk,Dk]; v, y, delta_log [B,T,Hv,Dv]; g, beta [B,T,Hv];
+    state [B,Hv,Dv,Dk] float32; mask [B,T] int32/uint32 (active iff > 0);
+    k_log [B,T,Hv,Dk]; g_log [B,T,Hv].
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _native
+from ._native import GdnError, lib
+
+__all__ = ["gdn_record", "gdn_replay", "gqa_expand", "GdnError", "IO_DTYPES"]
+
+IO_DTYPES = {torch.float32: _native.GDN_F32, torch.float16: _native.GDN_F16,
+             torch.bfloat16: _native.GDN_BF16}
+_MAPS = {"block": _native.GDN_GQA_BLOCK, "tiled": _native.GDN_GQA_TILED}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _want(name: str, t: torch.Tensor, shape, dtype, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if isinstance(dtype, tuple):
+        if t.dtype not in dtype:
+            raise TypeError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtype))
+    elif t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _io_code(t: torch.Tensor) -> int:
+    if t.dtype not in IO_DTYPES:
+        raise TypeError("I/O tensors must be float32, float16 or bfloat16, got %s" % t.dtype)
+    return IO_DTYPES[t.dtype]
+
+
+_MASK_DTYPES = (torch.int32, torch.uint32) if hasattr(torch, "uint32") else (torch.int32,)
+
+
+def gdn_record(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+               beta: torch.Tensor, state_in: torch.Tensor, mask: Optional[torch.Tensor] = None,
+               *, gqa_map: str = "block", y: Optional[torch.Tensor] = None,
+               state_out: Optional[torch.Tensor] = None,
+               delta_log: Optional[torch.Tensor] = None, write_tape: bool = True,
+               stream=None) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """Gated delta-rule step with tape capture; returns (y, state_out, delta_log).
+
+    Outputs that are not given are allocated (uninitialised: the positions of
+    inactive steps in y and delta_log are not written).  ``state_out`` may be
+    ``state_in`` itself.  With ``write_tape=False`` and no ``delta_log`` the
+    plain forward step runs and the third result is None.
+    """
+    if gqa_map not in _MAPS:
+        raise ValueError("gqa_map must be 'block' or 'tiled'")
+    dev = q.device
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    io = q.dtype
+    _io_code(q)
+    _want("q", q, (B, T, Hk, Dk), io, dev)
+    _want("k", k, (B, T, Hk, Dk), io, dev)
+    _want("v", v, (B, T, Hv, Dv), io, dev)
+    _want("g", g, (B, T, Hv), io, dev)
+    _want("beta", beta, (B, T, Hv), io, dev)
+    _want("state_in", state_in, (B, Hv, Dv, Dk), torch.float32, dev)
+    if mask is not None:
+        _want("mask", mask, (B, T), _MASK_DTYPES, dev)
+    if y is None:
+        y = torch.empty((B, T, Hv, Dv), dtype=io, device=dev)
+    _want("y", y, (B, T, Hv, Dv), io, dev)
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    _want("state_out", state_out, (B, Hv, Dv, Dk), torch.float32, dev)
+    if delta_log is None and write_tape:
+        delta_log = torch.empty((B, T, Hv, Dv), dtype=io, device=dev)
+    if delta_log is not None:
+        _want("delta_log", delta_log, (B, T, Hv, Dv), io, dev)
+    rc = lib.gdn_record(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+                        _ptr(mask), _ptr(y), _ptr(state_out), _ptr(delta_log),
+                        B, T, Hk, Hv, Dk, Dv, _io_code(q), _MAPS[gqa_map], _stream(stream, dev))
+    _native.check("gdn_record", rc)
+    return y, state_out, delta_log
+
+
+def gdn_replay(delta_log: torch.Tensor, k_log: torch.Tensor, g_log: torch.Tensor,
+               state_in: torch.Tensor, mask: Optional[torch.Tensor] = None,
+               accepted: Optional[int] = None, *, state_out: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """Re-fold tape positions [0, accepted) onto the snapshot; returns state_out.
+
+    ``accepted`` defaults to the tape length; values past it act as the tape
+    length.  ``state_out`` may be ``state_in`` itself.
+    """
+    dev = delta_log.device
+    B, T, Hv, Dv = delta_log.shape
+    Dk = k_log.shape[3]
+    io = delta_log.dtype
+    _io_code(delta_log)
+    _want("delta_log", delta_log, (B, T, Hv, Dv), io, dev)
+    _want("k_log", k_log, (B, T, Hv, Dk), io, dev)
+    _want("g_log", g_log, (B, T, Hv), io, dev)
+    _want("state_in", state_in, (B, Hv, Dv, Dk), torch.float32, dev)
+    if mask is not None:
+        _want("mask", mask, (B, T), _MASK_DTYPES, dev)
+    if accepted is None:
+        accepted = T
+    if not 0 <= int(accepted) < 2 ** 32:
+        raise ValueError("accepted must fit in uint32")
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    _want("state_out", state_out, (B, Hv, Dv, Dk), torch.float32, dev)
+    rc = lib.gdn_replay(_ptr(delta_log), _ptr(k_log), _ptr(g_log), _ptr(state_in), _ptr(mask),
+                        _ptr(state_out), B, T, Hv, Dk, Dv, int(accepted), _io_code(delta_log),
+                        _stream(stream, dev))
+    _native.check("gdn_replay", rc)
+    return state_out
+
+
+def gqa_expand(src: torch.Tensor, h: int, gqa_map: str = "tiled", *,
+               dst: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Head broadcast [..., hg, k] -> [..., h, k] (all leading dims flattened to seq)."""
+    if gqa_map not in _MAPS:
+        raise ValueError("gqa_map must be 'block' or 'tiled'")
+    if src.dim() < 2:
+        raise ValueError("src must be [..., hg, k]")
+    dev = src.device
+    hg, kk = src.shape[-2], src.shape[-1]
+    seq = 1
+    for d in src.shape[:-2]:
+        seq *= d
+    code = _io_code(src)
+    out_shape = tuple(src.shape[:-2]) + (h, kk)
+    _want("src", src, tuple(src.shape), src.dtype, dev)
+    if dst is None:
+        dst = torch.empty(out_shape, dtype=src.dtype, device=dev)
+    _want("dst", dst, out_shape, src.dtype, dev)
+    rc = lib.gqa_expand(_ptr(src), _ptr(dst), seq, hg, h, kk, code, _MAPS[gqa_map],
+                        _stream(stream, dev))
+    _native.check("gqa_expand", rc)
+    return dst

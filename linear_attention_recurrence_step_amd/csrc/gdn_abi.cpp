@@ -1,0 +1,220 @@
+// extern "C" boundary of libgdn: argument validation (entirely on the host,
+// before any HIP call) and dispatch to the kernel launchers.
+//
+// The validation rules follow `dispatch_repeat_tiled_f32` on the mlx-native
+// 0.6.5 page mlx_native/ops/repeat_tiled.rs (zero dimensions, the head ratio,
+// size overflow) and the dispatch invariants of the metaltile-std 0.1.0 page
+// src/ffai/gated_delta_replay.rs (Dk a multiple of 32), extended with the
+// checks a raw-pointer interface needs (NULL, alignment, overlap).
+#include "gdn.h"
+#include "gdn_internal.hpp"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <initializer_list>
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+// a * b * c * d * e in 64 bits; false on overflow.
+bool mul_u64(uint64_t* out, std::initializer_list<uint64_t> xs) {
+    uint64_t acc = 1;
+    for (uint64_t x : xs)
+        if (__builtin_mul_overflow(acc, x, &acc)) return false;
+    *out = acc;
+    return true;
+}
+
+constexpr uint64_t kMaxBytes = uint64_t(1) << 48;   // 256 TiB: far beyond any device, safe for offsets
+constexpr uint64_t kMaxGrid = 0x7fffffffull;
+
+struct Span {
+    const void* p;
+    uint64_t bytes;
+    const char* name;
+};
+
+bool overlaps(const Span& a, const Span& b) {
+    if (a.p == nullptr || b.p == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int io_bytes(int dtype) { return dtype == GDN_F32 ? 4 : 2; }
+
+bool valid_dtype(int d) { return d == GDN_F32 || d == GDN_F16 || d == GDN_BF16; }
+bool valid_map(int m) { return m == GDN_GQA_BLOCK || m == GDN_GQA_TILED; }
+
+int launch_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return GDN_OK;
+    return fail(GDN_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_last_error(void) { return g_last_error; }
+
+const char* gdn_strerror(int status) {
+    switch (status) {
+        case GDN_OK: return "ok";
+        case GDN_ERR_NULL: return "a required pointer is NULL";
+        case GDN_ERR_ZERO_DIM: return "a dimension is zero";
+        case GDN_ERR_GQA_RATIO: return "the key-head count does not divide the value-head count";
+        case GDN_ERR_UNSUPPORTED_SHAPE: return "unsupported head dimensions";
+        case GDN_ERR_OVERFLOW: return "tensor size or launch grid too large";
+        case GDN_ERR_ALIAS: return "an output overlaps an input or another output";
+        case GDN_ERR_BAD_ENUM: return "unknown dtype or GQA map";
+        case GDN_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
+        case GDN_ERR_MISALIGNED: return "a pointer is not aligned as required";
+        default: return "unknown status";
+    }
+}
+
+int gdn_record(const void* q, const void* k, const void* v, const void* g, const void* beta,
+               const float* state_in, const uint32_t* mask,
+               void* y, float* state_out, void* delta_log,
+               uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+               int io_dtype, int gqa_map, void* stream) {
+    static const char* kFn = "gdn_record";
+    if (!valid_dtype(io_dtype)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown io_dtype %d", kFn, io_dtype);
+    if (!valid_map(gqa_map)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown gqa_map %d", kFn, gqa_map);
+    if (!q || !k || !v || !g || !beta || !state_in || !y || !state_out)
+        return fail(GDN_ERR_NULL, "%s: q, k, v, g, beta, state_in, y and state_out must be non-NULL", kFn);
+    if (B == 0 || T == 0 || Hk == 0 || Hv == 0 || Dk == 0 || Dv == 0)
+        return fail(GDN_ERR_ZERO_DIM, "%s: B, T, Hk, Hv, Dk, Dv must all be > 0 (got %u,%u,%u,%u,%u,%u)",
+                    kFn, B, T, Hk, Hv, Dk, Dv);
+    if (Hv % Hk != 0) return fail(GDN_ERR_GQA_RATIO, "%s: Hv (%u) must be a multiple of Hk (%u)", kFn, Hv, Hk);
+    if (!gdn::dk_supported(Dk) || Dv % 16 != 0 || Dv > 1024)
+        return fail(GDN_ERR_UNSUPPORTED_SHAPE,
+                    "%s: Dk must be one of 32, 64, 128, 192, 256 and Dv a multiple of 16 up to 1024 "
+                    "(got Dk=%u, Dv=%u)", kFn, Dk, Dv);
+
+    const uint64_t e = io_bytes(io_dtype);
+    uint64_t n_qk, n_v, n_g, n_s, n_m;
+    if (!mul_u64(&n_qk, {B, T, Hk, Dk, e}) || !mul_u64(&n_v, {B, T, Hv, Dv, e}) ||
+        !mul_u64(&n_g, {B, T, Hv, e}) || !mul_u64(&n_s, {B, Hv, Dv, Dk, 4}) || !mul_u64(&n_m, {B, T, 4}) ||
+        n_qk > kMaxBytes || n_v > kMaxBytes || n_s > kMaxBytes)
+        return fail(GDN_ERR_OVERFLOW, "%s: tensor sizes overflow", kFn);
+
+    gdn::RecordArgs a{q, k, v, g, beta, state_in, mask, y, state_out, delta_log,
+                      B, T, Hk, Hv, Dk, Dv, io_dtype, gqa_map};
+    const gdn::RowTiling til = gdn::record_tiling(a);
+    uint64_t grid;
+    if (!mul_u64(&grid, {B, Hv, Dv / static_cast<uint32_t>(til.rows())}) || grid > kMaxGrid)
+        return fail(GDN_ERR_OVERFLOW, "%s: launch grid too large (B*Hv too large)", kFn);
+
+    const void* a16[] = {q, k, v, state_in, y, state_out, delta_log};
+    const char* a16n[] = {"q", "k", "v", "state_in", "y", "state_out", "delta_log"};
+    for (int i = 0; i < 7; ++i)
+        if (a16[i] && !aligned(a16[i], 16))
+            return fail(GDN_ERR_MISALIGNED, "%s: %s must be 16-byte aligned", kFn, a16n[i]);
+    if (mask && !aligned(mask, 4)) return fail(GDN_ERR_MISALIGNED, "%s: mask must be 4-byte aligned", kFn);
+    if (!aligned(g, e) || !aligned(beta, e))
+        return fail(GDN_ERR_MISALIGNED, "%s: g and beta must be element-aligned", kFn);
+
+    const Span ins[] = {{q, n_qk, "q"}, {k, n_qk, "k"}, {v, n_v, "v"}, {g, n_g, "g"},
+                        {beta, n_g, "beta"}, {state_in, n_s, "state_in"}, {mask, mask ? n_m : 0, "mask"}};
+    const Span outs[] = {{y, n_v, "y"}, {state_out, n_s, "state_out"},
+                         {delta_log, delta_log ? n_v : 0, "delta_log"}};
+    for (const Span& o : outs) {
+        for (const Span& i : ins) {
+            if (o.p == state_out && i.p == state_in && o.p == i.p) continue;   // exact in-place state
+            if (overlaps(o, i)) return fail(GDN_ERR_ALIAS, "%s: %s overlaps %s", kFn, o.name, i.name);
+        }
+    }
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(GDN_ERR_ALIAS, "%s: %s overlaps %s", kFn, outs[i].name, outs[j].name);
+
+    return launch_status(gdn::launch_record(a, static_cast<hipStream_t>(stream)), kFn);
+}
+
+int gdn_replay(const void* delta_log, const void* k_log, const void* g_log,
+               const float* state_in, const uint32_t* mask, float* state_out,
+               uint32_t B, uint32_t T_log, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+               uint32_t accepted, int io_dtype, void* stream) {
+    static const char* kFn = "gdn_replay";
+    if (!valid_dtype(io_dtype)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown io_dtype %d", kFn, io_dtype);
+    if (!delta_log || !k_log || !g_log || !state_in || !state_out)
+        return fail(GDN_ERR_NULL, "%s: delta_log, k_log, g_log, state_in and state_out must be non-NULL", kFn);
+    if (B == 0 || T_log == 0 || Hv == 0 || Dk == 0 || Dv == 0)
+        return fail(GDN_ERR_ZERO_DIM, "%s: B, T_log, Hv, Dk, Dv must all be > 0 (got %u,%u,%u,%u,%u)",
+                    kFn, B, T_log, Hv, Dk, Dv);
+    if (!gdn::dk_supported(Dk) || Dv % 16 != 0 || Dv > 1024)
+        return fail(GDN_ERR_UNSUPPORTED_SHAPE,
+                    "%s: Dk must be one of 32, 64, 128, 192, 256 and Dv a multiple of 16 up to 1024 "
+                    "(got Dk=%u, Dv=%u)", kFn, Dk, Dv);
+
+    const uint64_t e = io_bytes(io_dtype);
+    uint64_t n_d, n_k, n_g, n_s, n_m;
+    if (!mul_u64(&n_d, {B, T_log, Hv, Dv, e}) || !mul_u64(&n_k, {B, T_log, Hv, Dk, e}) ||
+        !mul_u64(&n_g, {B, T_log, Hv, e}) || !mul_u64(&n_s, {B, Hv, Dv, Dk, 4}) ||
+        !mul_u64(&n_m, {B, T_log, 4}) || n_d > kMaxBytes || n_k > kMaxBytes || n_s > kMaxBytes)
+        return fail(GDN_ERR_OVERFLOW, "%s: tensor sizes overflow", kFn);
+
+    gdn::ReplayArgs a{delta_log, k_log, g_log, state_in, mask, state_out,
+                      B, T_log, Hv, Dk, Dv, accepted < T_log ? accepted : T_log, io_dtype};
+    const gdn::RowTiling til = gdn::replay_tiling(a);
+    uint64_t grid;
+    if (!mul_u64(&grid, {B, Hv, Dv / static_cast<uint32_t>(til.rows())}) || grid > kMaxGrid)
+        return fail(GDN_ERR_OVERFLOW, "%s: launch grid too large (B*Hv too large)", kFn);
+
+    const void* a16[] = {delta_log, k_log, state_in, state_out};
+    const char* a16n[] = {"delta_log", "k_log", "state_in", "state_out"};
+    for (int i = 0; i < 4; ++i)
+        if (!aligned(a16[i], 16)) return fail(GDN_ERR_MISALIGNED, "%s: %s must be 16-byte aligned", kFn, a16n[i]);
+    if (mask && !aligned(mask, 4)) return fail(GDN_ERR_MISALIGNED, "%s: mask must be 4-byte aligned", kFn);
+    if (!aligned(g_log, e)) return fail(GDN_ERR_MISALIGNED, "%s: g_log must be element-aligned", kFn);
+
+    const Span out{state_out, n_s, "state_out"};
+    const Span ins[] = {{delta_log, n_d, "delta_log"}, {k_log, n_k, "k_log"}, {g_log, n_g, "g_log"},
+                        {state_in, n_s, "state_in"}, {mask, mask ? n_m : 0, "mask"}};
+    for (const Span& i : ins) {
+        if (i.p == state_in && out.p == state_in) continue;                   // exact in-place state
+        if (overlaps(out, i)) return fail(GDN_ERR_ALIAS, "%s: state_out overlaps %s", kFn, i.name);
+    }
+
+    return launch_status(gdn::launch_replay(a, static_cast<hipStream_t>(stream)), kFn);
+}
+
+int gqa_expand(const void* src, void* dst, uint32_t seq, uint32_t hg, uint32_t h, uint32_t k,
+               int dtype, int gqa_map, void* stream) {
+    static const char* kFn = "gqa_expand";
+    if (!valid_dtype(dtype)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown dtype %d", kFn, dtype);
+    if (!valid_map(gqa_map)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown gqa_map %d", kFn, gqa_map);
+    if (!src || !dst) return fail(GDN_ERR_NULL, "%s: src and dst must be non-NULL", kFn);
+    if (seq == 0 || hg == 0 || h == 0 || k == 0)
+        return fail(GDN_ERR_ZERO_DIM, "%s: seq, hg, h, k must all be > 0", kFn);
+    if (h % hg != 0) return fail(GDN_ERR_GQA_RATIO, "%s: h (%u) must be a multiple of hg (%u)", kFn, h, hg);
+    const uint64_t e = io_bytes(dtype);
+    uint64_t n_src, n_dst;
+    if (!mul_u64(&n_src, {seq, hg, k, e}) || !mul_u64(&n_dst, {seq, h, k, e}) || n_dst > kMaxBytes)
+        return fail(GDN_ERR_OVERFLOW, "%s: seq*h*k overflows", kFn);
+    if (!aligned(src, e) || !aligned(dst, e))
+        return fail(GDN_ERR_MISALIGNED, "%s: src and dst must be element-aligned", kFn);
+    if (overlaps(Span{src, n_src, "src"}, Span{dst, n_dst, "dst"}))
+        return fail(GDN_ERR_ALIAS, "%s: dst overlaps src", kFn);
+    gdn::ExpandArgs a{src, dst, seq, hg, h, k, static_cast<uint32_t>(e), gqa_map};
+    return launch_status(gdn::launch_expand(a, static_cast<hipStream_t>(stream)), kFn);
+}
+
+}  // extern "C"

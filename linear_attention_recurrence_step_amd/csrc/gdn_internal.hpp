@@ -1,0 +1,84 @@
+// Host-side interface between the C ABI (gdn_abi.cpp) and the kernel launchers
+// (gdn_record.hip, gdn_replay.hip, gqa_expand.hip).  Arguments arrive here
+// already validated.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct RecordArgs {
+    const void* q; const void* k; const void* v; const void* g; const void* beta;
+    const float* state_in; const uint32_t* mask;
+    void* y; float* state_out; void* delta_log;
+    uint32_t B, T, Hk, Hv, Dk, Dv;
+    int io;       // IoType
+    int map;      // 0 block, 1 tiled
+};
+
+struct ReplayArgs {
+    const void* delta_log; const void* k_log; const void* g_log;
+    const float* state_in; const uint32_t* mask; float* state_out;
+    uint32_t B, T_log, Hv, Dk, Dv, steps;   // steps = min(accepted, T_log)
+    int io;
+};
+
+struct ExpandArgs {
+    const void* src; void* dst;
+    uint32_t seq, hg, h, k;
+    uint32_t elem_bytes;
+    int map;
+};
+
+// Row blocking of a head: a workgroup of `threads` threads covers
+// rows_per_thread * threads / 16 consecutive value rows of one head.
+struct RowTiling {
+    int rows_per_thread;
+    int threads;
+    int rows() const { return rows_per_thread * threads / 16; }
+};
+
+// Does a kernel exist for this key width?
+bool dk_supported(uint32_t Dk);
+
+// Tiling the launchers will use (also used by the ABI for its grid-size check).
+RowTiling record_tiling(const RecordArgs& a);
+RowTiling replay_tiling(const ReplayArgs& a);
+
+hipError_t launch_record(const RecordArgs& a, hipStream_t stream);
+hipError_t launch_replay(const ReplayArgs& a, hipStream_t stream);
+hipError_t launch_expand(const ExpandArgs& a, hipStream_t stream);
+
+}  // namespace gdn
+
+namespace gdn {
+
+// Candidate row tilings, widest first.  A lane keeps rows_per_thread * Dk / 16
+// state values in registers; that is held to at most 64.
+inline constexpr RowTiling kTilings[] = {{8, 256}, {4, 256}, {2, 256}, {1, 256}, {1, 64}};
+inline constexpr int kNumTilings = 5;
+inline constexpr int kMaxStatePerLane = 64;
+
+inline bool tiling_fits(const RowTiling& t, uint32_t Dk, uint32_t Dv) {
+    return Dv % static_cast<uint32_t>(t.rows()) == 0 &&
+           static_cast<uint32_t>(t.rows_per_thread) * (Dk / 16) <= kMaxStatePerLane;
+}
+
+// Widest tiling that still yields `target_groups` workgroups; otherwise the
+// narrowest one that fits (more, smaller workgroups for few heads).
+inline RowTiling pick_tiling(uint64_t heads, uint32_t Dk, uint32_t Dv, uint64_t target_groups) {
+    for (int i = 0; i < kNumTilings; ++i) {
+        const RowTiling& t = kTilings[i];
+        if (tiling_fits(t, Dk, Dv) && heads * (Dv / t.rows()) >= target_groups) return t;
+    }
+    for (int i = kNumTilings - 1; i >= 0; --i)
+        if (tiling_fits(kTilings[i], Dk, Dv)) return kTilings[i];
+    return kTilings[kNumTilings - 1];
+}
+
+// Optional tiling forced through an environment variable ("rows_per_thread,threads"),
+// used for launch-shape sweeps; ignored unless it names a known tiling that fits.
+bool tiling_override(const char* env_name, uint32_t Dk, uint32_t Dv, RowTiling* out);
+
+}  // namespace gdn

@@ -1,0 +1,87 @@
+// gqa_expand: GQA head broadcast [seq, hg, k] -> [seq, h, k] as a bit copy, gfx950.
+//
+// What it computes: the mapping in the module documentation of the mlx-native
+// 0.6.5 page mlx_native/ops/repeat_tiled.rs, dst[t, hh, e] = src[t, hh % hg, e]
+// (tiled), and the block alternative dst[t, hh, e] = src[t, hh / (h / hg), e]
+// used by the metaltile-std record kernel.
+//
+// Mapping: one thread moves one VB-byte vector of a source head row and
+// writes it to each of the h / hg destination heads that replicate it, so the
+// source is read once and every destination byte is written once.  VB is the
+// widest of 16/8/4/2 bytes that divides the row and both base addresses.
+// Consecutive threads take consecutive vectors of a row, so loads and stores
+// are contiguous across a wavefront.  Each thread handles kUnroll vectors,
+// issuing all loads before the stores.
+#include "gdn_device.hpp"
+#include "gdn_internal.hpp"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+template <int VB>
+__global__ __launch_bounds__(kThreads) void gqa_expand_kernel(
+    const typename RawVec<VB>::T* __restrict__ src, typename RawVec<VB>::T* __restrict__ dst,
+    uint64_t nvec, uint32_t hg, uint32_t h, uint32_t row_vecs, int tiled)
+{
+    using V = typename RawVec<VB>::T;
+    const uint32_t group = h / hg;
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads * kUnroll;
+    for (uint64_t base = static_cast<uint64_t>(blockIdx.x) * kThreads * kUnroll + threadIdx.x;
+         base < nvec; base += stride) {
+        V val[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint64_t i = base + static_cast<uint64_t>(u) * kThreads;
+            if (i < nvec) val[u] = src[i];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint64_t i = base + static_cast<uint64_t>(u) * kThreads;
+            if (i >= nvec) break;
+            const uint64_t row = i / row_vecs;                 // s * hg + hs
+            const uint32_t c = static_cast<uint32_t>(i - row * row_vecs);
+            const uint64_t s = row / hg;
+            const uint32_t hs = static_cast<uint32_t>(row - s * hg);
+            for (uint32_t j = 0; j < group; ++j) {
+                const uint32_t hd = tiled ? j * hg + hs : hs * group + j;
+                dst[(s * h + hd) * row_vecs + c] = val[u];
+            }
+        }
+    }
+}
+
+template <int VB>
+hipError_t launch_vb(const ExpandArgs& a, hipStream_t stream) {
+    using V = typename RawVec<VB>::T;
+    const uint32_t row_vecs = static_cast<uint32_t>((static_cast<uint64_t>(a.k) * a.elem_bytes) / VB);
+    const uint64_t nvec = static_cast<uint64_t>(a.seq) * a.hg * row_vecs;
+    const uint64_t per_block = static_cast<uint64_t>(kThreads) * kUnroll;
+    uint64_t blocks = (nvec + per_block - 1) / per_block;
+    if (blocks > (1u << 20)) blocks = 1u << 20;               // grid-stride beyond this
+    hipLaunchKernelGGL((gqa_expand_kernel<VB>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads),
+                       0, stream, static_cast<const V*>(a.src), static_cast<V*>(a.dst), nvec, a.hg,
+                       a.h, row_vecs, a.map);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_expand(const ExpandArgs& a, hipStream_t stream) {
+    const uint64_t row_bytes = static_cast<uint64_t>(a.k) * a.elem_bytes;
+    const uintptr_t sa = reinterpret_cast<uintptr_t>(a.src);
+    const uintptr_t da = reinterpret_cast<uintptr_t>(a.dst);
+    uint32_t vb = 16;
+    while (vb > a.elem_bytes && (row_bytes % vb != 0 || sa % vb != 0 || da % vb != 0)) vb >>= 1;
+    switch (vb) {
+        case 16: return launch_vb<16>(a, stream);
+        case 8: return launch_vb<8>(a, stream);
+        case 4: return launch_vb<4>(a, stream);
+        case 2: return launch_vb<2>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gdn

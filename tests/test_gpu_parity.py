@@ -1,0 +1,351 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every input comes from the seeded generators in gdn_inputs; every expected
+value comes from the oracle (or, for the cross-kernel identities, from another
+call of the HIP path, compared bit for bit).  Floating-point outputs must be
+within 1e-3 (float32 I/O) or 2e-2 (float16 / bfloat16 I/O) of the oracle,
+scaled as |gpu - oracle| <= tol * (1 + |oracle|); GQA expansion must match
+byte for byte.  Positions of inactive steps must keep the caller's sentinel.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import oracle
+import linear_attention_recurrence_step_amd as gdn
+from gpu_util import TOL, assert_close, dev, f64, note, step_mask, to_dev
+
+pytestmark = pytest.mark.gpu
+
+Y_SENTINEL = -7.5       # exact in every I/O dtype
+D_SENTINEL = 3.25
+
+
+def _record_gpu(inp, gqa_map, write_tape=True):
+    d = to_dev(inp)
+    io = d["q"].dtype
+    y = torch.full(d["v"].shape, Y_SENTINEL, dtype=io, device=dev())
+    dl = torch.full(d["v"].shape, D_SENTINEL, dtype=io, device=dev()) if write_tape else None
+    y, s, dl = gdn.gdn_record(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"], d["mask"],
+                              gqa_map=gqa_map, y=y, delta_log=dl, write_tape=write_tape)
+    torch.cuda.synchronize()
+    return y, s, dl
+
+
+def _check_record(inp, gqa_map, what):
+    note("record %s map=%s" % (what, gqa_map))
+    y, s, dl = _record_gpu(inp, gqa_map)
+    ry, rs, rd = oracle.gdn_record(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                   inp["state_in"], inp["mask"], gqa_map=gqa_map)
+    io = inp["q"].dtype
+    B, T = inp["q"].shape[:2]
+    act = np.broadcast_to(step_mask(inp["mask"], B, T)[:, :, None, None], ry.shape)
+    assert_close(y, ry, io, what + " y", where=act)
+    assert_close(dl, rd, io, what + " delta", where=act)
+    assert_close(s, rs, io, what + " state")
+    assert np.all(f64(y)[~act] == Y_SENTINEL), what + ": y written at an inactive step"
+    assert np.all(f64(dl)[~act] == D_SENTINEL), what + ": delta written at an inactive step"
+
+
+def _check_replay(tape, accepted, what):
+    note("replay %s accepted=%d" % (what, accepted))
+    d = to_dev(tape)
+    s = gdn.gdn_replay(d["delta_log"], d["k_log"], d["g_log"], d["state_in"], d["mask"], accepted)
+    torch.cuda.synchronize()
+    rs = oracle.gdn_replay(tape["delta_log"], tape["k_log"], tape["g_log"], tape["state_in"],
+                           tape["mask"], accepted)
+    assert_close(s, rs, tape["delta_log"].dtype, what + " state")
+    return s
+
+
+# ------------------------------------------------------------------ record
+
+@pytest.mark.parametrize("name,seed", [("tiny", 0), ("tiny", 1), ("spec_decode", 0),
+                                       ("spec_decode", 1), ("large_batch_decode", 0)])
+def test_record_workloads(name, seed):
+    w = gi.WORKLOADS[name]
+    _check_record(gi.workload_inputs(name, seed), w.gqa_map, "%s/seed%d" % (name, seed))
+
+
+def test_record_chunk_prefill_sampled_heads():
+    """Full 4096-step prefill on the GPU; the oracle re-runs four sampled value
+    heads one by one (each head is an independent recurrence)."""
+    w = gi.WORKLOADS["chunk_prefill"]
+    inp = gi.workload_inputs("chunk_prefill", 0)
+    note("record chunk_prefill full size")
+    y, s, dl = _record_gpu(inp, w.gqa_map)
+    io = inp["q"].dtype
+    for hv in (0, 7, 16, 31):
+        hk = hv % w.Hk                                              # tiled map
+        sub = dict(q=inp["q"][:, :, hk:hk + 1], k=inp["k"][:, :, hk:hk + 1],
+                   v=inp["v"][:, :, hv:hv + 1], g=inp["g"][:, :, hv:hv + 1],
+                   beta=inp["beta"][:, :, hv:hv + 1], state_in=inp["state_in"][:, hv:hv + 1])
+        ry, rs, rd = oracle.gdn_record(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"],
+                                       sub["state_in"], None)
+        assert_close(y[:, :, hv:hv + 1], ry, io, "prefill y head %d" % hv)
+        assert_close(dl[:, :, hv:hv + 1], rd, io, "prefill delta head %d" % hv)
+        assert_close(s[:, hv:hv + 1], rs, io, "prefill state head %d" % hv)
+
+
+RAGGED = [
+    # B, T, Hk, Hv, Dk, Dv, io, map, mask
+    (3, 5, 1, 3, 32, 16, "f32", "block", "bernoulli"),
+    (2, 3, 2, 6, 64, 48, "bf16", "tiled", "trailing"),
+    (1, 7, 4, 4, 192, 128, "f16", "block", "bernoulli"),     # Dk=192, Dv=128, Hk=Hv=4 cell
+    (2, 2, 2, 2, 64, 32, "f32", "block", "ones"),            # Dk=64, Dv=32, Hk=Hv=2 cell
+    (1, 3, 3, 3, 256, 64, "bf16", "tiled", "none"),
+    (5, 1, 2, 8, 128, 80, "bf16", "block", "ones"),
+    (4, 9, 2, 4, 128, 128, "f16", "tiled", "bernoulli"),
+    (1, 33, 1, 2, 32, 32, "f32", "tiled", "none"),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: "B%d_T%d_Hk%d_Hv%d_Dk%d_Dv%d_%s_%s_%s" % c)
+def test_record_ragged_shapes(case):
+    B, T, Hk, Hv, Dk, Dv, io, m, mk = case
+    inp = gi.record_inputs(B, T, Hk, Hv, Dk, Dv, io, seed=B * 100 + T, mask=mk)
+    if mk == "bernoulli":
+        inp["mask"][0, 0] = 0          # make sure some step is inactive
+        inp["mask"][:, -1] *= 5        # and that mask values > 1 count as active
+    _check_record(inp, m, "ragged")
+
+
+def _hand_inputs(name, io):
+    """A golden hand case with Dk = Dv = 2, zero-padded into a 32 x 32 state."""
+    import json
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        c = json.load(f)
+    T = c.get("T", 1)
+    pad = lambda a, shape: torch.nn.functional.pad(torch.tensor(a, dtype=torch.float64).reshape(shape),
+                                                   (0, 30))
+    q = pad(c["q"], (1, T, 1, 2))
+    k = pad(c["k"], (1, T, 1, 2))
+    v = pad(c["v"], (1, T, 1, 2))
+    s0 = torch.zeros(1, 1, 32, 32, dtype=torch.float64)
+    s0[0, 0, :2, :2] = torch.tensor(c["S0"], dtype=torch.float64)
+    g = torch.tensor(c["g"], dtype=torch.float64).reshape(1, T, 1)
+    beta = torch.tensor(c["beta"], dtype=torch.float64).reshape(1, T, 1)
+    mask = torch.tensor(c.get("mask", [1] * T), dtype=torch.int32).reshape(1, T)
+    dt = gi.IO_DTYPES[io]
+    inp = dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), g=g.to(dt), beta=beta.to(dt),
+               state_in=s0.to(torch.float32), mask=mask)
+    return c, inp
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16", "f16"])
+def test_record_and_replay_hand_cases_exact(io):
+    """The golden hand cases use short dyadic numbers: every intermediate is
+    exact in float32 and every output exact in the I/O dtype."""
+    c, inp = _hand_inputs("hand_t1.json", io)
+    y, s, dl = _record_gpu(inp, "block")
+    assert f64(y)[0, 0, 0, :2].tolist() == c["expect"]["y"]
+    assert f64(dl)[0, 0, 0, :2].tolist() == c["expect"]["delta"]
+    assert f64(s)[0, 0, :2, :2].tolist() == c["expect"]["S1"]
+    assert np.all(f64(s)[0, 0, 2:] == 0) and np.all(f64(s)[0, 0, :, 2:] == 0)
+
+    c, inp = _hand_inputs("hand_t3_mask.json", io)
+    y, s, dl = _record_gpu(inp, "block")
+    e = c["expect"]
+    for t in range(3):
+        if e["y"][t] is None:
+            assert np.all(f64(y)[0, t] == Y_SENTINEL) and np.all(f64(dl)[0, t] == D_SENTINEL)
+        else:
+            assert f64(y)[0, t, 0, :2].tolist() == e["y"][t]
+            assert f64(dl)[0, t, 0, :2].tolist() == e["delta"][t]
+    assert f64(s)[0, 0, :2, :2].tolist() == e["S_final"]
+    d = to_dev(inp)
+    for a, want in e["replay"].items():
+        note("hand replay accepted=%s io=%s" % (a, io))
+        rs = gdn.gdn_replay(dl, d["k"], d["g"], d["state_in"], d["mask"], int(a))
+        torch.cuda.synchronize()
+        assert f64(rs)[0, 0, :2, :2].tolist() == want, a
+
+
+# ------------------------------------------------------------------ replay
+
+@pytest.mark.parametrize("accepted", [0, 1, 2, 3, 4, 9])
+def test_replay_spec_decode(accepted):
+    w = gi.WORKLOADS["spec_decode"]
+    tape = gi.tape_inputs(w.B, w.T, w.Hv, w.Dk, w.Dv, w.io, seed=accepted, mask="trailing")
+    _check_replay(gi.poison_untaken(tape, accepted), accepted, "spec_decode")
+
+
+def test_replay_large_batch_decode():
+    w = gi.WORKLOADS["large_batch_decode"]
+    tape = gi.tape_inputs(w.B, w.T, w.Hv, w.Dk, w.Dv, w.io, seed=3, mask="ones")
+    _check_replay(tape, 1, "large_batch_decode")
+
+
+@pytest.mark.parametrize("accepted", [0, 1, 16, 63, 64])
+def test_replay_long_tape_nan_poisoned(accepted):
+    """Untaken slots (masked, or at or past `accepted`) hold NaN: none may leak."""
+    w = gi.WORKLOADS["long_tape_replay"]
+    tape = gi.tape_inputs(w.B, w.T, w.Hv, w.Dk, w.Dv, w.io, seed=11, mask="bernoulli", mask_p=w.mask_p)
+    s = _check_replay(gi.poison_untaken(tape, accepted), accepted, "long_tape")
+    assert torch.isfinite(s).all()
+
+
+@pytest.mark.parametrize("case", [(3, 5, 2, 32, 16, "f32"), (2, 6, 3, 64, 48, "bf16"),
+                                  (1, 4, 4, 192, 128, "f16"), (2, 3, 2, 256, 32, "bf16")],
+                         ids=lambda c: "B%d_T%d_Hv%d_Dk%d_Dv%d_%s" % c)
+def test_replay_ragged_shapes(case):
+    B, T, Hv, Dk, Dv, io = case
+    tape = gi.tape_inputs(B, T, Hv, Dk, Dv, io, seed=B + T, mask="bernoulli", mask_p=0.6)
+    for a in (0, 1, T - 1, T, T + 3):
+        _check_replay(gi.poison_untaken(tape, a), a, "ragged")
+
+
+# ------------------------------------------------------- cross-kernel identities
+
+def _tape_from_record(inp, gqa_map):
+    y, s, dl = _record_gpu(inp, gqa_map)
+    d = to_dev(inp)
+    Hv = inp["v"].shape[2]
+    k_log = gdn.gqa_expand(d["k"], Hv, gqa_map)
+    return s, dl, k_log, d
+
+
+@pytest.mark.parametrize("gqa_map", ["block", "tiled"])
+def test_full_replay_reproduces_record_fp32_bitwise(gqa_map):
+    inp = gi.record_inputs(4, 6, 2, 4, 128, 128, "f32", seed=21, mask="bernoulli")
+    s_rec, dl, k_log, d = _tape_from_record(inp, gqa_map)
+    note("replay of a recorded fp32 tape, map=%s" % gqa_map)
+    s_rep = gdn.gdn_replay(dl, k_log, d["g"], d["state_in"], d["mask"], 6)
+    torch.cuda.synchronize()
+    assert torch.equal(s_rep, s_rec)
+
+
+def test_full_replay_reproduces_record_bf16_within_tolerance():
+    """With bf16 I/O the tape holds delta rounded to bf16 while the record
+    kernel updated its state with the unrounded value."""
+    w = gi.WORKLOADS["spec_decode"]
+    inp = gi.workload_inputs("spec_decode", 5)
+    s_rec, dl, k_log, d = _tape_from_record(inp, w.gqa_map)
+    for a in range(w.T + 1):
+        note("replay of a recorded bf16 tape, accepted=%d" % a)
+        s_rep = gdn.gdn_replay(dl, k_log, d["g"], d["state_in"], d["mask"], a)
+        torch.cuda.synchronize()
+        if a == w.T:
+            assert_close(s_rep, f64(s_rec), torch.bfloat16, "replay vs record")
+        # and the prefix replay equals recording only the prefix
+        sub = {k2: (v[:, :a] if k2 in ("q", "k", "v", "g", "beta", "mask") else v) for k2, v in inp.items()}
+        if a > 0:
+            _, s_pre, _ = _record_gpu(sub, w.gqa_map)
+            assert_close(s_rep, f64(s_pre), torch.bfloat16, "prefix replay vs prefix record")
+
+
+@pytest.mark.parametrize("gqa_map", ["block", "tiled"])
+def test_head_map_equals_pre_expanded_keys_bitwise(gqa_map):
+    inp = gi.record_inputs(2, 4, 4, 8, 64, 64, "bf16", seed=31, mask="trailing")
+    y1, s1, d1 = _record_gpu(inp, gqa_map)
+    d = to_dev(inp)
+    exp = dict(inp)
+    exp["q"] = gdn.gqa_expand(d["q"], 8, gqa_map).cpu()
+    exp["k"] = gdn.gqa_expand(d["k"], 8, gqa_map).cpu()
+    y2, s2, d2 = _record_gpu(exp, "block")
+    assert torch.equal(y1, y2) and torch.equal(s1, s2) and torch.equal(d1, d2)
+
+
+def test_chained_single_steps_equal_one_call_bitwise():
+    inp = gi.record_inputs(3, 5, 2, 4, 128, 64, "bf16", seed=41, mask="bernoulli")
+    y, s, dl = _record_gpu(inp, "block")
+    st = inp["state_in"]
+    for t in range(5):
+        sub = {k2: (v[:, t:t + 1] if k2 in ("q", "k", "v", "g", "beta", "mask") else v)
+               for k2, v in inp.items()}
+        sub["state_in"] = st
+        yt, st, dt = _record_gpu(sub, "block")
+        assert torch.equal(yt, y[:, t:t + 1]) and torch.equal(dt, dl[:, t:t + 1])
+        st = st.cpu()
+    assert torch.equal(st.to(dev()), s)
+
+
+def test_every_tiling_gives_identical_bits(monkeypatch):
+    inp = gi.record_inputs(2, 3, 2, 4, 128, 128, "bf16", seed=51, mask="bernoulli")
+    tape = gi.tape_inputs(2, 3, 4, 128, 128, "bf16", seed=52)
+    ref = None
+    for til in ("8,256", "4,256", "2,256", "1,256", "1,64"):
+        monkeypatch.setenv("GDN_RECORD_TILING", til)
+        monkeypatch.setenv("GDN_REPLAY_TILING", til)
+        note("tiling %s" % til)
+        out = _record_gpu(inp, "tiled")
+        d = to_dev(tape)
+        rs = gdn.gdn_replay(d["delta_log"], d["k_log"], d["g_log"], d["state_in"], d["mask"], 2)
+        torch.cuda.synchronize()
+        cur = [t.cpu() for t in out] + [rs.cpu()]
+        if ref is None:
+            ref = cur
+        else:
+            assert all(torch.equal(a, b) for a, b in zip(ref, cur)), til
+
+
+def test_in_place_state_and_tapeless_step():
+    inp = gi.record_inputs(2, 4, 2, 4, 128, 128, "bf16", seed=61, mask="trailing")
+    y, s, dl = _record_gpu(inp, "block")
+    d = to_dev(inp)
+    st = d["state_in"].clone()
+    note("record in place, no tape")
+    y2, s2, dl2 = gdn.gdn_record(d["q"], d["k"], d["v"], d["g"], d["beta"], st, d["mask"],
+                                 state_out=st, y=torch.full_like(y, Y_SENTINEL), write_tape=False)
+    torch.cuda.synchronize()
+    assert dl2 is None and s2.data_ptr() == st.data_ptr()
+    assert torch.equal(s2, s) and torch.equal(y2, y)
+    tape = to_dev(gi.tape_inputs(2, 4, 4, 128, 128, "bf16", seed=62))
+    ref = gdn.gdn_replay(tape["delta_log"], tape["k_log"], tape["g_log"], tape["state_in"], tape["mask"], 3)
+    st = tape["state_in"].clone()
+    gdn.gdn_replay(tape["delta_log"], tape["k_log"], tape["g_log"], st, tape["mask"], 3, state_out=st)
+    torch.cuda.synchronize()
+    assert torch.equal(st, ref)
+
+
+def test_repeated_runs_are_bitwise_identical():
+    inp = gi.workload_inputs("spec_decode", 7)
+    a = _record_gpu(inp, "block")
+    b = _record_gpu(inp, "block")
+    assert all(torch.equal(x, z) for x, z in zip(a, b))
+
+
+# ---------------------------------------------------------------- gqa_expand
+
+EXPAND = [
+    # seq, hg, h, k, dtype, map
+    (1, 1, 1, 1, "f32", "tiled"),
+    (5, 2, 4, 33, "f16", "block"),
+    (7, 3, 12, 64, "bf16", "tiled"),
+    (9, 4, 8, 7, "f32", "block"),
+    (32, 16, 32, 128, "bf16", "block"),
+    (4096, 16, 32, 128, "f32", "tiled"),      # chunk-prefill q/k expansion
+]
+
+
+@pytest.mark.parametrize("case", EXPAND, ids=lambda c: "%d_%d_%d_%d_%s_%s" % c)
+def test_gqa_expand_bit_exact(case):
+    seq, hg, h, kk, io, m = case
+    src = gi.expand_source(seq, hg, kk, io, seed=seq + kk)
+    raw = src.view(torch.int16 if src.element_size() == 2 else torch.int32)
+    raw.view(-1)[:: 97] = -1                 # plant NaN bit patterns: the copy must keep them
+    note("gqa_expand %s" % (case,))
+    out = gdn.gqa_expand(src.to(dev()), h, m)
+    torch.cuda.synchronize()
+    want = oracle.gqa_expand(raw.numpy(), h, m)
+    got = out.cpu().view(raw.dtype).numpy()
+    assert got.tobytes() == want.tobytes()
+
+
+def test_gqa_expand_unaligned_views_and_batch_dims():
+    src = gi.expand_source(3 * 5 + 1, 2, 24, "bf16", seed=5)
+    d = src.to(dev())
+    view = d[1:].view(3, 5, 2, 24)                 # base 96 bytes in: still fine, 2-byte vectors or wider
+    odd = torch.empty(3 * 5 * 6 * 24 + 1, dtype=torch.bfloat16, device=dev())[1:].view(3, 5, 6, 24)
+    note("gqa_expand unaligned")
+    out = gdn.gqa_expand(view, 6, "block", dst=odd)
+    torch.cuda.synchronize()
+    want = oracle.gqa_expand(src[1:].view(torch.int16).numpy().reshape(15, 2, 24), 6, "block")
+    assert out.cpu().view(torch.int16).numpy().reshape(15, 6, 24).tobytes() == want.tobytes()
+
+
+def test_tolerances_are_the_stated_ones():
+    assert TOL[torch.float32] == 1e-3 and TOL[torch.bfloat16] == 2e-2 and TOL[torch.float16] == 2e-2
