@@ -1,0 +1,378 @@
+"""Throughput of the Gated DeltaNet record / replay / GQA-expand path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one pass of the whole path over one batch of seeded synthetic
+input already resident in HBM:
+
+    large_batch_decode (default): gqa_expand(k -> k_log, block map)
+                                  + gdn_record + gdn_replay(accepted=1) on the fresh tape
+    spec_decode:      the same at B=8, T=4 with a drawn accepted count
+    chunk_prefill:    gqa_expand of fp32 q and k (tiled map) + gdn_record over 4096 steps
+    long_tape_replay: gdn_replay of a 64-step fp16 tape for accepted in {0,1,16,63,64}
+    tiny:             gdn_record + gdn_replay
+
+`value` is effective HBM bandwidth: the algorithmic bytes of the step (what
+the method must read and write, defined below) divided by the measured step
+time.  `roofline` describes the dominant kernel, timed with HIP events on the
+stream it runs on; `cpu_baseline` times the CPU oracle on a bounded sample of
+the same workload on this host.
+
+Algorithmic bytes (e = I/O element size, state float32, U = active (b,t) steps,
+A = taken tape positions, a' = min(accepted, T)):
+    record  8*B*Hv*Dv*Dk + 4*B*T [mask] + U*e*(2*Hk*Dk + 3*Hv*Dv + 2*Hv)
+    replay  8*B*Hv*Dv*Dk + 4*B*a' [mask] + A*e*Hv*(Dv + Dk + 1)
+    expand  e*seq*K*(Hg + H)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+METRIC = "GDN record+replay effective HBM GB/s (% of peak) and head-steps/sec"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "gdn_record": ["gdn_record.hip", "gdn_device.hpp"],
+    "gdn_replay": ["gdn_replay.hip", "gdn_device.hpp"],
+    "gqa_expand": ["gqa_expand.hip", "gdn_device.hpp"],
+}
+
+
+# ----------------------------------------------------------- byte accounting
+
+def record_bytes(B, T, Hk, Hv, Dk, Dv, e, active_steps, has_mask):
+    return (8 * B * Hv * Dv * Dk + (4 * B * T if has_mask else 0)
+            + active_steps * e * (2 * Hk * Dk + 3 * Hv * Dv + 2 * Hv))
+
+
+def replay_bytes(B, T, Hv, Dk, Dv, e, accepted, taken_steps, has_mask):
+    a = min(accepted, T)
+    return 8 * B * Hv * Dv * Dk + (4 * B * a if has_mask else 0) + taken_steps * e * Hv * (Dv + Dk + 1)
+
+
+def expand_bytes(seq, hg, h, k, e):
+    return e * seq * k * (hg + h)
+
+
+def kernel_source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "linear_attention_recurrence_step_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if there is none for this kernel and workload or the kernel's source
+    changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            entries = json.load(f)
+    except (OSError, ValueError):
+        return None
+    for ent in entries.get("entries", []):
+        if ent.get("kernel") == kernel and ent.get("workload") == workload:
+            if ent.get("source_sha256") == kernel_source_hash(kernel):
+                return ent.get("traffic_bytes")
+    return None
+
+
+# ------------------------------------------------------------------ workloads
+
+def _active(mask, B, T, upto=None):
+    upto = T if upto is None else min(upto, T)
+    if mask is None:
+        return B * upto
+    return int((mask[:, :upto] > 0).sum().item())
+
+
+class Step:
+    """Device buffers and launch sequence of one step of a workload."""
+
+    def __init__(self, name, dev, seed=0):
+        import torch
+        import gdn_inputs as gi
+        import linear_attention_recurrence_step_amd as gdn
+        self.gdn = gdn
+        self.name = name
+        self.w = w = gi.WORKLOADS[name]
+        self.e = 4 if w.io == "f32" else 2
+        self.kernels = []            # (label, kernel, algorithmic bytes, head-steps)
+        T = w.T
+        if name == "long_tape_replay":
+            tape = gi.tape_inputs(w.B, T, w.Hv, w.Dk, w.Dv, w.io, seed=seed, mask=w.mask, mask_p=w.mask_p)
+            self.cpu = tape
+            self.d = {k: (v.to(dev) if v is not None else None) for k, v in tape.items()}
+            self.out = torch.empty_like(self.d["state_in"])
+            for a in w.accepted:
+                taken = _active(tape["mask"], w.B, T, a)
+                self.kernels.append(("replay[a=%d]" % a, "gdn_replay",
+                                     replay_bytes(w.B, T, w.Hv, w.Dk, w.Dv, self.e, a, taken, True),
+                                     taken * w.Hv))
+            return
+        inp = gi.workload_inputs(name, seed)
+        self.cpu = inp
+        self.d = d = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
+        io = d["q"].dtype
+        self.y = torch.empty(d["v"].shape, dtype=io, device=dev)
+        self.dl = torch.empty(d["v"].shape, dtype=io, device=dev)
+        self.s_rec = torch.empty_like(d["state_in"])
+        self.s_rep = torch.empty_like(d["state_in"])
+        U = _active(inp["mask"], w.B, T)
+        has_mask = inp["mask"] is not None
+        if name == "chunk_prefill":
+            self.src = [gi.expand_source(w.B * T, w.Hk, w.Dk, w.expand_io, seed=seed + 1 + i).to(dev)
+                        for i in range(2)]
+            self.dst = [torch.empty((w.B * T, w.Hv, w.Dk), dtype=self.src[0].dtype, device=dev)
+                        for _ in range(2)]
+            eb = 4 if w.expand_io == "f32" else 2
+            for i, what in enumerate(("q", "k")):
+                self.kernels.append(("expand_%s" % what, "gqa_expand",
+                                     expand_bytes(w.B * T, w.Hk, w.Hv, w.Dk, eb), 0))
+        else:
+            self.k_log = torch.empty((w.B, T, w.Hv, w.Dk), dtype=io, device=dev)
+            self.kernels.append(("expand_k", "gqa_expand", expand_bytes(w.B * T, w.Hk, w.Hv, w.Dk, self.e), 0))
+        self.kernels.append(("record", "gdn_record",
+                             record_bytes(w.B, T, w.Hk, w.Hv, w.Dk, w.Dv, self.e, U, has_mask), U * w.Hv))
+        if name != "chunk_prefill":
+            if name == "spec_decode":
+                import numpy as np
+                self.accepted = int(np.random.Generator(np.random.PCG64(seed + 77)).integers(0, w.T + 1))
+            else:
+                self.accepted = w.accepted[0]
+            taken = _active(inp["mask"], w.B, T, self.accepted)
+            self.kernels.append(("replay", "gdn_replay",
+                                 replay_bytes(w.B, T, w.Hv, w.Dk, w.Dv, self.e, self.accepted, taken, has_mask),
+                                 taken * w.Hv))
+
+    def launches(self):
+        """Callables, one per kernel launch, in step order."""
+        gdn, d, w = self.gdn, self.d, self.w
+        if self.name == "long_tape_replay":
+            return [(lambda a=a: gdn.gdn_replay(d["delta_log"], d["k_log"], d["g_log"], d["state_in"],
+                                                d["mask"], a, state_out=self.out))
+                    for a in w.accepted]
+        out = []
+        if self.name == "chunk_prefill":
+            for i in range(2):
+                out.append(lambda i=i: gdn.gqa_expand(self.src[i], w.Hv, w.gqa_map, dst=self.dst[i]))
+        else:
+            out.append(lambda: gdn.gqa_expand(d["k"], w.Hv, w.gqa_map, dst=self.k_log))
+        out.append(lambda: gdn.gdn_record(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
+                                          d["mask"], gqa_map=w.gqa_map, y=self.y,
+                                          state_out=self.s_rec, delta_log=self.dl))
+        if self.name != "chunk_prefill":
+            out.append(lambda: gdn.gdn_replay(self.dl, self.k_log, d["g"], d["state_in"], d["mask"],
+                                              self.accepted, state_out=self.s_rep))
+        return out
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(name: str, budget_s: float):
+    """Time the CPU oracle on a bounded sample of the workload: batch rows
+    (independent recurrences) processed by a pool of threads, one slice each."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import torch
+
+    import gdn_inputs as gi
+    import oracle
+
+    w = gi.WORKLOADS[name]
+    bits_dtype = torch.int32 if w.io == "f32" else torch.int16
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    e = 4 if w.io == "f32" else 2
+    b_sample = min(w.B, max(cores, 16 if w.T <= 16 else 1))
+    if name == "chunk_prefill":
+        heads = min(w.Hv, max(cores, 4))     # value heads of the single batch row
+    seed = 123
+    if name == "long_tape_replay":
+        tape = gi.tape_inputs(b_sample, w.T, w.Hv, w.Dk, w.Dv, w.io, seed=seed, mask=w.mask, mask_p=w.mask_p)
+    else:
+        inp = gi.record_inputs(b_sample, w.T, w.Hk, w.Hv, w.Dk, w.Dv, w.io, seed, w.mask, w.mask_p)
+
+    def work(lo, hi):
+        nbytes = 0
+        if name == "long_tape_replay":
+            sl = {k: (v[lo:hi] if v is not None else None) for k, v in tape.items()}
+            for a in w.accepted:
+                oracle.gdn_replay(sl["delta_log"], sl["k_log"], sl["g_log"], sl["state_in"], sl["mask"], a)
+                taken = _active(sl["mask"], hi - lo, w.T, a)
+                nbytes += replay_bytes(hi - lo, w.T, w.Hv, w.Dk, w.Dv, e, a, taken, True)
+            return nbytes
+        if name == "chunk_prefill":
+            hk = [hv % w.Hk for hv in range(lo, hi)]
+            sub = dict(q=inp["q"][:, :, hk], k=inp["k"][:, :, hk], v=inp["v"][:, :, lo:hi],
+                       g=inp["g"][:, :, lo:hi], beta=inp["beta"][:, :, lo:hi],
+                       state_in=inp["state_in"][:, lo:hi])
+            oracle.gdn_record(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], sub["state_in"], None,
+                              gqa_map="block")
+            return record_bytes(1, w.T, hi - lo, hi - lo, w.Dk, w.Dv, e, w.T, False)
+        sl = {k: (v[lo:hi] if v is not None else None) for k, v in inp.items()}
+        nb = hi - lo
+        y, s, dlt = oracle.gdn_record(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["state_in"],
+                                      sl["mask"], gqa_map=w.gqa_map)
+        kbits = sl["k"].contiguous().view(bits_dtype).numpy().reshape(nb * w.T, w.Hk, w.Dk)
+        k_log = torch.from_numpy(oracle.gqa_expand(kbits, w.Hv, w.gqa_map)).view(sl["k"].dtype)
+        a = w.accepted[0] if name != "spec_decode" else w.T
+        oracle.gdn_replay(dlt, k_log.reshape(nb, w.T, w.Hv, w.Dk), sl["g"],
+                          sl["state_in"], sl["mask"], a)
+        U = _active(sl["mask"], nb, w.T)
+        taken = _active(sl["mask"], nb, w.T, a)
+        has_mask = sl["mask"] is not None
+        return (expand_bytes(nb * w.T, w.Hk, w.Hv, w.Dk, e)
+                + record_bytes(nb, w.T, w.Hk, w.Hv, w.Dk, w.Dv, e, U, has_mask)
+                + replay_bytes(nb, w.T, w.Hv, w.Dk, w.Dv, e, a, taken, has_mask))
+
+    units = heads if name == "chunk_prefill" else b_sample
+    per = max(1, units // cores)
+    chunks = [(lo, min(units, lo + per)) for lo in range(0, units, per)]
+    total_bytes, passes = 0, 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        while True:
+            total_bytes += sum(ex.map(lambda c: work(*c), chunks))
+            passes += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    unit_name = "value heads" if name == "chunk_prefill" else "batch rows"
+    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": min(cores, len(chunks)),
+            "kind": "oracle",
+            "sample": "%d of %d %s of %s, %d pass(es), %.1f s, threads over %s"
+                      % (units, w.Hv if name == "chunk_prefill" else w.B, unit_name, name, passes, dt,
+                         unit_name)}
+
+
+# ------------------------------------------------------- counter calibration
+
+COPY_BYTES = 512 << 20
+
+
+def calibrate_copy(dev, launches: int) -> None:
+    """A plain device copy of COPY_BYTES (read once, written once): gqa_expand
+    with one source and one destination head is exactly a copy.  Its byte
+    counters, divided by COPY_BYTES, give the scale of each counter."""
+    import torch
+    import linear_attention_recurrence_step_amd as gdn
+    k = 32768
+    seq = COPY_BYTES // (4 * k)
+    src = torch.randn(seq, 1, k, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(launches):
+        gdn.gqa_expand(src, 1, "tiled", dst=dst)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / launches
+    assert torch.equal(src, dst)
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES,
+                      "launches": launches, "us_per_launch": round(dt * 1e6, 1),
+                      "GB/s": round(2 * COPY_BYTES / dt / 1e9, 1)}), flush=True)
+
+
+# ----------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="large_batch_decode")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain copy of known size (gqa_expand with hg == h) for "
+                         "scaling the HBM byte counters, and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this path runs on a single MI355X and its "
+              "multi-GPU sharding is a design, not a build; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda", 0)
+    if args.calibrate_copy:
+        calibrate_copy(dev, args.steps)
+        return
+    step = Step(args.workload, dev, args.seed)
+    launches = step.launches()
+    w = step.w
+
+    for _ in range(args.warmup):
+        for f in launches:
+            f()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, f in enumerate(launches):
+            f()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    per_kernel_ms = [0.0] * len(launches)
+    for s in range(args.steps):
+        for i in range(len(launches)):
+            per_kernel_ms[i] += ev[s][i].elapsed_time(ev[s][i + 1])
+    per_kernel_ms = [m / args.steps for m in per_kernel_ms]
+
+    step_bytes = sum(k[2] for k in step.kernels)
+    head_steps = sum(k[3] for k in step.kernels)
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    kernels = []
+    for (label, kern, nbytes, hs), ms in zip(step.kernels, per_kernel_ms):
+        kernels.append({"name": label, "kernel": kern, "us": round(ms * 1e3, 2),
+                        "algorithmic_bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                        "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)})
+    dom = max(range(len(kernels)), key=lambda i: per_kernel_ms[i])
+    dk = kernels[dom]
+    roofline = {"bound": "hbm", "achieved": dk["GB/s"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(dk["GB/s"] / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(dk["kernel"], args.workload),
+                "kernel": dk["name"], "bytes_per_launch": dk["algorithmic_bytes"],
+                "us_per_launch": dk["us"]}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": args.workload, "B": w.B, "T": w.T, "Hk": w.Hk, "Hv": w.Hv,
+                   "Dk": w.Dk, "Dv": w.Dv, "io_dtype": w.io, "state_dtype": "f32",
+                   "gqa_map": w.gqa_map, "mask": w.mask,
+                   "step": " + ".join(k[0] for k in step.kernels)},
+        "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
+        "head_steps_per_s": round(head_steps / (ms_per_step * 1e-3), 1),
+        "head_steps_per_step": head_steps,
+        "algorithmic_bytes_per_step": step_bytes,
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -54,6 +54,16 @@ def _want(name: str, t: torch.Tensor, shape, dtype, device) -> None:
         raise ValueError("%s must be contiguous" % name)
 
 
+def _device_of(t: torch.Tensor) -> torch.device:
+    """The GPU all tensors of a call must live on; host tensors are refused
+    here, before any pointer reaches the library."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError("tensors must be on a HIP device, got %s" % t.device)
+    return t.device
+
+
 def _io_code(t: torch.Tensor) -> int:
     if t.dtype not in IO_DTYPES:
         raise TypeError("I/O tensors must be float32, float16 or bfloat16, got %s" % t.dtype)
@@ -78,7 +88,7 @@ def gdn_record(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tenso
     """
     if gqa_map not in _MAPS:
         raise ValueError("gqa_map must be 'block' or 'tiled'")
-    dev = q.device
+    dev = _device_of(q)
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     io = q.dtype
@@ -117,7 +127,7 @@ def gdn_replay(delta_log: torch.Tensor, k_log: torch.Tensor, g_log: torch.Tensor
     ``accepted`` defaults to the tape length; values past it act as the tape
     length.  ``state_out`` may be ``state_in`` itself.
     """
-    dev = delta_log.device
+    dev = _device_of(delta_log)
     B, T, Hv, Dv = delta_log.shape
     Dk = k_log.shape[3]
     io = delta_log.dtype
@@ -149,7 +159,7 @@ def gqa_expand(src: torch.Tensor, h: int, gqa_map: str = "tiled", *,
         raise ValueError("gqa_map must be 'block' or 'tiled'")
     if src.dim() < 2:
         raise ValueError("src must be [..., hg, k]")
-    dev = src.device
+    dev = _device_of(src)
     hg, kk = src.shape[-2], src.shape[-1]
     seq = 1
     for d in src.shape[:-2]:

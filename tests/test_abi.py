@@ -1,0 +1,195 @@
+"""The C ABI on the CPU: the library loads, exports every function include/gdn.h
+declares, and rejects bad arguments on the host before any HIP call.
+
+No call here reaches a kernel launch: every case carries an invalid argument,
+and the calls run in a child process that sees no GPU (HIP_VISIBLE_DEVICES and
+ROCR_VISIBLE_DEVICES hide every device), so even an unexpected pass of the
+validation could only end in a launch error, never in device work.
+"""
+import json
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+LIB = os.path.join(ROOT, "linear_attention_recurrence_step_amd", "libgdn.so")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_three_entry_points():
+    fns = _declared_functions()
+    for name in ("gdn_record", "gdn_replay", "gqa_expand", "gdn_strerror", "gdn_last_error",
+                 "gdn_abi_version"):
+        assert name in fns, fns
+
+
+def test_library_exports_every_declared_function():
+    assert os.path.exists(LIB), "libgdn.so is not built"
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [f for f in _declared_functions() if f not in exported]
+    assert not missing, missing
+
+
+CHILD = r"""
+import ctypes, json, sys
+lib = ctypes.CDLL(sys.argv[1])
+vp, u32, i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int
+lib.gdn_record.argtypes = [vp] * 10 + [u32] * 6 + [i32, i32, vp]
+lib.gdn_replay.argtypes = [vp] * 6 + [u32] * 6 + [i32, vp]
+lib.gqa_expand.argtypes = [vp, vp] + [u32] * 4 + [i32, i32, vp]
+lib.gdn_strerror.restype = ctypes.c_char_p
+lib.gdn_last_error.restype = ctypes.c_char_p
+cases = json.loads(sys.argv[2])
+out = []
+for c in cases:
+    fn = getattr(lib, c["fn"])
+    args = [None if a is None else a for a in c["args"]]
+    rc = fn(*args)
+    out.append({"id": c["id"], "rc": rc, "msg": lib.gdn_last_error().decode()})
+out.append({"id": "strerror", "rc": 0,
+            "msg": json.dumps({str(s): lib.gdn_strerror(s).decode() for s in range(-10, 1)})})
+print(json.dumps(out))
+"""
+
+BASE = 1 << 40
+SPAN = 1 << 36
+
+
+def P(i, off=0):
+    """A distinct, 256-byte aligned fake device address (never dereferenced)."""
+    return BASE + i * SPAN + off
+
+
+# gdn_record(q, k, v, g, beta, state_in, mask, y, state_out, delta_log, B, T, Hk, Hv, Dk, Dv, io, map, stream)
+def rec(**kw):
+    a = dict(q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), s_in=P(5), mask=P(6), y=P(7), s_out=P(8),
+             dl=P(9), B=2, T=3, Hk=2, Hv=4, Dk=128, Dv=128, io=2, map=0)
+    a.update(kw)
+    return [a["q"], a["k"], a["v"], a["g"], a["beta"], a["s_in"], a["mask"], a["y"], a["s_out"],
+            a["dl"], a["B"], a["T"], a["Hk"], a["Hv"], a["Dk"], a["Dv"], a["io"], a["map"], None]
+
+
+# gdn_replay(delta_log, k_log, g_log, state_in, mask, state_out, B, T_log, Hv, Dk, Dv, accepted, io, stream)
+def rep(**kw):
+    a = dict(dl=P(0), kl=P(1), gl=P(2), s_in=P(3), mask=P(4), s_out=P(5), B=2, T=3, Hv=4, Dk=128,
+             Dv=128, acc=2, io=1)
+    a.update(kw)
+    return [a["dl"], a["kl"], a["gl"], a["s_in"], a["mask"], a["s_out"], a["B"], a["T"], a["Hv"],
+            a["Dk"], a["Dv"], a["acc"], a["io"], None]
+
+
+# gqa_expand(src, dst, seq, hg, h, k, dtype, map, stream)
+def exp(**kw):
+    a = dict(src=P(0), dst=P(1), seq=4, hg=2, h=4, k=128, dt=0, map=1)
+    a.update(kw)
+    return [a["src"], a["dst"], a["seq"], a["hg"], a["h"], a["k"], a["dt"], a["map"], None]
+
+
+NULL, ZERO, RATIO, SHAPE, OVER, ALIAS, ENUM, LAUNCH, ALIGN = -1, -2, -3, -4, -5, -6, -7, -8, -9
+
+CASES = [
+    ("rec_bad_dtype", "gdn_record", rec(io=3), ENUM),
+    ("rec_bad_map", "gdn_record", rec(map=2), ENUM),
+    ("rec_null_q", "gdn_record", rec(q=None), NULL),
+    ("rec_null_state_out", "gdn_record", rec(s_out=None), NULL),
+    ("rec_zero_B", "gdn_record", rec(B=0), ZERO),
+    ("rec_zero_T", "gdn_record", rec(T=0), ZERO),
+    ("rec_ratio", "gdn_record", rec(Hk=3, Hv=4), RATIO),
+    ("rec_dk48", "gdn_record", rec(Dk=48), SHAPE),
+    ("rec_dk512", "gdn_record", rec(Dk=512), SHAPE),
+    ("rec_dv40", "gdn_record", rec(Dv=40), SHAPE),
+    ("rec_dv2048", "gdn_record", rec(Dv=2048), SHAPE),
+    ("rec_bytes_overflow", "gdn_record", rec(B=1 << 31, T=1 << 31), OVER),
+    ("rec_grid_overflow", "gdn_record", rec(B=1 << 20, T=1, Hk=1 << 12, Hv=1 << 12, Dk=32, Dv=16), OVER),
+    ("rec_misaligned_q", "gdn_record", rec(q=P(0, 2)), ALIGN),
+    ("rec_misaligned_state", "gdn_record", rec(s_in=P(5, 8)), ALIGN),
+    ("rec_misaligned_mask", "gdn_record", rec(mask=P(6, 2)), ALIGN),
+    ("rec_misaligned_g", "gdn_record", rec(g=P(3, 1)), ALIGN),
+    ("rec_y_overlaps_v", "gdn_record", rec(y=P(2, 256)), ALIAS),
+    ("rec_state_partial_alias", "gdn_record", rec(s_out=P(5, 4096)), ALIAS),
+    ("rec_delta_overlaps_y", "gdn_record", rec(dl=P(7, 64)), ALIAS),
+    ("rec_state_out_over_q", "gdn_record", rec(s_out=P(0)), ALIAS),
+    ("rec_y_over_mask", "gdn_record", rec(y=P(6)), ALIAS),
+    ("rep_bad_dtype", "gdn_replay", rep(io=-1), ENUM),
+    ("rep_null_k_log", "gdn_replay", rep(kl=None), NULL),
+    ("rep_zero_T", "gdn_replay", rep(T=0), ZERO),
+    ("rep_zero_Dv", "gdn_replay", rep(Dv=0), ZERO),
+    ("rep_dk96", "gdn_replay", rep(Dk=96), SHAPE),
+    ("rep_misaligned_delta", "gdn_replay", rep(dl=P(0, 4)), ALIGN),
+    ("rep_state_out_over_tape", "gdn_replay", rep(s_out=P(0, 1024)), ALIAS),
+    ("rep_state_partial_alias", "gdn_replay", rep(s_out=P(3, 16)), ALIAS),
+    ("rep_bytes_overflow", "gdn_replay", rep(B=1 << 31, T=1 << 31), OVER),
+    ("exp_bad_dtype", "gqa_expand", exp(dt=7), ENUM),
+    ("exp_bad_map", "gqa_expand", exp(map=-1), ENUM),
+    ("exp_null_dst", "gqa_expand", exp(dst=None), NULL),
+    ("exp_zero_k", "gqa_expand", exp(k=0), ZERO),
+    ("exp_zero_seq", "gqa_expand", exp(seq=0), ZERO),
+    ("exp_ratio", "gqa_expand", exp(hg=3, h=4), RATIO),
+    ("exp_overlap", "gqa_expand", exp(dst=P(0, 512)), ALIAS),
+    ("exp_misaligned", "gqa_expand", exp(dst=P(1, 2), dt=0), ALIGN),
+    ("exp_overflow", "gqa_expand", exp(seq=0xFFFFFFFF, h=0xFFFFFFFF, hg=1, k=0xFFFFFFFF), OVER),
+]
+
+
+@pytest.fixture(scope="module")
+def results():
+    cases = [{"id": i, "fn": f, "args": a} for i, f, a, _ in CASES]
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1",
+               CUDA_VISIBLE_DEVICES="-1")
+    r = subprocess.run([sys.executable, "-c", CHILD, LIB, json.dumps(cases)], capture_output=True,
+                       text=True, env=env, timeout=120)
+    assert r.returncode == 0, r.stderr
+    return {d["id"]: d for d in json.loads(r.stdout.strip().splitlines()[-1])}
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_invalid_arguments_are_rejected_before_any_hip_call(results, case):
+    cid, fn, _, want = case
+    got = results[cid]
+    assert got["rc"] == want, (cid, got)
+    assert got["msg"].startswith(fn + ":"), got["msg"]
+
+
+def test_strerror_covers_every_status(results):
+    table = json.loads(results["strerror"]["msg"])
+    for s in range(-9, 1):
+        assert table[str(s)] and table[str(s)] != "unknown status", s
+    assert table["-10"] == "unknown status"
+
+
+def test_python_binding_names_match_the_abi():
+    import linear_attention_recurrence_step_amd as gdn
+    from linear_attention_recurrence_step_amd import _native
+    for name in ("gdn_record", "gdn_replay", "gqa_expand"):
+        assert callable(getattr(gdn, name))
+        assert hasattr(_native.lib, name)
+    assert _native.lib.gdn_abi_version() == _native.ABI_VERSION
+    assert set(_native.EXPORTS) <= set(_declared_functions())
+
+
+def test_python_binding_rejects_host_tensors_before_the_library():
+    """Well-formed host tensors must never reach the library (a host pointer in a
+    kernel would fault the device)."""
+    import torch
+    import linear_attention_recurrence_step_amd as gdn
+    q = torch.zeros(1, 1, 1, 32)
+    v = torch.zeros(1, 1, 1, 32)
+    g = torch.zeros(1, 1, 1)
+    s = torch.zeros(1, 1, 32, 32)
+    with pytest.raises(ValueError, match="HIP device"):
+        gdn.gdn_record(q, q, v, g, g, s)
+    with pytest.raises(ValueError, match="HIP device"):
+        gdn.gdn_replay(v, q, g, s, None, 1)
+    with pytest.raises(ValueError, match="HIP device"):
+        gdn.gqa_expand(torch.zeros(2, 1, 32), 2)
