@@ -292,6 +292,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
+    ap.add_argument("--scrub", choices=("auto", "on", "off"), default="auto",
+                    help="overwrite a 1 GiB buffer before every timed step so no input is left in "
+                         "the L2 / 256 MB MALL (auto: on unless the step moves >= 1 GB anyway)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain copy of known size (gqa_expand with hg == h) for "
                          "scaling the HBM byte counters, and exit")
@@ -316,18 +319,27 @@ def main():
             f()
     torch.cuda.synchronize()
 
+    step_bytes = sum(k[2] for k in step.kernels)
+    scrub = args.scrub == "on" or (args.scrub == "auto" and step_bytes < (1 << 30))
+    scrub_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if scrub else None
+
     stream = torch.cuda.current_stream(dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
+        if scrub:
+            scrub_buf.fill_(float(s))          # outside the events: evicts L2 and MALL
         ev[s][0].record(stream)
         for i, f in enumerate(launches):
             f()
             ev[s][i + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    if scrub:
+        # the wall clock includes the scrubs: time the steps by their events instead
+        elapsed = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)) * 1e-3
 
     per_kernel_ms = [0.0] * len(launches)
     for s in range(args.steps):
@@ -335,7 +347,6 @@ def main():
             per_kernel_ms[i] += ev[s][i].elapsed_time(ev[s][i + 1])
     per_kernel_ms = [m / args.steps for m in per_kernel_ms]
 
-    step_bytes = sum(k[2] for k in step.kernels)
     head_steps = sum(k[3] for k in step.kernels)
     ms_per_step = elapsed * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -358,6 +369,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "cache_scrub": scrub,
         "config": {"workload": args.workload, "B": w.B, "T": w.T, "Hk": w.Hk, "Hv": w.Hv,
                    "Dk": w.Dk, "Dv": w.Dv, "io_dtype": w.io, "state_dtype": "f32",
                    "gqa_map": w.gqa_map, "mask": w.mask,

@@ -52,11 +52,14 @@ __device__ __forceinline__ float io_load1(const void* base, size_t idx) {
 
 // ---------------------------------------------------------------- vectors
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <int BYTES> struct RawVec;
 template <> struct RawVec<2>  { using T = uint16_t; };
 template <> struct RawVec<4>  { using T = uint32_t; };
-template <> struct RawVec<8>  { using T = uint2; };
-template <> struct RawVec<16> { using T = uint4; };
+template <> struct RawVec<8>  { using T = u32x2; };
+template <> struct RawVec<16> { using T = u32x4; };
 
 // Load N consecutive I/O elements starting at element `idx` and widen them to
 // float.  The address must be aligned to min(16, N * element size) bytes.
@@ -126,21 +129,24 @@ __device__ __forceinline__ void io_store_vec(void* base, size_t idx, const float
     }
 }
 
-// N consecutive float32 values (the recurrent state); 8- or 16-byte aligned.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Non-temporal load of N consecutive float32 values (the recurrent state,
+// read exactly once per launch); 8- or 16-byte aligned.  The streaming hint
+// keeps the state from evicting reusable lines and measurably raises read
+// bandwidth on this part.
 template <int N>
 __device__ __forceinline__ void f32_load_vec(const float* p, float (&out)[N]) {
     static_assert(N == 2 || N == 4, "state chunks are 2 or 4 floats");
     if constexpr (N == 4) {
-        float4 v = *reinterpret_cast<const float4*>(p);
+        f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
         out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
     } else {
-        float2 v = *reinterpret_cast<const float2*>(p);
+        f32x2 v = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
         out[0] = v.x; out[1] = v.y;
     }
 }
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Non-temporal store of N floats: the state written back is not re-read by
 // this launch, so it should not displace reusable lines from the caches.
@@ -154,6 +160,15 @@ __device__ __forceinline__ void f32_store_vec_nt(float* p, const float (&in)[N])
         f32x2 v = {in[0], in[1]};
         __builtin_nontemporal_store(v, reinterpret_cast<f32x2*>(p));
     }
+}
+
+// Wait until every vector memory load and store issued so far has completed
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left unconstrained).  Issued once
+// after a kernel's initial state loads: otherwise the compiler treats those
+// registers as possibly still loading inside later loops and waits on the
+// in-order counter there, which also waits for any prefetch issued meanwhile.
+__device__ __forceinline__ void wait_vector_memory() {
+    __builtin_amdgcn_s_waitcnt(0x0f70);
 }
 
 // ------------------------------------------------------------ reductions
@@ -173,12 +188,27 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// Row sums of N independent values at once: the stages are interleaved so
+// the wait states a DPP read needs after a VALU write are filled with the
+// other values' work.  Same bits as N separate row16_sum calls.
+template <int N>
+__device__ __forceinline__ void row16_sum_n(float (&x)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_read<0xb1>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_read<0x4e>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_read<0x141>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_read<0x140>(x[i]);
+}
+
 // ------------------------------------------------- workgroup ordering
 
 // Workgroups are handed to the 8 XCDs round-robin (block i -> XCD i % 8).
 // Renumber them so that each XCD receives one contiguous range of logical
-// indices: neighbouring logical work (the row blocks of one head, the value
-// heads sharing a key head) then shares that XCD's L2.
+// indices: neighbouring logical work (the row blocks of one head, and under
+// the block map the value heads sharing a key head) then shares that XCD's L2.
 __device__ __forceinline__ uint32_t xcd_contiguous_index(uint32_t bid, uint32_t nblk) {
     constexpr uint32_t kXcd = 8;
     const uint32_t xcd = bid % kXcd;
@@ -186,6 +216,164 @@ __device__ __forceinline__ uint32_t xcd_contiguous_index(uint32_t bid, uint32_t 
     const uint32_t per = nblk / kXcd;
     const uint32_t rem = nblk % kXcd;
     return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+}  // namespace gdn
+
+namespace gdn {
+
+// ------------------------------------------------------- chunk staging
+
+// LDS vector access of N floats; the address must be aligned to
+// min(16, 4 * N) bytes (N = 1, 2, 4 or a multiple of 4).
+template <int N>
+__device__ __forceinline__ void lds_store_vec(float* p, const float (&f)[N]) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4)
+            *reinterpret_cast<f32x4*>(p + i) = f32x4{f[i], f[i + 1], f[i + 2], f[i + 3]};
+    } else if constexpr (N == 2) {
+        *reinterpret_cast<f32x2*>(p) = f32x2{f[0], f[1]};
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) p[i] = f[i];
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void lds_load_vec(const float* p, float (&f)[N]) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(p + i);
+            f[i] = v.x; f[i + 1] = v.y; f[i + 2] = v.z; f[i + 3] = v.w;
+        }
+    } else if constexpr (N == 2) {
+        const f32x2 v = *reinterpret_cast<const f32x2*>(p);
+        f[0] = v.x; f[1] = v.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) f[i] = p[i];
+    }
+}
+
+// Cooperative copy of a [ROWS x COLS] block of I/O elements into LDS as
+// float32, split into a global-load phase (into registers) and an LDS-store
+// phase, so the loads of the next chunk of steps can be in flight while the
+// current chunk is being computed.  Source row i starts `stride` elements
+// after row i-1; pieces of P contiguous elements (P * element size <= 16
+// bytes, P dividing COLS) are spread over the NT threads of the workgroup.
+// Rows i >= valid (past the end of the tape) are not loaded and hold zeros.
+// Rows of inactive steps are loaded like any other (their consumers skip
+// them); predicating each load on its mask entry would put a dependent load
+// in front of every piece.
+template <int IO, int ROWS, int COLS, int P, int NT>
+struct ChunkStager {
+    static constexpr int EB = IoTraits<IO>::kBytes;
+    static constexpr int PER_ROW = COLS / P;
+    static constexpr int PIECES = ROWS * PER_ROW;
+    static constexpr int PER_THREAD = (PIECES + NT - 1) / NT;
+    using Raw = typename RawVec<P * EB>::T;
+    static_assert(COLS % P == 0 && P * EB <= 16, "bad piece size");
+
+    Raw buf[PER_THREAD];
+
+    __device__ __forceinline__ void load(const void* src, size_t stride, int valid) {
+        const char* base = static_cast<const char*>(src);
+#pragma unroll
+        for (int j = 0; j < PER_THREAD; ++j) {
+            const int p = static_cast<int>(threadIdx.x) + j * NT;
+            buf[j] = Raw{};
+            if (p < PIECES) {
+                const int row = p / PER_ROW;
+                const int col = (p - row * PER_ROW) * P;
+                if (row < valid)
+                    buf[j] = *reinterpret_cast<const Raw*>(base + (static_cast<size_t>(row) * stride + col) * EB);
+            }
+        }
+    }
+
+    // Rows [0, rows) go to LDS (rows <= ROWS: the LDS block may be shorter
+    // than the chunk when the whole tape is shorter).
+    __device__ __forceinline__ void store(float* lds, int rows) const {
+#pragma unroll
+        for (int j = 0; j < PER_THREAD; ++j) {
+            const int p = static_cast<int>(threadIdx.x) + j * NT;
+            if (p < PIECES && p < rows * PER_ROW) {
+                const int row = p / PER_ROW;
+                const int col = (p - row * PER_ROW) * P;
+                float f[P];
+                unpack(buf[j], f);
+                lds_store_vec<P>(lds + row * COLS + col, f);
+            }
+        }
+    }
+
+    // For single-column blocks: row i goes to lds[i * stride].
+    __device__ __forceinline__ void store_strided(float* lds, int stride, int rows) const {
+        static_assert(COLS == 1 && P == 1, "strided store is for one value per row");
+#pragma unroll
+        for (int j = 0; j < PER_THREAD; ++j) {
+            const int p = static_cast<int>(threadIdx.x) + j * NT;
+            if (p < PIECES && p < rows) {
+                float f[1];
+                unpack(buf[j], f);
+                lds[p * stride] = f[0];
+            }
+        }
+    }
+
+  private:
+    __device__ __forceinline__ static void unpack(const Raw& raw, float (&f)[P]) {
+        if constexpr (P * EB >= 4) {
+            uint32_t w[(P * EB) / 4];
+            __builtin_memcpy(w, &raw, P * EB);
+#pragma unroll
+            for (int e = 0; e < P; ++e) {
+                if constexpr (IO == kF32) {
+                    f[e] = __uint_as_float(w[e]);
+                } else {
+                    const uint32_t bits = (w[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+                    f[e] = (IO == kBF16) ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
+                }
+            }
+        } else {
+            const uint32_t bits = raw;
+            f[0] = (IO == kBF16) ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
+        }
+    }
+};
+
+// Mask entries of a chunk of steps (1 when there is no mask), for LDS.
+template <int ROWS, int NT>
+struct MaskStager {
+    static constexpr int PER_THREAD = (ROWS + NT - 1) / NT;
+    uint32_t buf[PER_THREAD];
+    __device__ __forceinline__ void load(const uint32_t* mask_row, int valid) {
+#pragma unroll
+        for (int j = 0; j < PER_THREAD; ++j) {
+            const int p = static_cast<int>(threadIdx.x) + j * NT;
+            buf[j] = 0u;
+            if (p < ROWS && p < valid) buf[j] = mask_row == nullptr ? 1u : mask_row[p];
+        }
+    }
+    __device__ __forceinline__ void store(uint32_t* lds, int rows) const { store_strided(lds, 1, rows); }
+    __device__ __forceinline__ void store_strided(uint32_t* lds, int stride, int rows) const {
+#pragma unroll
+        for (int j = 0; j < PER_THREAD; ++j) {
+            const int p = static_cast<int>(threadIdx.x) + j * NT;
+            if (p < ROWS && p < rows) lds[p * stride] = buf[j];
+        }
+    }
+};
+
+// Widest piece (in elements) for a row of COLS I/O elements: at most 16 bytes.
+template <int IO, int COLS>
+constexpr int piece_elems() {
+    constexpr int max_p = 16 / IoTraits<IO>::kBytes;
+    int p = max_p;
+    while (p > 1 && COLS % p != 0) p >>= 1;
+    return p;
 }
 
 }  // namespace gdn

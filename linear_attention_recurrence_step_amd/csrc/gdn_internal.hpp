@@ -65,11 +65,13 @@ inline bool tiling_fits(const RowTiling& t, uint32_t Dk, uint32_t Dv) {
            static_cast<uint32_t>(t.rows_per_thread) * (Dk / 16) <= kMaxStatePerLane;
 }
 
-// Widest tiling that still yields `target_groups` workgroups; otherwise the
-// narrowest one that fits (more, smaller workgroups for few heads).
-inline RowTiling pick_tiling(uint64_t heads, uint32_t Dk, uint32_t Dv, uint64_t target_groups) {
-    for (int i = 0; i < kNumTilings; ++i) {
-        const RowTiling& t = kTilings[i];
+// First tiling of `prefs` (a list of kTilings indices) that fits and still
+// yields `target_groups` workgroups; otherwise the narrowest tiling that fits
+// (more, smaller workgroups for few heads).
+inline RowTiling pick_tiling(uint64_t heads, uint32_t Dk, uint32_t Dv, uint64_t target_groups,
+                             const int* prefs, int nprefs) {
+    for (int i = 0; i < nprefs; ++i) {
+        const RowTiling& t = kTilings[prefs[i]];
         if (tiling_fits(t, Dk, Dv) && heads * (Dv / t.rows()) >= target_groups) return t;
     }
     for (int i = kNumTilings - 1; i >= 0; --i)
@@ -77,8 +79,14 @@ inline RowTiling pick_tiling(uint64_t heads, uint32_t Dk, uint32_t Dv, uint64_t 
     return kTilings[kNumTilings - 1];
 }
 
+// Largest row block (rows per workgroup) the staged record kernel takes; it
+// bounds that kernel's LDS below 64 KiB.
+inline constexpr int kStagedMaxRows = 64;
+
 // Optional tiling forced through an environment variable ("rows_per_thread,threads"),
-// used for launch-shape sweeps; ignored unless it names a known tiling that fits.
-bool tiling_override(const char* env_name, uint32_t Dk, uint32_t Dv, RowTiling* out);
+// used for launch-shape sweeps; ignored unless it names a known tiling that fits
+// and covers at most max_rows rows.
+bool tiling_override(const char* env_name, uint32_t Dk, uint32_t Dv, uint32_t max_rows,
+                     RowTiling* out);
 
 }  // namespace gdn

@@ -4,22 +4,31 @@
 // metaltile-std 0.1.0 page src/ffai/gated_delta_replay.rs: per (b, hv, dv) row
 // and active step t, decay the row by g, read it out against k, form the
 // innovation delta = (v - kv) * beta, write delta to the tape, add delta * k to
-// the row and read the row out against q into y.
+// the row and read the updated row out against q into y.
+//
+// The read-out of the updated row is evaluated as
+//     y = (g S) . q + delta * (k . q),
+// which equals (g S + delta k^T) . q exactly in real arithmetic and lets both
+// dot products run in one pass over the decayed row; only the rounding differs
+// from reading the updated row (within the stated tolerances).
 //
 // How it maps onto CDNA4 (not the page's one-32-lane-group-per-row layout):
 //  * 16 lanes (one DPP row) share a state row; lane l holds the Dk/16 columns
 //    {(c*16 + l)*W + w}, so every 16-lane vector access is contiguous.
 //  * A thread owns RPT consecutive rows of one head; a workgroup of NT threads
-//    covers RPT*NT/16 rows.  The rows stay in VGPRs for all T steps; the state
-//    is read once and written once (non-temporal) per launch.
-//  * Both Dk-length dot products finish with a 4-stage DPP butterfly inside the
-//    16-lane row, so no LDS and no barrier is involved.
-//  * k and q of a step are loaded per lane straight from global memory: the
-//    16 column slices of one key head are shared by every row of the
-//    workgroup, so the repeats hit the L1/L2, and HBM sees each key vector once
-//    per XCD.
+//    covers R = RPT*NT/16 consecutive rows.  The rows stay in VGPRs for all T
+//    steps; the state is read once and written once (non-temporal) per launch.
+//  * Dot products finish with a 4-stage DPP butterfly inside the 16-lane row
+//    (no LDS, no barrier); independent sums are reduced stage-interleaved.
+//  * One step (T = 1, decode): the direct kernel loads k, q, v, g, beta per
+//    lane straight from global memory (the repeats of a key vector across rows
+//    hit the L1/L2).
+//  * Several steps: the staged kernel brings the inputs of a chunk of steps
+//    into LDS in one round of coalesced loads, prefetches the next chunk into
+//    registers while computing, and buffers y and delta of the chunk in LDS so
+//    they leave as vector stores.
 //  * The mask row [B, T] is uniform over a workgroup, so inactive steps are a
-//    scalar branch around the whole step.
+//    scalar branch around the whole step and write nothing.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -28,6 +37,73 @@
 
 namespace gdn {
 namespace {
+
+// This lane's part of a Dk-length dot product over its E columns, in a fixed
+// order (two interleaved accumulators), shared by every kernel that needs it.
+template <int E>
+__device__ __forceinline__ float lane_dot(const float (&x)[E], const float (&y)[E]) {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int e = 0; e + 1 < E; e += 2) {
+        a0 = fmaf(x[e], y[e], a0);
+        a1 = fmaf(x[e + 1], y[e + 1], a1);
+    }
+    if constexpr (E % 2 == 1) a0 = fmaf(x[E - 1], y[E - 1], a0);
+    return a0 + a1;
+}
+
+// One active step on the RPT rows this lane holds (E columns of each):
+// decay, read-outs against k and q, innovation, rank-1 write.  kq = k . q of
+// the step.  d and out receive the innovation and the output of every row
+// (identical bits in all 16 lanes of the row).
+template <int RPT, int E>
+__device__ __forceinline__ void record_step(float (&s)[RPT][E], const float (&kk)[E],
+                                            const float (&qq)[E], const float (&vv)[RPT],
+                                            float gt, float beta, float kq, float (&d)[RPT],
+                                            float (&out)[RPT]) {
+    float red[2 * RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[r][e] = s[r][e] * gt;          // decay
+        red[r] = lane_dot<E>(s[r], kk);                              // (g S) . k
+        red[RPT + r] = lane_dot<E>(s[r], qq);                        // (g S) . q
+    }
+    row16_sum_n<2 * RPT>(red);
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        d[r] = (vv[r] - red[r]) * beta;
+        out[r] = fmaf(d[r], kq, red[RPT + r]);
+    }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[r][e] = fmaf(kk[e], d[r], s[r][e]);   // rank-1 write
+}
+
+template <int W, int NC, int E>
+__device__ __forceinline__ void load_state_row(const float* p, uint32_t lane, float (&row)[E]) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        float t4[W];
+        f32_load_vec<W>(p + (c * 16 + lane) * W, t4);
+#pragma unroll
+        for (int w = 0; w < W; ++w) row[c * W + w] = t4[w];
+    }
+}
+
+template <int W, int NC, int E>
+__device__ __forceinline__ void store_state_row(float* p, uint32_t lane, const float (&row)[E]) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        float t4[W];
+#pragma unroll
+        for (int w = 0; w < W; ++w) t4[w] = row[c * W + w];
+        f32_store_vec_nt<W>(p + (c * 16 + lane) * W, t4);
+    }
+}
+
+// ------------------------------------------------------------ direct kernel
 
 template <int IO, int DK, int RPT, int NT>
 __global__ __launch_bounds__(NT) void gdn_record_kernel(
@@ -48,32 +124,22 @@ __global__ __launch_bounds__(NT) void gdn_record_kernel(
     const uint32_t lane = threadIdx.x & (L - 1);
     const uint32_t slot = threadIdx.x / L;
 
-    // Logical work index: (b, key head, value head within the key head's
-    // group, row block), so the groups sharing a key head sit next to each other.
+    // Workgroup blk covers rows [blk*R, blk*R + R) of the flattened
+    // [B*Hv*Dv] row space (R divides Dv, so they belong to one head).  The
+    // state address needs no division, so the state loads go out first and
+    // the head arithmetic below overlaps their latency.
     const uint32_t blk = xcd_contiguous_index(blockIdx.x, gridDim.x);
-    const uint32_t rb = blk % row_blocks;
-    const uint32_t n = blk / row_blocks;
-    const uint32_t b = n / Hv;
-    const uint32_t m = n - b * Hv;
-    const uint32_t group = Hv / Hk;
-    const uint32_t hk = m / group;
-    const uint32_t j = m - hk * group;
-    const uint32_t hv = tiled ? j * Hk + hk : m;
-
-    const uint32_t row0 = rb * R + slot * RPT;               // first row of this thread
-    const size_t head = static_cast<size_t>(b) * Hv + hv;
-    const size_t srow = (head * Dv + row0) * DK;
+    const size_t srow = (static_cast<size_t>(blk) * R + slot * RPT) * DK;
 
     float s[RPT][E];
 #pragma unroll
-    for (int r = 0; r < RPT; ++r)
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            float t4[W];
-            f32_load_vec<W>(state_in + srow + r * DK + (c * L + lane) * W, t4);
-#pragma unroll
-            for (int w = 0; w < W; ++w) s[r][c * W + w] = t4[w];
-        }
+    for (int r = 0; r < RPT; ++r) load_state_row<W, NC, E>(state_in + srow + r * DK, lane, s[r]);
+
+    const uint32_t n = blk / row_blocks;                      // b * Hv + hv
+    const uint32_t row0 = (blk - n * row_blocks) * R + slot * RPT;  // first row within the head
+    const uint32_t b = n / Hv;
+    const uint32_t hv = n - b * Hv;
+    const uint32_t hk = tiled ? hv % Hk : hv / (Hv / Hk);
 
     for (uint32_t t = 0; t < T; ++t) {
         const size_t bt = static_cast<size_t>(b) * T + t;
@@ -96,48 +162,221 @@ __global__ __launch_bounds__(NT) void gdn_record_kernel(
         }
         io_load_vec<IO, RPT>(v, vo, vv);
 
-        // decay, then read the decayed row out against k
-        float kv[RPT];
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) {
-            float acc = 0.f;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                s[r][e] = s[r][e] * gt;
-                acc = fmaf(s[r][e], kk[e], acc);
-            }
-            kv[r] = row16_sum(acc);
-        }
-
-        float d[RPT];
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) d[r] = (vv[r] - kv[r]) * bt_beta;
+        float kqs[1] = {lane_dot<E>(kk, qq)};
+        row16_sum_n<1>(kqs);
+        float d[RPT], out[RPT];
+        record_step<RPT, E>(s, kk, qq, vv, gt, bt_beta, kqs[0], d, out);
         if (delta_log != nullptr && lane == 0) io_store_vec<IO, RPT>(delta_log, vo, d);
-
-        // rank-1 write, then read the updated row out against q
-        float out[RPT];
-#pragma unroll
-        for (int r = 0; r < RPT; ++r) {
-            float acc = 0.f;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                s[r][e] = fmaf(kk[e], d[r], s[r][e]);
-                acc = fmaf(s[r][e], qq[e], acc);
-            }
-            out[r] = row16_sum(acc);
-        }
         if (lane == 0) io_store_vec<IO, RPT>(y, vo, out);
     }
 
 #pragma unroll
-    for (int r = 0; r < RPT; ++r)
+    for (int r = 0; r < RPT; ++r) store_state_row<W, NC, E>(state_out + srow + r * DK, lane, s[r]);
+}
+
+// ------------------------------------------------------------ staged kernel
+
+// Chunk length of the staged kernel: the inputs of up to this many steps sit
+// in LDS at once (as float32).
+template <int DK>
+constexpr int staged_chunk() { return DK <= 128 ? 32 : 16; }
+
+// Steps whose LDS operands are read together; LDS chunks are padded to a
+// multiple of this many rows.
+constexpr int kGroup = 4;
+
+// LDS rows of a chunk: min(TC, T) rounded up to a whole group.
+__host__ __device__ constexpr uint32_t chunk_alloc_rows(uint32_t tc, uint32_t T) {
+    const uint32_t r = T < tc ? T : tc;
+    return (r + kGroup - 1) / kGroup * kGroup;
+}
+
+// LDS floats for a chunk of `rows` steps: k and q rows, the step scalars
+// (g, beta, k.q, mask), this group's v, and two buffers of y, delta and a
+// written-flag per step (the previous chunk's leave while the next is computed).
+__host__ __device__ constexpr size_t record_lds_floats(int rows, int dk, int r) {
+    return static_cast<size_t>(rows) * (2 * dk + 4 + r + 2 * (2 * r + 1));
+}
+
+// The LDS operands of one step for one lane.
+template <int E, int RPT>
+struct StepOperands {
+    float k[E], q[E], v[RPT];
+    f32x4 sc;                                  // g, beta, k.q, mask entry (as bits)
+
+    template <int DK, int R>
+    __device__ __forceinline__ void read(const float* sk, const float* sq, const float* sv,
+                                         const float* sc4, int tt, uint32_t lane, uint32_t slot) {
+        constexpr int W = E < 4 ? E : 4;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            float t4[W];
+        for (int c = 0; c < E / W; ++c) {
+            float tk[W], tq[W];
+            lds_load_vec<W>(sk + tt * DK + (c * 16 + lane) * W, tk);
+            lds_load_vec<W>(sq + tt * DK + (c * 16 + lane) * W, tq);
 #pragma unroll
-            for (int w = 0; w < W; ++w) t4[w] = s[r][c * W + w];
-            f32_store_vec_nt<W>(state_out + srow + r * DK + (c * L + lane) * W, t4);
+            for (int w = 0; w < W; ++w) { k[c * W + w] = tk[w]; q[c * W + w] = tq[w]; }
         }
+        lds_load_vec<RPT>(sv + tt * R + slot * RPT, v);
+        sc = *reinterpret_cast<const f32x4*>(sc4 + 4 * tt);
+    }
+};
+
+// Staged variant for T > 1: every step of the direct kernel would wait for its
+// own inputs to arrive from memory.  Here the steps are taken in chunks of TC:
+// the workgroup copies a chunk's k and q (of its key head), v (of its rows), g,
+// beta and mask entries into LDS as float32 in one round of coalesced loads,
+// computes k . q of each step once, and loads the following chunk into
+// registers while it computes the current one from LDS.  y and delta of the
+// chunk are gathered in LDS and written with vector stores after it.
+template <int IO, int DK, int RPT, int NT>
+__global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const void* __restrict__ g, const void* __restrict__ beta,
+    const float* state_in, const uint32_t* __restrict__ mask,
+    void* __restrict__ y, float* state_out, void* __restrict__ delta_log,
+    uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dv, uint32_t row_blocks, int tiled,
+    uint32_t chunk_rows)
+{
+    constexpr int L = 16;
+    constexpr int E = DK / L;
+    constexpr int W = E < 4 ? E : 4;
+    constexpr int NC = E / W;
+    constexpr int SLOTS = NT / L;
+    constexpr int R = SLOTS * RPT;
+    constexpr int TC = staged_chunk<DK>();
+    constexpr int EB = IoTraits<IO>::kBytes;
+    constexpr int PR = piece_elems<IO, R>();                  // v / y / delta piece (elements)
+    static_assert(DK % (L * W) == 0 && NC * W == E, "unsupported Dk");
+    static_assert(R <= kStagedMaxRows, "row block too large for the staged kernel");
+
+    extern __shared__ __align__(16) float lds[];
+    const int crow = static_cast<int>(chunk_rows);            // LDS rows allocated (whole groups)
+    float* sk = lds;                                          // [crow][DK]
+    float* sq = sk + crow * DK;                               // [crow][DK]
+    float* sc = sq + crow * DK;                               // [crow][4]: g, beta, k.q, mask
+    float* sv = sc + crow * 4;                                // [crow][R]
+    float* obuf = sv + crow * R;                              // 2 x {y [crow][R], delta [crow][R], flag [crow]}
+    const int obuf_stride = crow * (2 * R + 1);
+
+    const uint32_t lane = threadIdx.x & (L - 1);
+    const uint32_t slot = threadIdx.x / L;
+    const uint32_t blk = xcd_contiguous_index(blockIdx.x, gridDim.x);
+    const size_t srow = (static_cast<size_t>(blk) * R + slot * RPT) * DK;
+
+    float s[RPT][E];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) load_state_row<W, NC, E>(state_in + srow + r * DK, lane, s[r]);
+
+    const uint32_t n = blk / row_blocks;                      // b * Hv + hv
+    const uint32_t wrow0 = (blk - n * row_blocks) * R;        // first row of the group in its head
+    const uint32_t b = n / Hv;
+    const uint32_t hv = n - b * Hv;
+    const uint32_t hk = tiled ? hv % Hk : hv / (Hv / Hk);
+
+    ChunkStager<IO, TC, DK, piece_elems<IO, DK>(), NT> stk, stq;
+    ChunkStager<IO, TC, R, PR, NT> stv;
+    ChunkStager<IO, TC, 1, 1, NT> stg, stb;
+    MaskStager<TC, NT> stm;
+
+    auto chunk_len = [&](uint32_t t0) { return static_cast<int>(T - t0 < TC ? T - t0 : TC); };
+    auto load_chunk = [&](uint32_t t0) {
+        const int valid = chunk_len(t0);
+        const size_t bt0 = static_cast<size_t>(b) * T + t0;
+        const size_t kqo = (bt0 * Hk + hk) * DK;
+        stk.load(static_cast<const char*>(k) + kqo * EB, static_cast<size_t>(Hk) * DK, valid);
+        stq.load(static_cast<const char*>(q) + kqo * EB, static_cast<size_t>(Hk) * DK, valid);
+        stv.load(static_cast<const char*>(v) + ((bt0 * Hv + hv) * Dv + wrow0) * EB,
+                 static_cast<size_t>(Hv) * Dv, valid);
+        stg.load(static_cast<const char*>(g) + (bt0 * Hv + hv) * EB, Hv, valid);
+        stb.load(static_cast<const char*>(beta) + (bt0 * Hv + hv) * EB, Hv, valid);
+        stm.load(mask != nullptr ? mask + bt0 : nullptr, valid);
+    };
+    // y and delta of the chunk starting at t0 (in output buffer t0/TC mod 2),
+    // from LDS to global memory in pieces of PR elements; steps whose flag is
+    // 0 (inactive) are skipped.
+    auto flush_chunk = [&](uint32_t t0) {
+        const int valid = chunk_len(t0);
+        const float* oy = obuf + ((t0 / TC) & 1u) * obuf_stride;
+        const float* od = oy + crow * R;
+        const float* of = od + crow * R;
+        constexpr int PER_STEP = R / PR;
+        for (int p = static_cast<int>(threadIdx.x); p < valid * PER_STEP; p += NT) {
+            const int tt = p / PER_STEP;
+            const int col = (p - tt * PER_STEP) * PR;
+            if (of[tt] == 0.f) continue;
+            const size_t vo = ((static_cast<size_t>(b) * T + t0 + tt) * Hv + hv) * Dv + wrow0 + col;
+            float f[PR];
+            lds_load_vec<PR>(oy + tt * R + col, f);
+            io_store_vec<IO, PR>(y, vo, f);
+            if (delta_log != nullptr) {
+                lds_load_vec<PR>(od + tt * R + col, f);
+                io_store_vec<IO, PR>(delta_log, vo, f);
+            }
+        }
+    };
+
+    load_chunk(0);
+    wait_vector_memory();                                     // state rows and chunk 0 are in
+    for (uint32_t t0 = 0; t0 < T; t0 += TC) {
+        if (t0 != 0) __syncthreads();                         // the previous chunk is computed
+        const int valid = chunk_len(t0);
+        float* oy = obuf + ((t0 / TC) & 1u) * obuf_stride;    // this chunk's output buffer
+        float* od = oy + crow * R;
+        float* of = od + crow * R;
+        stk.store(sk, crow);
+        stq.store(sq, crow);
+        stv.store(sv, crow);
+        stg.store_strided(sc + 0, 4, crow);
+        stb.store_strided(sc + 1, 4, crow);
+        stm.store_strided(reinterpret_cast<uint32_t*>(sc + 3), 4, crow);
+        __syncthreads();
+        // k . q of each step: one 16-lane row group per step
+        for (int tt = static_cast<int>(slot); tt < valid; tt += SLOTS) {
+            float tk[E], tq[E];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                float a[W], bq[W];
+                lds_load_vec<W>(sk + tt * DK + (c * L + lane) * W, a);
+                lds_load_vec<W>(sq + tt * DK + (c * L + lane) * W, bq);
+#pragma unroll
+                for (int w = 0; w < W; ++w) { tk[c * W + w] = a[w]; tq[c * W + w] = bq[w]; }
+            }
+            float kqs[1] = {lane_dot<E>(tk, tq)};
+            row16_sum_n<1>(kqs);
+            if (lane == 0) sc[4 * tt + 2] = kqs[0];
+        }
+        for (int tt = static_cast<int>(threadIdx.x); tt < valid; tt += NT) of[tt] = 0.f;
+        __syncthreads();
+        if (t0 + TC < T) load_chunk(t0 + TC);                 // in flight during this chunk
+        if (t0 != 0) flush_chunk(t0 - TC);                    // the other output buffer
+
+        // Steps in groups of kGroup: the group's LDS reads are issued together
+        // (straight-line code, so each step waits only for its own operands),
+        // then its steps run.  Rows past the tape end are padding with mask 0.
+        StepOperands<E, RPT> op[kGroup];
+        auto run = [&](const StepOperands<E, RPT>& op, int tt) {
+            if (__builtin_amdgcn_readfirstlane(__float_as_uint(op.sc.w)) == 0u) return;   // inactive
+            const float gt = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(op.sc.x)));
+            const float bt_beta = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(op.sc.y)));
+            const float kq = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(op.sc.z)));
+            float d[RPT], out[RPT];
+            record_step<RPT, E>(s, op.k, op.q, op.v, gt, bt_beta, kq, d, out);
+            lds_store_vec<RPT>(od + tt * R + slot * RPT, d);  // all 16 lanes hold the same values
+            lds_store_vec<RPT>(oy + tt * R + slot * RPT, out);
+            if (threadIdx.x == 0) of[tt] = 1.f;
+        };
+        for (int t4 = 0; t4 < valid; t4 += kGroup) {
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) op[u].template read<DK, R>(sk, sq, sv, sc, t4 + u, lane, slot);
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) run(op[u], t4 + u);
+        }
+    }
+    __syncthreads();
+    flush_chunk(((T - 1) / TC) * TC);
+
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) store_state_row<W, NC, E>(state_out + srow + r * DK, lane, s[r]);
 }
 
 template <int IO, int DK, int RPT, int NT>
@@ -145,10 +384,22 @@ hipError_t launch_cfg(const RecordArgs& a, hipStream_t stream) {
     constexpr int R = RPT * NT / 16;
     const uint32_t row_blocks = a.Dv / R;
     const uint64_t grid = static_cast<uint64_t>(a.B) * a.Hv * row_blocks;
-    hipLaunchKernelGGL((gdn_record_kernel<IO, DK, RPT, NT>), dim3(static_cast<uint32_t>(grid)),
-                       dim3(NT), 0, stream, a.q, a.k, a.v, a.g, a.beta, a.state_in, a.mask, a.y,
-                       a.state_out, a.delta_log, a.T, a.Hk, a.Hv, a.Dv, row_blocks, a.map);
-    return hipGetLastError();
+    if (a.T == 1) {
+        hipLaunchKernelGGL((gdn_record_kernel<IO, DK, RPT, NT>), dim3(static_cast<uint32_t>(grid)),
+                           dim3(NT), 0, stream, a.q, a.k, a.v, a.g, a.beta, a.state_in, a.mask, a.y,
+                           a.state_out, a.delta_log, a.T, a.Hk, a.Hv, a.Dv, row_blocks, a.map);
+        return hipGetLastError();
+    }
+    if constexpr (R <= kStagedMaxRows) {
+        const uint32_t crow = chunk_alloc_rows(staged_chunk<DK>(), a.T);
+        const size_t lds = record_lds_floats(static_cast<int>(crow), DK, R) * sizeof(float);
+        hipLaunchKernelGGL((gdn_record_staged_kernel<IO, DK, RPT, NT>),
+                           dim3(static_cast<uint32_t>(grid)), dim3(NT), lds, stream, a.q, a.k, a.v,
+                           a.g, a.beta, a.state_in, a.mask, a.y, a.state_out, a.delta_log, a.T, a.Hk,
+                           a.Hv, a.Dv, row_blocks, a.map, crow);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidConfiguration;         // record_tiling never picks this for T > 1
 }
 
 template <int IO, int DK>
@@ -187,14 +438,15 @@ bool dk_supported(uint32_t Dk) {
     return Dk == 32 || Dk == 64 || Dk == 128 || Dk == 192 || Dk == 256;
 }
 
-bool tiling_override(const char* env_name, uint32_t Dk, uint32_t Dv, RowTiling* out) {
+bool tiling_override(const char* env_name, uint32_t Dk, uint32_t Dv, uint32_t max_rows,
+                     RowTiling* out) {
     const char* s = std::getenv(env_name);
     if (s == nullptr || *s == '\0') return false;
     int rpt = 0, nt = 0;
     if (std::sscanf(s, "%d,%d", &rpt, &nt) != 2) return false;
     for (int i = 0; i < kNumTilings; ++i) {
         if (kTilings[i].rows_per_thread == rpt && kTilings[i].threads == nt &&
-            tiling_fits(kTilings[i], Dk, Dv)) {
+            tiling_fits(kTilings[i], Dk, Dv) && static_cast<uint32_t>(kTilings[i].rows()) <= max_rows) {
             *out = kTilings[i];
             return true;
         }
@@ -204,11 +456,18 @@ bool tiling_override(const char* env_name, uint32_t Dk, uint32_t Dv, RowTiling* 
 
 RowTiling record_tiling(const RecordArgs& a) {
     RowTiling t;
-    if (tiling_override("GDN_RECORD_TILING", a.Dk, a.Dv, &t)) return t;
-    // Short tapes stream the state: wide row blocks keep many bytes in flight.
-    // Long tapes are a serial chain per row: spread the rows over more CUs.
-    const uint64_t target = a.T <= 16 ? 2048 : 4096;
-    return pick_tiling(static_cast<uint64_t>(a.B) * a.Hv, a.Dk, a.Dv, target);
+    const uint32_t max_rows = a.T == 1 ? 1024u : static_cast<uint32_t>(kStagedMaxRows);
+    if (tiling_override("GDN_RECORD_TILING", a.Dk, a.Dv, max_rows, &t)) return t;
+    // One step: the launch streams the state, and one row per thread over
+    // 256-thread groups measured fastest (many groups in flight, each with a
+    // small footprint).  Several steps: the staged kernel, with at most 64 rows
+    // per group; few heads (long prefills) get one-wave groups so the serial
+    // row chains spread over as many SIMDs as possible.
+    static const int kShort[] = {3, 2, 4};          // (1,256), (2,256), (1,64)
+    static const int kLong[] = {4};                 // (1,64)
+    const uint64_t heads = static_cast<uint64_t>(a.B) * a.Hv;
+    if (a.T <= 16) return pick_tiling(heads, a.Dk, a.Dv, 2048, kShort, 3);
+    return pick_tiling(heads, a.Dk, a.Dv, 4096, kLong, 1);
 }
 
 hipError_t launch_record(const RecordArgs& a, hipStream_t stream) {

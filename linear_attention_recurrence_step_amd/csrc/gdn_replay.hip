@@ -12,11 +12,13 @@
 // written once.  The page expresses "skip this position" as a per-lane select
 // between new and old state.  Here the step flag depends only on (b, t), which
 // is uniform over a workgroup, so it becomes a scalar branch around the whole
-// position: an untaken slot is never fetched (less tape traffic) and can never
-// leak into the state, NaN or not.  The loop stops at min(accepted, T_log).
+// position: an untaken slot can never leak into the state, NaN or not.  The
+// loop stops at min(accepted, T_log), so positions past it are never fetched.
 // The update is fma(k, delta, S * g): the same two roundings as the record
 // kernel's decay followed by its rank-1 write, so replaying a full fp32 tape
-// reproduces the record kernel's state bit for bit.
+// reproduces the record kernel's state bit for bit.  A fold of one position
+// runs the direct kernel below; longer folds run the staged kernel, which
+// brings the tape in through LDS a chunk of positions at a time.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -41,14 +43,10 @@ __global__ __launch_bounds__(NT) void gdn_replay_kernel(
     const uint32_t lane = threadIdx.x & (L - 1);
     const uint32_t slot = threadIdx.x / L;
 
+    // Rows [blk*R, blk*R + R) of the flattened [B*Hv*Dv] row space; the state
+    // address needs no division, so its loads are issued first.
     const uint32_t blk = xcd_contiguous_index(blockIdx.x, gridDim.x);
-    const uint32_t rb = blk % row_blocks;
-    const uint32_t n = blk / row_blocks;          // b * Hv + hv
-    const uint32_t b = n / Hv;
-    const uint32_t hv = n - b * Hv;
-
-    const uint32_t row0 = rb * R + slot * RPT;
-    const size_t srow = (static_cast<size_t>(n) * Dv + row0) * DK;
+    const size_t srow = (static_cast<size_t>(blk) * R + slot * RPT) * DK;
 
     float s[RPT][E];
 #pragma unroll
@@ -60,6 +58,11 @@ __global__ __launch_bounds__(NT) void gdn_replay_kernel(
 #pragma unroll
             for (int w = 0; w < W; ++w) s[r][c * W + w] = t4[w];
         }
+
+    const uint32_t n = blk / row_blocks;          // b * Hv + hv
+    const uint32_t row0 = (blk - n * row_blocks) * R + slot * RPT;
+    const uint32_t b = n / Hv;
+    const uint32_t hv = n - b * Hv;
 
     for (uint32_t t = 0; t < steps; ++t) {
         const size_t bt = static_cast<size_t>(b) * T_log + t;
@@ -94,14 +97,171 @@ __global__ __launch_bounds__(NT) void gdn_replay_kernel(
         }
 }
 
+// The LDS operands of one tape position for one lane: its E columns of k_log,
+// the delta values of its RPT rows, the gate and the mask entry.
+template <int E, int RPT, int R>
+struct TapeOperands {
+    float k[E], d[RPT], g;
+    uint32_t m;
+    __device__ __forceinline__ void read(const float* sk, const float* sd, const float* sg,
+                                         const uint32_t* sm, int tt, uint32_t lane, uint32_t slot) {
+        constexpr int L = 16;
+        constexpr int W = E < 4 ? E : 4;
+        constexpr int DK = E * L;
+#pragma unroll
+        for (int c = 0; c < E / W; ++c) {
+            float tk[W];
+            lds_load_vec<W>(sk + tt * DK + (c * L + lane) * W, tk);
+#pragma unroll
+            for (int w = 0; w < W; ++w) k[c * W + w] = tk[w];
+        }
+        lds_load_vec<RPT>(sd + tt * R + slot * RPT, d);
+        g = sg[tt];
+        m = sm[tt];
+    }
+};
+
+template <int DK>
+constexpr int replay_chunk() { return DK <= 128 ? 32 : 16; }
+
+// Positions whose LDS operands are read together; LDS chunks are padded to a
+// multiple of this many rows.
+constexpr int kGroup = 4;
+
+// LDS floats for a chunk of `rows` positions: k_log rows, this group's delta, g, mask.
+__host__ __device__ constexpr size_t replay_lds_floats(int rows, int dk, int r) {
+    return static_cast<size_t>(rows) * (dk + r + 2);
+}
+
+// Staged variant for more than one position: the tape data of a chunk of TC
+// positions (the k_log row and g of this head, delta of this group's rows, the
+// mask entries) is copied into LDS as float32 in one round of coalesced loads,
+// and the following chunk is loaded into registers while the current one is
+// folded.  Positions whose mask entry is zero are skipped, never folded.
+template <int IO, int DK, int RPT, int NT>
+__global__ __launch_bounds__(NT) void gdn_replay_staged_kernel(
+    const void* __restrict__ delta_log, const void* __restrict__ k_log,
+    const void* __restrict__ g_log, const float* state_in,
+    const uint32_t* __restrict__ mask, float* state_out,
+    uint32_t T_log, uint32_t Hv, uint32_t Dv, uint32_t row_blocks, uint32_t steps,
+    uint32_t chunk_rows)
+{
+    constexpr int L = 16;
+    constexpr int E = DK / L;
+    constexpr int W = E < 4 ? E : 4;
+    constexpr int NC = E / W;
+    constexpr int SLOTS = NT / L;
+    constexpr int R = SLOTS * RPT;
+    constexpr int TC = replay_chunk<DK>();
+    constexpr int EB = IoTraits<IO>::kBytes;
+    static_assert(DK % (L * W) == 0 && NC * W == E, "unsupported Dk");
+
+    extern __shared__ __align__(16) float lds[];
+    const int crow = static_cast<int>(chunk_rows);            // min(TC, steps) rounded up to kGroup
+    float* sk = lds;
+    float* sd = sk + crow * DK;
+    float* sg = sd + crow * R;
+    uint32_t* sm = reinterpret_cast<uint32_t*>(sg + crow);
+
+    const uint32_t lane = threadIdx.x & (L - 1);
+    const uint32_t slot = threadIdx.x / L;
+    const uint32_t blk = xcd_contiguous_index(blockIdx.x, gridDim.x);
+    const size_t srow = (static_cast<size_t>(blk) * R + slot * RPT) * DK;
+
+    float s[RPT][E];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            float t4[W];
+            f32_load_vec<W>(state_in + srow + r * DK + (c * L + lane) * W, t4);
+#pragma unroll
+            for (int w = 0; w < W; ++w) s[r][c * W + w] = t4[w];
+        }
+
+    const uint32_t n = blk / row_blocks;          // b * Hv + hv
+    const uint32_t wrow0 = (blk - n * row_blocks) * R;
+    const uint32_t b = n / Hv;
+    const uint32_t hv = n - b * Hv;
+
+    ChunkStager<IO, TC, DK, piece_elems<IO, DK>(), NT> stk;
+    ChunkStager<IO, TC, R, piece_elems<IO, R>(), NT> std_;
+    ChunkStager<IO, TC, 1, 1, NT> stg;
+    MaskStager<TC, NT> stm;
+
+    auto load_chunk = [&](uint32_t t0) {
+        const int valid = static_cast<int>(steps - t0 < TC ? steps - t0 : TC);
+        const size_t bt0 = static_cast<size_t>(b) * T_log + t0;
+        stk.load(static_cast<const char*>(k_log) + ((bt0 * Hv + hv) * DK) * EB,
+                 static_cast<size_t>(Hv) * DK, valid);
+        std_.load(static_cast<const char*>(delta_log) + ((bt0 * Hv + hv) * Dv + wrow0) * EB,
+                  static_cast<size_t>(Hv) * Dv, valid);
+        stg.load(static_cast<const char*>(g_log) + (bt0 * Hv + hv) * EB, Hv, valid);
+        stm.load(mask != nullptr ? mask + bt0 : nullptr, valid);
+    };
+
+    if (steps > 0) load_chunk(0);
+    wait_vector_memory();                                     // snapshot rows and chunk 0 are in
+    for (uint32_t t0 = 0; t0 < steps; t0 += TC) {
+        if (t0 != 0) __syncthreads();
+        stk.store(sk, crow);
+        std_.store(sd, crow);
+        stg.store(sg, crow);
+        stm.store(sm, crow);
+        __syncthreads();
+        if (t0 + TC < steps) load_chunk(t0 + TC);
+        const int valid = static_cast<int>(steps - t0 < TC ? steps - t0 : TC);
+
+        // Positions in groups of kGroup: the group's LDS reads are issued
+        // together (straight-line code, so each fold waits only for its own
+        // operands), then the positions are folded in order.  Rows past the
+        // end of the fold are padding with mask 0.
+        TapeOperands<E, RPT, R> op[kGroup];
+        auto fold = [&](const TapeOperands<E, RPT, R>& op) {
+            if (__builtin_amdgcn_readfirstlane(op.m) == 0u) return;      // untaken position
+            const float gt = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(op.g)));
+#pragma unroll
+            for (int r = 0; r < RPT; ++r)
+#pragma unroll
+                for (int e = 0; e < E; ++e) s[r][e] = fmaf(op.k[e], op.d[r], s[r][e] * gt);
+        };
+        for (int t4 = 0; t4 < valid; t4 += kGroup) {
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) op[u].read(sk, sd, sg, sm, t4 + u, lane, slot);
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) fold(op[u]);
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            float t4[W];
+#pragma unroll
+            for (int w = 0; w < W; ++w) t4[w] = s[r][c * W + w];
+            f32_store_vec_nt<W>(state_out + srow + r * DK + (c * L + lane) * W, t4);
+        }
+}
+
 template <int IO, int DK, int RPT, int NT>
 hipError_t launch_cfg(const ReplayArgs& a, hipStream_t stream) {
     constexpr int R = RPT * NT / 16;
     const uint32_t row_blocks = a.Dv / R;
     const uint64_t grid = static_cast<uint64_t>(a.B) * a.Hv * row_blocks;
-    hipLaunchKernelGGL((gdn_replay_kernel<IO, DK, RPT, NT>), dim3(static_cast<uint32_t>(grid)),
-                       dim3(NT), 0, stream, a.delta_log, a.k_log, a.g_log, a.state_in, a.mask,
-                       a.state_out, a.T_log, a.Hv, a.Dv, row_blocks, a.steps);
+    if (a.steps <= 1) {
+        hipLaunchKernelGGL((gdn_replay_kernel<IO, DK, RPT, NT>), dim3(static_cast<uint32_t>(grid)),
+                           dim3(NT), 0, stream, a.delta_log, a.k_log, a.g_log, a.state_in, a.mask,
+                           a.state_out, a.T_log, a.Hv, a.Dv, row_blocks, a.steps);
+    } else {
+        constexpr int TC = replay_chunk<DK>();
+        const uint32_t crow = ((a.steps < static_cast<uint32_t>(TC) ? a.steps : TC) + kGroup - 1) / kGroup * kGroup;
+        const size_t lds = replay_lds_floats(static_cast<int>(crow), DK, R) * sizeof(float);
+        hipLaunchKernelGGL((gdn_replay_staged_kernel<IO, DK, RPT, NT>),
+                           dim3(static_cast<uint32_t>(grid)), dim3(NT), lds, stream, a.delta_log,
+                           a.k_log, a.g_log, a.state_in, a.mask, a.state_out, a.T_log, a.Hv, a.Dv,
+                           row_blocks, a.steps, crow);
+    }
     return hipGetLastError();
 }
 
@@ -139,8 +299,15 @@ hipError_t launch_io(const ReplayArgs& a, const RowTiling& t, hipStream_t stream
 
 RowTiling replay_tiling(const ReplayArgs& a) {
     RowTiling t;
-    if (tiling_override("GDN_REPLAY_TILING", a.Dk, a.Dv, &t)) return t;
-    return pick_tiling(static_cast<uint64_t>(a.B) * a.Hv, a.Dk, a.Dv, 2048);
+    if (tiling_override("GDN_REPLAY_TILING", a.Dk, a.Dv, 1024u, &t)) return t;
+    // One or two taken positions: a pure state stream, fastest with one row
+    // per thread.  Longer folds load tape data every position, which wide
+    // groups share better.
+    static const int kShort[] = {3, 4, 2};          // (1,256), (1,64), (2,256)
+    static const int kLong[] = {0, 1, 2, 3, 4};     // widest first
+    const uint64_t heads = static_cast<uint64_t>(a.B) * a.Hv;
+    if (a.steps <= 2) return pick_tiling(heads, a.Dk, a.Dv, 2048, kShort, 3);
+    return pick_tiling(heads, a.Dk, a.Dv, 2048, kLong, 5);
 }
 
 hipError_t launch_replay(const ReplayArgs& a, hipStream_t stream) {

@@ -10,8 +10,10 @@
 // source is read once and every destination byte is written once.  VB is the
 // widest of 16/8/4/2 bytes that divides the row and both base addresses.
 // Consecutive threads take consecutive vectors of a row, so loads and stores
-// are contiguous across a wavefront.  Each thread handles kUnroll vectors,
-// issuing all loads before the stores.
+// are contiguous across a wavefront.  Loads and stores are non-temporal (the
+// source is read once and the copy is not re-read by this launch), and each
+// thread moves a single vector per pass of its grid-stride loop: on this part
+// that streams faster than several vectors per thread.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -19,7 +21,6 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
 
 template <int VB>
 __global__ __launch_bounds__(kThreads) void gqa_expand_kernel(
@@ -28,27 +29,16 @@ __global__ __launch_bounds__(kThreads) void gqa_expand_kernel(
 {
     using V = typename RawVec<VB>::T;
     const uint32_t group = h / hg;
-    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads * kUnroll;
-    for (uint64_t base = static_cast<uint64_t>(blockIdx.x) * kThreads * kUnroll + threadIdx.x;
-         base < nvec; base += stride) {
-        V val[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint64_t i = base + static_cast<uint64_t>(u) * kThreads;
-            if (i < nvec) val[u] = src[i];
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint64_t i = base + static_cast<uint64_t>(u) * kThreads;
-            if (i >= nvec) break;
-            const uint64_t row = i / row_vecs;                 // s * hg + hs
-            const uint32_t c = static_cast<uint32_t>(i - row * row_vecs);
-            const uint64_t s = row / hg;
-            const uint32_t hs = static_cast<uint32_t>(row - s * hg);
-            for (uint32_t j = 0; j < group; ++j) {
-                const uint32_t hd = tiled ? j * hg + hs : hs * group + j;
-                dst[(s * h + hd) * row_vecs + c] = val[u];
-            }
+    const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+    for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < nvec; i += stride) {
+        const V val = __builtin_nontemporal_load(src + i);
+        const uint64_t row = i / row_vecs;                     // s * hg + hs
+        const uint32_t c = static_cast<uint32_t>(i - row * row_vecs);
+        const uint64_t s = row / hg;
+        const uint32_t hs = static_cast<uint32_t>(row - s * hg);
+        for (uint32_t j = 0; j < group; ++j) {
+            const uint32_t hd = tiled ? j * hg + hs : hs * group + j;
+            __builtin_nontemporal_store(val, dst + (s * h + hd) * row_vecs + c);
         }
     }
 }
@@ -58,9 +48,8 @@ hipError_t launch_vb(const ExpandArgs& a, hipStream_t stream) {
     using V = typename RawVec<VB>::T;
     const uint32_t row_vecs = static_cast<uint32_t>((static_cast<uint64_t>(a.k) * a.elem_bytes) / VB);
     const uint64_t nvec = static_cast<uint64_t>(a.seq) * a.hg * row_vecs;
-    const uint64_t per_block = static_cast<uint64_t>(kThreads) * kUnroll;
-    uint64_t blocks = (nvec + per_block - 1) / per_block;
-    if (blocks > (1u << 20)) blocks = 1u << 20;               // grid-stride beyond this
+    uint64_t blocks = (nvec + kThreads - 1) / kThreads;
+    if (blocks > (1u << 22)) blocks = 1u << 22;               // grid-stride beyond this
     hipLaunchKernelGGL((gqa_expand_kernel<VB>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads),
                        0, stream, static_cast<const V*>(a.src), static_cast<V*>(a.dst), nvec, a.hg,
                        a.h, row_vecs, a.map);
