@@ -461,13 +461,13 @@ RowTiling record_tiling(const RecordArgs& a) {
     // One step: the launch streams the state, and one row per thread over
     // 256-thread groups measured fastest (many groups in flight, each with a
     // small footprint).  Several steps: the staged kernel, with at most 64 rows
-    // per group; few heads (long prefills) get one-wave groups so the serial
-    // row chains spread over as many SIMDs as possible.
+    // per group; long tapes take 16-row groups (one per CU at a 32-head
+    // prefill), or one-wave groups when even that leaves CUs idle.
     static const int kShort[] = {3, 2, 4};          // (1,256), (2,256), (1,64)
-    static const int kLong[] = {4};                 // (1,64)
+    static const int kLong[] = {3, 4};              // (1,256), (1,64)
     const uint64_t heads = static_cast<uint64_t>(a.B) * a.Hv;
     if (a.T <= 16) return pick_tiling(heads, a.Dk, a.Dv, 2048, kShort, 3);
-    return pick_tiling(heads, a.Dk, a.Dv, 4096, kLong, 1);
+    return pick_tiling(heads, a.Dk, a.Dv, 256, kLong, 2);
 }
 
 hipError_t launch_record(const RecordArgs& a, hipStream_t stream) {
