@@ -18,7 +18,10 @@
 // kernel's decay followed by its rank-1 write, so replaying a full fp32 tape
 // reproduces the record kernel's state bit for bit.  A fold of one position
 // runs the direct kernel below; longer folds run the staged kernel, which
-// brings the tape in through LDS a chunk of positions at a time.
+// brings the tape in through LDS a chunk of positions at a time.  Folds of 16
+// or more positions carry the state as scale * s (S = g S + delta k^T becomes
+// scale *= g, s += (delta / scale) k), which halves the arithmetic per
+// position; the result equals the direct fold up to rounding.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -128,6 +131,30 @@ constexpr int replay_chunk() { return DK <= 128 ? 32 : 16; }
 // multiple of this many rows.
 constexpr int kGroup = 4;
 
+// Whether c0 times every prefix product of the taken gates of a chunk (up to
+// 32 positions, from LDS) stays within [2^-64, 2^64], so that a scaled fold
+// of the chunk keeps a finite, well-scaled 1 / scale.  Lane i of each wave
+// takes position i; a log-step prefix product and a ballot make the answer
+// uniform.  NaN or infinite gates fail the test.
+__device__ __forceinline__ bool scale_stays_in_range(const float* sg, const uint32_t* sm,
+                                                     int valid, float c0) {
+    const int i = static_cast<int>(threadIdx.x & 31u);
+    float f = (i < valid && sm[i] != 0u) ? sg[i] : 1.f;
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {
+        const float o = __shfl_up(f, off, 32);
+        if (i >= off) f *= o;
+    }
+    const uint32_t mag = __float_as_uint(f * c0) & 0x7fffffffu;
+    const bool bad = i < valid && !(mag >= 0x1f800000u && mag <= 0x5f800000u);
+    return (__ballot(bad) & 0xffffffffull) == 0ull;
+}
+
+// Folds of at least this many positions carry the state with a running scale
+// (one FMA per value and position); shorter folds use the direct update,
+// which reproduces the record kernel's roundings exactly.
+constexpr uint32_t kScaledFromSteps = 16;
+
 // LDS floats for a chunk of `rows` positions: k_log rows, this group's delta, g, mask.
 __host__ __device__ constexpr size_t replay_lds_floats(int rows, int dk, int r) {
     return static_cast<size_t>(rows) * (dk + r + 2);
@@ -138,7 +165,7 @@ __host__ __device__ constexpr size_t replay_lds_floats(int rows, int dk, int r) 
 // mask entries) is copied into LDS as float32 in one round of coalesced loads,
 // and the following chunk is loaded into registers while the current one is
 // folded.  Positions whose mask entry is zero are skipped, never folded.
-template <int IO, int DK, int RPT, int NT>
+template <int IO, int DK, int RPT, int NT, bool SCALED>
 __global__ __launch_bounds__(NT) void gdn_replay_staged_kernel(
     const void* __restrict__ delta_log, const void* __restrict__ k_log,
     const void* __restrict__ g_log, const float* state_in,
@@ -200,6 +227,10 @@ __global__ __launch_bounds__(NT) void gdn_replay_staged_kernel(
         stm.load(mask != nullptr ? mask + bt0 : nullptr, valid);
     };
 
+    // SCALED: the state is carried as scale * s with a workgroup-uniform
+    // scale (the gate is per head), so a taken position costs one FMA per
+    // state value instead of a multiply and an FMA.
+    float scale = 1.f;
     if (steps > 0) load_chunk(0);
     wait_vector_memory();                                     // snapshot rows and chunk 0 are in
     for (uint32_t t0 = 0; t0 < steps; t0 += TC) {
@@ -217,7 +248,7 @@ __global__ __launch_bounds__(NT) void gdn_replay_staged_kernel(
         // operands), then the positions are folded in order.  Rows past the
         // end of the fold are padding with mask 0.
         TapeOperands<E, RPT, R> op[kGroup];
-        auto fold = [&](const TapeOperands<E, RPT, R>& op) {
+        auto fold_direct = [&](const TapeOperands<E, RPT, R>& op) {
             if (__builtin_amdgcn_readfirstlane(op.m) == 0u) return;      // untaken position
             const float gt = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(op.g)));
 #pragma unroll
@@ -225,12 +256,56 @@ __global__ __launch_bounds__(NT) void gdn_replay_staged_kernel(
 #pragma unroll
                 for (int e = 0; e < E; ++e) s[r][e] = fmaf(op.k[e], op.d[r], s[r][e] * gt);
         };
-        for (int t4 = 0; t4 < valid; t4 += kGroup) {
+        // S = scale * s: a taken position does scale *= g, s += (delta / scale) k.
+        auto fold_scaled = [&](const TapeOperands<E, RPT, R>& op) {
+            if (__builtin_amdgcn_readfirstlane(op.m) == 0u) return;      // untaken position
+            const float gt = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(op.g)));
+            scale *= gt;
+            const float inv = __builtin_amdgcn_rcpf(scale);
+            float dd[RPT];
 #pragma unroll
-            for (int u = 0; u < kGroup; ++u) op[u].read(sk, sd, sg, sm, t4 + u, lane, slot);
+            for (int r = 0; r < RPT; ++r) dd[r] = op.d[r] * inv;
 #pragma unroll
-            for (int u = 0; u < kGroup; ++u) fold(op[u]);
+            for (int r = 0; r < RPT; ++r)
+#pragma unroll
+                for (int e = 0; e < E; ++e) s[r][e] = fmaf(op.k[e], dd[r], s[r][e]);
+        };
+        bool scaled_chunk = false;
+        if constexpr (SCALED) {
+            scaled_chunk = scale_stays_in_range(sg, sm, valid, scale);
+            if (!scaled_chunk) {
+                // fold the scale into the state, then try again from 1
+                if (scale != 1.f) {
+#pragma unroll
+                    for (int r = 0; r < RPT; ++r)
+#pragma unroll
+                        for (int e = 0; e < E; ++e) s[r][e] *= scale;
+                    scale = 1.f;
+                }
+                scaled_chunk = scale_stays_in_range(sg, sm, valid, 1.f);
+            }
         }
+        if (scaled_chunk) {
+            for (int t4 = 0; t4 < valid; t4 += kGroup) {
+#pragma unroll
+                for (int u = 0; u < kGroup; ++u) op[u].read(sk, sd, sg, sm, t4 + u, lane, slot);
+#pragma unroll
+                for (int u = 0; u < kGroup; ++u) fold_scaled(op[u]);
+            }
+        } else {
+            for (int t4 = 0; t4 < valid; t4 += kGroup) {
+#pragma unroll
+                for (int u = 0; u < kGroup; ++u) op[u].read(sk, sd, sg, sm, t4 + u, lane, slot);
+#pragma unroll
+                for (int u = 0; u < kGroup; ++u) fold_direct(op[u]);
+            }
+        }
+    }
+    if (SCALED && scale != 1.f) {
+#pragma unroll
+        for (int r = 0; r < RPT; ++r)
+#pragma unroll
+            for (int e = 0; e < E; ++e) s[r][e] *= scale;
     }
 
 #pragma unroll
@@ -257,10 +332,16 @@ hipError_t launch_cfg(const ReplayArgs& a, hipStream_t stream) {
         constexpr int TC = replay_chunk<DK>();
         const uint32_t crow = ((a.steps < static_cast<uint32_t>(TC) ? a.steps : TC) + kGroup - 1) / kGroup * kGroup;
         const size_t lds = replay_lds_floats(static_cast<int>(crow), DK, R) * sizeof(float);
-        hipLaunchKernelGGL((gdn_replay_staged_kernel<IO, DK, RPT, NT>),
-                           dim3(static_cast<uint32_t>(grid)), dim3(NT), lds, stream, a.delta_log,
-                           a.k_log, a.g_log, a.state_in, a.mask, a.state_out, a.T_log, a.Hv, a.Dv,
-                           row_blocks, a.steps, crow);
+        if (a.steps >= kScaledFromSteps)
+            hipLaunchKernelGGL((gdn_replay_staged_kernel<IO, DK, RPT, NT, true>),
+                               dim3(static_cast<uint32_t>(grid)), dim3(NT), lds, stream, a.delta_log,
+                               a.k_log, a.g_log, a.state_in, a.mask, a.state_out, a.T_log, a.Hv, a.Dv,
+                               row_blocks, a.steps, crow);
+        else
+            hipLaunchKernelGGL((gdn_replay_staged_kernel<IO, DK, RPT, NT, false>),
+                               dim3(static_cast<uint32_t>(grid)), dim3(NT), lds, stream, a.delta_log,
+                               a.k_log, a.g_log, a.state_in, a.mask, a.state_out, a.T_log, a.Hv, a.Dv,
+                               row_blocks, a.steps, crow);
     }
     return hipGetLastError();
 }

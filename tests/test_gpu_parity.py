@@ -188,6 +188,22 @@ def test_replay_long_tape_nan_poisoned(accepted):
     assert torch.isfinite(s).all()
 
 
+@pytest.mark.parametrize("io", ["f32", "f16"])
+def test_replay_long_fold_with_extreme_gates(io):
+    """Long folds carry the state with a running scale; gates of 0, 1e-20, 1e-6
+    and runs of 1.9 (the scale leaves its range both ways) must still match."""
+    B, T, Hv, Dk, Dv = 2, 48, 2, 64, 32
+    tape = gi.tape_inputs(B, T, Hv, Dk, Dv, io, seed=71, mask="bernoulli", mask_p=0.9)
+    g = torch.full((B, T, Hv), 0.8)
+    g[:, 3] = 0.0
+    g[:, 7, 0] = 1e-20 if io == "f32" else 1e-7
+    g[:, 11:45, 1] = 1.9
+    g[:, 20] = 1e-6 if io == "f32" else 1e-4
+    tape["g_log"] = g.to(gi.IO_DTYPES[io])
+    for a in (T, 30):
+        _check_replay(tape, a, "extreme gates")
+
+
 @pytest.mark.parametrize("case", [(3, 5, 2, 32, 16, "f32"), (2, 6, 3, 64, 48, "bf16"),
                                   (1, 4, 4, 192, 128, "f16"), (2, 3, 2, 256, 32, "bf16")],
                          ids=lambda c: "B%d_T%d_Hv%d_Dk%d_Dv%d_%s" % c)
