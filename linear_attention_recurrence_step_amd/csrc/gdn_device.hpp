@@ -309,8 +309,10 @@ struct ChunkStager {
         }
     }
 
-    // For single-column blocks: row i goes to lds[i * stride].
-    __device__ __forceinline__ void store_strided(float* lds, int stride, int rows) const {
+    // For single-column blocks: row i goes to lds[i * stride]; rows at or
+    // past `valid` (not loaded) get `pad` instead.
+    __device__ __forceinline__ void store_strided(float* lds, int stride, int rows, int valid,
+                                                  float pad) const {
         static_assert(COLS == 1 && P == 1, "strided store is for one value per row");
 #pragma unroll
         for (int j = 0; j < PER_THREAD; ++j) {
@@ -318,7 +320,7 @@ struct ChunkStager {
             if (p < PIECES && p < rows) {
                 float f[1];
                 unpack(buf[j], f);
-                lds[p * stride] = f[0];
+                lds[p * stride] = p < valid ? f[0] : pad;
             }
         }
     }

@@ -39,17 +39,15 @@ namespace gdn {
 namespace {
 
 // This lane's part of a Dk-length dot product over its E columns, in a fixed
-// order (two interleaved accumulators), shared by every kernel that needs it.
+// order, shared by every kernel that needs it.  A step computes two of these
+// chains side by side, which keeps the FMA pipeline busy without splitting
+// each chain.
 template <int E>
 __device__ __forceinline__ float lane_dot(const float (&x)[E], const float (&y)[E]) {
-    float a0 = 0.f, a1 = 0.f;
+    float a = 0.f;
 #pragma unroll
-    for (int e = 0; e + 1 < E; e += 2) {
-        a0 = fmaf(x[e], y[e], a0);
-        a1 = fmaf(x[e + 1], y[e + 1], a1);
-    }
-    if constexpr (E % 2 == 1) a0 = fmaf(x[E - 1], y[E - 1], a0);
-    return a0 + a1;
+    for (int e = 0; e < E; ++e) a = fmaf(x[e], y[e], a);
+    return a;
 }
 
 // One active step on the RPT rows this lane holds (E columns of each):
@@ -192,8 +190,9 @@ __host__ __device__ constexpr uint32_t chunk_alloc_rows(uint32_t tc, uint32_t T)
 }
 
 // LDS floats for a chunk of `rows` steps: k and q rows, the step scalars
-// (g, beta, k.q, mask), this group's v, and two buffers of y, delta and a
-// written-flag per step (the previous chunk's leave while the next is computed).
+// (g, beta, k.q, mask), this group's v, and two buffers of interleaved
+// (y, delta) pairs plus an active flag per step (the previous chunk's outputs
+// leave while the next chunk is computed).
 __host__ __device__ constexpr size_t record_lds_floats(int rows, int dk, int r) {
     return static_cast<size_t>(rows) * (2 * dk + 4 + r + 2 * (2 * r + 1));
 }
@@ -228,7 +227,7 @@ struct StepOperands {
 // computes k . q of each step once, and loads the following chunk into
 // registers while it computes the current one from LDS.  y and delta of the
 // chunk are gathered in LDS and written with vector stores after it.
-template <int IO, int DK, int RPT, int NT>
+template <int IO, int DK, int RPT, int NT, bool MASKED>
 __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ g, const void* __restrict__ beta,
@@ -255,7 +254,7 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
     float* sq = sk + crow * DK;                               // [crow][DK]
     float* sc = sq + crow * DK;                               // [crow][4]: g, beta, k.q, mask
     float* sv = sc + crow * 4;                                // [crow][R]
-    float* obuf = sv + crow * R;                              // 2 x {y [crow][R], delta [crow][R], flag [crow]}
+    float* obuf = sv + crow * R;                              // 2 x {(y, delta) [crow][R][2], flag [crow]}
     const int obuf_stride = crow * (2 * R + 1);
 
     const uint32_t lane = threadIdx.x & (L - 1);
@@ -292,26 +291,24 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
         stm.load(mask != nullptr ? mask + bt0 : nullptr, valid);
     };
     // y and delta of the chunk starting at t0 (in output buffer t0/TC mod 2),
-    // from LDS to global memory in pieces of PR elements; steps whose flag is
-    // 0 (inactive) are skipped.
+    // from LDS to global memory in pieces of PR elements; inactive steps
+    // (flag 0) are skipped.
     auto flush_chunk = [&](uint32_t t0) {
         const int valid = chunk_len(t0);
-        const float* oy = obuf + ((t0 / TC) & 1u) * obuf_stride;
-        const float* od = oy + crow * R;
-        const float* of = od + crow * R;
+        const float* oyd = obuf + ((t0 / TC) & 1u) * obuf_stride;   // [crow][R][2]: y, delta
+        const uint32_t* of = reinterpret_cast<const uint32_t*>(oyd + crow * R * 2);
         constexpr int PER_STEP = R / PR;
         for (int p = static_cast<int>(threadIdx.x); p < valid * PER_STEP; p += NT) {
             const int tt = p / PER_STEP;
             const int col = (p - tt * PER_STEP) * PR;
-            if (of[tt] == 0.f) continue;
+            if (MASKED && of[tt] == 0u) continue;
             const size_t vo = ((static_cast<size_t>(b) * T + t0 + tt) * Hv + hv) * Dv + wrow0 + col;
-            float f[PR];
-            lds_load_vec<PR>(oy + tt * R + col, f);
-            io_store_vec<IO, PR>(y, vo, f);
-            if (delta_log != nullptr) {
-                lds_load_vec<PR>(od + tt * R + col, f);
-                io_store_vec<IO, PR>(delta_log, vo, f);
-            }
+            float f[2 * PR], fy[PR], fd[PR];
+            lds_load_vec<2 * PR>(oyd + (tt * R + col) * 2, f);
+#pragma unroll
+            for (int i = 0; i < PR; ++i) { fy[i] = f[2 * i]; fd[i] = f[2 * i + 1]; }
+            io_store_vec<IO, PR>(y, vo, fy);
+            if (delta_log != nullptr) io_store_vec<IO, PR>(delta_log, vo, fd);
         }
     };
 
@@ -320,15 +317,18 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
     for (uint32_t t0 = 0; t0 < T; t0 += TC) {
         if (t0 != 0) __syncthreads();                         // the previous chunk is computed
         const int valid = chunk_len(t0);
-        float* oy = obuf + ((t0 / TC) & 1u) * obuf_stride;    // this chunk's output buffer
-        float* od = oy + crow * R;
-        float* of = od + crow * R;
+        float* oyd = obuf + ((t0 / TC) & 1u) * obuf_stride;   // this chunk's output buffer
         stk.store(sk, crow);
         stq.store(sq, crow);
         stv.store(sv, crow);
-        stg.store_strided(sc + 0, 4, crow);
-        stb.store_strided(sc + 1, 4, crow);
-        stm.store_strided(reinterpret_cast<uint32_t*>(sc + 3), 4, crow);
+        // Padding rows (past the tape end, up to a whole group) become exact
+        // identity steps: g = 1, beta = 0, k = q = v = 0.
+        stg.store_strided(sc + 0, 4, crow, valid, 1.f);
+        stb.store_strided(sc + 1, 4, crow, valid, 0.f);
+        if constexpr (MASKED) {
+            stm.store_strided(reinterpret_cast<uint32_t*>(sc + 3), 4, crow);
+            stm.store(reinterpret_cast<uint32_t*>(oyd + crow * R * 2), crow);   // flags for the flush
+        }
         __syncthreads();
         // k . q of each step: one 16-lane row group per step
         for (int tt = static_cast<int>(slot); tt < valid; tt += SLOTS) {
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
             row16_sum_n<1>(kqs);
             if (lane == 0) sc[4 * tt + 2] = kqs[0];
         }
-        for (int tt = static_cast<int>(threadIdx.x); tt < valid; tt += NT) of[tt] = 0.f;
+        for (int tt = valid + static_cast<int>(threadIdx.x); tt < crow; tt += NT) sc[4 * tt + 2] = 0.f;
         __syncthreads();
         if (t0 + TC < T) load_chunk(t0 + TC);                 // in flight during this chunk
         if (t0 != 0) flush_chunk(t0 - TC);                    // the other output buffer
@@ -355,15 +355,15 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
         // then its steps run.  Rows past the tape end are padding with mask 0.
         StepOperands<E, RPT> op[kGroup];
         auto run = [&](const StepOperands<E, RPT>& op, int tt) {
-            if (__builtin_amdgcn_readfirstlane(__float_as_uint(op.sc.w)) == 0u) return;   // inactive
-            const float gt = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(op.sc.x)));
-            const float bt_beta = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(op.sc.y)));
-            const float kq = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(op.sc.z)));
+            if constexpr (MASKED) {
+                if (__builtin_amdgcn_readfirstlane(__float_as_uint(op.sc.w)) == 0u) return;   // inactive
+            }
             float d[RPT], out[RPT];
-            record_step<RPT, E>(s, op.k, op.q, op.v, gt, bt_beta, kq, d, out);
-            lds_store_vec<RPT>(od + tt * R + slot * RPT, d);  // all 16 lanes hold the same values
-            lds_store_vec<RPT>(oy + tt * R + slot * RPT, out);
-            if (threadIdx.x == 0) of[tt] = 1.f;
+            record_step<RPT, E>(s, op.k, op.q, op.v, op.sc.x, op.sc.y, op.sc.z, d, out);
+            float pair[2 * RPT];                              // all 16 lanes hold the same values
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) { pair[2 * r] = out[r]; pair[2 * r + 1] = d[r]; }
+            lds_store_vec<2 * RPT>(oyd + (tt * R + slot * RPT) * 2, pair);
         };
         for (int t4 = 0; t4 < valid; t4 += kGroup) {
 #pragma unroll
@@ -393,10 +393,16 @@ hipError_t launch_cfg(const RecordArgs& a, hipStream_t stream) {
     if constexpr (R <= kStagedMaxRows) {
         const uint32_t crow = chunk_alloc_rows(staged_chunk<DK>(), a.T);
         const size_t lds = record_lds_floats(static_cast<int>(crow), DK, R) * sizeof(float);
-        hipLaunchKernelGGL((gdn_record_staged_kernel<IO, DK, RPT, NT>),
-                           dim3(static_cast<uint32_t>(grid)), dim3(NT), lds, stream, a.q, a.k, a.v,
-                           a.g, a.beta, a.state_in, a.mask, a.y, a.state_out, a.delta_log, a.T, a.Hk,
-                           a.Hv, a.Dv, row_blocks, a.map, crow);
+        if (a.mask != nullptr)
+            hipLaunchKernelGGL((gdn_record_staged_kernel<IO, DK, RPT, NT, true>),
+                               dim3(static_cast<uint32_t>(grid)), dim3(NT), lds, stream, a.q, a.k, a.v,
+                               a.g, a.beta, a.state_in, a.mask, a.y, a.state_out, a.delta_log, a.T,
+                               a.Hk, a.Hv, a.Dv, row_blocks, a.map, crow);
+        else
+            hipLaunchKernelGGL((gdn_record_staged_kernel<IO, DK, RPT, NT, false>),
+                               dim3(static_cast<uint32_t>(grid)), dim3(NT), lds, stream, a.q, a.k, a.v,
+                               a.g, a.beta, a.state_in, a.mask, a.y, a.state_out, a.delta_log, a.T,
+                               a.Hk, a.Hv, a.Dv, row_blocks, a.map, crow);
         return hipGetLastError();
     }
     return hipErrorInvalidConfiguration;         // record_tiling never picks this for T > 1
