@@ -183,6 +183,10 @@ constexpr int staged_chunk() { return DK <= 128 ? 32 : 16; }
 // multiple of this many rows.
 constexpr int kGroup = 4;
 
+// Tapes of at most this many steps run the short configuration of the staged
+// kernel (one chunk of this length, operands read one step at a time).
+constexpr uint32_t kShortChunk = 8;
+
 // LDS rows of a chunk: min(TC, T) rounded up to a whole group.
 __host__ __device__ constexpr uint32_t chunk_alloc_rows(uint32_t tc, uint32_t T) {
     const uint32_t r = T < tc ? T : tc;
@@ -227,7 +231,10 @@ struct StepOperands {
 // computes k . q of each step once, and loads the following chunk into
 // registers while it computes the current one from LDS.  y and delta of the
 // chunk are gathered in LDS and written with vector stores after it.
-template <int IO, int DK, int RPT, int NT, bool MASKED>
+// SHORT: tapes of at most kShortChunk steps take one small chunk and read the
+// operands of one step at a time, which keeps the register count (and so
+// the occupancy) of this latency-bound case low.
+template <int IO, int DK, int RPT, int NT, bool MASKED, bool SHORT>
 __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ g, const void* __restrict__ beta,
@@ -242,7 +249,8 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
     constexpr int NC = E / W;
     constexpr int SLOTS = NT / L;
     constexpr int R = SLOTS * RPT;
-    constexpr int TC = staged_chunk<DK>();
+    constexpr int TC = SHORT ? kShortChunk : staged_chunk<DK>();
+    constexpr int G = SHORT ? 1 : kGroup;                     // steps whose operands are read together
     constexpr int EB = IoTraits<IO>::kBytes;
     constexpr int PR = piece_elems<IO, R>();                  // v / y / delta piece (elements)
     static_assert(DK % (L * W) == 0 && NC * W == E, "unsupported Dk");
@@ -353,7 +361,7 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
         // Steps in groups of kGroup: the group's LDS reads are issued together
         // (straight-line code, so each step waits only for its own operands),
         // then its steps run.  Rows past the tape end are padding with mask 0.
-        StepOperands<E, RPT> op[kGroup];
+        StepOperands<E, RPT> op[G];
         auto run = [&](const StepOperands<E, RPT>& op, int tt) {
             if constexpr (MASKED) {
                 if (__builtin_amdgcn_readfirstlane(__float_as_uint(op.sc.w)) == 0u) return;   // inactive
@@ -365,11 +373,11 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
             for (int r = 0; r < RPT; ++r) { pair[2 * r] = out[r]; pair[2 * r + 1] = d[r]; }
             lds_store_vec<2 * RPT>(oyd + (tt * R + slot * RPT) * 2, pair);
         };
-        for (int t4 = 0; t4 < valid; t4 += kGroup) {
+        for (int t4 = 0; t4 < valid; t4 += G) {
 #pragma unroll
-            for (int u = 0; u < kGroup; ++u) op[u].template read<DK, R>(sk, sq, sv, sc, t4 + u, lane, slot);
+            for (int u = 0; u < G; ++u) op[u].template read<DK, R>(sk, sq, sv, sc, t4 + u, lane, slot);
 #pragma unroll
-            for (int u = 0; u < kGroup; ++u) run(op[u], t4 + u);
+            for (int u = 0; u < G; ++u) run(op[u], t4 + u);
         }
     }
     __syncthreads();
@@ -391,18 +399,22 @@ hipError_t launch_cfg(const RecordArgs& a, hipStream_t stream) {
         return hipGetLastError();
     }
     if constexpr (R <= kStagedMaxRows) {
-        const uint32_t crow = chunk_alloc_rows(staged_chunk<DK>(), a.T);
+        const bool short_tape = a.T <= kShortChunk;
+        const uint32_t crow = short_tape ? a.T : chunk_alloc_rows(staged_chunk<DK>(), a.T);
         const size_t lds = record_lds_floats(static_cast<int>(crow), DK, R) * sizeof(float);
-        if (a.mask != nullptr)
-            hipLaunchKernelGGL((gdn_record_staged_kernel<IO, DK, RPT, NT, true>),
-                               dim3(static_cast<uint32_t>(grid)), dim3(NT), lds, stream, a.q, a.k, a.v,
-                               a.g, a.beta, a.state_in, a.mask, a.y, a.state_out, a.delta_log, a.T,
-                               a.Hk, a.Hv, a.Dv, row_blocks, a.map, crow);
-        else
-            hipLaunchKernelGGL((gdn_record_staged_kernel<IO, DK, RPT, NT, false>),
-                               dim3(static_cast<uint32_t>(grid)), dim3(NT), lds, stream, a.q, a.k, a.v,
-                               a.g, a.beta, a.state_in, a.mask, a.y, a.state_out, a.delta_log, a.T,
-                               a.Hk, a.Hv, a.Dv, row_blocks, a.map, crow);
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(grid)), dim3(NT), lds, stream, a.q,
+                               a.k, a.v, a.g, a.beta, a.state_in, a.mask, a.y, a.state_out,
+                               a.delta_log, a.T, a.Hk, a.Hv, a.Dv, row_blocks, a.map, crow);
+        };
+        const bool masked = a.mask != nullptr;
+        if (short_tape) {
+            if (masked) go(gdn_record_staged_kernel<IO, DK, RPT, NT, true, true>);
+            else go(gdn_record_staged_kernel<IO, DK, RPT, NT, false, true>);
+        } else {
+            if (masked) go(gdn_record_staged_kernel<IO, DK, RPT, NT, true, false>);
+            else go(gdn_record_staged_kernel<IO, DK, RPT, NT, false, false>);
+        }
         return hipGetLastError();
     }
     return hipErrorInvalidConfiguration;         // record_tiling never picks this for T > 1
