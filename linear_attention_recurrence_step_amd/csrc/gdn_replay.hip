@@ -180,6 +180,10 @@ __global__ __launch_bounds__(NT) void gdn_replay_staged_kernel(
     constexpr int SLOTS = NT / L;
     constexpr int R = SLOTS * RPT;
     constexpr int TC = replay_chunk<DK>();
+    // positions whose operands are read together: with several rows per
+    // thread one position's FMAs already cover an LDS read, and fewer
+    // operand sets in flight keep the register count down
+    constexpr int G = RPT >= 4 ? 1 : kGroup / RPT;
     constexpr int EB = IoTraits<IO>::kBytes;
     static_assert(DK % (L * W) == 0 && NC * W == E, "unsupported Dk");
 
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(NT) void gdn_replay_staged_kernel(
         // together (straight-line code, so each fold waits only for its own
         // operands), then the positions are folded in order.  Rows past the
         // end of the fold are padding with mask 0.
-        TapeOperands<E, RPT, R> op[kGroup];
+        TapeOperands<E, RPT, R> op[G];
         auto fold_direct = [&](const TapeOperands<E, RPT, R>& op) {
             if (__builtin_amdgcn_readfirstlane(op.m) == 0u) return;      // untaken position
             const float gt = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(op.g)));
@@ -286,18 +290,18 @@ __global__ __launch_bounds__(NT) void gdn_replay_staged_kernel(
             }
         }
         if (scaled_chunk) {
-            for (int t4 = 0; t4 < valid; t4 += kGroup) {
+            for (int t4 = 0; t4 < valid; t4 += G) {
 #pragma unroll
-                for (int u = 0; u < kGroup; ++u) op[u].read(sk, sd, sg, sm, t4 + u, lane, slot);
+                for (int u = 0; u < G; ++u) op[u].read(sk, sd, sg, sm, t4 + u, lane, slot);
 #pragma unroll
-                for (int u = 0; u < kGroup; ++u) fold_scaled(op[u]);
+                for (int u = 0; u < G; ++u) fold_scaled(op[u]);
             }
         } else {
-            for (int t4 = 0; t4 < valid; t4 += kGroup) {
+            for (int t4 = 0; t4 < valid; t4 += G) {
 #pragma unroll
-                for (int u = 0; u < kGroup; ++u) op[u].read(sk, sd, sg, sm, t4 + u, lane, slot);
+                for (int u = 0; u < G; ++u) op[u].read(sk, sd, sg, sm, t4 + u, lane, slot);
 #pragma unroll
-                for (int u = 0; u < kGroup; ++u) fold_direct(op[u]);
+                for (int u = 0; u < G; ++u) fold_direct(op[u]);
             }
         }
     }
@@ -382,10 +386,11 @@ RowTiling replay_tiling(const ReplayArgs& a) {
     RowTiling t;
     if (tiling_override("GDN_REPLAY_TILING", a.Dk, a.Dv, 1024u, &t)) return t;
     // One or two taken positions: a pure state stream, fastest with one row
-    // per thread.  Longer folds load tape data every position, which wide
-    // groups share better.
+    // per thread.  Longer folds share each position's tape data over more
+    // rows per workgroup; four rows per thread measured fastest (eight cost
+    // too many registers).
     static const int kShort[] = {3, 4, 2};          // (1,256), (1,64), (2,256)
-    static const int kLong[] = {0, 1, 2, 3, 4};     // widest first
+    static const int kLong[] = {1, 2, 0, 3, 4};     // (4,256), (2,256), (8,256), ...
     const uint64_t heads = static_cast<uint64_t>(a.B) * a.Hv;
     if (a.steps <= 2) return pick_tiling(heads, a.Dk, a.Dv, 2048, kShort, 3);
     return pick_tiling(heads, a.Dk, a.Dv, 2048, kLong, 5);
