@@ -29,7 +29,8 @@
  *   enqueues nothing and returns a negative gdn_status.  gdn_last_error()
  *   then holds a human-readable reason (per calling thread).
  * - Pointers to tensors other than mask, g, beta and g_log must be 16-byte
- *   aligned (mask 4-byte, the others element-aligned).
+ *   aligned (mask 4-byte, the others element-aligned); gqa_expand needs only
+ *   element alignment.
  * - Raw pointers carry no length: the caller guarantees each buffer holds the
  *   elements its shape implies.
  */
@@ -42,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_dtype {
     GDN_F32 = 0,
@@ -85,6 +86,12 @@ typedef enum gdn_status {
  * An inactive step changes nothing and writes nothing: y and delta_log keep
  * whatever the caller's buffers held at those positions.
  *
+ * Optionally the call also captures the rest of the innovation tape that the
+ * module documentation ("Tape layout") lists next to delta_log: at every
+ * active step, k_log[b,t,hv,:] <- k[b,t,hk,:] (the keys expanded to value
+ * heads under gqa_map) and g_log[b,t,hv] <- g[b,t,hv], both as bit copies.
+ * gdn_replay then takes (delta_log, k_log, g_log) with no separate pass.
+ *
  * Arguments
  *   q, k, v, g, beta  inputs, io_dtype, layouts above.
  *   state_in          float32 [B,Hv,Dv,Dk].
@@ -94,6 +101,8 @@ typedef enum gdn_status {
  *                     (in place), but must not overlap it otherwise.
  *   delta_log         output tape, io_dtype [B,T,Hv,Dv], or NULL for the plain
  *                     forward step without a tape.
+ *   k_log             optional output, io_dtype [B,T,Hv,Dk], or NULL.
+ *   g_log             optional output, io_dtype [B,T,Hv], or NULL.
  *   B, T, Hk, Hv, Dk, Dv  sizes; Hk must divide Hv.  Dk in {32,64,128,192,256};
  *                     Dv a multiple of 16, at most 1024.
  *   io_dtype          gdn_dtype of every non-state tensor.
@@ -103,7 +112,7 @@ typedef enum gdn_status {
  */
 int gdn_record(const void* q, const void* k, const void* v, const void* g, const void* beta,
                const float* state_in, const uint32_t* mask,
-               void* y, float* state_out, void* delta_log,
+               void* y, float* state_out, void* delta_log, void* k_log, void* g_log,
                uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
                int io_dtype, int gqa_map, void* stream);
 

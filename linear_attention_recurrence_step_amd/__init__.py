@@ -78,13 +78,16 @@ def gdn_record(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tenso
                *, gqa_map: str = "block", y: Optional[torch.Tensor] = None,
                state_out: Optional[torch.Tensor] = None,
                delta_log: Optional[torch.Tensor] = None, write_tape: bool = True,
+               k_log: Optional[torch.Tensor] = None, g_log: Optional[torch.Tensor] = None,
                stream=None) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
     """Gated delta-rule step with tape capture; returns (y, state_out, delta_log).
 
     Outputs that are not given are allocated (uninitialised: the positions of
     inactive steps in y and delta_log are not written).  ``state_out`` may be
     ``state_in`` itself.  With ``write_tape=False`` and no ``delta_log`` the
-    plain forward step runs and the third result is None.
+    plain forward step runs and the third result is None.  ``k_log``
+    [B,T,Hv,Dk] and ``g_log`` [B,T,Hv], if given, receive the rest of the tape
+    (keys expanded to value heads, and gates) at active steps.
     """
     if gqa_map not in _MAPS:
         raise ValueError("gqa_map must be 'block' or 'tiled'")
@@ -111,9 +114,14 @@ def gdn_record(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tenso
         delta_log = torch.empty((B, T, Hv, Dv), dtype=io, device=dev)
     if delta_log is not None:
         _want("delta_log", delta_log, (B, T, Hv, Dv), io, dev)
+    if k_log is not None:
+        _want("k_log", k_log, (B, T, Hv, Dk), io, dev)
+    if g_log is not None:
+        _want("g_log", g_log, (B, T, Hv), io, dev)
     rc = lib.gdn_record(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
-                        _ptr(mask), _ptr(y), _ptr(state_out), _ptr(delta_log),
-                        B, T, Hk, Hv, Dk, Dv, _io_code(q), _MAPS[gqa_map], _stream(stream, dev))
+                        _ptr(mask), _ptr(y), _ptr(state_out), _ptr(delta_log), _ptr(k_log),
+                        _ptr(g_log), B, T, Hk, Hv, Dk, Dv, _io_code(q), _MAPS[gqa_map],
+                        _stream(stream, dev))
     _native.check("gdn_record", rc)
     return y, state_out, delta_log
 

@@ -24,7 +24,7 @@ STATUS = {
 }
 EXPORTS = ("gdn_record", "gdn_replay", "gqa_expand", "gdn_strerror", "gdn_last_error",
            "gdn_abi_version")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 def _load() -> ctypes.CDLL:
@@ -34,7 +34,7 @@ def _load() -> ctypes.CDLL:
             % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     vp, u32, i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int
-    lib.gdn_record.argtypes = [vp] * 10 + [u32] * 6 + [i32, i32, vp]
+    lib.gdn_record.argtypes = [vp] * 12 + [u32] * 6 + [i32, i32, vp]
     lib.gdn_record.restype = i32
     lib.gdn_replay.argtypes = [vp] * 6 + [u32] * 6 + [i32, vp]
     lib.gdn_replay.restype = i32

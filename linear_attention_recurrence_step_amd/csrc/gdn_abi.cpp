@@ -90,7 +90,7 @@ const char* gdn_strerror(int status) {
 
 int gdn_record(const void* q, const void* k, const void* v, const void* g, const void* beta,
                const float* state_in, const uint32_t* mask,
-               void* y, float* state_out, void* delta_log,
+               void* y, float* state_out, void* delta_log, void* k_log, void* g_log,
                uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
                int io_dtype, int gqa_map, void* stream) {
     static const char* kFn = "gdn_record";
@@ -108,40 +108,43 @@ int gdn_record(const void* q, const void* k, const void* v, const void* g, const
                     "(got Dk=%u, Dv=%u)", kFn, Dk, Dv);
 
     const uint64_t e = io_bytes(io_dtype);
-    uint64_t n_qk, n_v, n_g, n_s, n_m;
+    uint64_t n_qk, n_v, n_g, n_s, n_m, n_kl;
     if (!mul_u64(&n_qk, {B, T, Hk, Dk, e}) || !mul_u64(&n_v, {B, T, Hv, Dv, e}) ||
         !mul_u64(&n_g, {B, T, Hv, e}) || !mul_u64(&n_s, {B, Hv, Dv, Dk, 4}) || !mul_u64(&n_m, {B, T, 4}) ||
-        n_qk > kMaxBytes || n_v > kMaxBytes || n_s > kMaxBytes)
+        !mul_u64(&n_kl, {B, T, Hv, Dk, e}) ||
+        n_qk > kMaxBytes || n_v > kMaxBytes || n_s > kMaxBytes || n_kl > kMaxBytes)
         return fail(GDN_ERR_OVERFLOW, "%s: tensor sizes overflow", kFn);
 
-    gdn::RecordArgs a{q, k, v, g, beta, state_in, mask, y, state_out, delta_log,
+    gdn::RecordArgs a{q, k, v, g, beta, state_in, mask, y, state_out, delta_log, k_log, g_log,
                       B, T, Hk, Hv, Dk, Dv, io_dtype, gqa_map};
     const gdn::RowTiling til = gdn::record_tiling(a);
     uint64_t grid;
     if (!mul_u64(&grid, {B, Hv, Dv / static_cast<uint32_t>(til.rows())}) || grid > kMaxGrid)
         return fail(GDN_ERR_OVERFLOW, "%s: launch grid too large (B*Hv too large)", kFn);
 
-    const void* a16[] = {q, k, v, state_in, y, state_out, delta_log};
-    const char* a16n[] = {"q", "k", "v", "state_in", "y", "state_out", "delta_log"};
-    for (int i = 0; i < 7; ++i)
+    const void* a16[] = {q, k, v, state_in, y, state_out, delta_log, k_log};
+    const char* a16n[] = {"q", "k", "v", "state_in", "y", "state_out", "delta_log", "k_log"};
+    for (int i = 0; i < 8; ++i)
         if (a16[i] && !aligned(a16[i], 16))
             return fail(GDN_ERR_MISALIGNED, "%s: %s must be 16-byte aligned", kFn, a16n[i]);
     if (mask && !aligned(mask, 4)) return fail(GDN_ERR_MISALIGNED, "%s: mask must be 4-byte aligned", kFn);
-    if (!aligned(g, e) || !aligned(beta, e))
-        return fail(GDN_ERR_MISALIGNED, "%s: g and beta must be element-aligned", kFn);
+    if (!aligned(g, e) || !aligned(beta, e) || (g_log && !aligned(g_log, e)))
+        return fail(GDN_ERR_MISALIGNED, "%s: g, beta and g_log must be element-aligned", kFn);
 
     const Span ins[] = {{q, n_qk, "q"}, {k, n_qk, "k"}, {v, n_v, "v"}, {g, n_g, "g"},
                         {beta, n_g, "beta"}, {state_in, n_s, "state_in"}, {mask, mask ? n_m : 0, "mask"}};
     const Span outs[] = {{y, n_v, "y"}, {state_out, n_s, "state_out"},
-                         {delta_log, delta_log ? n_v : 0, "delta_log"}};
+                         {delta_log, delta_log ? n_v : 0, "delta_log"},
+                         {k_log, k_log ? n_kl : 0, "k_log"}, {g_log, g_log ? n_g : 0, "g_log"}};
+    constexpr int kOuts = 5;
     for (const Span& o : outs) {
         for (const Span& i : ins) {
             if (o.p == state_out && i.p == state_in && o.p == i.p) continue;   // exact in-place state
             if (overlaps(o, i)) return fail(GDN_ERR_ALIAS, "%s: %s overlaps %s", kFn, o.name, i.name);
         }
     }
-    for (int i = 0; i < 3; ++i)
-        for (int j = i + 1; j < 3; ++j)
+    for (int i = 0; i < kOuts; ++i)
+        for (int j = i + 1; j < kOuts; ++j)
             if (overlaps(outs[i], outs[j]))
                 return fail(GDN_ERR_ALIAS, "%s: %s overlaps %s", kFn, outs[i].name, outs[j].name);
 

@@ -129,6 +129,20 @@ __device__ __forceinline__ void io_store_vec(void* base, size_t idx, const float
     }
 }
 
+// Bit copy of N consecutive I/O elements (aligned to min(16, N * element size)).
+template <int IO, int N>
+__device__ __forceinline__ void io_copy_vec(const void* src, size_t si, void* dst, size_t di) {
+    constexpr int EB = IoTraits<IO>::kBytes;
+    constexpr int BYTES = N * EB;
+    constexpr int PIECE = BYTES < 16 ? BYTES : 16;
+    using V = typename RawVec<PIECE>::T;
+    const char* s = static_cast<const char*>(src) + si * EB;
+    char* d = static_cast<char*>(dst) + di * EB;
+#pragma unroll
+    for (int i = 0; i < BYTES / PIECE; ++i)
+        *reinterpret_cast<V*>(d + i * PIECE) = *reinterpret_cast<const V*>(s + i * PIECE);
+}
+
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -305,6 +319,24 @@ struct ChunkStager {
                 float f[P];
                 unpack(buf[j], f);
                 lds_store_vec<P>(lds + row * COLS + col, f);
+            }
+        }
+    }
+
+    // The raw (unconverted) pieces to global memory: row i of the block goes to
+    // dst + i * stride elements, for rows i < valid whose step flag is set
+    // (flags are read from LDS at flag4[4 * i]; NULL: every row).  A bit copy.
+    __device__ __forceinline__ void store_global(void* dst, size_t stride, int valid,
+                                                 const float* flag4) const {
+        char* base = static_cast<char*>(dst);
+#pragma unroll
+        for (int j = 0; j < PER_THREAD; ++j) {
+            const int p = static_cast<int>(threadIdx.x) + j * NT;
+            if (p < PIECES) {
+                const int row = p / PER_ROW;
+                const int col = (p - row * PER_ROW) * P;
+                if (row < valid && (flag4 == nullptr || __float_as_uint(flag4[4 * row]) != 0u))
+                    *reinterpret_cast<Raw*>(base + (static_cast<size_t>(row) * stride + col) * EB) = buf[j];
             }
         }
     }

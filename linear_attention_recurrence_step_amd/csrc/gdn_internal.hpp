@@ -12,6 +12,7 @@ struct RecordArgs {
     const void* q; const void* k; const void* v; const void* g; const void* beta;
     const float* state_in; const uint32_t* mask;
     void* y; float* state_out; void* delta_log;
+    void* k_log; void* g_log;             // optional tape capture
     uint32_t B, T, Hk, Hv, Dk, Dv;
     int io;       // IoType
     int map;      // 0 block, 1 tiled

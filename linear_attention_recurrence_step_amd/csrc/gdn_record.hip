@@ -29,6 +29,9 @@
 //    they leave as vector stores.
 //  * The mask row [B, T] is uniform over a workgroup, so inactive steps are a
 //    scalar branch around the whole step and write nothing.
+//  * Optional tape capture: the first row group of each head also copies the
+//    raw bits of the step's keys (expanded to the value head) and gate into
+//    k_log and g_log, so the replay's tape needs no separate pass.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -109,6 +112,7 @@ __global__ __launch_bounds__(NT) void gdn_record_kernel(
     const void* __restrict__ g, const void* __restrict__ beta,
     const float* state_in, const uint32_t* __restrict__ mask,
     void* __restrict__ y, float* state_out, void* __restrict__ delta_log,
+    void* __restrict__ k_log, void* __restrict__ g_log,
     uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dv, uint32_t row_blocks, int tiled)
 {
     constexpr int L = 16;                 // lanes per state row
@@ -138,6 +142,7 @@ __global__ __launch_bounds__(NT) void gdn_record_kernel(
     const uint32_t b = n / Hv;
     const uint32_t hv = n - b * Hv;
     const uint32_t hk = tiled ? hv % Hk : hv / (Hv / Hk);
+    const bool capture = row0 == 0;                           // first row group of the head
 
     for (uint32_t t = 0; t < T; ++t) {
         const size_t bt = static_cast<size_t>(b) * T + t;
@@ -148,6 +153,13 @@ __global__ __launch_bounds__(NT) void gdn_record_kernel(
         const float bt_beta = io_load1<IO>(beta, gi);
         const size_t kq = (bt * Hk + hk) * DK;
         const size_t vo = gi * Dv + row0;
+        if (capture) {                                        // tape capture: bit copies
+            if (k_log != nullptr)
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    io_copy_vec<IO, W>(k, kq + (c * L + lane) * W, k_log, gi * DK + (c * L + lane) * W);
+            if (g_log != nullptr && lane == 0) io_copy_vec<IO, 1>(g, gi, g_log, gi);
+        }
 
         float kk[E], qq[E], vv[RPT];
 #pragma unroll
@@ -240,6 +252,7 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
     const void* __restrict__ g, const void* __restrict__ beta,
     const float* state_in, const uint32_t* __restrict__ mask,
     void* __restrict__ y, float* state_out, void* __restrict__ delta_log,
+    void* __restrict__ k_log, void* __restrict__ g_log,
     uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dv, uint32_t row_blocks, int tiled,
     uint32_t chunk_rows)
 {
@@ -338,6 +351,15 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
             stm.store(reinterpret_cast<uint32_t*>(oyd + crow * R * 2), crow);   // flags for the flush
         }
         __syncthreads();
+        if (wrow0 == 0) {                                     // tape capture: bit copies
+            const size_t bt0 = static_cast<size_t>(b) * T + t0;
+            const float* flags = MASKED ? sc + 3 : nullptr;
+            if (k_log != nullptr)
+                stk.store_global(static_cast<char*>(k_log) + ((bt0 * Hv + hv) * DK) * EB,
+                                 static_cast<size_t>(Hv) * DK, valid, flags);
+            if (g_log != nullptr)
+                stg.store_global(static_cast<char*>(g_log) + (bt0 * Hv + hv) * EB, Hv, valid, flags);
+        }
         // k . q of each step: one 16-lane row group per step
         for (int tt = static_cast<int>(slot); tt < valid; tt += SLOTS) {
             float tk[E], tq[E];
@@ -395,7 +417,8 @@ hipError_t launch_cfg(const RecordArgs& a, hipStream_t stream) {
     if (a.T == 1) {
         hipLaunchKernelGGL((gdn_record_kernel<IO, DK, RPT, NT>), dim3(static_cast<uint32_t>(grid)),
                            dim3(NT), 0, stream, a.q, a.k, a.v, a.g, a.beta, a.state_in, a.mask, a.y,
-                           a.state_out, a.delta_log, a.T, a.Hk, a.Hv, a.Dv, row_blocks, a.map);
+                           a.state_out, a.delta_log, a.k_log, a.g_log, a.T, a.Hk, a.Hv, a.Dv,
+                           row_blocks, a.map);
         return hipGetLastError();
     }
     if constexpr (R <= kStagedMaxRows) {
@@ -405,7 +428,8 @@ hipError_t launch_cfg(const RecordArgs& a, hipStream_t stream) {
         auto go = [&](auto kernel) {
             hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(grid)), dim3(NT), lds, stream, a.q,
                                a.k, a.v, a.g, a.beta, a.state_in, a.mask, a.y, a.state_out,
-                               a.delta_log, a.T, a.Hk, a.Hv, a.Dv, row_blocks, a.map, crow);
+                               a.delta_log, a.k_log, a.g_log, a.T, a.Hk, a.Hv, a.Dv, row_blocks,
+                               a.map, crow);
         };
         const bool masked = a.mask != nullptr;
         if (short_tape) {

@@ -45,7 +45,7 @@ CHILD = r"""
 import ctypes, json, sys
 lib = ctypes.CDLL(sys.argv[1])
 vp, u32, i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int
-lib.gdn_record.argtypes = [vp] * 10 + [u32] * 6 + [i32, i32, vp]
+lib.gdn_record.argtypes = [vp] * 12 + [u32] * 6 + [i32, i32, vp]
 lib.gdn_replay.argtypes = [vp] * 6 + [u32] * 6 + [i32, vp]
 lib.gqa_expand.argtypes = [vp, vp] + [u32] * 4 + [i32, i32, vp]
 lib.gdn_strerror.restype = ctypes.c_char_p
@@ -71,13 +71,15 @@ def P(i, off=0):
     return BASE + i * SPAN + off
 
 
-# gdn_record(q, k, v, g, beta, state_in, mask, y, state_out, delta_log, B, T, Hk, Hv, Dk, Dv, io, map, stream)
+# gdn_record(q, k, v, g, beta, state_in, mask, y, state_out, delta_log, k_log, g_log,
+#            B, T, Hk, Hv, Dk, Dv, io, map, stream)
 def rec(**kw):
     a = dict(q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), s_in=P(5), mask=P(6), y=P(7), s_out=P(8),
-             dl=P(9), B=2, T=3, Hk=2, Hv=4, Dk=128, Dv=128, io=2, map=0)
+             dl=P(9), kl=P(10), gl=P(11), B=2, T=3, Hk=2, Hv=4, Dk=128, Dv=128, io=2, map=0)
     a.update(kw)
     return [a["q"], a["k"], a["v"], a["g"], a["beta"], a["s_in"], a["mask"], a["y"], a["s_out"],
-            a["dl"], a["B"], a["T"], a["Hk"], a["Hv"], a["Dk"], a["Dv"], a["io"], a["map"], None]
+            a["dl"], a["kl"], a["gl"], a["B"], a["T"], a["Hk"], a["Hv"], a["Dk"], a["Dv"], a["io"],
+            a["map"], None]
 
 
 # gdn_replay(delta_log, k_log, g_log, state_in, mask, state_out, B, T_log, Hv, Dk, Dv, accepted, io, stream)
@@ -121,6 +123,12 @@ CASES = [
     ("rec_delta_overlaps_y", "gdn_record", rec(dl=P(7, 64)), ALIAS),
     ("rec_state_out_over_q", "gdn_record", rec(s_out=P(0)), ALIAS),
     ("rec_y_over_mask", "gdn_record", rec(y=P(6)), ALIAS),
+    ("rec_k_log_over_k", "gdn_record", rec(kl=P(1, 512)), ALIAS),
+    ("rec_g_log_over_delta", "gdn_record", rec(gl=P(9, 2)), ALIAS),
+    ("rec_k_log_over_y", "gdn_record", rec(kl=P(7)), ALIAS),
+    ("rec_misaligned_k_log", "gdn_record", rec(kl=P(10, 8)), ALIGN),
+    ("rec_misaligned_g_log", "gdn_record", rec(gl=P(11, 1)), ALIGN),
+    ("rec_k_log_bytes_overflow", "gdn_record", rec(B=1 << 20, T=1 << 20, Hk=1, Hv=1 << 12), OVER),
     ("rep_bad_dtype", "gdn_replay", rep(io=-1), ENUM),
     ("rep_null_k_log", "gdn_replay", rep(kl=None), NULL),
     ("rep_zero_T", "gdn_replay", rep(T=0), ZERO),

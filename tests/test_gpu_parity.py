@@ -324,6 +324,103 @@ def test_repeated_runs_are_bitwise_identical():
     assert all(torch.equal(x, z) for x, z in zip(a, b))
 
 
+# ---------------------------------------------------------------- tape capture
+
+K_SENTINEL = 5.5        # exact in every I/O dtype
+G_SENTINEL = -0.625
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    """Raw element bits of a tensor as a numpy integer array."""
+    t = t.detach().cpu().contiguous()
+    return t.view(torch.int32 if t.element_size() == 4 else torch.int16).numpy()
+
+
+def _record_capture(inp, gqa_map, want_k=True, want_g=True):
+    d = to_dev(inp)
+    B, T, Hk, Dk = d["k"].shape
+    Hv = d["v"].shape[2]
+    io = d["q"].dtype
+    y = torch.full(d["v"].shape, Y_SENTINEL, dtype=io, device=dev())
+    dl = torch.full(d["v"].shape, D_SENTINEL, dtype=io, device=dev())
+    kl = torch.full((B, T, Hv, Dk), K_SENTINEL, dtype=io, device=dev()) if want_k else None
+    gl = torch.full((B, T, Hv), G_SENTINEL, dtype=io, device=dev()) if want_g else None
+    y, s, dl = gdn.gdn_record(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"], d["mask"],
+                              gqa_map=gqa_map, y=y, delta_log=dl, k_log=kl, g_log=gl)
+    torch.cuda.synchronize()
+    return y, s, dl, kl, gl
+
+
+CAPTURE = [
+    # B, T, Hk, Hv, Dk, Dv, io, map, mask
+    (4, 1, 2, 4, 128, 128, "bf16", "block", "bernoulli"),     # single step
+    (3, 1, 3, 6, 64, 48, "f32", "tiled", "none"),
+    (2, 3, 2, 4, 128, 128, "bf16", "tiled", "bernoulli"),     # short tape
+    (2, 5, 1, 3, 256, 64, "f16", "block", "none"),
+    (2, 37, 2, 4, 128, 64, "bf16", "block", "trailing"),      # several chunks, ragged last one
+    (1, 20, 3, 3, 192, 32, "f32", "tiled", "bernoulli"),
+    (2, 9, 4, 8, 32, 16, "bf16", "tiled", "none"),
+    (2, 4, 2, 4, 64, 64, "bf16", "block", "zeros"),
+]
+
+
+@pytest.mark.parametrize("case", CAPTURE, ids=lambda c: "B%d_T%d_Hk%d_Hv%d_Dk%d_Dv%d_%s_%s_%s" % c)
+def test_record_captures_expanded_keys_and_gates(case):
+    B, T, Hk, Hv, Dk, Dv, io, gqa_map, mask = case
+    inp = gi.record_inputs(B, T, Hk, Hv, Dk, Dv, io, seed=81 + T, mask=mask)
+    note("record with capture %s" % (case,))
+    y, s, dl, kl, gl = _record_capture(inp, gqa_map)
+    # capturing changes none of the other outputs
+    y0, s0, dl0 = _record_gpu(inp, gqa_map)
+    assert torch.equal(y, y0) and torch.equal(s, s0) and torch.equal(dl, dl0)
+    act = step_mask(inp["mask"], B, T)
+    ref_k = oracle.gqa_expand(_bits(inp["k"]).reshape(B * T, Hk, Dk), Hv, gqa_map)
+    got_k = _bits(kl).reshape(B * T, Hv, Dk)
+    a = act.reshape(B * T)
+    assert np.array_equal(got_k[a], ref_k[a]), "k_log differs from the expanded keys"
+    assert np.all(f64(kl).reshape(B * T, Hv, Dk)[~a] == K_SENTINEL), "k_log written at an inactive step"
+    got_g, ref_g = _bits(gl), _bits(inp["g"])
+    assert np.array_equal(got_g[act], ref_g[act]), "g_log differs from g"
+    assert np.all(f64(gl)[~act] == G_SENTINEL), "g_log written at an inactive step"
+    # the captured tape replays exactly like one expanded by a separate pass
+    d = to_dev(inp)
+    k_exp = gdn.gqa_expand(d["k"], Hv, gqa_map)
+    for acc in sorted({0, 1, T}):
+        note("replay of a captured tape, accepted=%d" % acc)
+        r1 = gdn.gdn_replay(dl, kl, gl, d["state_in"], d["mask"], acc)
+        r2 = gdn.gdn_replay(dl, k_exp, d["g"], d["state_in"], d["mask"], acc)
+        torch.cuda.synchronize()
+        assert torch.equal(r1, r2), acc
+    if io == "f32" and T < 16:   # longer folds keep a running scale: equal within rounding only
+        assert torch.equal(r1, s), "fp32 replay of the whole captured tape differs from the record"
+
+
+@pytest.mark.parametrize("want_k,want_g", [(True, False), (False, True)])
+def test_record_captures_one_log_alone(want_k, want_g):
+    inp = gi.record_inputs(2, 6, 2, 4, 128, 64, "bf16", seed=91, mask="bernoulli")
+    note("record capturing k_log=%s g_log=%s" % (want_k, want_g))
+    y, s, dl, kl, gl = _record_capture(inp, "tiled", want_k, want_g)
+    ref = _record_capture(inp, "tiled")
+    assert torch.equal(y, ref[0]) and torch.equal(s, ref[1]) and torch.equal(dl, ref[2])
+    if want_k:
+        assert gl is None and torch.equal(kl, ref[3])
+    else:
+        assert kl is None and torch.equal(gl, ref[4])
+
+
+def test_capture_identical_under_every_tiling(monkeypatch):
+    inp = gi.record_inputs(2, 11, 2, 4, 128, 128, "bf16", seed=93, mask="bernoulli")
+    ref = None
+    for til in ("8,256", "4,256", "2,256", "1,256", "1,64"):
+        monkeypatch.setenv("GDN_RECORD_TILING", til)
+        note("capture under tiling %s" % til)
+        cur = [t.cpu() for t in _record_capture(inp, "block")]
+        if ref is None:
+            ref = cur
+        else:
+            assert all(torch.equal(a, b) for a, b in zip(ref, cur)), til
+
+
 # ---------------------------------------------------------------- gqa_expand
 
 EXPAND = [
