@@ -1,6 +1,7 @@
 """Throughput of the Gated DeltaNet record / replay / GQA-expand path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--capture separate|fused]
 
 One step is one pass of the whole path over one batch of seeded synthetic
 input already resident in HBM:
@@ -11,6 +12,9 @@ input already resident in HBM:
     chunk_prefill:    gqa_expand of fp32 q and k (tiled map) + gdn_record over 4096 steps
     long_tape_replay: gdn_replay of a 64-step fp16 tape for accepted in {0,1,16,63,64}
     tiny:             gdn_record + gdn_replay
+
+With --capture fused (decode workloads) the record writes k_log and g_log
+itself and the separate gqa_expand launch goes away.
 
 `value` is effective HBM bandwidth: the algorithmic bytes of the step (what
 the method must read and write, defined below) divided by the measured step
@@ -23,6 +27,9 @@ A = taken tape positions, a' = min(accepted, T)):
     record  8*B*Hv*Dv*Dk + 4*B*T [mask] + U*e*(2*Hk*Dk + 3*Hv*Dv + 2*Hv)
     replay  8*B*Hv*Dv*Dk + 4*B*a' [mask] + A*e*Hv*(Dv + Dk + 1)
     expand  e*seq*K*(Hg + H)
+    capture U*e*Hv*(Dk + 1) on top of the record (k_log and g_log writes)
+The replay's "touched" bytes count every position below a' (the select reads
+masked positions too): A is replaced by B*a'.
 """
 from __future__ import annotations
 
@@ -62,6 +69,10 @@ def expand_bytes(seq, hg, h, k, e):
     return e * seq * k * (hg + h)
 
 
+def capture_bytes(Hv, Dk, e, active_steps):
+    return active_steps * e * Hv * (Dk + 1)
+
+
 def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
@@ -98,13 +109,16 @@ def _active(mask, B, T, upto=None):
 class Step:
     """Device buffers and launch sequence of one step of a workload."""
 
-    def __init__(self, name, dev, seed=0):
+    def __init__(self, name, dev, seed=0, capture="separate"):
         import torch
         import gdn_inputs as gi
         import linear_attention_recurrence_step_amd as gdn
         self.gdn = gdn
         self.name = name
         self.w = w = gi.WORKLOADS[name]
+        self.fused = capture == "fused"
+        if self.fused and name in ("long_tape_replay", "chunk_prefill"):
+            raise SystemExit("--capture fused applies to workloads with a record and a replay")
         self.e = 4 if w.io == "f32" else 2
         self.kernels = []            # (label, kernel, algorithmic bytes, head-steps)
         T = w.T
@@ -113,14 +127,18 @@ class Step:
             self.cpu = tape
             self.d = {k: (v.to(dev) if v is not None else None) for k, v in tape.items()}
             self.out = torch.empty_like(self.d["state_in"])
+            self.touched = {}
             for a in w.accepted:
                 taken = _active(tape["mask"], w.B, T, a)
                 self.kernels.append(("replay[a=%d]" % a, "gdn_replay",
                                      replay_bytes(w.B, T, w.Hv, w.Dk, w.Dv, self.e, a, taken, True),
                                      taken * w.Hv))
+                self.touched["replay[a=%d]" % a] = replay_bytes(w.B, T, w.Hv, w.Dk, w.Dv, self.e, a,
+                                                                w.B * min(a, T), True)
             return
         inp = gi.workload_inputs(name, seed)
         self.cpu = inp
+        self.touched = {}
         self.d = d = {k: (v.to(dev) if v is not None else None) for k, v in inp.items()}
         io = d["q"].dtype
         self.y = torch.empty(d["v"].shape, dtype=io, device=dev)
@@ -140,9 +158,16 @@ class Step:
                                      expand_bytes(w.B * T, w.Hk, w.Hv, w.Dk, eb), 0))
         else:
             self.k_log = torch.empty((w.B, T, w.Hv, w.Dk), dtype=io, device=dev)
-            self.kernels.append(("expand_k", "gqa_expand", expand_bytes(w.B * T, w.Hk, w.Hv, w.Dk, self.e), 0))
-        self.kernels.append(("record", "gdn_record",
-                             record_bytes(w.B, T, w.Hk, w.Hv, w.Dk, w.Dv, self.e, U, has_mask), U * w.Hv))
+            self.g_log = torch.empty((w.B, T, w.Hv), dtype=io, device=dev) if self.fused else None
+            if not self.fused:
+                self.kernels.append(("expand_k", "gqa_expand",
+                                     expand_bytes(w.B * T, w.Hk, w.Hv, w.Dk, self.e), 0))
+        rb = record_bytes(w.B, T, w.Hk, w.Hv, w.Dk, w.Dv, self.e, U, has_mask)
+        if self.fused:
+            self.kernels.append(("record+capture", "gdn_record",
+                                 rb + capture_bytes(w.Hv, w.Dk, self.e, U), U * w.Hv))
+        else:
+            self.kernels.append(("record", "gdn_record", rb, U * w.Hv))
         if name != "chunk_prefill":
             if name == "spec_decode":
                 import numpy as np
@@ -153,6 +178,8 @@ class Step:
             self.kernels.append(("replay", "gdn_replay",
                                  replay_bytes(w.B, T, w.Hv, w.Dk, w.Dv, self.e, self.accepted, taken, has_mask),
                                  taken * w.Hv))
+            self.touched = {"replay": replay_bytes(w.B, T, w.Hv, w.Dk, w.Dv, self.e, self.accepted,
+                                                   w.B * min(self.accepted, T), has_mask)}
 
     def launches(self):
         """Callables, one per kernel launch, in step order."""
@@ -165,13 +192,20 @@ class Step:
         if self.name == "chunk_prefill":
             for i in range(2):
                 out.append(lambda i=i: gdn.gqa_expand(self.src[i], w.Hv, w.gqa_map, dst=self.dst[i]))
-        else:
+        elif not self.fused:
             out.append(lambda: gdn.gqa_expand(d["k"], w.Hv, w.gqa_map, dst=self.k_log))
-        out.append(lambda: gdn.gdn_record(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
-                                          d["mask"], gqa_map=w.gqa_map, y=self.y,
-                                          state_out=self.s_rec, delta_log=self.dl))
+        if self.fused:
+            out.append(lambda: gdn.gdn_record(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
+                                              d["mask"], gqa_map=w.gqa_map, y=self.y,
+                                              state_out=self.s_rec, delta_log=self.dl,
+                                              k_log=self.k_log, g_log=self.g_log))
+        else:
+            out.append(lambda: gdn.gdn_record(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
+                                              d["mask"], gqa_map=w.gqa_map, y=self.y,
+                                              state_out=self.s_rec, delta_log=self.dl))
         if self.name != "chunk_prefill":
-            out.append(lambda: gdn.gdn_replay(self.dl, self.k_log, d["g"], d["state_in"], d["mask"],
+            g_log = self.g_log if self.fused else d["g"]
+            out.append(lambda: gdn.gdn_replay(self.dl, self.k_log, g_log, d["state_in"], d["mask"],
                                               self.accepted, state_out=self.s_rep))
         return out
 
@@ -246,12 +280,33 @@ def cpu_baseline(name: str, budget_s: float):
             if time.perf_counter() - t0 >= budget_s:
                 break
     dt = time.perf_counter() - t0
+    # one thread over one unit, for the per-core figure
+    one_bytes, t1 = 0, time.perf_counter()
+    while True:
+        one_bytes += work(0, 1)
+        if time.perf_counter() - t1 >= budget_s / 4:
+            break
+    dt1 = time.perf_counter() - t1
     unit_name = "value heads" if name == "chunk_prefill" else "batch rows"
     return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": min(cores, len(chunks)),
             "kind": "oracle",
             "sample": "%d of %d %s of %s, %d pass(es), %.1f s, threads over %s"
                       % (units, w.Hv if name == "chunk_prefill" else w.B, unit_name, name, passes, dt,
-                         unit_name)}
+                         unit_name),
+            "single_thread_value": round(one_bytes / dt1 / 1e9, 4),
+            "cpu_model": _cpu_model(),
+            "label": "CPU baseline, not the target"}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ------------------------------------------------------- counter calibration
@@ -281,6 +336,53 @@ def calibrate_copy(dev, launches: int) -> None:
                       "GB/s": round(2 * COPY_BYTES / dt / 1e9, 1)}), flush=True)
 
 
+def copy_bandwidth(dev, launches: int = 20) -> float:
+    """GB/s of a plain 512 MiB device copy (gqa_expand with one head each
+    side), timed with HIP events: the practical HBM peak beside the published one."""
+    import torch
+    import linear_attention_recurrence_step_amd as gdn
+    k = 32768
+    seq = COPY_BYTES // (4 * k)
+    src = torch.randn(seq, 1, k, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        gdn.gqa_expand(src, 1, "tiled", dst=dst)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(launches):
+        gdn.gqa_expand(src, 1, "tiled", dst=dst)
+    b.record()
+    torch.cuda.synchronize()
+    return 2 * COPY_BYTES * launches / (a.elapsed_time(b) * 1e-3) / 1e9
+
+
+def reported_hbm_figure():
+    """Memory bus width (bits) and clock (kHz) as the HIP runtime reports
+    them, and clock x width / 8 in GB/s (None if unavailable).  HBM3E moves
+    several bits per pin per reported clock, so this product is a fraction of
+    the published peak, not a peak itself."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return None
+    vals = []
+    # hipDeviceAttributeMemoryBusWidth = 59, hipDeviceAttributeMemoryClockRate = 60 (ROCm 7 headers)
+    for attr in (59, 60):
+        v = ctypes.c_int()
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, 0) != 0:
+            return None
+        vals.append(v.value)
+    return {"bus_width_bits": vals[0], "memory_clock_khz": vals[1],
+            "clock_x_width_GBps": round(vals[1] * 1e3 * vals[0] / 8 / 1e9, 1),
+            "published_GBps": HBM_PEAK_GBPS}
+
+
+def _pct(xs, p):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, int(round(p / 100.0 * (len(xs) - 1))))]
+
+
 # ----------------------------------------------------------------------- main
 
 def main():
@@ -295,6 +397,11 @@ def main():
     ap.add_argument("--scrub", choices=("auto", "on", "off"), default="auto",
                     help="overwrite a 1 GiB buffer before every timed step so no input is left in "
                          "the L2 / 256 MB MALL (auto: on unless the step moves >= 1 GB anyway)")
+    ap.add_argument("--capture", choices=("separate", "fused"), default="separate",
+                    help="separate: k_log by a gqa_expand launch and g_log = g; fused: the record "
+                         "writes k_log and g_log itself")
+    ap.add_argument("--no-peak-probe", action="store_true",
+                    help="skip the 512 MiB copy that measures the practical HBM peak")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain copy of known size (gqa_expand with hg == h) for "
                          "scaling the HBM byte counters, and exit")
@@ -310,7 +417,7 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(dev, args.steps)
         return
-    step = Step(args.workload, dev, args.seed)
+    step = Step(args.workload, dev, args.seed, args.capture)
     launches = step.launches()
     w = step.w
 
@@ -341,21 +448,24 @@ def main():
         # the wall clock includes the scrubs: time the steps by their events instead
         elapsed = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)) * 1e-3
 
-    per_kernel_ms = [0.0] * len(launches)
-    for s in range(args.steps):
-        for i in range(len(launches)):
-            per_kernel_ms[i] += ev[s][i].elapsed_time(ev[s][i + 1])
-    per_kernel_ms = [m / args.steps for m in per_kernel_ms]
+    samples = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]
+               for i in range(len(launches))]
+    per_kernel_ms = [sum(x) / args.steps for x in samples]
 
     head_steps = sum(k[3] for k in step.kernels)
     ms_per_step = elapsed * 1e3 / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     kernels = []
-    for (label, kern, nbytes, hs), ms in zip(step.kernels, per_kernel_ms):
-        kernels.append({"name": label, "kernel": kern, "us": round(ms * 1e3, 2),
-                        "algorithmic_bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                        "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)})
+    for (label, kern, nbytes, hs), ms, xs in zip(step.kernels, per_kernel_ms, samples):
+        ent = {"name": label, "kernel": kern, "us": round(ms * 1e3, 2),
+               "us_p10_p50_p90": [round(_pct(xs, p) * 1e3, 2) for p in (10, 50, 90)],
+               "algorithmic_bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+               "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        if label in step.touched:
+            ent["touched_bytes"] = step.touched[label]
+            ent["touched_GB/s"] = round(step.touched[label] / (ms * 1e-3) / 1e9, 1)
+        kernels.append(ent)
     dom = max(range(len(kernels)), key=lambda i: per_kernel_ms[i])
     dk = kernels[dom]
     roofline = {"bound": "hbm", "achieved": dk["GB/s"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -372,7 +482,7 @@ def main():
         "cache_scrub": scrub,
         "config": {"workload": args.workload, "B": w.B, "T": w.T, "Hk": w.Hk, "Hv": w.Hv,
                    "Dk": w.Dk, "Dv": w.Dv, "io_dtype": w.io, "state_dtype": "f32",
-                   "gqa_map": w.gqa_map, "mask": w.mask,
+                   "gqa_map": w.gqa_map, "mask": w.mask, "capture": args.capture,
                    "step": " + ".join(k[0] for k in step.kernels)},
         "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
         "head_steps_per_s": round(head_steps / (ms_per_step * 1e-3), 1),
@@ -381,6 +491,12 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
     }
+    if args.workload == "chunk_prefill":
+        out["tokens_per_s"] = round(w.B * w.T / (ms_per_step * 1e-3), 1)
+    if not args.no_peak_probe:
+        out["practical_peak"] = {"copy_GB/s": round(copy_bandwidth(dev), 1),
+                                 "copy_bytes_each_way": COPY_BYTES,
+                                 "reported": reported_hbm_figure()}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_budget)
     print(json.dumps(out), flush=True)
