@@ -48,7 +48,7 @@ METRIC = "GDN record+replay effective HBM GB/s (% of peak) and head-steps/sec"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "gdn_record": ["gdn_record.hip", "gdn_device.hpp"],
-    "gdn_replay": ["gdn_replay.hip", "gdn_device.hpp"],
+    "gdn_replay": ["gdn_replay.hip", "gdn_replay_mfma.hip", "gdn_device.hpp"],
     "gqa_expand": ["gqa_expand.hip", "gdn_device.hpp"],
 }
 

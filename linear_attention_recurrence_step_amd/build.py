@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_abi.cpp", "gdn_record.hip", "gdn_replay.hip", "gqa_expand.hip"]
+SOURCES = ["gdn_abi.cpp", "gdn_record.hip", "gdn_replay.hip", "gdn_replay_mfma.hip", "gqa_expand.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -29,9 +29,15 @@ FLAGS = [
 ]
 
 
+# Per-source flags.  The matrix-core replay keeps its MFMA accumulators in
+# ordinary VGPRs (gfx950 allows either file): it also scales them with VALU
+# instructions, and one register file instead of two doubles its occupancy.
+SOURCE_FLAGS = {"gdn_replay_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, extra) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + SOURCE_FLAGS.get(src, []) + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed on %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

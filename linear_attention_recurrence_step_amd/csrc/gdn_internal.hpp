@@ -49,6 +49,12 @@ RowTiling replay_tiling(const ReplayArgs& a);
 
 hipError_t launch_record(const RecordArgs& a, hipStream_t stream);
 hipError_t launch_replay(const ReplayArgs& a, hipStream_t stream);
+
+// Folds of at least this many positions of a 16-bit tape run as matrix
+// products on the matrix cores (gdn_replay_mfma.hip).
+inline constexpr uint32_t kReplayMfmaFromSteps = 16;
+bool replay_mfma_applies(const ReplayArgs& a);
+hipError_t launch_replay_mfma(const ReplayArgs& a, hipStream_t stream);
 hipError_t launch_expand(const ExpandArgs& a, hipStream_t stream);
 
 }  // namespace gdn

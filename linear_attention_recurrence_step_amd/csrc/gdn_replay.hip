@@ -397,6 +397,7 @@ RowTiling replay_tiling(const ReplayArgs& a) {
 }
 
 hipError_t launch_replay(const ReplayArgs& a, hipStream_t stream) {
+    if (replay_mfma_applies(a)) return launch_replay_mfma(a, stream);
     const RowTiling t = replay_tiling(a);
     switch (a.io) {
         case kF32: return launch_io<kF32>(a, t, stream);

@@ -204,6 +204,38 @@ def test_replay_long_fold_with_extreme_gates(io):
         _check_replay(tape, a, "extreme gates")
 
 
+MFMA_REPLAY = [
+    # B, T_log, Hv, Dk, Dv, io, mask, accepted values (Dv a multiple of 64 takes the
+    # matrix cores; the Dv = 48 case checks that other shapes keep the VALU fold)
+    (2, 40, 3, 128, 128, "f16", "bernoulli", (16, 17, 33, 40)),
+    (3, 20, 2, 64, 64, "bf16", "none", (16, 20)),
+    (1, 35, 2, 32, 64, "f16", "trailing", (35,)),
+    (2, 18, 2, 192, 64, "bf16", "bernoulli", (18,)),
+    (1, 24, 1, 256, 128, "f16", "none", (24,)),
+    (2, 64, 4, 128, 192, "bf16", "bernoulli", (64,)),
+    (2, 20, 2, 64, 48, "f16", "bernoulli", (20,)),
+]
+
+
+@pytest.mark.parametrize("case", MFMA_REPLAY, ids=lambda c: "B%d_T%d_Hv%d_Dk%d_Dv%d_%s_%s" % c[:7])
+def test_replay_long_fold_on_matrix_cores(case, monkeypatch):
+    """Folds of 16+ positions of a 16-bit tape run as MFMA products over
+    chunks of positions; against the oracle at the I/O tolerance, untaken
+    slots NaN-poisoned, and against the VALU fold of the same tape."""
+    B, T, Hv, Dk, Dv, io, mask, accepted = case
+    tape = gi.tape_inputs(B, T, Hv, Dk, Dv, io, seed=111 + Dk + T, mask=mask)
+    for a in accepted:
+        pt = gi.poison_untaken(tape, a)
+        monkeypatch.delenv("GDN_REPLAY_MFMA", raising=False)
+        s_mfma = _check_replay(pt, a, "matrix-core fold %s" % (case[:7],))
+        monkeypatch.setenv("GDN_REPLAY_MFMA", "0")
+        note("VALU fold of the same tape, accepted=%d" % a)
+        d = to_dev(pt)
+        s_valu = gdn.gdn_replay(d["delta_log"], d["k_log"], d["g_log"], d["state_in"], d["mask"], a)
+        torch.cuda.synchronize()
+        assert_close(s_mfma, f64(s_valu), torch.float32, "matrix-core vs VALU fold")
+
+
 @pytest.mark.parametrize("case", [(3, 5, 2, 32, 16, "f32"), (2, 6, 3, 64, 48, "bf16"),
                                   (1, 4, 4, 192, 128, "f16"), (2, 3, 2, 256, 32, "bf16")],
                          ids=lambda c: "B%d_T%d_Hv%d_Dk%d_Dv%d_%s" % c)
