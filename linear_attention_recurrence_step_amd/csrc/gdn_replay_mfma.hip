@@ -61,6 +61,18 @@ __device__ __forceinline__ float half_to_f32(uint32_t bits) {
     return IO == kF16 ? f16_bits_to_f32(bits) : bf16_bits_to_f32(bits);
 }
 
+// Raw bits of one 16-bit element, widened later (so the load is not waited
+// for where it is issued).
+template <int IO>
+__device__ __forceinline__ uint32_t io_load_bits(const void* base, size_t idx) {
+    return *reinterpret_cast<const uint16_t*>(static_cast<const char*>(base) + idx * 2);
+}
+
+template <int IO>
+__device__ __forceinline__ float io_bits_to_f32(uint32_t bits) {
+    return IO == kF16 ? f16_bits_to_f32(bits) : bf16_bits_to_f32(bits);
+}
+
 template <int IO>
 __device__ __forceinline__ uint32_t f32_to_half(float f) {
     return IO == kF16 ? f32_to_f16_bits(f) : f32_to_bf16_bits(f);
@@ -84,8 +96,8 @@ struct MfmaLds {
     static constexpr int BYTES = STATE > CHUNK ? STATE : CHUNK;   // the two are never live together
 };
 
-template <int IO, int DK, int NW>
-__global__ __launch_bounds__(64 * NW, (DK <= 128 ? 16 : 8) / NW) void gdn_replay_mfma_kernel(
+template <int IO, int DK, int NW, bool MASKED>
+__global__ __launch_bounds__(64 * NW, DK <= 128 ? 4 : 2) void gdn_replay_mfma_kernel(
     const void* __restrict__ delta_log, const void* __restrict__ k_log,
     const void* __restrict__ g_log, const float* state_in,
     const uint32_t* __restrict__ mask, float* state_out,
@@ -129,64 +141,56 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 16 : 8) / NW) void gdn_replay
     };
     auto frag_lds = [&](int i) { return sbuf + lr * Lds::SROW + (4 * i + lg) * 16; };
 
-    f32x4 sreg[NI];
-#pragma unroll
-    for (int u = 0; u < NI; ++u)
-        sreg[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sin + (l + 64 * u) * 4));
-
     // Registers of the chunk in flight: job u of this thread covers positions
     // 2q, 2q+1 and 8-element group cg, with q = job / groups and cg = job mod
     // groups, so each row is read contiguously.  Every slot below `steps` is
     // loaded; untaken ones are zeroed when written to LDS.
     u32x4 kr[KPT][2], dr[DPT][2];
-    uint32_t kmw[KPT][2], dmw[DPT][2], gw[2];
+    uint32_t kmw[KPT][2], dmw[DPT][2], gmw, graw;
     const char* kb = static_cast<const char*>(k_log);
     const char* db = static_cast<const char*>(delta_log);
-    auto slot_mask = [&](int tt, int valid, uint32_t t0) -> uint32_t {
-        return tt < valid ? (mask != nullptr ? mask[static_cast<size_t>(b) * T_log + t0 + tt] : 1u) : 0u;
+    // Every load below is unconditional, from an index clamped into the chunk
+    // (straight-line code keeps the compiler's wait counts exact, so waiting
+    // for one chunk never waits for loads issued after it); what a clamped
+    // load brought in is discarded when the chunk is written to LDS.
+    auto mask_at = [&](uint32_t t) -> uint32_t {
+        if constexpr (MASKED) return mask[static_cast<size_t>(b) * T_log + t];
+        else return 1u;
     };
     auto load_chunk = [&](uint32_t t0) {
-        const int valid = static_cast<int>(steps - t0 < kPos ? steps - t0 : kPos);
+        const int last = static_cast<int>(steps - t0 < kPos ? steps - t0 : kPos) - 1;
 #pragma unroll
         for (int u = 0; u < KPT; ++u) {
-            const int jb = static_cast<int>(tid) + u * NT;
+            int jb = static_cast<int>(tid) + u * NT;
+            jb = jb < kPairs * KG ? jb : kPairs * KG - 1;
             const int q = jb / KG, cg = jb - q * KG;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int tt = 2 * q + h;
-                kr[u][h] = u32x4{0u, 0u, 0u, 0u};
-                kmw[u][h] = 0u;
-                if (jb < kPairs * KG && tt < valid) {
-                    const size_t bt = static_cast<size_t>(b) * T_log + t0 + tt;
-                    kr[u][h] = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4*>(kb + ((bt * Hv + hv) * DK + cg * 8) * 2));
-                    kmw[u][h] = slot_mask(tt, valid, t0);
-                }
+                const int tt = 2 * q + h < last ? 2 * q + h : last;
+                const size_t bt = static_cast<size_t>(b) * T_log + t0 + tt;
+                kr[u][h] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(kb + ((bt * Hv + hv) * DK + cg * 8) * 2));
+                kmw[u][h] = mask_at(t0 + tt);
             }
         }
 #pragma unroll
         for (int u = 0; u < DPT; ++u) {
-            const int jb = static_cast<int>(tid) + u * NT;
+            int jb = static_cast<int>(tid) + u * NT;
+            jb = jb < kPairs * DG ? jb : kPairs * DG - 1;
             const int q = jb / DG, dg = jb - q * DG;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int tt = 2 * q + h;
-                dr[u][h] = u32x4{0u, 0u, 0u, 0u};
-                dmw[u][h] = 0u;
-                if (jb < kPairs * DG && tt < valid) {
-                    const size_t bt = static_cast<size_t>(b) * T_log + t0 + tt;
-                    dr[u][h] = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4*>(db + ((bt * Hv + hv) * Dv + dv0 + dg * 8) * 2));
-                    dmw[u][h] = slot_mask(tt, valid, t0);
-                }
+                const int tt = 2 * q + h < last ? 2 * q + h : last;
+                const size_t bt = static_cast<size_t>(b) * T_log + t0 + tt;
+                dr[u][h] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(db + ((bt * Hv + hv) * Dv + dv0 + dg * 8) * 2));
+                dmw[u][h] = mask_at(t0 + tt);
             }
         }
-        if (tid < kPos) {                                     // gate and flag of position tid
-            const int tt = static_cast<int>(tid);
-            const uint32_t m = slot_mask(tt, valid, t0);
-            gw[0] = m;
-            gw[1] = m != 0u ? __builtin_bit_cast(uint32_t, io_load1<IO>(
-                                  g_log, (static_cast<size_t>(b) * T_log + t0 + tt) * Hv + hv)) : 0u;
+        {                                                     // gate and mask of position tid (wave 0)
+            const int tt = static_cast<int>(l) < last ? static_cast<int>(l) : last;
+            gmw = mask_at(t0 + tt);
+            graw = io_load_bits<IO>(g_log, (static_cast<size_t>(b) * T_log + t0 + tt) * Hv + hv);
         }
     };
     // Positions 2q, 2q+1 of element e of two 8-element rows, packed in one dword.
@@ -196,24 +200,32 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 16 : 8) / NW) void gdn_replay
         return a | (c << 16);
     };
 
-    if (steps > 0) load_chunk(0);
-    wait_vector_memory();                                     // state and chunk 0 are in
-
-    // State: row layout -> LDS -> accumulator layout.  acc[i] is the 16x16
-    // tile of S^T for columns 16i.. and the wave's 16 rows; lane l holds
+    // The fold is accumulated apart from the state, U = sum over chunks of
+    // (later gammas) * (chunk's w-weighted products), starting from zero, and
+    // S = Gamma * S0 + U at the end (Gamma = product of every taken gate).  So
+    // the state loads, issued after the first chunk's, stay in flight while
+    // the tape is folded.  acc[i] is the 16x16 tile of U^T for columns 16i..
+    // and the wave's 16 rows; lane l holds columns 16i + 4*lg + 0..3 of row lr.
+    // The fold is accumulated apart from the state, U = sum over chunks of
+    // (later gammas) * (chunk's w-weighted products), starting from zero, and
+    // S = Gamma * S0 + U at the end (Gamma = product of every taken gate).  So
+    // the state loads (issued with a single chunk, or while the last chunk of
+    // a longer fold is folded) are in flight during the fold, and they never
+    // hold registers at the same time as a prefetched chunk.  acc[i] is the
+    // 16x16 tile of U^T for columns 16i.. and the wave's 16 rows; lane l holds
     // columns 16i + 4*lg + 0..3 of row lr.
+    f32x4 sreg[NI];
+    auto load_state = [&]() {
 #pragma unroll
-    for (int u = 0; u < NI; ++u) *reinterpret_cast<f32x4*>(piece_lds(u)) = sreg[u];
-    __syncthreads();
+        for (int u = 0; u < NI; ++u)
+            sreg[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sin + (l + 64 * u) * 4));
+    };
     f32x4v acc[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(frag_lds(i));
-        acc[i] = f32x4v{v.x, v.y, v.z, v.w};
-    }
-    __syncthreads();                                          // the state area becomes the chunk area
+    for (int i = 0; i < NI; ++i) acc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    float Gamma = 1.f;
 
-    for (uint32_t t0 = 0; t0 < steps; t0 += kPos) {
+    auto chunk = [&](uint32_t t0, auto prefetch) {
         const int valid = static_cast<int>(steps - t0 < kPos ? steps - t0 : kPos);
 #pragma unroll
         for (int u = 0; u < KPT; ++u) {
@@ -221,7 +233,8 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 16 : 8) / NW) void gdn_replay
             if (jb < kPairs * KG) {
                 const int q = jb / KG, cg = jb - q * KG;
                 const u32x4 z = {0u, 0u, 0u, 0u};
-                const u32x4 r0 = kmw[u][0] != 0u ? kr[u][0] : z, r1 = kmw[u][1] != 0u ? kr[u][1] : z;
+                const u32x4 r0 = 2 * q < valid && kmw[u][0] != 0u ? kr[u][0] : z;
+                const u32x4 r1 = 2 * q + 1 < valid && kmw[u][1] != 0u ? kr[u][1] : z;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) kT[(cg * 8 + e) * kStride + q] = pair_word(r0, r1, e);
             }
@@ -232,23 +245,19 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 16 : 8) / NW) void gdn_replay
             if (jb < kPairs * DG) {
                 const int q = jb / DG, dg = jb - q * DG;
                 const u32x4 z = {0u, 0u, 0u, 0u};
-                const u32x4 r0 = dmw[u][0] != 0u ? dr[u][0] : z, r1 = dmw[u][1] != 0u ? dr[u][1] : z;
+                const u32x4 r0 = 2 * q < valid && dmw[u][0] != 0u ? dr[u][0] : z;
+                const u32x4 r1 = 2 * q + 1 < valid && dmw[u][1] != 0u ? dr[u][1] : z;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) dT[(dg * 8 + e) * kStride + q] = pair_word(r0, r1, e);
             }
         }
-        if (tid < kPos) {
-            fl[tid] = gw[0] != 0u ? 1u : 0u;
-            gs[tid] = gw[0] != 0u ? __builtin_bit_cast(float, gw[1]) : 0.f;
-        }
-        if (tid == 0) misc[1] = 1.f;
-        __syncthreads();
         if (tid < 64) {
-            // w_t = product of the taken gates after t (a suffix scan over the
-            // chunk's positions in lanes 0..kPos-1); gamma = product of all.
+            // Wave 0: the chunk's gates and flags (lane t holds position t),
+            // and w_t = product of the taken gates after t by a suffix scan;
+            // gamma = product of all.
             const int t = static_cast<int>(tid);
-            const bool mine = t < kPos && fl[t] != 0u;
-            const float gt = mine ? gs[t] : 1.f;
+            const bool mine = t < valid && gmw != 0u;
+            const float gt = mine ? io_bits_to_f32<IO>(graw) : 1.f;
             float p = gt;                                     // becomes prod_{s >= t} f_s
 #pragma unroll
             for (int d = 1; d < kPos; d *= 2) {
@@ -256,14 +265,20 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 16 : 8) / NW) void gdn_replay
                 if (t + d < kPos) p *= y;
             }
             const float after = __shfl_down(p, 1, kPos);
+            const bool bad = mine && !(gt >= 0.f && gt <= 1.f);
+            const bool ok = __ballot(bad) == 0ull;
             if (t < kPos) {
+                fl[t] = mine ? 1u : 0u;
+                gs[t] = mine ? gt : 0.f;
                 wv[t] = mine ? (t + 1 < kPos ? after : 1.f) : 0.f;
-                if (mine && !(gt >= 0.f && gt <= 1.f)) misc[1] = 0.f;
-                if (t == 0) misc[0] = p;
+                if (t == 0) {
+                    misc[0] = p;
+                    misc[1] = ok ? 1.f : 0.f;
+                }
             }
         }
         __syncthreads();
-        if (t0 + kPos < steps) load_chunk(t0 + kPos);         // in flight during this chunk
+        prefetch();                                           // in flight during this chunk
 
         // One pass over the chunk when its gates allow (w and gamma from the
         // chunk), else one pass per taken position (gamma = that gate, w = 1,
@@ -285,6 +300,7 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 16 : 8) / NW) void gdn_replay
                 keep[1] = only == 1 ? m : 0ull;
                 ++tt;
             }
+            Gamma *= gamma;
 #pragma unroll
             for (int i = 0; i < NI; ++i) acc[i] *= gamma;
 #pragma unroll
@@ -312,17 +328,34 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 16 : 8) / NW) void gdn_replay
             if (whole) break;
         }
         __syncthreads();                                      // LDS is restaged next
+    };
+    auto none = [] {};
+    if (steps <= kPos) {
+        if (steps > 0) load_chunk(0);
+        load_state();
+        // vmcnt(NI): the chunk is in, the NI state loads may be pending
+        __builtin_amdgcn_s_waitcnt((NI & 15) | ((NI >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+        if (steps > 0) chunk(0, none);
+    } else {
+        load_chunk(0);
+        uint32_t t0 = 0;
+        for (; t0 + kPos < steps; t0 += kPos) chunk(t0, [&] { load_chunk(t0 + kPos); });
+        chunk(t0, load_state);
     }
 
-    // accumulator layout -> LDS -> row layout -> HBM
+
+    // U: accumulator layout -> LDS -> row layout; S = Gamma * S0 + U -> HBM
 #pragma unroll
     for (int i = 0; i < NI; ++i)
         *reinterpret_cast<f32x4*>(frag_lds(i)) = f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < NI; ++u)
-        __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(piece_lds(u)),
-                                    reinterpret_cast<f32x4*>(sout + (l + 64 * u) * 4));
+    for (int u = 0; u < NI; ++u) {
+        const f32x4 uu = *reinterpret_cast<const f32x4*>(piece_lds(u));
+        const f32x4 r = {fmaf(Gamma, sreg[u].x, uu.x), fmaf(Gamma, sreg[u].y, uu.y),
+                         fmaf(Gamma, sreg[u].z, uu.z), fmaf(Gamma, sreg[u].w, uu.w)};
+        __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(sout + (l + 64 * u) * 4));
+    }
 }
 
 template <int IO, int DK, int NW>
@@ -330,15 +363,23 @@ hipError_t launch_nw(const ReplayArgs& a, hipStream_t stream) {
     constexpr uint32_t rows = 16u * NW;
     const uint32_t slices = a.Dv / rows;
     const uint64_t grid = static_cast<uint64_t>(a.B) * a.Hv * slices;
-    hipLaunchKernelGGL((gdn_replay_mfma_kernel<IO, DK, NW>), dim3(static_cast<uint32_t>(grid)),
-                       dim3(64 * NW), 0, stream, a.delta_log, a.k_log, a.g_log, a.state_in, a.mask,
-                       a.state_out, a.T_log, a.Hv, a.Dv, slices, a.steps);
+    if (a.mask != nullptr)
+        hipLaunchKernelGGL((gdn_replay_mfma_kernel<IO, DK, NW, true>), dim3(static_cast<uint32_t>(grid)),
+                           dim3(64 * NW), 0, stream, a.delta_log, a.k_log, a.g_log, a.state_in, a.mask,
+                           a.state_out, a.T_log, a.Hv, a.Dv, slices, a.steps);
+    else
+        hipLaunchKernelGGL((gdn_replay_mfma_kernel<IO, DK, NW, false>), dim3(static_cast<uint32_t>(grid)),
+                           dim3(64 * NW), 0, stream, a.delta_log, a.k_log, a.g_log, a.state_in, a.mask,
+                           a.state_out, a.T_log, a.Hv, a.Dv, slices, a.steps);
     return hipGetLastError();
 }
 
-// Four waves (64 value rows) per workgroup.
+// Four waves (64 value rows) per workgroup; GDN_REPLAY_MFMA_WAVES=2 selects
+// two (launch-shape sweeps).
 template <int IO, int DK>
 hipError_t launch_dk(const ReplayArgs& a, hipStream_t stream) {
+    const char* e = std::getenv("GDN_REPLAY_MFMA_WAVES");
+    if (e != nullptr && std::strtoul(e, nullptr, 10) == 2) return launch_nw<IO, DK, 2>(a, stream);
     return launch_nw<IO, DK, 4>(a, stream);
 }
 
