@@ -12,6 +12,8 @@ input already resident in HBM:
     chunk_prefill:    gqa_expand of fp32 q and k (tiled map) + gdn_record over 4096 steps
     long_tape_replay: gdn_replay of a 64-step fp16 tape for accepted in {0,1,16,63,64}
     tiny:             gdn_record + gdn_replay
+    cell_d192_128, cell_d64_32: the page's other two head-shape cells as decode
+                      steps (B=1024 / 16384), same launches as large_batch_decode
 
 With --capture fused (decode workloads) the record writes k_log and g_log
 itself and the separate gqa_expand launch goes away.
@@ -226,7 +228,10 @@ def cpu_baseline(name: str, budget_s: float):
     bits_dtype = torch.int32 if w.io == "f32" else torch.int16
     cores = max(1, min(len(os.sched_getaffinity(0)), 16))
     e = 4 if w.io == "f32" else 2
-    b_sample = min(w.B, max(cores, 16 if w.T <= 16 else 1))
+    # batch rows per sample: about 32 MiB of state (16 rows of the 128x128x32-head
+    # shape), so that small heads are not timed as Python call overhead
+    per_row = w.Hv * w.Dv * w.Dk * 4
+    b_sample = min(w.B, max(cores, (32 << 20) // per_row if w.T <= 16 else 1))
     if name == "chunk_prefill":
         heads = min(w.Hv, max(cores, 4))     # value heads of the single batch row
     seed = 123

@@ -71,6 +71,15 @@ WORKLOADS = {
                                  Dv=128, io="f16", gqa_map="block", mask="bernoulli",
                                  accepted=(0, 1, 16, 63, 64), mask_p=0.7,
                                  note="replay of a 64-step fp16 tape, keys pre-expanded"),
+    # The two head-shape cells the record/replay page instantiates besides the
+    # main one, as decode steps with a state of a few hundred MiB (the page
+    # gives no batch size for them).
+    "cell_d192_128": Workload("cell_d192_128", B=1024, T=1, Hk=4, Hv=4, Dk=192, Dv=128,
+                              io="bf16", gqa_map="block", mask="ones", accepted=(1,),
+                              note="Dk=192, Dv=128, Hk=Hv=4 decode step; 384 MiB of fp32 state"),
+    "cell_d64_32": Workload("cell_d64_32", B=16384, T=1, Hk=2, Hv=2, Dk=64, Dv=32,
+                            io="bf16", gqa_map="block", mask="ones", accepted=(1,),
+                            note="Dk=64, Dv=32, Hk=Hv=2 decode step; 256 MiB of fp32 state"),
 }
 
 

@@ -90,6 +90,44 @@ def test_record_chunk_prefill_sampled_heads():
         assert_close(s[:, hv:hv + 1], rs, io, "prefill state head %d" % hv)
 
 
+# The page's two other head-shape cells: decode at the workload size (sampled
+# batch rows re-run by the oracle), and short tapes with masks at small B.
+@pytest.mark.parametrize("name", ["cell_d192_128", "cell_d64_32"])
+def test_shape_cell_decode_workloads(name):
+    w = gi.WORKLOADS[name]
+    inp = gi.workload_inputs(name, 3)
+    note("record %s at full size" % name)
+    y, s, dl = _record_gpu(inp, w.gqa_map)
+    rows = np.random.Generator(np.random.PCG64(5)).choice(w.B, size=8, replace=False)
+    sub = {k2: (v[rows] if isinstance(v, torch.Tensor) else v) for k2, v in inp.items()}
+    ry, rs, rd = oracle.gdn_record(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"],
+                                   sub["state_in"], sub["mask"], gqa_map=w.gqa_map)
+    io = inp["q"].dtype
+    assert_close(y[rows], ry, io, name + " y")
+    assert_close(dl[rows], rd, io, name + " delta")
+    assert_close(s[rows], rs, io, name + " state")
+    d = to_dev(inp)
+    k_log = gdn.gqa_expand(d["k"], w.Hv, w.gqa_map)
+    s_rep = gdn.gdn_replay(dl, k_log, d["g"], d["state_in"], d["mask"], 1)
+    torch.cuda.synchronize()
+    if io == torch.float32:
+        assert torch.equal(s_rep, s)
+    else:
+        assert_close(s_rep[rows], rs, io, name + " replay")
+
+
+@pytest.mark.parametrize("cell", [(192, 128, 4, 4), (64, 32, 2, 2)])
+@pytest.mark.parametrize("T,mask", [(4, "trailing"), (3, "bernoulli"), (37, "none")])
+def test_shape_cell_short_tapes(cell, T, mask):
+    Dk, Dv, Hk, Hv = cell
+    for io in ("bf16", "f32"):
+        inp = gi.record_inputs(3, T, Hk, Hv, Dk, Dv, io, seed=7 + T, mask=mask)
+        _check_record(inp, "block", "cell %s T=%d %s %s" % (cell, T, mask, io))
+        tape = gi.tape_inputs(2, T, Hv, Dk, Dv, io, seed=9 + T, mask="bernoulli")
+        for a in sorted({1, T // 2, T}):
+            _check_replay(gi.poison_untaken(tape, a), a, "cell %s T=%d %s" % (cell, T, io))
+
+
 RAGGED = [
     # B, T, Hk, Hv, Dk, Dv, io, map, mask
     (3, 5, 1, 3, 32, 16, "f32", "block", "bernoulli"),
