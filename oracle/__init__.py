@@ -40,7 +40,7 @@ def build(force: bool = True) -> str:
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC]
+           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
     return _LIB
@@ -69,6 +69,9 @@ def _load():
         lib.oracle_gqa_expand.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
                                           u32, u32, u32, u32, u32, ctypes.c_int]
         lib.oracle_gqa_expand.restype = ctypes.c_int
+        lib.oracle_rms_norm_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, dp, u32, u32,
+                                             ctypes.c_double]
+        lib.oracle_rms_norm_bf16.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -174,4 +177,30 @@ def gqa_expand(src: np.ndarray, h: int, gqa_map="tiled") -> np.ndarray:
                                    a.dtype.itemsize, _MAPS[gqa_map])
     if rc != 0:
         raise ValueError("oracle_gqa_expand rejected its arguments")
+    return out
+
+
+def rms_norm_bf16(x, weight, eps: float) -> np.ndarray:
+    """RMSNorm with bf16 weights ([P2] "GPU RMSNorm"), in float64.
+
+    x: float32 [n, dim] (numpy or a torch tensor); weight: the bf16 weight [dim],
+    given as a torch bfloat16 tensor or as its raw uint16 bits.  Returns
+    out [n, dim] float64: out[t, i] = x[t, i] / sqrt(mean_i x[t]^2 + eps) * w[i].
+    """
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    xa = np.ascontiguousarray(x, dtype=np.float32)
+    if hasattr(weight, "detach"):
+        import torch  # only reached when the caller already holds torch tensors
+        weight = weight.detach().cpu().contiguous().view(torch.int16).numpy()
+    wa = np.asarray(weight)
+    if wa.dtype.itemsize != 2 or wa.dtype.kind not in "iu":
+        raise TypeError("weight must be a bfloat16 tensor or its raw 16-bit pattern")
+    wa = np.ascontiguousarray(wa.view(np.uint16))
+    if xa.ndim != 2 or wa.shape != (xa.shape[1],):
+        raise ValueError("x must be [n, dim] and weight [dim]")
+    n, dim = xa.shape
+    out = np.empty((n, dim), dtype=np.float64)
+    if _load().oracle_rms_norm_bf16(xa.ctypes.data, wa.ctypes.data, _dp(out), n, dim, float(eps)) != 0:
+        raise ValueError("oracle_rms_norm_bf16 rejected its arguments")
     return out

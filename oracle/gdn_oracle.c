@@ -20,6 +20,9 @@
  *        `state_replay!`).
  *   [P3] mlx-native 0.6.5, mlx_native/ops/repeat_tiled.rs -- the module
  *        documentation ("Mapping") and `dispatch_repeat_tiled_f32`.
+ *   [P2] moeflux 0.1.0-pre.3, src/riir/backend/gpu/gpu_norm.rs -- the
+ *        documentation of `gpu_rms_norm_fused` (GPU RMSNorm with bf16 weights)
+ *        and of `encode_rms_norm_bf16_fused_n_tokens` (one row per token).
  *
  * Layouts (dense, row-major, no strides), following [P1] "Tape layout" and the
  * index arithmetic of both [P1] kernels:
@@ -35,8 +38,12 @@
  * hand-computed values, closed forms and independent formulations (the
  * transition-matrix form of the gated delta rule, numpy repeat / tile for the
  * head maps).  The summation order of the two Dk-length dot products is not
- * fixed by the pages; that order is "parity unpinned" beyond tolerance.
+ * fixed by the pages; that order is "parity unpinned" beyond tolerance.  The
+ * RMSNorm is pinned by a hand-worked case, closed forms (constant and one-hot
+ * rows, unit RMS), scale invariance and the per-column weight; the order of
+ * its sum of squares is likewise unpinned beyond tolerance.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stddef.h>
 #include <string.h>
@@ -206,6 +213,35 @@ int oracle_gqa_expand(const void* src, void* dst, uint32_t seq, uint32_t hg, uin
                 size_t dO = (((size_t)t * h + hh) * k + e) * elem_bytes;
                 for (uint32_t c = 0; c < elem_bytes; ++c) d[dO + c] = s[so + c];
             }
+        }
+    }
+    return 0;
+}
+
+/*
+ * oracle_rms_norm_bf16 -- [P2] "GPU RMSNorm": for every token t of an
+ * [n, dim] float32 input,
+ *     r = 1 / sqrt( (sum_i x[t,i]^2) / dim + eps )
+ *     out[t,i] = x[t,i] * r * w[i]
+ * where w[i] is the bf16 weight widened exactly (its 16 bits are the upper
+ * half of a float32).  The sum runs over i in order, in double.
+ *
+ * Returns 0, or -1 for a zero dimension.
+ */
+int oracle_rms_norm_bf16(const float* x, const uint16_t* w, double* out, uint32_t n,
+                         uint32_t dim, double eps)
+{
+    if (n == 0 || dim == 0) return -1;
+    for (uint32_t t = 0; t < n; ++t) {
+        const float* xt = x + (size_t)t * dim;
+        double ss = 0.0;
+        for (uint32_t i = 0; i < dim; ++i) ss = ss + (double)xt[i] * (double)xt[i];
+        double r = 1.0 / sqrt(ss / (double)dim + eps);
+        for (uint32_t i = 0; i < dim; ++i) {
+            uint32_t bits = (uint32_t)w[i] << 16;
+            float wf;
+            memcpy(&wf, &bits, sizeof wf);
+            out[(size_t)t * dim + i] = (double)xt[i] * r * (double)wf;
         }
     }
     return 0;

@@ -43,6 +43,15 @@ MUTANTS = {
                                  "double d = delta_log[(bt * Hv + hv) * Dv];"),
     "replay_gate_from_next_step": ("double gt = g_log[bt * Hv + hv];",
                                    "double gt = g_log[(t + 1 < T_log ? bt + 1 : bt) * Hv + hv];"),
+    "rms_sum_not_mean": ("double r = 1.0 / sqrt(ss / (double)dim + eps);",
+                         "double r = 1.0 / sqrt(ss + eps);"),
+    "rms_eps_outside_sqrt": ("double r = 1.0 / sqrt(ss / (double)dim + eps);",
+                             "double r = 1.0 / (sqrt(ss / (double)dim) + eps);"),
+    "rms_no_sqrt": ("double r = 1.0 / sqrt(ss / (double)dim + eps);",
+                    "double r = 1.0 / (ss / (double)dim + eps);"),
+    "rms_weight_reversed": ("uint32_t bits = (uint32_t)w[i] << 16;",
+                            "uint32_t bits = (uint32_t)w[dim - 1 - i] << 16;"),
+    "rms_abs_not_square": ("ss = ss + (double)xt[i] * (double)xt[i];", "ss = ss + fabs((double)xt[i]);"),
     "expand_source_head_zero": ("size_t so = (((size_t)t * hg + from) * k + e) * elem_bytes;",
                                 "size_t so = (((size_t)t * hg) * k + e) * elem_bytes;"),
 }
@@ -58,7 +67,7 @@ def _run_mutant(name, tmp_path):
     with open(csrc, "w") as f:
         f.write(mutated)
     subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
-                    "-o", lib, csrc], check=True)
+                    "-o", lib, csrc, "-lm"], check=True)
     env = dict(os.environ, GDN_ORACLE_LIB=lib)
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py")],

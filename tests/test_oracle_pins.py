@@ -364,3 +364,71 @@ def test_tapeless_step_matches_taped_step():
     y2, s2, _ = oracle.gdn_record(q, k, v, g, beta, s0, mask)
     np.testing.assert_array_equal(y, y2)
     assert np.array_equal(s, s2)
+
+
+# --------------------------------------------------------------- RMSNorm (bf16 weight)
+
+def _bf16_bits(a):
+    """bf16 bit patterns of float values that bf16 holds exactly."""
+    import torch
+    t = torch.tensor(np.asarray(a, dtype=np.float32)).to(torch.bfloat16)
+    assert torch.equal(t.float(), torch.tensor(np.asarray(a, dtype=np.float32))), "not exact in bf16"
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_rms_norm_hand_case():
+    g = json.load(open(os.path.join(GOLD, "rms_norm_hand.json")))
+    out = oracle.rms_norm_bf16(np.array(g["x"], dtype=np.float32), _bf16_bits(g["weight"]), g["eps"])
+    np.testing.assert_allclose(out, np.array(g["out"]), rtol=1e-15, atol=0)
+
+
+def test_rms_norm_constant_row_closed_form():
+    r = np.random.Generator(np.random.PCG64(301))
+    dim = 96
+    w = np.round(r.normal(1.0, 0.25, dim) * 64) / 64          # exact in bf16
+    for c, eps in ((0.75, 1e-6), (-3.0, 0.5), (1e-3, 1e-5)):
+        x = np.full((2, dim), c, dtype=np.float32)
+        out = oracle.rms_norm_bf16(x, _bf16_bits(w), eps)
+        cx = float(np.float32(c))
+        ref = cx / np.sqrt(cx * cx + eps) * w
+        np.testing.assert_allclose(out[0], ref, rtol=1e-13, atol=0)
+        np.testing.assert_array_equal(out[0], out[1])
+
+
+def test_rms_norm_one_hot_and_unit_rms():
+    dim = 40
+    w = np.ones(dim)
+    x = np.zeros((1, dim), dtype=np.float32)
+    x[0, 7] = -2.5
+    out = oracle.rms_norm_bf16(x, _bf16_bits(w), 0.0)
+    ref = np.zeros(dim)
+    ref[7] = -np.sqrt(dim)
+    np.testing.assert_allclose(out[0], ref, rtol=1e-14, atol=0)
+    r = np.random.Generator(np.random.PCG64(302))
+    x = r.standard_normal((5, dim)).astype(np.float32)
+    out = oracle.rms_norm_bf16(x, _bf16_bits(w), 0.0)
+    np.testing.assert_allclose((out ** 2).mean(axis=1), 1.0, rtol=1e-13)
+
+
+def test_rms_norm_scale_invariance_and_weight_per_column():
+    r = np.random.Generator(np.random.PCG64(303))
+    dim = 64
+    w = np.round(r.normal(1.0, 0.5, dim) * 32) / 32
+    wb = _bf16_bits(w)
+    x = r.standard_normal((3, dim)).astype(np.float32)
+    base = oracle.rms_norm_bf16(x, wb, 0.0)
+    np.testing.assert_allclose(oracle.rms_norm_bf16(x * np.float32(4.0), wb, 0.0), base, rtol=1e-13)
+    np.testing.assert_allclose(oracle.rms_norm_bf16(-x, wb, 0.0), -base, rtol=1e-13)
+    # out / (x * w) is the same 1/rms for every column of a row, and equals it
+    ratio = base / (x.astype(np.float64) * w)
+    rms = np.sqrt((x.astype(np.float64) ** 2).mean(axis=1, keepdims=True))
+    np.testing.assert_allclose(ratio, np.broadcast_to(1.0 / rms, ratio.shape), rtol=1e-12)
+
+
+def test_rms_norm_rows_are_independent():
+    r = np.random.Generator(np.random.PCG64(304))
+    x = r.standard_normal((6, 33)).astype(np.float32)
+    wb = _bf16_bits(np.round(r.normal(1.0, 0.2, 33) * 16) / 16)
+    out = oracle.rms_norm_bf16(x, wb, 1e-6)
+    perm = r.permutation(6)
+    np.testing.assert_array_equal(oracle.rms_norm_bf16(x[perm], wb, 1e-6), out[perm])
