@@ -14,6 +14,7 @@ input already resident in HBM:
     tiny:             gdn_record + gdn_replay
     cell_d192_128, cell_d64_32: the page's other two head-shape cells as decode
                       steps (B=1024 / 16384), same launches as large_batch_decode
+    rms_norm_prefill: rms_norm_bf16 of 4096 fp32 hidden states of width 2048
 
 With --capture fused (decode workloads) the record writes k_log and g_log
 itself and the separate gqa_expand launch goes away.
@@ -30,6 +31,7 @@ A = taken tape positions, a' = min(accepted, T)):
     replay  8*B*Hv*Dv*Dk + 4*B*a' [mask] + A*e*Hv*(Dv + Dk + 1)
     expand  e*seq*K*(Hg + H)
     capture U*e*Hv*(Dk + 1) on top of the record (k_log and g_log writes)
+    rms_norm 8*n*dim + 2*dim (x in, out out, the bf16 weight)
 The replay's "touched" bytes count every position below a' (the select reads
 masked positions too): A is replaced by B*a'.
 """
@@ -52,6 +54,7 @@ KERNEL_SOURCES = {
     "gdn_record": ["gdn_record.hip", "gdn_device.hpp"],
     "gdn_replay": ["gdn_replay.hip", "gdn_replay_mfma.hip", "gdn_device.hpp"],
     "gqa_expand": ["gqa_expand.hip", "gdn_device.hpp"],
+    "rms_norm_bf16": ["rms_norm.hip", "gdn_device.hpp"],
 }
 
 
@@ -69,6 +72,10 @@ def replay_bytes(B, T, Hv, Dk, Dv, e, accepted, taken_steps, has_mask):
 
 def expand_bytes(seq, hg, h, k, e):
     return e * seq * k * (hg + h)
+
+
+def rms_norm_bytes(n, dim):
+    return 8 * n * dim + 2 * dim
 
 
 def capture_bytes(Hv, Dk, e, active_steps):
@@ -117,8 +124,21 @@ class Step:
         import linear_attention_recurrence_step_amd as gdn
         self.gdn = gdn
         self.name = name
-        self.w = w = gi.WORKLOADS[name]
+        self.gi_norm = gi.NORM_WORKLOADS
         self.fused = capture == "fused"
+        self.kernels = []            # (label, kernel, algorithmic bytes, head-steps)
+        self.touched = {}
+        if name in gi.NORM_WORKLOADS:
+            if self.fused:
+                raise SystemExit("--capture fused applies to workloads with a record and a replay")
+            self.w = w = gi.NORM_WORKLOADS[name]
+            x, wt = gi.norm_inputs(w["n_tokens"], w["dim"], seed)
+            self.cpu = (x, wt)
+            self.x, self.wt = x.to(dev), wt.to(dev)
+            self.out = torch.empty_like(self.x)
+            self.kernels.append(("rms_norm", "rms_norm_bf16", rms_norm_bytes(w["n_tokens"], w["dim"]), 0))
+            return
+        self.w = w = gi.WORKLOADS[name]
         if self.fused and name in ("long_tape_replay", "chunk_prefill"):
             raise SystemExit("--capture fused applies to workloads with a record and a replay")
         self.e = 4 if w.io == "f32" else 2
@@ -185,6 +205,8 @@ class Step:
 
     def launches(self):
         """Callables, one per kernel launch, in step order."""
+        if self.name in self.gi_norm:
+            return [lambda: self.gdn.rms_norm_bf16(self.x, self.wt, self.w["eps"], out=self.out)]
         gdn, d, w = self.gdn, self.d, self.w
         if self.name == "long_tape_replay":
             return [(lambda a=a: gdn.gdn_replay(d["delta_log"], d["k_log"], d["g_log"], d["state_in"],
@@ -224,6 +246,8 @@ def cpu_baseline(name: str, budget_s: float):
     import gdn_inputs as gi
     import oracle
 
+    if name in gi.NORM_WORKLOADS:
+        return _cpu_baseline_norm(name, budget_s)
     w = gi.WORKLOADS[name]
     bits_dtype = torch.int32 if w.io == "f32" else torch.int16
     cores = max(1, min(len(os.sched_getaffinity(0)), 16))
@@ -300,6 +324,47 @@ def cpu_baseline(name: str, budget_s: float):
                          unit_name),
             "single_thread_value": round(one_bytes / dt1 / 1e9, 4),
             "cpu_model": _cpu_model(),
+            "label": "CPU baseline, not the target"}
+
+
+def _cpu_baseline_norm(name: str, budget_s: float):
+    """The RMSNorm oracle on a sample of 1024 tokens, threads over token slices."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import gdn_inputs as gi
+    import oracle
+
+    w = gi.NORM_WORKLOADS[name]
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    n = min(w["n_tokens"], 1024)
+    x, wt = gi.norm_inputs(n, w["dim"], 123)
+    xn = x.numpy()
+    per = max(1, n // cores)
+    chunks = [(lo, min(n, lo + per)) for lo in range(0, n, per)]
+
+    def work(lo, hi):
+        oracle.rms_norm_bf16(xn[lo:hi], wt, w["eps"])
+        return rms_norm_bytes(hi - lo, w["dim"])
+
+    total, passes, t0 = 0, 0, time.perf_counter()
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        while True:
+            total += sum(ex.map(lambda c: work(*c), chunks))
+            passes += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    one, t1 = 0, time.perf_counter()
+    while True:
+        one += work(0, min(n, 16))
+        if time.perf_counter() - t1 >= budget_s / 4:
+            break
+    dt1 = time.perf_counter() - t1
+    return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": min(cores, len(chunks)),
+            "kind": "oracle",
+            "sample": "%d of %d tokens of %s, %d pass(es), %.1f s, threads over tokens"
+                      % (n, w["n_tokens"], name, passes, dt),
+            "single_thread_value": round(one / dt1 / 1e9, 4), "cpu_model": _cpu_model(),
             "label": "CPU baseline, not the target"}
 
 
@@ -485,10 +550,13 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "cache_scrub": scrub,
-        "config": {"workload": args.workload, "B": w.B, "T": w.T, "Hk": w.Hk, "Hv": w.Hv,
-                   "Dk": w.Dk, "Dv": w.Dv, "io_dtype": w.io, "state_dtype": "f32",
-                   "gqa_map": w.gqa_map, "mask": w.mask, "capture": args.capture,
-                   "step": " + ".join(k[0] for k in step.kernels)},
+        "config": ({"workload": args.workload, "n_tokens": w["n_tokens"], "dim": w["dim"],
+                    "eps": w["eps"], "x_dtype": "f32", "weight_dtype": "bf16",
+                    "step": "rms_norm"} if isinstance(w, dict) else
+                   {"workload": args.workload, "B": w.B, "T": w.T, "Hk": w.Hk, "Hv": w.Hv,
+                    "Dk": w.Dk, "Dv": w.Dv, "io_dtype": w.io, "state_dtype": "f32",
+                    "gqa_map": w.gqa_map, "mask": w.mask, "capture": args.capture,
+                    "step": " + ".join(k[0] for k in step.kernels)}),
         "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
         "head_steps_per_s": round(head_steps / (ms_per_step * 1e-3), 1),
         "head_steps_per_step": head_steps,
@@ -496,6 +564,8 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
     }
+    if isinstance(w, dict):
+        out["tokens_per_s"] = round(w["n_tokens"] / (ms_per_step * 1e-3), 1)
     if args.workload == "chunk_prefill":
         out["tokens_per_s"] = round(w.B * w.T / (ms_per_step * 1e-3), 1)
     if not args.no_peak_probe:

@@ -174,3 +174,20 @@ def workload_inputs(name: str, seed: int = 0, B: Optional[int] = None):
     """Record inputs for a named workload (optionally with a smaller batch)."""
     w = WORKLOADS[name]
     return record_inputs(B or w.B, w.T, w.Hk, w.Hv, w.Dk, w.Dv, w.io, seed, w.mask, w.mask_p)
+
+
+# RMSNorm workload: the pre-norm of the layer over a prefill's tokens.  The
+# page gives no hidden size; 2048 is taken, with the prefill length above.
+NORM_WORKLOADS = {
+    "rms_norm_prefill": dict(n_tokens=4096, dim=2048, eps=1e-6,
+                             note="RMSNorm of 4096 fp32 hidden states of width 2048, bf16 weight"),
+}
+
+
+def norm_inputs(n_tokens, dim, seed=0):
+    """Hidden states x ~ N(0, 1) in float32 [n, dim] and a bf16 weight near 1,
+    1 + N(0, 0.1), [dim] (torch CPU tensors)."""
+    r = rng(seed)
+    x = torch.from_numpy(r.standard_normal((n_tokens, dim)).astype(np.float32))
+    w = torch.from_numpy((1.0 + 0.1 * r.standard_normal(dim)).astype(np.float32)).to(torch.bfloat16)
+    return x, w

@@ -1,6 +1,7 @@
 /*
  * gdn.h -- C ABI of the Gated DeltaNet record / replay / GQA-expand library
- * for AMD Instinct MI355X (gfx950).  Link with libgdn.so.
+ * (and the RMSNorm that precedes the layer) for AMD Instinct MI355X (gfx950).
+ * Link with libgdn.so.
  *
  * Plain C: callers need neither HIP nor PyTorch headers.  Device pointers are
  * HIP device allocations; `stream` is a hipStream_t passed as void* (NULL is
@@ -43,7 +44,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum gdn_dtype {
     GDN_F32 = 0,
@@ -171,6 +172,31 @@ int gdn_replay(const void* delta_log, const void* k_log, const void* g_log,
  */
 int gqa_expand(const void* src, void* dst, uint32_t seq, uint32_t hg, uint32_t h, uint32_t k,
                int dtype, int gqa_map, void* stream);
+
+/*
+ * rms_norm_bf16 -- RMSNorm with bf16 weights over a batch of tokens.
+ *
+ * Defined on the moeflux 0.1.0-pre.3 page src/riir/backend/gpu/gpu_norm.rs
+ * (documentation of `gpu_rms_norm_fused`, "GPU RMSNorm", and of the batched
+ * `encode_rms_norm_bf16_fused_n_tokens`, one row per token): for every token t,
+ *     out[t,i] = x[t,i] * (1 / sqrt(sum_i x[t,i]^2 / dim + eps)) * w[i],
+ * w[i] the bf16 weight widened exactly.  Arithmetic is float32.
+ *
+ * Arguments
+ *   x         float32 [n_tokens, dim], 4-byte aligned.
+ *   weight    the bf16 weight [dim] as raw 16-bit patterns, 2-byte aligned.
+ *   out       float32 [n_tokens, dim], 4-byte aligned; may be exactly x (in
+ *             place), but must not overlap x otherwise, nor the weight.
+ *   n_tokens, dim   sizes, non-zero.
+ *   eps       added to the mean square (any value; the page passes a small
+ *             positive constant).
+ *   stream    hipStream_t or NULL.
+ * The fastest path needs dim a multiple of 4 and at most 8192, x and out
+ * 16-byte aligned and weight 8-byte aligned; other cases take a general path.
+ * Returns GDN_OK or a negative gdn_status (nothing is enqueued on error).
+ */
+int rms_norm_bf16(const float* x, const uint16_t* weight, float* out, uint32_t n_tokens,
+                  uint32_t dim, float eps, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* gdn_strerror(int status);

@@ -21,7 +21,7 @@ import torch
 from . import _native
 from ._native import GdnError, lib
 
-__all__ = ["gdn_record", "gdn_replay", "gqa_expand", "GdnError", "IO_DTYPES"]
+__all__ = ["gdn_record", "gdn_replay", "gqa_expand", "rms_norm_bf16", "GdnError", "IO_DTYPES"]
 
 IO_DTYPES = {torch.float32: _native.GDN_F32, torch.float16: _native.GDN_F16,
              torch.bfloat16: _native.GDN_BF16}
@@ -182,3 +182,25 @@ def gqa_expand(src: torch.Tensor, h: int, gqa_map: str = "tiled", *,
                         _stream(stream, dev))
     _native.check("gqa_expand", rc)
     return dst
+
+
+def rms_norm_bf16(x: torch.Tensor, weight: torch.Tensor, eps: float, *,
+                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """RMSNorm with a bf16 weight: out[t] = x[t] / sqrt(mean(x[t]^2) + eps) * weight.
+
+    x: float32 [..., dim] (leading dims flattened to tokens); weight: bfloat16
+    [dim].  ``out`` may be ``x`` itself.
+    """
+    if x.dim() < 1:
+        raise ValueError("x must be [..., dim]")
+    dev = _device_of(x)
+    dim = x.shape[-1]
+    n = x.numel() // dim if dim else 0
+    _want("x", x, tuple(x.shape), torch.float32, dev)
+    _want("weight", weight, (dim,), torch.bfloat16, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _want("out", out, tuple(x.shape), torch.float32, dev)
+    rc = lib.rms_norm_bf16(_ptr(x), _ptr(weight), _ptr(out), n, dim, float(eps), _stream(stream, dev))
+    _native.check("rms_norm_bf16", rc)
+    return out

@@ -22,9 +22,9 @@ STATUS = {
     -4: "GDN_ERR_UNSUPPORTED_SHAPE", -5: "GDN_ERR_OVERFLOW", -6: "GDN_ERR_ALIAS",
     -7: "GDN_ERR_BAD_ENUM", -8: "GDN_ERR_LAUNCH", -9: "GDN_ERR_MISALIGNED",
 }
-EXPORTS = ("gdn_record", "gdn_replay", "gqa_expand", "gdn_strerror", "gdn_last_error",
-           "gdn_abi_version")
-ABI_VERSION = 2
+EXPORTS = ("gdn_record", "gdn_replay", "gqa_expand", "rms_norm_bf16", "gdn_strerror",
+           "gdn_last_error", "gdn_abi_version")
+ABI_VERSION = 3
 
 
 def _load() -> ctypes.CDLL:
@@ -40,6 +40,8 @@ def _load() -> ctypes.CDLL:
     lib.gdn_replay.restype = i32
     lib.gqa_expand.argtypes = [vp, vp] + [u32] * 4 + [i32, i32, vp]
     lib.gqa_expand.restype = i32
+    lib.rms_norm_bf16.argtypes = [vp, vp, vp, u32, u32, ctypes.c_float, vp]
+    lib.rms_norm_bf16.restype = i32
     lib.gdn_strerror.argtypes = [i32]
     lib.gdn_strerror.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_abi.cpp", "gdn_record.hip", "gdn_replay.hip", "gdn_replay_mfma.hip", "gqa_expand.hip"]
+SOURCES = ["gdn_abi.cpp", "gdn_record.hip", "gdn_replay.hip", "gdn_replay_mfma.hip", "gqa_expand.hip",
+           "rms_norm.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -220,4 +220,22 @@ int gqa_expand(const void* src, void* dst, uint32_t seq, uint32_t hg, uint32_t h
     return launch_status(gdn::launch_expand(a, static_cast<hipStream_t>(stream)), kFn);
 }
 
+int rms_norm_bf16(const float* x, const uint16_t* weight, float* out, uint32_t n_tokens,
+                  uint32_t dim, float eps, void* stream) {
+    static const char* kFn = "rms_norm_bf16";
+    if (!x || !weight || !out) return fail(GDN_ERR_NULL, "%s: x, weight and out must be non-NULL", kFn);
+    if (n_tokens == 0 || dim == 0) return fail(GDN_ERR_ZERO_DIM, "%s: n_tokens and dim must be > 0", kFn);
+    uint64_t n_x;
+    if (!mul_u64(&n_x, {n_tokens, dim, 4}) || n_x > kMaxBytes)
+        return fail(GDN_ERR_OVERFLOW, "%s: n_tokens*dim overflows", kFn);
+    if (n_tokens > kMaxGrid) return fail(GDN_ERR_OVERFLOW, "%s: too many tokens for one launch", kFn);
+    if (!aligned(x, 4) || !aligned(out, 4) || !aligned(weight, 2))
+        return fail(GDN_ERR_MISALIGNED, "%s: x and out must be 4-byte aligned, weight 2-byte", kFn);
+    const Span sx{x, n_x, "x"}, so{out, n_x, "out"}, sw{weight, uint64_t(dim) * 2, "weight"};
+    if ((out != x && overlaps(so, sx)) || overlaps(so, sw))
+        return fail(GDN_ERR_ALIAS, "%s: out overlaps x (other than exactly) or the weight", kFn);
+    gdn::RmsNormArgs a{x, weight, out, n_tokens, dim, eps};
+    return launch_status(gdn::launch_rms_norm(a, static_cast<hipStream_t>(stream)), kFn);
+}
+
 }  // extern "C"

@@ -50,6 +50,13 @@ RowTiling replay_tiling(const ReplayArgs& a);
 hipError_t launch_record(const RecordArgs& a, hipStream_t stream);
 hipError_t launch_replay(const ReplayArgs& a, hipStream_t stream);
 
+struct RmsNormArgs {
+    const float* x; const uint16_t* weight; float* out;
+    uint32_t n_tokens, dim;
+    float eps;
+};
+hipError_t launch_rms_norm(const RmsNormArgs& a, hipStream_t stream);
+
 // Folds of at least this many positions of a 16-bit tape run as matrix
 // products on the matrix cores (gdn_replay_mfma.hip).
 inline constexpr uint32_t kReplayMfmaFromSteps = 16;

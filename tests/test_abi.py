@@ -27,8 +27,8 @@ def _declared_functions():
 
 def test_header_declares_the_three_entry_points():
     fns = _declared_functions()
-    for name in ("gdn_record", "gdn_replay", "gqa_expand", "gdn_strerror", "gdn_last_error",
-                 "gdn_abi_version"):
+    for name in ("gdn_record", "gdn_replay", "gqa_expand", "rms_norm_bf16", "gdn_strerror",
+                 "gdn_last_error", "gdn_abi_version"):
         assert name in fns, fns
 
 
@@ -48,6 +48,7 @@ vp, u32, i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int
 lib.gdn_record.argtypes = [vp] * 12 + [u32] * 6 + [i32, i32, vp]
 lib.gdn_replay.argtypes = [vp] * 6 + [u32] * 6 + [i32, vp]
 lib.gqa_expand.argtypes = [vp, vp] + [u32] * 4 + [i32, i32, vp]
+lib.rms_norm_bf16.argtypes = [vp, vp, vp, u32, u32, ctypes.c_float, vp]
 lib.gdn_strerror.restype = ctypes.c_char_p
 lib.gdn_last_error.restype = ctypes.c_char_p
 cases = json.loads(sys.argv[2])
@@ -98,6 +99,13 @@ def exp(**kw):
     return [a["src"], a["dst"], a["seq"], a["hg"], a["h"], a["k"], a["dt"], a["map"], None]
 
 
+# rms_norm_bf16(x, weight, out, n_tokens, dim, eps, stream)
+def rms(**kw):
+    a = dict(x=P(0), w=P(1), out=P(2), n=8, dim=2048, eps=1e-6)
+    a.update(kw)
+    return [a["x"], a["w"], a["out"], a["n"], a["dim"], a["eps"], None]
+
+
 NULL, ZERO, RATIO, SHAPE, OVER, ALIAS, ENUM, LAUNCH, ALIGN = -1, -2, -3, -4, -5, -6, -7, -8, -9
 
 CASES = [
@@ -138,6 +146,18 @@ CASES = [
     ("rep_state_out_over_tape", "gdn_replay", rep(s_out=P(0, 1024)), ALIAS),
     ("rep_state_partial_alias", "gdn_replay", rep(s_out=P(3, 16)), ALIAS),
     ("rep_bytes_overflow", "gdn_replay", rep(B=1 << 31, T=1 << 31), OVER),
+    ("rms_null_x", "rms_norm_bf16", rms(x=None), NULL),
+    ("rms_null_weight", "rms_norm_bf16", rms(w=None), NULL),
+    ("rms_null_out", "rms_norm_bf16", rms(out=None), NULL),
+    ("rms_zero_dim", "rms_norm_bf16", rms(dim=0), ZERO),
+    ("rms_zero_tokens", "rms_norm_bf16", rms(n=0), ZERO),
+    ("rms_misaligned_x", "rms_norm_bf16", rms(x=P(0, 2)), ALIGN),
+    ("rms_misaligned_out", "rms_norm_bf16", rms(out=P(2, 6)), ALIGN),
+    ("rms_misaligned_weight", "rms_norm_bf16", rms(w=P(1, 1)), ALIGN),
+    ("rms_out_overlaps_x", "rms_norm_bf16", rms(out=P(0, 16)), ALIAS),
+    ("rms_out_overlaps_weight", "rms_norm_bf16", rms(out=P(1, 64)), ALIAS),
+    ("rms_bytes_overflow", "rms_norm_bf16", rms(n=1 << 31, dim=1 << 20), OVER),
+    ("rms_too_many_tokens", "rms_norm_bf16", rms(n=1 << 31, dim=1), OVER),
     ("exp_bad_dtype", "gqa_expand", exp(dt=7), ENUM),
     ("exp_bad_map", "gqa_expand", exp(map=-1), ENUM),
     ("exp_null_dst", "gqa_expand", exp(dst=None), NULL),
@@ -179,7 +199,7 @@ def test_strerror_covers_every_status(results):
 def test_python_binding_names_match_the_abi():
     import linear_attention_recurrence_step_amd as gdn
     from linear_attention_recurrence_step_amd import _native
-    for name in ("gdn_record", "gdn_replay", "gqa_expand"):
+    for name in ("gdn_record", "gdn_replay", "gqa_expand", "rms_norm_bf16"):
         assert callable(getattr(gdn, name))
         assert hasattr(_native.lib, name)
     assert _native.lib.gdn_abi_version() == _native.ABI_VERSION
@@ -201,3 +221,5 @@ def test_python_binding_rejects_host_tensors_before_the_library():
         gdn.gdn_replay(v, q, g, s, None, 1)
     with pytest.raises(ValueError, match="HIP device"):
         gdn.gqa_expand(torch.zeros(2, 1, 32), 2)
+    with pytest.raises(ValueError, match="HIP device"):
+        gdn.rms_norm_bf16(torch.zeros(2, 32), torch.zeros(32, dtype=torch.bfloat16), 1e-6)
