@@ -532,3 +532,57 @@ def test_gqa_expand_unaligned_views_and_batch_dims():
 
 def test_tolerances_are_the_stated_ones():
     assert TOL[torch.float32] == 1e-3 and TOL[torch.bfloat16] == 2e-2 and TOL[torch.float16] == 2e-2
+
+
+# ------------------------------------------------------------------ HIP graphs
+
+def test_graph_captured_step_replays_match_eager_bitwise():
+    """record (with tape capture) + replay + RMSNorm captured once in a HIP
+    graph and replayed with fresh inputs copied into the captured buffers, with
+    eager work and synchronisations between replays: every replay equals the
+    eager calls bit for bit."""
+    w = gi.WORKLOADS["spec_decode"]
+    d = to_dev(gi.workload_inputs("spec_decode", 0))
+    io = d["q"].dtype
+    B, T, Hk, Dk = d["k"].shape
+    Hv, Dv = w.Hv, w.Dv
+    y = torch.empty(d["v"].shape, dtype=io, device=dev())
+    dl = torch.empty_like(y)
+    kl = torch.empty((B, T, Hv, Dk), dtype=io, device=dev())
+    gl = torch.empty((B, T, Hv), dtype=io, device=dev())
+    s1 = torch.empty_like(d["state_in"])
+    s2 = torch.empty_like(d["state_in"])
+    xn, wn = (t.to(dev()) for t in gi.norm_inputs(64, 2048, seed=1))
+    on = torch.empty_like(xn)
+
+    def step():
+        gdn.gdn_record(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"], d["mask"],
+                       gqa_map=w.gqa_map, y=y, state_out=s1, delta_log=dl, k_log=kl, g_log=gl)
+        gdn.gdn_replay(dl, kl, gl, d["state_in"], d["mask"], 3, state_out=s2)
+        gdn.rms_norm_bf16(xn, wn, 1e-6, out=on)
+
+    note("graph capture of record + replay + rms_norm")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                                # warm-up off the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        fresh = to_dev(gi.workload_inputs("spec_decode", 10 + rep))
+        for name in ("q", "k", "v", "g", "beta", "state_in", "mask"):
+            d[name].copy_(fresh[name])
+        xn.copy_(gi.norm_inputs(64, 2048, seed=20 + rep)[0].to(dev()))
+        note("graph replay %d" % rep)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (y, dl, kl, gl, s1, s2, on)]
+        step()                                                # eager, same buffers
+        torch.cuda.synchronize()
+        # inactive positions are written by neither run, so whole tensors compare
+        for i, (a, b) in enumerate(zip(got, (y, dl, kl, gl, s1, s2, on))):
+            assert torch.equal(a, b), (rep, i)
