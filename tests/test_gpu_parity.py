@@ -583,6 +583,8 @@ def test_graph_captured_step_replays_match_eager_bitwise():
         got = [t.clone() for t in (y, dl, kl, gl, s1, s2, on)]
         step()                                                # eager, same buffers
         torch.cuda.synchronize()
-        # inactive positions are written by neither run, so whole tensors compare
+        # inactive positions are written by neither run, so whole tensors compare,
+        # as bit patterns (never-written memory may hold NaNs)
         for i, (a, b) in enumerate(zip(got, (y, dl, kl, gl, s1, s2, on))):
-            assert torch.equal(a, b), (rep, i)
+            bits = torch.int32 if a.element_size() == 4 else torch.int16
+            assert torch.equal(a.view(bits), b.view(bits)), (rep, i)
