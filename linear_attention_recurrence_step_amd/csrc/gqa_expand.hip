@@ -22,20 +22,57 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <int VB>
+// Division of a 32-bit index by a launch-constant divisor d >= 1 with a
+// multiply-high, an add and two shifts (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994, the round-up method with a
+// 33-bit multiplier folded into the add-and-shift):
+//     l = ceil(log2 d),  m = floor(2^32 (2^l - d) / d) + 1,
+//     t = mulhi(x, m),   x / d = (t + ((x - t) >> 1)) >> (l - 1)   (d >= 2).
+struct FastDiv {
+    uint32_t m, s1, s2;
+};
+
+FastDiv make_fastdiv(uint32_t d) {
+    if (d == 1) return FastDiv{0u, 0u, 0u};                // t = 0: x / 1 = (0 + x) >> 0
+    const uint32_t l = 32u - static_cast<uint32_t>(__builtin_clz(d - 1u));
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1u;
+    return FastDiv{static_cast<uint32_t>(m), 1u, l - 1u};
+}
+
+__device__ __forceinline__ uint32_t fastdiv(uint32_t x, const FastDiv& f) {
+    const uint32_t t = __umulhi(x, f.m);
+    return (t + ((x - t) >> f.s1)) >> f.s2;
+}
+
+// One VB-byte source vector per thread per pass.  With fewer than 2^32
+// vectors the index arithmetic is 32-bit with precomputed divisions; larger
+// copies take the 64-bit path.
+template <int VB, bool WIDE>
 __global__ __launch_bounds__(kThreads) void gqa_expand_kernel(
     const typename RawVec<VB>::T* __restrict__ src, typename RawVec<VB>::T* __restrict__ dst,
-    uint64_t nvec, uint32_t hg, uint32_t h, uint32_t row_vecs, int tiled)
+    uint64_t nvec, uint32_t hg, uint32_t h, uint32_t row_vecs, int tiled, FastDiv div_row,
+    FastDiv div_hg)
 {
     using V = typename RawVec<VB>::T;
     const uint32_t group = h / hg;
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
     for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < nvec; i += stride) {
         const V val = __builtin_nontemporal_load(src + i);
-        const uint64_t row = i / row_vecs;                     // s * hg + hs
-        const uint32_t c = static_cast<uint32_t>(i - row * row_vecs);
-        const uint64_t s = row / hg;
-        const uint32_t hs = static_cast<uint32_t>(row - s * hg);
+        uint64_t s;
+        uint32_t c, hs;
+        if constexpr (WIDE) {
+            const uint64_t row = i / row_vecs;                 // s * hg + hs
+            c = static_cast<uint32_t>(i - row * row_vecs);
+            s = row / hg;
+            hs = static_cast<uint32_t>(row - s * hg);
+        } else {
+            const uint32_t i32 = static_cast<uint32_t>(i);
+            const uint32_t row = fastdiv(i32, div_row);
+            c = i32 - row * row_vecs;
+            const uint32_t s32 = fastdiv(row, div_hg);
+            hs = row - s32 * hg;
+            s = s32;
+        }
         for (uint32_t j = 0; j < group; ++j) {
             const uint32_t hd = tiled ? j * hg + hs : hs * group + j;
             __builtin_nontemporal_store(val, dst + (s * h + hd) * row_vecs + c);
@@ -50,9 +87,15 @@ hipError_t launch_vb(const ExpandArgs& a, hipStream_t stream) {
     const uint64_t nvec = static_cast<uint64_t>(a.seq) * a.hg * row_vecs;
     uint64_t blocks = (nvec + kThreads - 1) / kThreads;
     if (blocks > (1u << 22)) blocks = 1u << 22;               // grid-stride beyond this
-    hipLaunchKernelGGL((gqa_expand_kernel<VB>), dim3(static_cast<uint32_t>(blocks)), dim3(kThreads),
-                       0, stream, static_cast<const V*>(a.src), static_cast<V*>(a.dst), nvec, a.hg,
-                       a.h, row_vecs, a.map);
+    const FastDiv dr = make_fastdiv(row_vecs), dh = make_fastdiv(a.hg);
+    if (nvec + static_cast<uint64_t>(blocks) * kThreads <= 0xffffffffull)   // every index fits 32 bits
+        hipLaunchKernelGGL((gqa_expand_kernel<VB, false>), dim3(static_cast<uint32_t>(blocks)),
+                           dim3(kThreads), 0, stream, static_cast<const V*>(a.src), static_cast<V*>(a.dst),
+                           nvec, a.hg, a.h, row_vecs, a.map, dr, dh);
+    else
+        hipLaunchKernelGGL((gqa_expand_kernel<VB, true>), dim3(static_cast<uint32_t>(blocks)),
+                           dim3(kThreads), 0, stream, static_cast<const V*>(a.src), static_cast<V*>(a.dst),
+                           nvec, a.hg, a.h, row_vecs, a.map, dr, dh);
     return hipGetLastError();
 }
 
