@@ -501,6 +501,11 @@ EXPAND = [
     (9, 4, 8, 7, "f32", "block"),
     (32, 16, 32, 128, "bf16", "block"),
     (4096, 16, 32, 128, "f32", "tiled"),      # chunk-prefill q/k expansion
+    # divisors that are not powers of two in both index decompositions
+    (37, 5, 15, 200, "f32", "tiled"),         # 50 vectors per row, hg = 5
+    (101, 7, 21, 96, "bf16", "block"),        # 12 vectors per row, hg = 7
+    (33, 12, 48, 40, "f16", "tiled"),         # 5 vectors per row, hg = 12
+    (3, 48, 96, 24, "bf16", "block"),         # 3 vectors per row, hg = 48
 ]
 
 
