@@ -6,11 +6,11 @@
 // innovation delta = (v - kv) * beta, write delta to the tape, add delta * k to
 // the row and read the updated row out against q into y.
 //
-// The read-out of the updated row is evaluated as
-//     y = (g S) . q + delta * (k . q),
-// which equals (g S + delta k^T) . q exactly in real arithmetic and lets both
-// dot products run in one pass over the decayed row; only the rounding differs
-// from reading the updated row (within the stated tolerances).
+// The read-outs are evaluated as
+//     kv = g (S . k),   y = g (S . q) + delta * (k . q),
+// which equal (g S) . k and (g S + delta k^T) . q exactly in real arithmetic
+// and let both dot products run in one pass over the row before its decay;
+// only the rounding differs (within the stated tolerances).
 //
 // How it maps onto CDNA4 (not the page's one-32-lane-group-per-row layout):
 //  * 16 lanes (one DPP row) share a state row; lane l holds the Dk/16 columns
@@ -42,21 +42,30 @@ namespace gdn {
 namespace {
 
 // This lane's part of a Dk-length dot product over its E columns, in a fixed
-// order, shared by every kernel that needs it.  A step computes two of these
-// chains side by side, which keeps the FMA pipeline busy without splitting
-// each chain.
+// order shared by every kernel that needs it: two interleaved partial sums
+// (even and odd columns) added at the end, so the dependent chain is E/2
+// fused multiply-adds long.
 template <int E>
 __device__ __forceinline__ float lane_dot(const float (&x)[E], const float (&y)[E]) {
-    float a = 0.f;
+    float a = 0.f, b = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) a = fmaf(x[e], y[e], a);
-    return a;
+    for (int e = 0; e + 1 < E; e += 2) {
+        a = fmaf(x[e], y[e], a);
+        b = fmaf(x[e + 1], y[e + 1], b);
+    }
+    if constexpr (E % 2 == 1) a = fmaf(x[E - 1], y[E - 1], a);
+    return a + b;
 }
 
 // One active step on the RPT rows this lane holds (E columns of each):
-// decay, read-outs against k and q, innovation, rank-1 write.  kq = k . q of
-// the step.  d and out receive the innovation and the output of every row
-// (identical bits in all 16 lanes of the row).
+// read-outs against k and q, innovation, decay and rank-1 write.  The
+// read-outs are taken on the row before the decay and scaled by the gate
+// afterwards, kv = g (S . k) and (g S) . q = g (S . q), which equal the
+// read-outs of the decayed row in real arithmetic and take the decay off the
+// step-to-step dependence chain; the state update itself is
+// S <- fma(k, delta, S * g), the same two roundings as the replay's fold.
+// kq = k . q of the step.  d and out receive the innovation and the output of
+// every row (identical bits in all 16 lanes of the row).
 template <int RPT, int E>
 __device__ __forceinline__ void record_step(float (&s)[RPT][E], const float (&kk)[E],
                                             const float (&qq)[E], const float (&vv)[RPT],
@@ -65,16 +74,18 @@ __device__ __forceinline__ void record_step(float (&s)[RPT][E], const float (&kk
     float red[2 * RPT];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) s[r][e] = s[r][e] * gt;          // decay
-        red[r] = lane_dot<E>(s[r], kk);                              // (g S) . k
-        red[RPT + r] = lane_dot<E>(s[r], qq);                        // (g S) . q
+        red[r] = lane_dot<E>(s[r], kk);                              // S . k
+        red[RPT + r] = lane_dot<E>(s[r], qq);                        // S . q
     }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[r][e] = s[r][e] * gt;          // decay, off the chain
     row16_sum_n<2 * RPT>(red);
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
-        d[r] = (vv[r] - red[r]) * beta;
-        out[r] = fmaf(d[r], kq, red[RPT + r]);
+        d[r] = (vv[r] - gt * red[r]) * beta;
+        out[r] = fmaf(d[r], kq, gt * red[RPT + r]);
     }
 #pragma unroll
     for (int r = 0; r < RPT; ++r)
@@ -383,7 +394,6 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
         // Steps in groups of kGroup: the group's LDS reads are issued together
         // (straight-line code, so each step waits only for its own operands),
         // then its steps run.  Rows past the tape end are padding with mask 0.
-        StepOperands<E, RPT> op[G];
         auto run = [&](const StepOperands<E, RPT>& op, int tt) {
             if constexpr (MASKED) {
                 if (__builtin_amdgcn_readfirstlane(__float_as_uint(op.sc.w)) == 0u) return;   // inactive
@@ -395,6 +405,7 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
             for (int r = 0; r < RPT; ++r) { pair[2 * r] = out[r]; pair[2 * r + 1] = d[r]; }
             lds_store_vec<2 * RPT>(oyd + (tt * R + slot * RPT) * 2, pair);
         };
+        StepOperands<E, RPT> op[G];
         for (int t4 = 0; t4 < valid; t4 += G) {
 #pragma unroll
             for (int u = 0; u < G; ++u) op[u].template read<DK, R>(sk, sq, sv, sc, t4 + u, lane, slot);
