@@ -138,6 +138,10 @@ RAGGED = [
     (5, 1, 2, 8, 128, 80, "bf16", "block", "ones"),
     (4, 9, 2, 4, 128, 128, "f16", "tiled", "bernoulli"),
     (1, 33, 1, 2, 32, 32, "f32", "tiled", "none"),
+    # the largest head the library takes: Dk = 256, Dv = 1024 (1 MiB of state per head)
+    (2, 1, 1, 2, 256, 1024, "bf16", "block", "ones"),
+    (1, 5, 1, 1, 256, 1024, "f32", "block", "bernoulli"),
+    (1, 40, 1, 1, 256, 1024, "bf16", "block", "none"),
 ]
 
 
@@ -275,6 +279,7 @@ def test_replay_long_fold_on_matrix_cores(case, monkeypatch):
 
 
 @pytest.mark.parametrize("case", [(3, 5, 2, 32, 16, "f32"), (2, 6, 3, 64, 48, "bf16"),
+                                  (1, 20, 1, 256, 1024, "f16"), (2, 3, 1, 256, 1024, "f32"),
                                   (1, 4, 4, 192, 128, "f16"), (2, 3, 2, 256, 32, "bf16")],
                          ids=lambda c: "B%d_T%d_Hv%d_Dk%d_Dv%d_%s" % c)
 def test_replay_ragged_shapes(case):
