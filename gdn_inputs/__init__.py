@@ -191,3 +191,14 @@ def norm_inputs(n_tokens, dim, seed=0):
     x = torch.from_numpy(r.standard_normal((n_tokens, dim)).astype(np.float32))
     w = torch.from_numpy((1.0 + 0.1 * r.standard_normal(dim)).astype(np.float32)).to(torch.bfloat16)
     return x, w
+
+
+def norm_inputs_on_device(n_tokens, dim, device, seed=0):
+    """norm_inputs' distributions for sizes too large to draw on the host: x
+    ~ N(0, 1) float32 [n, dim] drawn on `device` by torch's seeded generator,
+    and the bf16 weight [dim] as a CPU tensor (from the host generator)."""
+    x = torch.empty((n_tokens, dim), dtype=torch.float32, device=device)
+    x.normal_(generator=torch.Generator(device=device).manual_seed(seed))
+    r = rng(seed)
+    w = torch.from_numpy((1.0 + 0.1 * r.standard_normal(dim)).astype(np.float32)).to(torch.bfloat16)
+    return x, w

@@ -105,7 +105,11 @@ typedef enum gdn_status {
  *   k_log             optional output, io_dtype [B,T,Hv,Dk], or NULL.
  *   g_log             optional output, io_dtype [B,T,Hv], or NULL.
  *   B, T, Hk, Hv, Dk, Dv  sizes; Hk must divide Hv.  Dk in {32,64,128,192,256};
- *                     Dv a multiple of 16, at most 1024.
+ *                     Dv a multiple of 16, at most 1024.  One launch covers
+ *                     all B*Hv*Dv state rows with at most 2^32 - 1 threads
+ *                     (16 per row, fewer with several rows per thread);
+ *                     past that the call fails with GDN_ERR_OVERFLOW (split
+ *                     the batch).
  *   io_dtype          gdn_dtype of every non-state tensor.
  *   gqa_map           gdn_gqa_map.
  *   stream            hipStream_t or NULL.
@@ -139,7 +143,7 @@ int gdn_record(const void* q, const void* k, const void* v, const void* g, const
  *   state_in    float32 [B,Hv,Dv,Dk], the snapshot taken before the record.
  *   mask        uint32 [B,T_log] or NULL.
  *   state_out   float32 [B,Hv,Dv,Dk]; may be exactly state_in.
- *   B, T_log, Hv, Dk, Dv, accepted   sizes as for gdn_record.
+ *   B, T_log, Hv, Dk, Dv, accepted   sizes and limits as for gdn_record.
  *   io_dtype, stream                 as for gdn_record.
  * Returns GDN_OK or a negative gdn_status.
  */

@@ -38,7 +38,9 @@ bool mul_u64(uint64_t* out, std::initializer_list<uint64_t> xs) {
 }
 
 constexpr uint64_t kMaxBytes = uint64_t(1) << 48;   // 256 TiB: far beyond any device, safe for offsets
-constexpr uint64_t kMaxGrid = 0x7fffffffull;
+// A launch covers at most 2^32 - 1 work-items (the dispatch packet's grid
+// size is 32 bits wide).
+constexpr uint64_t kMaxWorkItems = 0xffffffffull;
 
 struct Span {
     const void* p;
@@ -118,9 +120,10 @@ int gdn_record(const void* q, const void* k, const void* v, const void* g, const
     gdn::RecordArgs a{q, k, v, g, beta, state_in, mask, y, state_out, delta_log, k_log, g_log,
                       B, T, Hk, Hv, Dk, Dv, io_dtype, gqa_map};
     const gdn::RowTiling til = gdn::record_tiling(a);
-    uint64_t grid;
-    if (!mul_u64(&grid, {B, Hv, Dv / static_cast<uint32_t>(til.rows())}) || grid > kMaxGrid)
-        return fail(GDN_ERR_OVERFLOW, "%s: launch grid too large (B*Hv too large)", kFn);
+    uint64_t items;
+    if (!mul_u64(&items, {B, Hv, Dv / static_cast<uint32_t>(til.rows()), static_cast<uint32_t>(til.threads)}) ||
+        items > kMaxWorkItems)
+        return fail(GDN_ERR_OVERFLOW, "%s: launch grid too large (B*Hv*Dv too large for one launch)", kFn);
 
     const void* a16[] = {q, k, v, state_in, y, state_out, delta_log, k_log};
     const char* a16n[] = {"q", "k", "v", "state_in", "y", "state_out", "delta_log", "k_log"};
@@ -177,9 +180,10 @@ int gdn_replay(const void* delta_log, const void* k_log, const void* g_log,
     gdn::ReplayArgs a{delta_log, k_log, g_log, state_in, mask, state_out,
                       B, T_log, Hv, Dk, Dv, accepted < T_log ? accepted : T_log, io_dtype};
     const gdn::RowTiling til = gdn::replay_tiling(a);
-    uint64_t grid;
-    if (!mul_u64(&grid, {B, Hv, Dv / static_cast<uint32_t>(til.rows())}) || grid > kMaxGrid)
-        return fail(GDN_ERR_OVERFLOW, "%s: launch grid too large (B*Hv too large)", kFn);
+    uint64_t items;
+    if (!mul_u64(&items, {B, Hv, Dv / static_cast<uint32_t>(til.rows()), static_cast<uint32_t>(til.threads)}) ||
+        items > kMaxWorkItems)
+        return fail(GDN_ERR_OVERFLOW, "%s: launch grid too large (B*Hv*Dv too large for one launch)", kFn);
 
     const void* a16[] = {delta_log, k_log, state_in, state_out};
     const char* a16n[] = {"delta_log", "k_log", "state_in", "state_out"};
@@ -228,7 +232,6 @@ int rms_norm_bf16(const float* x, const uint16_t* weight, float* out, uint32_t n
     uint64_t n_x;
     if (!mul_u64(&n_x, {n_tokens, dim, 4}) || n_x > kMaxBytes)
         return fail(GDN_ERR_OVERFLOW, "%s: n_tokens*dim overflows", kFn);
-    if (n_tokens > kMaxGrid) return fail(GDN_ERR_OVERFLOW, "%s: too many tokens for one launch", kFn);
     if (!aligned(x, 4) || !aligned(out, 4) || !aligned(weight, 2))
         return fail(GDN_ERR_MISALIGNED, "%s: x and out must be 4-byte aligned, weight 2-byte", kFn);
     const Span sx{x, n_x, "x"}, so{out, n_x, "out"}, sw{weight, uint64_t(dim) * 2, "weight"};

@@ -407,8 +407,8 @@ bool replay_mfma_applies(const ReplayArgs& a) {
         from = static_cast<uint32_t>(v);
     }
     if (a.steps < from || a.Dv % 64 != 0) return false;       // whole 64-row workgroups
-    // grid: one workgroup per (head, slice of at least 16 rows)
-    return static_cast<uint64_t>(a.B) * a.Hv * (a.Dv / 16) <= 0x7fffffffull;
+    // four work-items per state row (64 per 16-row wave), 2^32 - 1 at most per launch
+    return static_cast<uint64_t>(a.B) * a.Hv * a.Dv * 4 <= 0xffffffffull;
 }
 
 hipError_t launch_replay_mfma(const ReplayArgs& a, hipStream_t stream) {

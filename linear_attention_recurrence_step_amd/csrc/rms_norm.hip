@@ -47,34 +47,38 @@ __device__ __forceinline__ float rms_scale(float ss, uint32_t dim, float eps) {
 // row, so the row is read from HBM once and written once.
 template <int NT, int MAXV>
 __global__ __launch_bounds__(NT) void rms_norm_vec_kernel(
-    const float* x, const uint16_t* __restrict__ w, float* out, uint32_t dim, float eps)
+    const float* x, const uint16_t* __restrict__ w, float* out, uint32_t n_tokens, uint32_t dim,
+    float eps)
 {
     __shared__ float red[NT / 64];
-    const size_t row = static_cast<size_t>(blockIdx.x) * dim;
     const uint32_t nv = dim / 4;
-    f32x4 v[MAXV];
-    float ss = 0.f;
+    for (uint32_t t = blockIdx.x; t < n_tokens; t += gridDim.x) {
+        const size_t row = static_cast<size_t>(t) * dim;
+        f32x4 v[MAXV];
+        float ss = 0.f;
 #pragma unroll
-    for (int j = 0; j < MAXV; ++j) {
-        const uint32_t p = threadIdx.x + j * NT;
-        v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (p < nv) v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x + row) + p);
-    }
-#pragma unroll
-    for (int j = 0; j < MAXV; ++j)
-        ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
-    const float r = rms_scale(block_sum<NT>(ss, red), dim, eps);
-#pragma unroll
-    for (int j = 0; j < MAXV; ++j) {
-        const uint32_t p = threadIdx.x + j * NT;
-        if (p < nv) {
-            const u32x2 wb = *reinterpret_cast<const u32x2*>(w + 4 * p);
-            const f32x4 o = {v[j].x * r * bf16_bits_to_f32(wb.x & 0xffffu),
-                             v[j].y * r * bf16_bits_to_f32(wb.x >> 16),
-                             v[j].z * r * bf16_bits_to_f32(wb.y & 0xffffu),
-                             v[j].w * r * bf16_bits_to_f32(wb.y >> 16)};
-            reinterpret_cast<f32x4*>(out + row)[p] = o;
+        for (int j = 0; j < MAXV; ++j) {
+            const uint32_t p = threadIdx.x + j * NT;
+            v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (p < nv) v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x + row) + p);
         }
+#pragma unroll
+        for (int j = 0; j < MAXV; ++j)
+            ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+        const float r = rms_scale(block_sum<NT>(ss, red), dim, eps);
+#pragma unroll
+        for (int j = 0; j < MAXV; ++j) {
+            const uint32_t p = threadIdx.x + j * NT;
+            if (p < nv) {
+                const u32x2 wb = *reinterpret_cast<const u32x2*>(w + 4 * p);
+                const f32x4 o = {v[j].x * r * bf16_bits_to_f32(wb.x & 0xffffu),
+                                 v[j].y * r * bf16_bits_to_f32(wb.x >> 16),
+                                 v[j].z * r * bf16_bits_to_f32(wb.y & 0xffffu),
+                                 v[j].w * r * bf16_bits_to_f32(wb.y >> 16)};
+                reinterpret_cast<f32x4*>(out + row)[p] = o;
+            }
+        }
+        if constexpr (NT > 64) __syncthreads();               // red is reused by the next token
     }
 }
 
@@ -83,23 +87,33 @@ __global__ __launch_bounds__(NT) void rms_norm_vec_kernel(
 // before any of them is written, and no thread writes an element another one
 // reads, so out may be x itself.
 __global__ __launch_bounds__(kNormThreads) void rms_norm_any_kernel(
-    const float* x, const uint16_t* __restrict__ w, float* out, uint32_t dim, float eps)
+    const float* x, const uint16_t* __restrict__ w, float* out, uint32_t n_tokens, uint32_t dim,
+    float eps)
 {
     __shared__ float red[kNormThreads / 64];
-    const size_t row = static_cast<size_t>(blockIdx.x) * dim;
-    float ss = 0.f;
-    for (uint32_t i = threadIdx.x; i < dim; i += kNormThreads) ss += x[row + i] * x[row + i];
-    const float r = rms_scale(block_sum<kNormThreads>(ss, red), dim, eps);
-    for (uint32_t i = threadIdx.x; i < dim; i += kNormThreads)
-        out[row + i] = x[row + i] * r * bf16_bits_to_f32(w[i]);
+    for (uint32_t t = blockIdx.x; t < n_tokens; t += gridDim.x) {
+        const size_t row = static_cast<size_t>(t) * dim;
+        float ss = 0.f;
+        for (uint32_t i = threadIdx.x; i < dim; i += kNormThreads) ss += x[row + i] * x[row + i];
+        const float r = rms_scale(block_sum<kNormThreads>(ss, red), dim, eps);
+        for (uint32_t i = threadIdx.x; i < dim; i += kNormThreads)
+            out[row + i] = x[row + i] * r * bf16_bits_to_f32(w[i]);
+        __syncthreads();                                      // red is reused by the next token
+    }
 }
 
 }  // namespace
 
+// One workgroup per token, up to this many workgroups; beyond, each one
+// takes every kMaxNormGroups-th token (a launch covers at most 2^32 - 1
+// work-items).
+constexpr uint32_t kMaxNormGroups = 1u << 16;
+
 template <int NT, int MAXV>
 hipError_t launch_vec(const RmsNormArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((rms_norm_vec_kernel<NT, MAXV>), dim3(a.n_tokens), dim3(NT), 0, stream,
-                       a.x, a.weight, a.out, a.dim, a.eps);
+    const uint32_t grid = a.n_tokens < kMaxNormGroups ? a.n_tokens : kMaxNormGroups;
+    hipLaunchKernelGGL((rms_norm_vec_kernel<NT, MAXV>), dim3(grid), dim3(NT), 0, stream,
+                       a.x, a.weight, a.out, a.n_tokens, a.dim, a.eps);
     return hipGetLastError();
 }
 
@@ -118,8 +132,9 @@ hipError_t launch_rms_norm(const RmsNormArgs& a, hipStream_t stream) {
     }
     if (vec && nv <= 128u * 8) return launch_vec<128, 8>(a, stream);
     if (vec && nv <= 256u * 8) return launch_vec<256, 8>(a, stream);
-    hipLaunchKernelGGL(rms_norm_any_kernel, dim3(a.n_tokens), dim3(kNormThreads), 0, stream, a.x,
-                       a.weight, a.out, a.dim, a.eps);
+    const uint32_t grid = a.n_tokens < kMaxNormGroups ? a.n_tokens : kMaxNormGroups;
+    hipLaunchKernelGGL(rms_norm_any_kernel, dim3(grid), dim3(kNormThreads), 0, stream, a.x,
+                       a.weight, a.out, a.n_tokens, a.dim, a.eps);
     return hipGetLastError();
 }
 

@@ -122,6 +122,9 @@ CASES = [
     ("rec_dv2048", "gdn_record", rec(Dv=2048), SHAPE),
     ("rec_bytes_overflow", "gdn_record", rec(B=1 << 31, T=1 << 31), OVER),
     ("rec_grid_overflow", "gdn_record", rec(B=1 << 20, T=1, Hk=1 << 12, Hv=1 << 12, Dk=32, Dv=16), OVER),
+    # 2^30 state rows: 2^25 workgroups of 256 threads, 2^33 threads in one launch
+    ("rec_work_items_overflow", "gdn_record", rec(B=1 << 20, T=1, Hk=1, Hv=1, Dk=32, Dv=1024), OVER),
+    ("rep_work_items_overflow", "gdn_replay", rep(B=1 << 20, T=1, Hv=1, Dk=32, Dv=1024, acc=1), OVER),
     ("rec_misaligned_q", "gdn_record", rec(q=P(0, 2)), ALIGN),
     ("rec_misaligned_state", "gdn_record", rec(s_in=P(5, 8)), ALIGN),
     ("rec_misaligned_mask", "gdn_record", rec(mask=P(6, 2)), ALIGN),
@@ -157,7 +160,6 @@ CASES = [
     ("rms_out_overlaps_x", "rms_norm_bf16", rms(out=P(0, 16)), ALIAS),
     ("rms_out_overlaps_weight", "rms_norm_bf16", rms(out=P(1, 64)), ALIAS),
     ("rms_bytes_overflow", "rms_norm_bf16", rms(n=1 << 31, dim=1 << 20), OVER),
-    ("rms_too_many_tokens", "rms_norm_bf16", rms(n=1 << 31, dim=1), OVER),
     ("exp_bad_dtype", "gqa_expand", exp(dt=7), ENUM),
     ("exp_bad_map", "gqa_expand", exp(map=-1), ENUM),
     ("exp_null_dst", "gqa_expand", exp(dst=None), NULL),

@@ -92,3 +92,21 @@ def test_rms_norm_golden_case_exact():
     ref = np.array(gold["out"])
     np.testing.assert_allclose(f64(got)[[0, 2]], ref[[0, 2]], rtol=0, atol=0)
     np.testing.assert_allclose(f64(got)[1], ref[1], rtol=1e-6)
+
+
+# Past 65536 tokens each workgroup takes several tokens in turn (a launch
+# covers at most 2^32 - 1 threads); rows on both sides of the wrap are checked
+# against the oracle, for every thread count and for the general path.
+@pytest.mark.parametrize("dim", [4, 2048, 4096, 8192, 3])
+def test_rms_norm_more_tokens_than_workgroups(dim):
+    n = 65536 + 37
+    note("rms_norm n=%d dim=%d (workgroups take several tokens)" % (n, dim))
+    xd, w = gi.norm_inputs_on_device(n, dim, dev(), seed=dim)
+    got = gdn.rms_norm_bf16(xd, w.to(dev()), 1e-6)
+    torch.cuda.synchronize()
+    rows = [0, 1, 65535, 65536, 65537, n - 1]
+    x = xd[rows].cpu()
+    ref = oracle.rms_norm_bf16(x, w, 1e-6)
+    out = f64(got[rows])
+    assert np.max(np.abs(out - ref) / (np.abs(ref) + 1e-6)) <= RTOL
+    del xd, got
