@@ -354,6 +354,55 @@ def test_chained_single_steps_equal_one_call_bitwise():
     assert torch.equal(st.to(dev()), s)
 
 
+def _bit_view(t):
+    """The raw bit patterns of a device tensor (so that -0 differs from +0)."""
+    return t.view({4: torch.int32, 2: torch.int16}[t.element_size()])
+
+
+# P-h on the HIP path: accepting a positions equals taking the whole tape with
+# the mask cleared from position a on.  Both calls run the same path (the VALU
+# fold below 16 positions and for float32 tapes, the matrix-core fold from 16
+# positions of a 16-bit tape), so the bits agree.
+@pytest.mark.parametrize("case", [(3, 6, 4, 128, 64, "f32", (0, 1, 4, 6)),
+                                  (4, 12, 4, 128, 128, "bf16", (0, 3, 11)),
+                                  (4, 64, 4, 128, 128, "f16", (16, 20, 40, 63))],
+                         ids=lambda c: "T%d_%s" % (c[1], c[5]))
+def test_accepted_equals_masking_the_tail_bitwise(case):
+    B, T, Hv, Dk, Dv, io, accepted = case
+    tape = gi.tape_inputs(B, T, Hv, Dk, Dv, io, seed=61 + T, mask="bernoulli")
+    d = to_dev(tape)
+    for a in accepted:
+        note("replay accepted=%d vs tail-masked full tape, T=%d %s" % (a, T, io))
+        m2 = d["mask"].clone()
+        m2[:, a:] = 0
+        s1 = gdn.gdn_replay(d["delta_log"], d["k_log"], d["g_log"], d["state_in"], d["mask"], a)
+        s2 = gdn.gdn_replay(d["delta_log"], d["k_log"], d["g_log"], d["state_in"], m2, T)
+        torch.cuda.synchronize()
+        assert torch.equal(_bit_view(s1), _bit_view(s2)), a
+
+
+# P-l on the HIP path: batch rows are independent, so permuting them permutes
+# every output bit for bit (record with its tape, then the replay of that tape).
+def test_batch_permutation_permutes_outputs_bitwise():
+    inp = gi.record_inputs(6, 4, 2, 4, 128, 128, "bf16", seed=71, mask="trailing")
+    perm = torch.tensor([3, 0, 5, 1, 4, 2])
+    pinp = {k2: (v[perm] if v is not None else None) for k2, v in inp.items()}
+    note("record of permuted batch rows")
+    s_a, dl_a, kl_a, d_a = _tape_from_record(inp, "block")
+    s_b, dl_b, kl_b, d_b = _tape_from_record(pinp, "block")
+    y_a, _, _ = _record_gpu(inp, "block")
+    y_b, _, _ = _record_gpu(pinp, "block")
+    pd = perm.to(dev())
+    assert torch.equal(_bit_view(y_a[pd]), _bit_view(y_b))
+    assert torch.equal(_bit_view(dl_a[pd]), _bit_view(dl_b))
+    assert torch.equal(_bit_view(s_a[pd]), _bit_view(s_b))
+    note("replay of permuted batch rows")
+    r_a = gdn.gdn_replay(dl_a, kl_a, d_a["g"], d_a["state_in"], d_a["mask"], 3)
+    r_b = gdn.gdn_replay(dl_b, kl_b, d_b["g"], d_b["state_in"], d_b["mask"], 3)
+    torch.cuda.synchronize()
+    assert torch.equal(_bit_view(r_a[pd]), _bit_view(r_b))
+
+
 def test_every_tiling_gives_identical_bits(monkeypatch):
     inp = gi.record_inputs(2, 3, 2, 4, 128, 128, "bf16", seed=51, mask="bernoulli")
     tape = gi.tape_inputs(2, 3, 4, 128, 128, "bf16", seed=52)
