@@ -35,6 +35,7 @@
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
+#include <atomic>
 #include <cstdlib>
 #include <cstdio>
 
@@ -197,10 +198,17 @@ __global__ __launch_bounds__(NT) void gdn_record_kernel(
 
 // ------------------------------------------------------------ staged kernel
 
-// Chunk length of the staged kernel: the inputs of up to this many steps sit
-// in LDS at once (as float32).
+// Chunk lengths of the staged kernel: the inputs of up to TC steps sit in LDS
+// at once (as float32), and the next chunk's loads wait in registers.  A
+// longer chunk pays its barriers and staging over more steps but costs LDS
+// and registers, so the length follows the launch: 8 (short tapes), 16 (up to
+// 16 steps), 32 (16 at Dk above 128) for long tapes, and 64 for long tapes
+// whose grid leaves each CU at most one workgroup (a prefill over few heads),
+// where occupancy is not at stake.
 template <int DK>
 constexpr int staged_chunk() { return DK <= 128 ? 32 : 16; }
+constexpr int kMediumChunk = 16;
+constexpr int kWideChunk = 64;
 
 // Steps whose LDS operands are read together; LDS chunks are padded to a
 // multiple of this many rows.
@@ -254,10 +262,10 @@ struct StepOperands {
 // computes k . q of each step once, and loads the following chunk into
 // registers while it computes the current one from LDS.  y and delta of the
 // chunk are gathered in LDS and written with vector stores after it.
-// SHORT: tapes of at most kShortChunk steps take one small chunk and read the
-// operands of one step at a time, which keeps the register count (and so
-// the occupancy) of this latency-bound case low.
-template <int IO, int DK, int RPT, int NT, bool MASKED, bool SHORT>
+// TC = kShortChunk (tapes of at most that many steps): one small chunk whose
+// operands are read one step at a time, which keeps the register count (and
+// so the occupancy) of this latency-bound case low.
+template <int IO, int DK, int RPT, int NT, bool MASKED, int TC>
 __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const void* __restrict__ g, const void* __restrict__ beta,
@@ -273,7 +281,7 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
     constexpr int NC = E / W;
     constexpr int SLOTS = NT / L;
     constexpr int R = SLOTS * RPT;
-    constexpr int TC = SHORT ? kShortChunk : staged_chunk<DK>();
+    constexpr bool SHORT = TC <= static_cast<int>(kShortChunk);
     constexpr int G = SHORT ? 1 : kGroup;                     // steps whose operands are read together
     constexpr int EB = IoTraits<IO>::kBytes;
     constexpr int PR = piece_elems<IO, R>();                  // v / y / delta piece (elements)
@@ -420,6 +428,24 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
     for (int r = 0; r < RPT; ++r) store_state_row<W, NC, E>(state_out + srow + r * DK, lane, s[r]);
 }
 
+// Compute units of the current device (cached per device; 256, the MI355X
+// count, if the runtime cannot say).
+uint32_t compute_units() {
+    constexpr int kDevices = 64;
+    static std::atomic<uint32_t> cache[kDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 256;
+    uint32_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        c = static_cast<uint32_t>(n);
+        cache[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
+
 template <int IO, int DK, int RPT, int NT>
 hipError_t launch_cfg(const RecordArgs& a, hipStream_t stream) {
     constexpr int R = RPT * NT / 16;
@@ -433,22 +459,33 @@ hipError_t launch_cfg(const RecordArgs& a, hipStream_t stream) {
         return hipGetLastError();
     }
     if constexpr (R <= kStagedMaxRows) {
-        const bool short_tape = a.T <= kShortChunk;
-        const uint32_t crow = short_tape ? a.T : chunk_alloc_rows(staged_chunk<DK>(), a.T);
-        const size_t lds = record_lds_floats(static_cast<int>(crow), DK, R) * sizeof(float);
-        auto go = [&](auto kernel) {
-            hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(grid)), dim3(NT), lds, stream, a.q,
-                               a.k, a.v, a.g, a.beta, a.state_in, a.mask, a.y, a.state_out,
-                               a.delta_log, a.k_log, a.g_log, a.T, a.Hk, a.Hv, a.Dv, row_blocks,
-                               a.map, crow);
-        };
         const bool masked = a.mask != nullptr;
-        if (short_tape) {
-            if (masked) go(gdn_record_staged_kernel<IO, DK, RPT, NT, true, true>);
-            else go(gdn_record_staged_kernel<IO, DK, RPT, NT, false, true>);
+        auto go = [&](auto kernel_masked, auto kernel_plain, uint32_t crow) {
+            const size_t lds = record_lds_floats(static_cast<int>(crow), DK, R) * sizeof(float);
+            hipLaunchKernelGGL(masked ? kernel_masked : kernel_plain, dim3(static_cast<uint32_t>(grid)),
+                               dim3(NT), lds, stream, a.q, a.k, a.v, a.g, a.beta, a.state_in, a.mask,
+                               a.y, a.state_out, a.delta_log, a.k_log, a.g_log, a.T, a.Hk, a.Hv, a.Dv,
+                               row_blocks, a.map, crow);
+        };
+        if (a.T <= kShortChunk) {
+            go(gdn_record_staged_kernel<IO, DK, RPT, NT, true, kShortChunk>,
+               gdn_record_staged_kernel<IO, DK, RPT, NT, false, kShortChunk>, a.T);
+        } else if (a.T <= static_cast<uint32_t>(kMediumChunk) || staged_chunk<DK>() <= kMediumChunk) {
+            go(gdn_record_staged_kernel<IO, DK, RPT, NT, true, kMediumChunk>,
+               gdn_record_staged_kernel<IO, DK, RPT, NT, false, kMediumChunk>,
+               chunk_alloc_rows(kMediumChunk, a.T));
         } else {
-            if (masked) go(gdn_record_staged_kernel<IO, DK, RPT, NT, true, false>);
-            else go(gdn_record_staged_kernel<IO, DK, RPT, NT, false, false>);
+            constexpr int TC = staged_chunk<DK>();
+            if constexpr (RPT == 1 && DK <= 128) {
+                if (grid <= compute_units()) {
+                    go(gdn_record_staged_kernel<IO, DK, RPT, NT, true, kWideChunk>,
+                       gdn_record_staged_kernel<IO, DK, RPT, NT, false, kWideChunk>,
+                       chunk_alloc_rows(kWideChunk, a.T));
+                    return hipGetLastError();
+                }
+            }
+            go(gdn_record_staged_kernel<IO, DK, RPT, NT, true, TC>,
+               gdn_record_staged_kernel<IO, DK, RPT, NT, false, TC>, chunk_alloc_rows(TC, a.T));
         }
         return hipGetLastError();
     }

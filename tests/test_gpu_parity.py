@@ -138,6 +138,12 @@ RAGGED = [
     (5, 1, 2, 8, 128, 80, "bf16", "block", "ones"),
     (4, 9, 2, 4, 128, 128, "f16", "tiled", "bernoulli"),
     (1, 33, 1, 2, 32, 32, "f32", "tiled", "none"),
+    # chunk lengths: 16 (up to 16 steps), 32 (a grid of more workgroups than
+    # CUs), 64 (long tapes over few heads), each with a ragged last chunk
+    (2, 14, 2, 4, 64, 64, "f32", "block", "none"),
+    (4, 37, 8, 16, 128, 128, "bf16", "block", "bernoulli"),
+    (1, 150, 2, 4, 128, 128, "bf16", "tiled", "bernoulli"),
+    (1, 131, 1, 2, 64, 32, "f16", "block", "none"),
     # the largest head the library takes: Dk = 256, Dv = 1024 (1 MiB of state per head)
     (2, 1, 1, 2, 256, 1024, "bf16", "block", "ones"),
     (1, 5, 1, 1, 256, 1024, "f32", "block", "bernoulli"),
@@ -403,8 +409,12 @@ def test_batch_permutation_permutes_outputs_bitwise():
     assert torch.equal(_bit_view(r_a[pd]), _bit_view(r_b))
 
 
-def test_every_tiling_gives_identical_bits(monkeypatch):
-    inp = gi.record_inputs(2, 3, 2, 4, 128, 128, "bf16", seed=51, mask="bernoulli")
+@pytest.mark.parametrize("T", [3, 12, 40])
+def test_every_tiling_gives_identical_bits(monkeypatch, T):
+    """Row tilings (and with them the staged kernel's chunk lengths: one row
+    per thread over few heads takes 64-step chunks, more rows per thread 32)
+    change no bit of any output."""
+    inp = gi.record_inputs(2, T, 2, 4, 128, 128, "bf16", seed=51, mask="bernoulli")
     tape = gi.tape_inputs(2, 3, 4, 128, 128, "bf16", seed=52)
     ref = None
     for til in ("8,256", "4,256", "2,256", "1,256", "1,64"):
