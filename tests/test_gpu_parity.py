@@ -657,3 +657,41 @@ def test_graph_captured_step_replays_match_eager_bitwise():
         for i, (a, b) in enumerate(zip(got, (y, dl, kl, gl, s1, s2, on))):
             bits = torch.int32 if a.element_size() == 4 else torch.int16
             assert torch.equal(a.view(bits), b.view(bits)), (rep, i)
+
+
+# ------------------------------------------------------- seeded shape sweep
+
+def _sweep_cases(n=48, seed=2026):
+    """A fixed, seeded list of mixed configurations: every supported Dk, value
+    widths that are and are not multiples of the row blocks, GQA ratios,
+    tapes that are short, medium and long (every staged chunk length, ragged
+    last chunks), all I/O dtypes, maps and mask kinds, and replays on either
+    fold (VALU, or matrix cores for 16+ positions of a 16-bit tape)."""
+    r = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        Dk = int(r.choice([32, 64, 128, 192, 256]))
+        Dv = int(r.choice([16, 32, 48, 64, 80, 128, 192, 256]))
+        Hk = int(r.integers(1, 4))
+        Hv = Hk * int(r.integers(1, 4))
+        B = int(r.integers(1, 5))
+        T = int(r.choice([1, 2, 5, 8, 9, 13, 16, 17, 31, 40, 65, 70]))
+        while B * Hv * Dv * Dk * T > 6_000_000 and T > 1:   # keep the oracle to about a second
+            T //= 2
+        io = str(r.choice(["f32", "f16", "bf16"]))
+        gmap = str(r.choice(["block", "tiled"]))
+        mask = str(r.choice(["none", "ones", "trailing", "bernoulli", "zeros"]))
+        acc = int(r.integers(0, T + 3))
+        cases.append((B, T, Hk, Hv, Dk, Dv, io, gmap, mask, acc, seed + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(),
+                         ids=lambda c: "B%d_T%d_Hk%d_Hv%d_Dk%d_Dv%d_%s_%s_%s_a%d_s%d" % c)
+def test_seeded_shape_sweep(case):
+    B, T, Hk, Hv, Dk, Dv, io, gmap, mask, acc, seed = case
+    inp = gi.record_inputs(B, T, Hk, Hv, Dk, Dv, io, seed=seed, mask=mask)
+    _check_record(inp, gmap, "sweep %s" % (case,))
+    tape = gi.tape_inputs(B, T, Hv, Dk, Dv, io, seed=seed + 1,
+                          mask=mask if mask != "none" else "bernoulli")
+    _check_replay(gi.poison_untaken(tape, acc), acc, "sweep %s" % (case,))
