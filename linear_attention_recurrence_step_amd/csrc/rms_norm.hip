@@ -75,7 +75,7 @@ __global__ __launch_bounds__(NT) void rms_norm_vec_kernel(
                                  v[j].y * r * bf16_bits_to_f32(wb.x >> 16),
                                  v[j].z * r * bf16_bits_to_f32(wb.y & 0xffffu),
                                  v[j].w * r * bf16_bits_to_f32(wb.y >> 16)};
-                reinterpret_cast<f32x4*>(out + row)[p] = o;
+                __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(out + row) + p);
             }
         }
         if constexpr (NT > 64) __syncthreads();               // red is reused by the next token
