@@ -90,17 +90,19 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, label: str = None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if there is none for this kernel and workload or the kernel's source
-    changed since the counters were taken."""
+    None if there is none for this kernel, workload and launch label (an
+    entry without a label stands for every launch of the kernel) or the
+    kernel's source changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             entries = json.load(f)
     except (OSError, ValueError):
         return None
     for ent in entries.get("entries", []):
-        if ent.get("kernel") == kernel and ent.get("workload") == workload:
+        if ent.get("kernel") == kernel and ent.get("workload") == workload and \
+                ent.get("label", label) == label:
             if ent.get("source_sha256") == kernel_source_hash(kernel):
                 return ent.get("traffic_bytes")
     return None
@@ -540,7 +542,7 @@ def main():
     dk = kernels[dom]
     roofline = {"bound": "hbm", "achieved": dk["GB/s"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(dk["GB/s"] / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic(dk["kernel"], args.workload),
+                "traffic": measured_traffic(dk["kernel"], args.workload, dk["name"]),
                 "kernel": dk["name"], "bytes_per_launch": dk["algorithmic_bytes"],
                 "us_per_launch": dk["us"]}
 
