@@ -300,17 +300,28 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
     const uint32_t lane = threadIdx.x & (L - 1);
     const uint32_t slot = threadIdx.x / L;
     const uint32_t blk = xcd_contiguous_index(blockIdx.x, gridDim.x);
-    const size_t srow = (static_cast<size_t>(blk) * R + slot * RPT) * DK;
+
+    // Workgroups are ordered (b, key head, value head of that key head, row
+    // block), so the value heads that read one key head's q and k run next
+    // to each other, on one XCD and its L2.  Under the block map that is the
+    // natural head order; under the tiled map value head hv = j * Hk + hk.
+    const uint32_t nord = blk / row_blocks;
+    const uint32_t wrow0 = (blk - nord * row_blocks) * R;     // first row of the group in its head
+    const uint32_t b = nord / Hv;
+    const uint32_t hpos = nord - b * Hv;                      // position of the head in that order
+    uint32_t hv = hpos, hk;
+    if (tiled) {
+        const uint32_t group = Hv / Hk;
+        hk = hpos / group;
+        hv = (hpos - hk * group) * Hk + hk;
+    } else {
+        hk = hpos / (Hv / Hk);
+    }
+    const size_t srow = ((static_cast<size_t>(b) * Hv + hv) * Dv + wrow0 + slot * RPT) * DK;
 
     float s[RPT][E];
 #pragma unroll
     for (int r = 0; r < RPT; ++r) load_state_row<W, NC, E>(state_in + srow + r * DK, lane, s[r]);
-
-    const uint32_t n = blk / row_blocks;                      // b * Hv + hv
-    const uint32_t wrow0 = (blk - n * row_blocks) * R;        // first row of the group in its head
-    const uint32_t b = n / Hv;
-    const uint32_t hv = n - b * Hv;
-    const uint32_t hk = tiled ? hv % Hk : hv / (Hv / Hk);
 
     ChunkStager<IO, TC, DK, piece_elems<IO, DK>(), NT> stk, stq;
     ChunkStager<IO, TC, R, PR, NT> stv;
