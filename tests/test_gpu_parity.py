@@ -695,3 +695,41 @@ def test_seeded_shape_sweep(case):
     tape = gi.tape_inputs(B, T, Hv, Dk, Dv, io, seed=seed + 1,
                           mask=mask if mask != "none" else "bernoulli")
     _check_replay(gi.poison_untaken(tape, acc), acc, "sweep %s" % (case,))
+
+
+# ------------------------------------------------------- record edge values
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 5, 12, 40, 70])
+def test_record_with_extreme_gates_and_betas(io, T):
+    """Gates of exactly 0 (the state resets to the step's rank-1 write), 1
+    (no decay), tiny and above 1, and beta of exactly 0 and 1, on every path
+    (direct, short, 16-, 32- and 64-step chunks), against the oracle."""
+    B, Hk, Hv, Dk, Dv = 2, 2, 4, 64, 32
+    inp = gi.record_inputs(B, T, Hk, Hv, Dk, Dv, io, seed=81 + T, mask="bernoulli")
+    g = inp["g"].float().clone()
+    beta = inp["beta"].float().clone()
+    g[:, 0::7] = 0.0
+    g[:, 1::5, 0] = 1.0
+    g[:, 2::9, 1] = 1e-6
+    g[:, 3::4, 2] = 1.25
+    beta[:, 1::3] = 0.0
+    beta[:, 2::6] = 1.0
+    inp["g"] = g.to(inp["g"].dtype)
+    inp["beta"] = beta.to(inp["beta"].dtype)
+    _check_record(inp, "tiled", "extreme gates/betas T=%d %s" % (T, io))
+
+
+@pytest.mark.parametrize("T", [3, 12, 40])
+def test_record_ignores_nan_inputs_at_inactive_steps(T):
+    """q, k, v, g and beta are NaN at every inactive step: those steps are
+    skipped, so nothing non-finite reaches y, delta or the state."""
+    inp = gi.record_inputs(3, T, 2, 4, 128, 64, "bf16", seed=91 + T, mask="bernoulli")
+    off = ~(inp["mask"] > 0)
+    for name in ("q", "k", "v", "g", "beta"):
+        t = inp[name].clone()
+        t[off] = float("nan")
+        inp[name] = t
+    _check_record(inp, "block", "NaN at inactive steps T=%d" % T)
+    _, s, _ = _record_gpu(inp, "block")
+    assert torch.isfinite(s).all()
