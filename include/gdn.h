@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum gdn_dtype {
     GDN_F32 = 0,
@@ -67,7 +67,8 @@ typedef enum gdn_status {
     GDN_ERR_ALIAS = -6,             /* an output overlaps an input or another output       */
     GDN_ERR_BAD_ENUM = -7,          /* unknown dtype or GQA map                            */
     GDN_ERR_LAUNCH = -8,            /* the HIP runtime refused the launch                  */
-    GDN_ERR_MISALIGNED = -9         /* a pointer lacks the alignment stated above          */
+    GDN_ERR_MISALIGNED = -9,        /* a pointer lacks the alignment stated above          */
+    GDN_ERR_WORKSPACE = -10         /* workspace NULL or smaller than the call needs       */
 } gdn_status;
 
 /*
@@ -176,6 +177,49 @@ int gdn_replay(const void* delta_log, const void* k_log, const void* g_log,
  */
 int gqa_expand(const void* src, void* dst, uint32_t seq, uint32_t hg, uint32_t h, uint32_t k,
                int dtype, int gqa_map, void* stream);
+
+/*
+ * gdn_prefill -- the record step of gdn_record over a long sequence (a
+ * prefill), computed a chunk of 64 steps at a time on the matrix cores.
+ *
+ * Computes the same outputs as gdn_record with delta_log given (or NULL), from
+ * the same definition: the record kernel (macro `gated_delta_record!`) on the
+ * metaltile-std 0.1.0 page src/ffai/gated_delta_replay.rs.  The mlx-native
+ * 0.6.5 page mlx_native/ops/repeat_tiled.rs names the "chunk-prefill" caller
+ * that feeds it expanded keys; the chunk algorithm is this library's own: over
+ * a chunk, the innovations solve a unit lower-triangular system in the chunk's
+ * keys, gates and betas, and y and the state follow from matrix products.  The
+ * arithmetic is reordered, so results agree with gdn_record to rounding (float32
+ * accumulation; float32 operands enter the bf16 matrix cores as a sum of two
+ * bf16 numbers, about 16 significant bits), not bit for bit.  Inactive steps
+ * (mask entry 0) change nothing and write nothing, as in gdn_record.
+ *
+ * Arguments
+ *   q .. delta_log    as for gdn_record (k_log and g_log capture is not offered).
+ *   workspace         device scratch of at least gdn_prefill_workspace_size(B,
+ *                     T, Hv) bytes, 256-byte aligned, owned by the caller and
+ *                     overlapping no other argument.  Its contents on entry do
+ *                     not matter; on return they are undefined.  Two calls in
+ *                     flight at once need two workspaces.
+ *   workspace_bytes   its size.
+ *   B, T, Hk, Hv      sizes; Hk must divide Hv.
+ *   Dk, Dv            Dk must be 128 and Dv a multiple of 16 up to 1024.
+ *   io_dtype          must be GDN_BF16 (keys and queries enter the matrix
+ *                     cores exactly).
+ *   gqa_map, stream   as for gdn_record.
+ * The call enqueues two kernels on `stream`.
+ * Returns GDN_OK or a negative gdn_status (nothing is enqueued on error):
+ * GDN_ERR_UNSUPPORTED_SHAPE for another dtype or head size, GDN_ERR_WORKSPACE
+ * for a missing or short workspace.
+ */
+uint64_t gdn_prefill_workspace_size(uint32_t B, uint32_t T, uint32_t Hv);
+
+int gdn_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                const float* state_in, const uint32_t* mask,
+                void* y, float* state_out, void* delta_log,
+                void* workspace, uint64_t workspace_bytes,
+                uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+                int io_dtype, int gqa_map, void* stream);
 
 /*
  * rms_norm_bf16 -- RMSNorm with bf16 weights over a batch of tokens.

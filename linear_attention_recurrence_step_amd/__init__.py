@@ -21,7 +21,8 @@ import torch
 from . import _native
 from ._native import GdnError, lib
 
-__all__ = ["gdn_record", "gdn_replay", "gqa_expand", "rms_norm_bf16", "GdnError", "IO_DTYPES"]
+__all__ = ["gdn_record", "gdn_replay", "gqa_expand", "gdn_prefill", "gdn_prefill_workspace_size",
+           "rms_norm_bf16", "GdnError", "IO_DTYPES"]
 
 IO_DTYPES = {torch.float32: _native.GDN_F32, torch.float16: _native.GDN_F16,
              torch.bfloat16: _native.GDN_BF16}
@@ -123,6 +124,62 @@ def gdn_record(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tenso
                         _ptr(g_log), B, T, Hk, Hv, Dk, Dv, _io_code(q), _MAPS[gqa_map],
                         _stream(stream, dev))
     _native.check("gdn_record", rc)
+    return y, state_out, delta_log
+
+
+def gdn_prefill_workspace_size(B: int, T: int, Hv: int) -> int:
+    """Bytes of device workspace gdn_prefill needs for these sizes."""
+    return int(lib.gdn_prefill_workspace_size(B, T, Hv))
+
+
+def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                beta: torch.Tensor, state_in: torch.Tensor, mask: Optional[torch.Tensor] = None,
+                *, gqa_map: str = "block", y: Optional[torch.Tensor] = None,
+                state_out: Optional[torch.Tensor] = None,
+                delta_log: Optional[torch.Tensor] = None, write_tape: bool = True,
+                workspace: Optional[torch.Tensor] = None,
+                stream=None) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """The record step over a long sequence, 64 steps at a time on the matrix
+    cores; returns (y, state_out, delta_log) as gdn_record does.
+
+    bf16 I/O, Dk = 128, Dv a multiple of 16.  ``workspace`` (a uint8 device
+    tensor of at least gdn_prefill_workspace_size(B, T, Hv) bytes) is allocated
+    when not given; pass one to reuse it across calls on one stream.
+    """
+    if gqa_map not in _MAPS:
+        raise ValueError("gqa_map must be 'block' or 'tiled'")
+    dev = _device_of(q)
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    io = q.dtype
+    _io_code(q)
+    _want("q", q, (B, T, Hk, Dk), io, dev)
+    _want("k", k, (B, T, Hk, Dk), io, dev)
+    _want("v", v, (B, T, Hv, Dv), io, dev)
+    _want("g", g, (B, T, Hv), io, dev)
+    _want("beta", beta, (B, T, Hv), io, dev)
+    _want("state_in", state_in, (B, Hv, Dv, Dk), torch.float32, dev)
+    if mask is not None:
+        _want("mask", mask, (B, T), _MASK_DTYPES, dev)
+    if y is None:
+        y = torch.empty((B, T, Hv, Dv), dtype=io, device=dev)
+    _want("y", y, (B, T, Hv, Dv), io, dev)
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    _want("state_out", state_out, (B, Hv, Dv, Dk), torch.float32, dev)
+    if delta_log is None and write_tape:
+        delta_log = torch.empty((B, T, Hv, Dv), dtype=io, device=dev)
+    if delta_log is not None:
+        _want("delta_log", delta_log, (B, T, Hv, Dv), io, dev)
+    need = gdn_prefill_workspace_size(B, T, Hv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _want("workspace", workspace, (workspace.numel(),), torch.uint8, dev)
+    rc = lib.gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+                         _ptr(mask), _ptr(y), _ptr(state_out), _ptr(delta_log), _ptr(workspace),
+                         workspace.numel(), B, T, Hk, Hv, Dk, Dv, _io_code(q), _MAPS[gqa_map],
+                         _stream(stream, dev))
+    _native.check("gdn_prefill", rc)
     return y, state_out, delta_log
 
 

@@ -21,10 +21,11 @@ STATUS = {
     0: "GDN_OK", -1: "GDN_ERR_NULL", -2: "GDN_ERR_ZERO_DIM", -3: "GDN_ERR_GQA_RATIO",
     -4: "GDN_ERR_UNSUPPORTED_SHAPE", -5: "GDN_ERR_OVERFLOW", -6: "GDN_ERR_ALIAS",
     -7: "GDN_ERR_BAD_ENUM", -8: "GDN_ERR_LAUNCH", -9: "GDN_ERR_MISALIGNED",
+    -10: "GDN_ERR_WORKSPACE",
 }
-EXPORTS = ("gdn_record", "gdn_replay", "gqa_expand", "rms_norm_bf16", "gdn_strerror",
-           "gdn_last_error", "gdn_abi_version")
-ABI_VERSION = 3
+EXPORTS = ("gdn_record", "gdn_replay", "gqa_expand", "gdn_prefill", "gdn_prefill_workspace_size",
+           "rms_norm_bf16", "gdn_strerror", "gdn_last_error", "gdn_abi_version")
+ABI_VERSION = 4
 
 
 def _load() -> ctypes.CDLL:
@@ -40,6 +41,10 @@ def _load() -> ctypes.CDLL:
     lib.gdn_replay.restype = i32
     lib.gqa_expand.argtypes = [vp, vp] + [u32] * 4 + [i32, i32, vp]
     lib.gqa_expand.restype = i32
+    lib.gdn_prefill.argtypes = [vp] * 11 + [ctypes.c_uint64] + [u32] * 6 + [i32, i32, vp]
+    lib.gdn_prefill.restype = i32
+    lib.gdn_prefill_workspace_size.argtypes = [u32] * 3
+    lib.gdn_prefill_workspace_size.restype = ctypes.c_uint64
     lib.rms_norm_bf16.argtypes = [vp, vp, vp, u32, u32, ctypes.c_float, vp]
     lib.rms_norm_bf16.restype = i32
     lib.gdn_strerror.argtypes = [i32]

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = ["gdn_abi.cpp", "gdn_record.hip", "gdn_replay.hip", "gdn_replay_mfma.hip", "gqa_expand.hip",
-           "rms_norm.hip"]
+           "rms_norm.hip", "gdn_prefill.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -33,7 +33,8 @@ FLAGS = [
 # Per-source flags.  The matrix-core replay keeps its MFMA accumulators in
 # ordinary VGPRs (gfx950 allows either file): it also scales them with VALU
 # instructions, and one register file instead of two doubles its occupancy.
-SOURCE_FLAGS = {"gdn_replay_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {"gdn_replay_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "gdn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, extra) -> str:

@@ -86,6 +86,7 @@ const char* gdn_strerror(int status) {
         case GDN_ERR_BAD_ENUM: return "unknown dtype or GQA map";
         case GDN_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
         case GDN_ERR_MISALIGNED: return "a pointer is not aligned as required";
+        case GDN_ERR_WORKSPACE: return "workspace missing or too small";
         default: return "unknown status";
     }
 }
@@ -152,6 +153,78 @@ int gdn_record(const void* q, const void* k, const void* v, const void* g, const
                 return fail(GDN_ERR_ALIAS, "%s: %s overlaps %s", kFn, outs[i].name, outs[j].name);
 
     return launch_status(gdn::launch_record(a, static_cast<hipStream_t>(stream)), kFn);
+}
+
+uint64_t gdn_prefill_workspace_size(uint32_t B, uint32_t T, uint32_t Hv) {
+    return gdn::prefill_workspace_bytes(B, T, Hv);
+}
+
+int gdn_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                const float* state_in, const uint32_t* mask,
+                void* y, float* state_out, void* delta_log,
+                void* workspace, uint64_t workspace_bytes,
+                uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+                int io_dtype, int gqa_map, void* stream) {
+    static const char* kFn = "gdn_prefill";
+    if (!valid_dtype(io_dtype)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown io_dtype %d", kFn, io_dtype);
+    if (!valid_map(gqa_map)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown gqa_map %d", kFn, gqa_map);
+    if (!q || !k || !v || !g || !beta || !state_in || !y || !state_out)
+        return fail(GDN_ERR_NULL, "%s: q, k, v, g, beta, state_in, y and state_out must be non-NULL", kFn);
+    if (B == 0 || T == 0 || Hk == 0 || Hv == 0 || Dk == 0 || Dv == 0)
+        return fail(GDN_ERR_ZERO_DIM, "%s: B, T, Hk, Hv, Dk, Dv must all be > 0 (got %u,%u,%u,%u,%u,%u)",
+                    kFn, B, T, Hk, Hv, Dk, Dv);
+    if (Hv % Hk != 0) return fail(GDN_ERR_GQA_RATIO, "%s: Hv (%u) must be a multiple of Hk (%u)", kFn, Hv, Hk);
+    if (!gdn::prefill_supported(Dk, Dv, io_dtype) || Dv > 1024)
+        return fail(GDN_ERR_UNSUPPORTED_SHAPE,
+                    "%s: needs bf16 I/O, Dk = 128 and Dv a multiple of 16 up to 1024 "
+                    "(got io_dtype=%d, Dk=%u, Dv=%u)", kFn, io_dtype, Dk, Dv);
+
+    const uint64_t e = io_bytes(io_dtype);
+    uint64_t n_qk, n_v, n_g, n_s, n_m;
+    if (!mul_u64(&n_qk, {B, T, Hk, Dk, e}) || !mul_u64(&n_v, {B, T, Hv, Dv, e}) ||
+        !mul_u64(&n_g, {B, T, Hv, e}) || !mul_u64(&n_s, {B, Hv, Dv, Dk, 4}) || !mul_u64(&n_m, {B, T, 4}) ||
+        n_qk > kMaxBytes || n_v > kMaxBytes || n_s > kMaxBytes)
+        return fail(GDN_ERR_OVERFLOW, "%s: tensor sizes overflow", kFn);
+    const uint64_t nchunks = (uint64_t(T) + 63) / 64;
+    uint64_t prep_items, scan_items;
+    if (!mul_u64(&prep_items, {B, Hv, nchunks, 256}) || prep_items > kMaxWorkItems ||
+        !mul_u64(&scan_items, {B, Hv, Dv / 16, 256}) || scan_items > kMaxWorkItems)
+        return fail(GDN_ERR_OVERFLOW, "%s: launch grid too large (split the batch)", kFn);
+    const uint64_t need = gdn::prefill_workspace_bytes(B, T, Hv);
+    if (!workspace || workspace_bytes < need)
+        return fail(GDN_ERR_WORKSPACE, "%s: workspace of %llu bytes needed, %llu given%s", kFn,
+                    static_cast<unsigned long long>(need), static_cast<unsigned long long>(workspace_bytes),
+                    workspace ? "" : " (NULL)");
+
+    const void* a16[] = {q, k, v, state_in, y, state_out, delta_log};
+    const char* a16n[] = {"q", "k", "v", "state_in", "y", "state_out", "delta_log"};
+    for (int i = 0; i < 7; ++i)
+        if (a16[i] && !aligned(a16[i], 16))
+            return fail(GDN_ERR_MISALIGNED, "%s: %s must be 16-byte aligned", kFn, a16n[i]);
+    if (!aligned(workspace, 256)) return fail(GDN_ERR_MISALIGNED, "%s: workspace must be 256-byte aligned", kFn);
+    if (mask && !aligned(mask, 4)) return fail(GDN_ERR_MISALIGNED, "%s: mask must be 4-byte aligned", kFn);
+    if (!aligned(g, e) || !aligned(beta, e))
+        return fail(GDN_ERR_MISALIGNED, "%s: g and beta must be element-aligned", kFn);
+
+    const Span ins[] = {{q, n_qk, "q"}, {k, n_qk, "k"}, {v, n_v, "v"}, {g, n_g, "g"},
+                        {beta, n_g, "beta"}, {state_in, n_s, "state_in"}, {mask, mask ? n_m : 0, "mask"}};
+    const Span outs[] = {{y, n_v, "y"}, {state_out, n_s, "state_out"},
+                         {delta_log, delta_log ? n_v : 0, "delta_log"}, {workspace, need, "workspace"}};
+    constexpr int kOuts = 4;
+    for (const Span& o : outs) {
+        for (const Span& i : ins) {
+            if (o.p == state_out && i.p == state_in && o.p == i.p) continue;   // exact in-place state
+            if (overlaps(o, i)) return fail(GDN_ERR_ALIAS, "%s: %s overlaps %s", kFn, o.name, i.name);
+        }
+    }
+    for (int i = 0; i < kOuts; ++i)
+        for (int j = i + 1; j < kOuts; ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(GDN_ERR_ALIAS, "%s: %s overlaps %s", kFn, outs[i].name, outs[j].name);
+
+    gdn::PrefillArgs a{q, k, v, g, beta, state_in, mask, y, state_out, delta_log, workspace,
+                       B, T, Hk, Hv, Dk, Dv, io_dtype, gqa_map};
+    return launch_status(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)), kFn);
 }
 
 int gdn_replay(const void* delta_log, const void* k_log, const void* g_log,

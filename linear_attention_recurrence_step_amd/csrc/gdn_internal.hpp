@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace gdn {
@@ -63,6 +64,21 @@ inline constexpr uint32_t kReplayMfmaFromSteps = 16;
 bool replay_mfma_applies(const ReplayArgs& a);
 hipError_t launch_replay_mfma(const ReplayArgs& a, hipStream_t stream);
 hipError_t launch_expand(const ExpandArgs& a, hipStream_t stream);
+
+// Chunked prefill (gdn_prefill.hip): the record step computed 64 steps at a
+// time on the matrix cores, through a caller-provided workspace.
+struct PrefillArgs {
+    const void* q; const void* k; const void* v; const void* g; const void* beta;
+    const float* state_in; const uint32_t* mask;
+    void* y; float* state_out; void* delta_log;
+    void* workspace;
+    uint32_t B, T, Hk, Hv, Dk, Dv;
+    int io;
+    int map;      // 0 block, 1 tiled
+};
+size_t prefill_workspace_bytes(uint32_t B, uint32_t T, uint32_t Hv);
+bool prefill_supported(uint32_t Dk, uint32_t Dv, int io);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace gdn
 

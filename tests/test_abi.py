@@ -27,7 +27,8 @@ def _declared_functions():
 
 def test_header_declares_the_three_entry_points():
     fns = _declared_functions()
-    for name in ("gdn_record", "gdn_replay", "gqa_expand", "rms_norm_bf16", "gdn_strerror",
+    for name in ("gdn_record", "gdn_replay", "gqa_expand", "gdn_prefill", "gdn_prefill_workspace_size",
+                 "rms_norm_bf16", "gdn_strerror",
                  "gdn_last_error", "gdn_abi_version"):
         assert name in fns, fns
 
@@ -49,6 +50,9 @@ lib.gdn_record.argtypes = [vp] * 12 + [u32] * 6 + [i32, i32, vp]
 lib.gdn_replay.argtypes = [vp] * 6 + [u32] * 6 + [i32, vp]
 lib.gqa_expand.argtypes = [vp, vp] + [u32] * 4 + [i32, i32, vp]
 lib.rms_norm_bf16.argtypes = [vp, vp, vp, u32, u32, ctypes.c_float, vp]
+lib.gdn_prefill.argtypes = [vp] * 11 + [ctypes.c_uint64] + [u32] * 6 + [i32, i32, vp]
+lib.gdn_prefill_workspace_size.argtypes = [u32] * 3
+lib.gdn_prefill_workspace_size.restype = ctypes.c_uint64
 lib.gdn_strerror.restype = ctypes.c_char_p
 lib.gdn_last_error.restype = ctypes.c_char_p
 cases = json.loads(sys.argv[2])
@@ -59,7 +63,9 @@ for c in cases:
     rc = fn(*args)
     out.append({"id": c["id"], "rc": rc, "msg": lib.gdn_last_error().decode()})
 out.append({"id": "strerror", "rc": 0,
-            "msg": json.dumps({str(s): lib.gdn_strerror(s).decode() for s in range(-10, 1)})})
+            "msg": json.dumps({str(s): lib.gdn_strerror(s).decode() for s in range(-11, 1)})})
+out.append({"id": "ws_size", "rc": 0,
+            "msg": json.dumps([lib.gdn_prefill_workspace_size(*x) for x in ([1, 4096, 32], [2, 65, 3], [1, 1, 1])])})
 print(json.dumps(out))
 """
 
@@ -106,7 +112,22 @@ def rms(**kw):
     return [a["x"], a["w"], a["out"], a["n"], a["dim"], a["eps"], None]
 
 
+# gdn_prefill(q, k, v, g, beta, state_in, mask, y, state_out, delta_log, workspace, workspace_bytes,
+#             B, T, Hk, Hv, Dk, Dv, io, map, stream)
+WS_NEED = 2 * 4 * 1 * 33280          # B=2, Hv=4, one chunk of 64 steps
+
+
+def pre(**kw):
+    a = dict(q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), s_in=P(5), mask=P(6), y=P(7), s_out=P(8),
+             dl=P(9), ws=P(10), wsb=WS_NEED, B=2, T=3, Hk=2, Hv=4, Dk=128, Dv=128, io=2, map=1)
+    a.update(kw)
+    return [a["q"], a["k"], a["v"], a["g"], a["beta"], a["s_in"], a["mask"], a["y"], a["s_out"],
+            a["dl"], a["ws"], a["wsb"], a["B"], a["T"], a["Hk"], a["Hv"], a["Dk"], a["Dv"], a["io"],
+            a["map"], None]
+
+
 NULL, ZERO, RATIO, SHAPE, OVER, ALIAS, ENUM, LAUNCH, ALIGN = -1, -2, -3, -4, -5, -6, -7, -8, -9
+WORKSPACE = -10
 
 CASES = [
     ("rec_bad_dtype", "gdn_record", rec(io=3), ENUM),
@@ -160,6 +181,26 @@ CASES = [
     ("rms_out_overlaps_x", "rms_norm_bf16", rms(out=P(0, 16)), ALIAS),
     ("rms_out_overlaps_weight", "rms_norm_bf16", rms(out=P(1, 64)), ALIAS),
     ("rms_bytes_overflow", "rms_norm_bf16", rms(n=1 << 31, dim=1 << 20), OVER),
+    ("pre_bad_dtype", "gdn_prefill", pre(io=5), ENUM),
+    ("pre_bad_map", "gdn_prefill", pre(map=3), ENUM),
+    ("pre_null_v", "gdn_prefill", pre(v=None), NULL),
+    ("pre_zero_T", "gdn_prefill", pre(T=0), ZERO),
+    ("pre_ratio", "gdn_prefill", pre(Hk=3), RATIO),
+    ("pre_f16", "gdn_prefill", pre(io=1), SHAPE),
+    ("pre_f32", "gdn_prefill", pre(io=0), SHAPE),
+    ("pre_dk64", "gdn_prefill", pre(Dk=64), SHAPE),
+    ("pre_dv40", "gdn_prefill", pre(Dv=40), SHAPE),
+    ("pre_dv2048", "gdn_prefill", pre(Dv=2048), SHAPE),
+    ("pre_null_workspace", "gdn_prefill", pre(ws=None), WORKSPACE),
+    ("pre_short_workspace", "gdn_prefill", pre(wsb=WS_NEED - 1), WORKSPACE),
+    ("pre_short_workspace_T65", "gdn_prefill", pre(T=65), WORKSPACE),
+    ("pre_misaligned_workspace", "gdn_prefill", pre(ws=P(10, 16)), ALIGN),
+    ("pre_misaligned_q", "gdn_prefill", pre(q=P(0, 8)), ALIGN),
+    ("pre_workspace_over_k", "gdn_prefill", pre(ws=P(1)), ALIAS),
+    ("pre_workspace_over_y", "gdn_prefill", pre(ws=P(7, 256)), ALIAS),
+    ("pre_y_over_v", "gdn_prefill", pre(y=P(2, 512)), ALIAS),
+    ("pre_state_partial_alias", "gdn_prefill", pre(s_out=P(5, 4096)), ALIAS),
+    ("pre_grid_overflow", "gdn_prefill", pre(B=1 << 16, T=1 << 15, Hk=1, Hv=1 << 8, Dv=16), OVER),
     ("exp_bad_dtype", "gqa_expand", exp(dt=7), ENUM),
     ("exp_bad_map", "gqa_expand", exp(map=-1), ENUM),
     ("exp_null_dst", "gqa_expand", exp(dst=None), NULL),
@@ -193,15 +234,21 @@ def test_invalid_arguments_are_rejected_before_any_hip_call(results, case):
 
 def test_strerror_covers_every_status(results):
     table = json.loads(results["strerror"]["msg"])
-    for s in range(-9, 1):
+    for s in range(-10, 1):
         assert table[str(s)] and table[str(s)] != "unknown status", s
-    assert table["-10"] == "unknown status"
+    assert table["-11"] == "unknown status"
+
+
+def test_prefill_workspace_size(results):
+    """33280 bytes per (batch row, value head, chunk of 64 steps)."""
+    assert json.loads(results["ws_size"]["msg"]) == [32 * 64 * 33280, 2 * 3 * 2 * 33280, 33280]
 
 
 def test_python_binding_names_match_the_abi():
     import linear_attention_recurrence_step_amd as gdn
     from linear_attention_recurrence_step_amd import _native
-    for name in ("gdn_record", "gdn_replay", "gqa_expand", "rms_norm_bf16"):
+    for name in ("gdn_record", "gdn_replay", "gqa_expand", "gdn_prefill", "gdn_prefill_workspace_size",
+                 "rms_norm_bf16"):
         assert callable(getattr(gdn, name))
         assert hasattr(_native.lib, name)
     assert _native.lib.gdn_abi_version() == _native.ABI_VERSION
@@ -221,6 +268,8 @@ def test_python_binding_rejects_host_tensors_before_the_library():
         gdn.gdn_record(q, q, v, g, g, s)
     with pytest.raises(ValueError, match="HIP device"):
         gdn.gdn_replay(v, q, g, s, None, 1)
+    with pytest.raises(ValueError, match="HIP device"):
+        gdn.gdn_prefill(q, q, v, g, g, s)
     with pytest.raises(ValueError, match="HIP device"):
         gdn.gqa_expand(torch.zeros(2, 1, 32), 2)
     with pytest.raises(ValueError, match="HIP device"):

@@ -1,0 +1,152 @@
+"""GPU parity of gdn_prefill (the record step computed 64 steps at a time on the
+matrix cores) against the CPU oracle's record, through the C ABI.
+
+gdn_prefill computes the record kernel's outputs with the arithmetic reordered
+into chunk products, so the oracle's plain per-step record is the reference:
+y and delta_log at active steps and the final state must be within 2e-2
+(bf16 I/O) of it, scaled as |gpu - oracle| <= tol * (1 + |oracle|), and
+positions of inactive steps must keep the caller's sentinel.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import oracle
+import linear_attention_recurrence_step_amd as gdn
+from gpu_util import assert_close, dev, f64, note, step_mask, to_dev
+
+pytestmark = pytest.mark.gpu
+
+Y_SENTINEL = -7.5
+D_SENTINEL = 3.25
+
+
+def _prefill_gpu(inp, gqa_map, write_tape=True, workspace=None, in_place=False):
+    d = to_dev(inp)
+    io = d["q"].dtype
+    y = torch.full(d["v"].shape, Y_SENTINEL, dtype=io, device=dev())
+    dl = torch.full(d["v"].shape, D_SENTINEL, dtype=io, device=dev()) if write_tape else None
+    s_out = d["state_in"] if in_place else None
+    y, s, dl = gdn.gdn_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"], d["mask"],
+                               gqa_map=gqa_map, y=y, delta_log=dl, write_tape=write_tape,
+                               state_out=s_out, workspace=workspace)
+    torch.cuda.synchronize()
+    return y, s, dl
+
+
+def _check(inp, gqa_map, what):
+    note("prefill %s map=%s" % (what, gqa_map))
+    y, s, dl = _prefill_gpu(inp, gqa_map)
+    ry, rs, rd = oracle.gdn_record(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                   inp["state_in"], inp["mask"], gqa_map=gqa_map)
+    io = inp["q"].dtype
+    B, T = inp["q"].shape[:2]
+    act = np.broadcast_to(step_mask(inp["mask"], B, T)[:, :, None, None], ry.shape)
+    assert_close(y, ry, io, what + " y", where=act)
+    assert_close(dl, rd, io, what + " delta", where=act)
+    assert_close(s, rs, io, what + " state")
+    assert np.all(f64(y)[~act] == Y_SENTINEL), what + ": y written at an inactive step"
+    assert np.all(f64(dl)[~act] == D_SENTINEL), what + ": delta written at an inactive step"
+    return y, s, dl
+
+
+# (B, T, Hk, Hv, Dv, mask, map): one step, exactly one chunk, ragged chunk
+# tails, several chunks, masks, both GQA maps, several row blocks per head.
+CASES = [
+    (1, 1, 1, 1, 16, "ones", "block"),
+    (1, 64, 2, 4, 32, "ones", "block"),
+    (1, 65, 1, 1, 16, "ones", "tiled"),
+    (2, 200, 2, 4, 128, "bernoulli", "tiled"),
+    (1, 130, 1, 2, 48, "trailing", "block"),
+    (3, 127, 4, 4, 16, "bernoulli", "block"),
+    (2, 256, 2, 6, 64, "none", "tiled"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["B%d_T%d_Hk%d_Hv%d_Dv%d_%s_%s" % c for c in CASES])
+def test_prefill_matches_oracle(case):
+    B, T, Hk, Hv, Dv, mask, gmap = case
+    inp = gi.record_inputs(B, T, Hk, Hv, 128, Dv, io="bf16", seed=11 + T, mask=mask)
+    _check(inp, gmap, "B%d T%d Dv%d %s" % (B, T, Dv, mask))
+
+
+def test_prefill_workload_sampled_heads():
+    """The 4096-step prefill at full size; the oracle re-runs four sampled
+    value heads one by one (each head is an independent recurrence)."""
+    w = gi.WORKLOADS["chunk_prefill"]
+    inp = gi.workload_inputs("chunk_prefill", 0)
+    note("prefill chunk_prefill full size")
+    y, s, dl = _prefill_gpu(inp, w.gqa_map)
+    io = inp["q"].dtype
+    for hv in (0, 5, 16, 31):
+        hk = hv % w.Hk                                              # tiled map
+        sub = dict(q=inp["q"][:, :, hk:hk + 1], k=inp["k"][:, :, hk:hk + 1],
+                   v=inp["v"][:, :, hv:hv + 1], g=inp["g"][:, :, hv:hv + 1],
+                   beta=inp["beta"][:, :, hv:hv + 1], state_in=inp["state_in"][:, hv:hv + 1])
+        ry, rs, rd = oracle.gdn_record(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"],
+                                       sub["state_in"], None)
+        assert_close(y[:, :, hv:hv + 1], ry, io, "prefill y head %d" % hv)
+        assert_close(dl[:, :, hv:hv + 1], rd, io, "prefill delta head %d" % hv)
+        assert_close(s[:, hv:hv + 1], rs, io, "prefill state head %d" % hv)
+
+
+def test_prefill_workload_all_heads_near_sequential_record():
+    """Every head of the 4096-step workload: the chunked and the sequential
+    GPU records agree to the bf16 tolerance (the sequential record is itself
+    pinned to the oracle by the record parity tests)."""
+    w = gi.WORKLOADS["chunk_prefill"]
+    inp = gi.workload_inputs("chunk_prefill", 1)
+    note("prefill vs sequential record, chunk_prefill full size")
+    y, s, dl = _prefill_gpu(inp, w.gqa_map)
+    d = to_dev(inp)
+    y2, s2, dl2 = gdn.gdn_record(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"], None,
+                                 gqa_map=w.gqa_map)
+    torch.cuda.synchronize()
+    io = inp["q"].dtype
+    assert_close(y, f64(y2), io, "y vs sequential record")
+    assert_close(dl, f64(dl2), io, "delta vs sequential record")
+    assert_close(s, f64(s2), io, "state vs sequential record")
+
+
+def test_prefill_in_place_reused_workspace_and_no_tape():
+    """state_out == state_in, a workspace holding an earlier call's contents,
+    and delta_log = NULL all give the same bits as a fresh out-of-place call."""
+    inp = gi.record_inputs(2, 150, 2, 4, 128, 64, io="bf16", seed=5, mask="bernoulli")
+    note("prefill in place / reused workspace / no tape")
+    ws = torch.empty(gdn.gdn_prefill_workspace_size(2, 150, 4), dtype=torch.uint8, device=dev())
+    y0, s0, d0 = _prefill_gpu(inp, "block", workspace=ws)
+    other = gi.record_inputs(2, 150, 2, 4, 128, 64, io="bf16", seed=6, mask="ones")
+    _prefill_gpu(other, "tiled", workspace=ws)                       # leave other contents behind
+    y1, s1, d1 = _prefill_gpu(inp, "block", workspace=ws, in_place=True)
+    y2, s2, _ = _prefill_gpu(inp, "block", write_tape=False)
+    assert torch.equal(y0, y1) and torch.equal(s0, s1) and torch.equal(d0, d1)
+    assert torch.equal(y0, y2) and torch.equal(s0, s2)
+
+
+def test_prefill_zero_and_unit_gates():
+    """Gates of exactly 0 (the state is reset) and identity steps (g = 1,
+    beta = 0) inside chunks: the gate products are formed without division."""
+    inp = gi.record_inputs(1, 192, 1, 2, 128, 32, io="bf16", seed=9, mask="ones")
+    g = inp["g"].clone()
+    beta = inp["beta"].clone()
+    g[0, [3, 64, 100, 101, 191], :] = 0.0
+    g[0, 10:30, 1] = 1.0
+    beta[0, 10:30, 1] = 0.0
+    inp = dict(inp, g=g, beta=beta)
+    _check(inp, "block", "zero and unit gates")
+
+
+def test_prefill_nan_at_inactive_steps_never_reaches_an_output():
+    """Inactive steps are skipped by selection, not by a product with zero:
+    NaN in their q, k, v, g and beta cannot reach y, delta or the state."""
+    inp = gi.record_inputs(2, 100, 2, 4, 128, 32, io="bf16", seed=4, mask="bernoulli")
+    m = inp["mask"].numpy() > 0
+    poisoned = {}
+    for name in ("q", "k", "v", "g", "beta"):
+        t = inp[name].clone()
+        t[torch.from_numpy(~m)] = float("nan")
+        poisoned[name] = t
+    inp = dict(inp, **poisoned)
+    y, s, dl = _check(inp, "tiled", "NaN at inactive steps")
+    assert not torch.isnan(s).any()
