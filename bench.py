@@ -9,7 +9,8 @@ input already resident in HBM:
     large_batch_decode (default): gqa_expand(k -> k_log, block map)
                                   + gdn_record + gdn_replay(accepted=1) on the fresh tape
     spec_decode:      the same at B=8, T=4 with a drawn accepted count
-    chunk_prefill:    gqa_expand of fp32 q and k (tiled map) + gdn_record over 4096 steps
+    chunk_prefill:    gqa_expand of fp32 q and k (tiled map) + the record over 4096 steps,
+                      by gdn_prefill (chunks of 64 steps; --prefill sequential: gdn_record)
     long_tape_replay: gdn_replay of a 64-step fp16 tape for accepted in {0,1,16,63,64}
     tiny:             gdn_record + gdn_replay
     cell_d192_128, cell_d64_32: the page's other two head-shape cells as decode
@@ -55,6 +56,7 @@ KERNEL_SOURCES = {
     "gdn_replay": ["gdn_replay.hip", "gdn_replay_mfma.hip", "gdn_device.hpp"],
     "gqa_expand": ["gqa_expand.hip", "gdn_device.hpp"],
     "rms_norm_bf16": ["rms_norm.hip", "gdn_device.hpp"],
+    "gdn_prefill": ["gdn_prefill.hip", "gdn_device.hpp"],
 }
 
 
@@ -120,7 +122,7 @@ def _active(mask, B, T, upto=None):
 class Step:
     """Device buffers and launch sequence of one step of a workload."""
 
-    def __init__(self, name, dev, seed=0, capture="separate"):
+    def __init__(self, name, dev, seed=0, capture="separate", prefill="chunked"):
         import torch
         import gdn_inputs as gi
         import linear_attention_recurrence_step_amd as gdn
@@ -128,6 +130,7 @@ class Step:
         self.name = name
         self.gi_norm = gi.NORM_WORKLOADS
         self.fused = capture == "fused"
+        self.chunked = prefill == "chunked" and name == "chunk_prefill"
         self.kernels = []            # (label, kernel, algorithmic bytes, head-steps)
         self.touched = {}
         if name in gi.NORM_WORKLOADS:
@@ -190,6 +193,12 @@ class Step:
         if self.fused:
             self.kernels.append(("record+capture", "gdn_record",
                                  rb + capture_bytes(w.Hv, w.Dk, self.e, U), U * w.Hv))
+        elif self.chunked:
+            # the chunked record: same outputs, same algorithmic bytes; its
+            # workspace is allocated once, outside the timed steps
+            self.ws = torch.empty(gdn.gdn_prefill_workspace_size(w.B, T, w.Hv), dtype=torch.uint8,
+                                  device=dev)
+            self.kernels.append(("prefill", "gdn_prefill", rb, U * w.Hv))
         else:
             self.kernels.append(("record", "gdn_record", rb, U * w.Hv))
         if name != "chunk_prefill":
@@ -220,7 +229,12 @@ class Step:
                 out.append(lambda i=i: gdn.gqa_expand(self.src[i], w.Hv, w.gqa_map, dst=self.dst[i]))
         elif not self.fused:
             out.append(lambda: gdn.gqa_expand(d["k"], w.Hv, w.gqa_map, dst=self.k_log))
-        if self.fused:
+        if self.chunked:
+            out.append(lambda: gdn.gdn_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
+                                               d["mask"], gqa_map=w.gqa_map, y=self.y,
+                                               state_out=self.s_rec, delta_log=self.dl,
+                                               workspace=self.ws))
+        elif self.fused:
             out.append(lambda: gdn.gdn_record(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
                                               d["mask"], gqa_map=w.gqa_map, y=self.y,
                                               state_out=self.s_rec, delta_log=self.dl,
@@ -472,6 +486,9 @@ def main():
     ap.add_argument("--capture", choices=("separate", "fused"), default="separate",
                     help="separate: k_log by a gqa_expand launch and g_log = g; fused: the record "
                          "writes k_log and g_log itself")
+    ap.add_argument("--prefill", choices=("chunked", "sequential"), default="chunked",
+                    help="chunk_prefill's record step: gdn_prefill (chunks of 64 steps on the "
+                         "matrix cores) or gdn_record (one step after another)")
     ap.add_argument("--no-peak-probe", action="store_true",
                     help="skip the 512 MiB copy that measures the practical HBM peak")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -489,7 +506,7 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(dev, args.steps)
         return
-    step = Step(args.workload, dev, args.seed, args.capture)
+    step = Step(args.workload, dev, args.seed, args.capture, args.prefill)
     launches = step.launches()
     w = step.w
 
@@ -558,6 +575,7 @@ def main():
                    {"workload": args.workload, "B": w.B, "T": w.T, "Hk": w.Hk, "Hv": w.Hv,
                     "Dk": w.Dk, "Dv": w.Dv, "io_dtype": w.io, "state_dtype": "f32",
                     "gqa_map": w.gqa_map, "mask": w.mask, "capture": args.capture,
+                    **({"prefill": args.prefill} if args.workload == "chunk_prefill" else {}),
                     "step": " + ".join(k[0] for k in step.kernels)}),
         "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
         "head_steps_per_s": round(head_steps / (ms_per_step * 1e-3), 1),

@@ -55,29 +55,26 @@ __device__ __forceinline__ f32x4v mfma_bf16(u32x2 a, u32x2 b, f32x4v acc) {
                                                      __builtin_bit_cast(i16x4, b), acc, 0, 0, 0);
 }
 
-__device__ __forceinline__ u32x2 pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-    u32x2 r;
-    r.x = a | (b << 16);
-    r.y = c | (d << 16);
-    return r;
+// Two floats rounded to nearest-even bf16 and packed (v_cvt_pk_bf16_f32),
+// the first in the low half.  Used only for the internal hi/lo operands.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{a, b}, bf16x2v));
 }
 
 // x = hi + lo in bf16, for four values at once (fragment order kept).
 __device__ __forceinline__ void split4(const f32x4v& x, u32x2& hi, u32x2& lo) {
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        h[r] = f32_to_bf16_bits(x[r]);
-        l[r] = f32_to_bf16_bits(x[r] - bf16_bits_to_f32(h[r]));
-    }
-    hi = pack4(h[0], h[1], h[2], h[3]);
-    lo = pack4(l[0], l[1], l[2], l[3]);
+    hi.x = cvt_pk_bf16(x[0], x[1]);
+    hi.y = cvt_pk_bf16(x[2], x[3]);
+    lo.x = cvt_pk_bf16(x[0] - __uint_as_float(hi.x << 16), x[1] - __uint_as_float(hi.x & 0xffff0000u));
+    lo.y = cvt_pk_bf16(x[2] - __uint_as_float(hi.y << 16), x[3] - __uint_as_float(hi.y & 0xffff0000u));
 }
 
 __device__ __forceinline__ void split1(float x, uint16_t& hi, uint16_t& lo) {
-    const uint32_t h = f32_to_bf16_bits(x);
+    const uint32_t h = cvt_pk_bf16(x, 0.0f) & 0xffffu;
     hi = static_cast<uint16_t>(h);
-    lo = static_cast<uint16_t>(f32_to_bf16_bits(x - bf16_bits_to_f32(h)));
+    lo = static_cast<uint16_t>(cvt_pk_bf16(x - bf16_bits_to_f32(h), 0.0f));
 }
 
 __device__ __forceinline__ u32x2 zero2() {
@@ -108,23 +105,36 @@ struct PrefillWs {
 
 namespace {
 
-// Row I of the forward substitution (I + A) T = identity for the column this
-// lane owns, then the rows after it.  A is read from LDS (row stride AS, four
-// entries per read, the same address for every lane); the row index is a
-// template parameter so that col[] stays in registers.
-template <int I, int AS>
-__device__ __forceinline__ void forward_row(float (&col)[kC], const float* Al, int lane) {
-    float acc0 = I == lane ? 1.0f : 0.0f, acc1 = 0.0f;
+// Row I of the forward substitution (I + A) T = identity, then the rows after
+// it.  Four consecutive lanes share column c of T; lane q of the four keeps
+// col[j] for j = 4m + q in mine[m] and sums the terms of those j, and a quad
+// reduction gives every lane of the four the whole sum.  A is read from LDS
+// in the layout Aq[(i * 4 + q) * kAqRow + m] = A[i, 4m + q], so one 16-byte
+// read covers four of a lane's terms (the same address for every column).
+// Entries of A at and above the diagonal are stored zeros, and mine[] of rows
+// not yet reached is zero, so the sums need no masks.  Row indices are
+// template parameters so that mine[] stays in registers.
+constexpr int kAqRow = 20;       // floats per (row, q): 16 used, padded
+
+template <int I>
+__device__ __forceinline__ void forward_quad_row(float (&mine)[16], const float* Aq, int c, int q) {
+    constexpr int NM = (I + 3) / 4;                 // m with 4m + q < I for some q
+    const float* row = Aq + (I * 4 + q) * kAqRow;
+    float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
-    for (int j4 = 0; j4 < (I + 3) / 4; ++j4) {
-        const float4 a = *reinterpret_cast<const float4*>(&Al[I * AS + 4 * j4]);
-        if (4 * j4 + 0 < I) acc0 -= a.x * col[4 * j4 + 0];
-        if (4 * j4 + 1 < I) acc1 -= a.y * col[4 * j4 + 1];
-        if (4 * j4 + 2 < I) acc0 -= a.z * col[4 * j4 + 2];
-        if (4 * j4 + 3 < I) acc1 -= a.w * col[4 * j4 + 3];
+    for (int m4 = 0; m4 < (NM + 3) / 4; ++m4) {
+        const float4 a = *reinterpret_cast<const float4*>(row + 4 * m4);
+        if (4 * m4 + 0 < NM) p0 = fmaf(a.x, mine[4 * m4 + 0], p0);
+        if (4 * m4 + 1 < NM) p1 = fmaf(a.y, mine[4 * m4 + 1], p1);
+        if (4 * m4 + 2 < NM) p0 = fmaf(a.z, mine[4 * m4 + 2], p0);
+        if (4 * m4 + 3 < NM) p1 = fmaf(a.w, mine[4 * m4 + 3], p1);
     }
-    col[I] = acc0 + acc1;
-    if constexpr (I + 1 < kC) forward_row<I + 1, AS>(col, Al, lane);
+    float part = p0 + p1;
+    part += dpp_read<0xb1>(part);      // quad_perm [1,0,3,2]
+    part += dpp_read<0x4e>(part);      // quad_perm [2,3,0,1]: the same bits on all four lanes
+    const float val = (I == c ? 1.0f : 0.0f) - part;
+    mine[I >> 2] = (I & 3) == q ? val : mine[I >> 2];
+    if constexpr (I + 1 < kC) forward_quad_row<I + 1>(mine, Aq, c, q);
 }
 
 // ------------------------------------------------------------------ prep
@@ -140,10 +150,10 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(
 {
     static_assert(IO == kBF16, "the chunked prefill takes bf16 I/O");
     constexpr int MS = kC + 1;       // row stride of M in floats
-    constexpr int AS = kC + 4;       // row stride of A in floats (16-byte rows for float4 reads)
-    __shared__ float gs[kC], bs[kC];
+    __shared__ __align__(16) float gs[kC];
+    __shared__ float bs[kC];
     __shared__ float Ml[kC * MS];
-    __shared__ __align__(16) float Al[kC * AS];
+    __shared__ __align__(16) float Aq[kC * 4 * kAqRow];
 
     const uint32_t tid = threadIdx.x, l = tid & 63u, w = tid >> 6;
     const uint32_t lr = l & 15u, lg = l >> 4;
@@ -154,58 +164,73 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(
     const uint32_t t0 = c * kC;
     unsigned char* wsb = ws + (static_cast<size_t>(n) * nchunks + c) * PrefillWs::kBytes;
 
-    if (tid < kC) {
-        const uint32_t t = t0 + tid;
-        const bool act = step_active(mask, b, T, t);
-        float gv = 1.0f, bv = 0.0f;
-        if (t < T) {
-            const size_t i = (static_cast<size_t>(b) * T + t) * Hv + hv;
-            const float gl = io_load1<IO>(g, i), bl = io_load1<IO>(beta, i);
-            gv = act ? gl : 1.0f;
-            bv = act ? bl : 0.0f;
-        }
-        gs[tid] = gv;
-        bs[tid] = bv;
-    }
-
-    // Key fragments of all four row tiles and query fragments of this wave's
-    // tile: lane holds x[16 tile + lr][16 ks + 4 lg .. +3].  Rows of inactive
-    // steps are zero (selected, so a NaN there cannot enter a product).
+    // Key fragments of all four row tiles, and key and query fragments of
+    // this wave's tile: lane holds x[16 tile + lr][16 ks + 4 lg .. +3].  All
+    // loads are issued first (steps past T read row T-1); rows of inactive
+    // steps are then replaced by zeros (a select, so a NaN there cannot enter
+    // a product).
     u32x2 kf[4][kDk / 16], kw[kDk / 16], qf[kDk / 16];
+    uint32_t mt[4], mw;
     const size_t kq_row = static_cast<size_t>(Hk) * kDk * 2;   // bytes per step
-    const size_t kq_base = (static_cast<size_t>(b) * T * Hk + hk) * kDk * 2;
+    const size_t kq_base = (static_cast<size_t>(b) * T * Hk + hk) * kDk * 2 + lg * 8;
 #pragma unroll
     for (int tile = 0; tile < 4; ++tile) {
-        const uint32_t t = t0 + 16u * tile + lr;
-        const bool act = step_active(mask, b, T, t);
-        const size_t off = kq_base + static_cast<size_t>(t < T ? t : 0) * kq_row + lg * 8;
+        const uint32_t t = t0 + 16u * tile + lr, tc = t < T ? t : T - 1;
+        const size_t off = kq_base + static_cast<size_t>(tc) * kq_row;
 #pragma unroll
-        for (int ks = 0; ks < kDk / 16; ++ks) {
-            const u32x2 kv = t < T ? load8(k, off + ks * 32) : zero2();
-            kf[tile][ks] = act ? kv : zero2();
-        }
+        for (int ks = 0; ks < kDk / 16; ++ks) kf[tile][ks] = load8(k, off + ks * 32);
+        mt[tile] = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
     }
     {
-        const uint32_t t = t0 + 16u * w + lr;
-        const bool act = step_active(mask, b, T, t);
-        const size_t off = kq_base + static_cast<size_t>(t < T ? t : 0) * kq_row + lg * 8;
+        const uint32_t t = t0 + 16u * w + lr, tc = t < T ? t : T - 1;
+        const size_t off = kq_base + static_cast<size_t>(tc) * kq_row;
 #pragma unroll
         for (int ks = 0; ks < kDk / 16; ++ks) {
-            const u32x2 kv = t < T ? load8(k, off + ks * 32) : zero2();
-            const u32x2 qv = t < T ? load8(q, off + ks * 32) : zero2();
-            kw[ks] = act ? kv : zero2();
-            qf[ks] = act ? qv : zero2();
+            kw[ks] = load8(k, off + ks * 32);
+            qf[ks] = load8(q, off + ks * 32);
+        }
+        mw = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
+    }
+    if (tid < kC) {
+        const uint32_t t = t0 + tid, tc = t < T ? t : T - 1;
+        const size_t i = (static_cast<size_t>(b) * T + tc) * Hv + hv;
+        const float gl = io_load1<IO>(g, i), bl = io_load1<IO>(beta, i);
+        const uint32_t m = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
+        const bool act = t < T && m > 0u;
+        gs[tid] = act ? gl : 1.0f;
+        bs[tid] = act ? bl : 0.0f;
+    }
+#pragma unroll
+    for (int tile = 0; tile < 4; ++tile) {
+        const bool act = t0 + 16u * tile + lr < T && mt[tile] > 0u;
+#pragma unroll
+        for (int ks = 0; ks < kDk / 16; ++ks) kf[tile][ks] = act ? kf[tile][ks] : zero2();
+    }
+    {
+        const bool act = t0 + 16u * w + lr < T && mw > 0u;
+#pragma unroll
+        for (int ks = 0; ks < kDk / 16; ++ks) {
+            kw[ks] = act ? kw[ks] : zero2();
+            qf[ks] = act ? qf[ks] : zero2();
         }
     }
     __syncthreads();
 
-    // M by running products of the gates: thread t walks s = t, t-1, .., 0.
+    // M by running products of the gates (gates held in registers): thread t
+    // walks s = 63 .. 0, multiplying in g_s once s <= t.
     if (tid < kC) {
+        float gr[kC];
+#pragma unroll
+        for (int s4 = 0; s4 < kC / 4; ++s4) {
+            const float4 v4 = *reinterpret_cast<const float4*>(&gs[4 * s4]);
+            gr[4 * s4] = v4.x; gr[4 * s4 + 1] = v4.y; gr[4 * s4 + 2] = v4.z; gr[4 * s4 + 3] = v4.w;
+        }
         const int t = static_cast<int>(tid);
         float p = 1.0f;
+#pragma unroll
         for (int s = kC - 1; s >= 0; --s) {
             Ml[t * MS + s] = s <= t ? p : 0.0f;
-            if (s <= t) p *= gs[s];
+            p = s <= t ? p * gr[s] : p;
         }
         reinterpret_cast<float*>(wsb + PrefillWs::kGamma)[t] = p;   // gamma_t = g_0 .. g_t
     }
@@ -233,7 +258,7 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(
             const int t = 16 * static_cast<int>(w) + 4 * static_cast<int>(lg) + r;
             const int s = 16 * st + static_cast<int>(lr);
             const float m = Ml[t * MS + s];
-            Al[t * AS + s] = s < t ? bs[t] * (m * (G[r] + G2[r])) : 0.0f;
+            Aq[(t * 4 + (s & 3)) * kAqRow + (s >> 2)] = s < t ? bs[t] * (m * (G[r] + G2[r])) : 0.0f;
             uint16_t hi, lo;
             split1(s <= t ? m * (H[r] + H2[r]) : 0.0f, hi, lo);
             phi[t * kC + s] = hi;
@@ -242,20 +267,24 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(
     }
     __syncthreads();
 
-    // (I + A)^-1 by forward substitution, one column per lane of wave 0:
-    // col[i] = [i == c] - sum_{j<i} A[i,j] col[j].  Then Tb = (I + A)^-1 diag(beta).
-    if (w == 0) {
-        float col[kC];
-        forward_row<0, AS>(col, Al, static_cast<int>(l));
-        const float bc = bs[l];
+    // (I + A)^-1 by forward substitution over all four waves (four lanes per
+    // column), then Tb = (I + A)^-1 diag(beta).
+    {
+        const int col = static_cast<int>(tid >> 2), qq = static_cast<int>(tid & 3u);
+        float mine[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) mine[m] = 0.0f;
+        forward_quad_row<0>(mine, Aq, col, qq);
+        const float bc = bs[col];
         uint16_t* thi = reinterpret_cast<uint16_t*>(wsb + PrefillWs::kTbHi);
         uint16_t* tlo = reinterpret_cast<uint16_t*>(wsb + PrefillWs::kTbLo);
 #pragma unroll
-        for (int i = 0; i < kC; ++i) {
+        for (int m = 0; m < 16; ++m) {
+            const int i = 4 * m + qq;
             uint16_t hi, lo;
-            split1(col[i] * bc, hi, lo);
-            thi[i * kC + l] = hi;
-            tlo[i * kC + l] = lo;
+            split1(mine[m] * bc, hi, lo);
+            thi[i * kC + col] = hi;
+            tlo[i * kC + col] = lo;
         }
     }
 }
@@ -269,13 +298,17 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(
 // X = K S^T for the key step it covers.  Wave w computes the chunk's step
 // tile w (steps 16w .. 16w+15) of X, Delta and Y.
 struct ScanIn {
-    u32x2 kf[kDk / 16], qf[kDk / 16];   // K, Q [16w + lr][16 ks + 4 lg ..]
+    u32x2 kf[kDk / 16], qf[kDk / 16];   // K, Q [16w + lr][16 ks + 4 lg ..], as loaded
     u32x2 th[4], tl[4], ph[4], pl[4];   // Tb and P [16w + lr][16 ks + 4 lg ..]
-    f32x4v v, gam, rho;                 // at steps 16w + 4 lg + r, row lr
+    uint32_t vb[4];                     // word holding v at steps 16w + 4 lg + r, row lr
+    uint32_t mA, mC[4];                 // mask words of those steps (1 without a mask)
+    f32x4v gam, rho;                    // gamma, rho at steps 16w + 4 lg + r
     float gC;                           // gamma_63
-    uint32_t act;                       // bit r: step 16w + 4 lg + r is active
 };
 
+// Issue the loads of one chunk.  Nothing here consumes a loaded value, so the
+// loads stay in flight while the previous chunk is computed; steps past T
+// read step T-1 and are zeroed where the values are used.
 template <int IO>
 __device__ __forceinline__ void scan_load(ScanIn& in, const void* q, const void* k, const void* v,
                                           const uint32_t* mask, const unsigned char* wsb,
@@ -283,26 +316,23 @@ __device__ __forceinline__ void scan_load(ScanIn& in, const void* q, const void*
                                           uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dv,
                                           uint32_t t0, uint32_t w, uint32_t lr, uint32_t lg) {
     {
-        const uint32_t t = t0 + 16u * w + lr;
-        const bool act = step_active(mask, b, T, t);
-        const size_t off = ((static_cast<size_t>(b) * T + (t < T ? t : 0)) * Hk + hk) * kDk * 2 + lg * 8;
+        const uint32_t t = t0 + 16u * w + lr, tc = t < T ? t : T - 1;
+        const size_t off = ((static_cast<size_t>(b) * T + tc) * Hk + hk) * kDk * 2 + lg * 8;
 #pragma unroll
         for (int ks = 0; ks < kDk / 16; ++ks) {
-            const u32x2 kv = t < T ? load8(k, off + ks * 32) : zero2();
-            const u32x2 qv = t < T ? load8(q, off + ks * 32) : zero2();
-            in.kf[ks] = act ? kv : zero2();
-            in.qf[ks] = act ? qv : zero2();
+            in.kf[ks] = load8(k, off + ks * 32);
+            in.qf[ks] = load8(q, off + ks * 32);
         }
+        in.mA = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
     }
-    in.act = 0u;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const uint32_t t = t0 + 16u * w + 4u * lg + r;
-        const bool act = step_active(mask, b, T, t);
-        const float vv = t < T ? io_load1<IO>(v, ((static_cast<size_t>(b) * T + t) * Hv + hv) * Dv + dv0 + lr)
-                               : 0.0f;
-        in.v[r] = act ? vv : 0.0f;
-        in.act |= act ? (1u << r) : 0u;
+        const uint32_t t = t0 + 16u * w + 4u * lg + r, tc = t < T ? t : T - 1;
+        // The aligned 32-bit word holding the element (Dv is even, so it lies
+        // inside v); the half is picked where the value is used.
+        const size_t e = ((static_cast<size_t>(b) * T + tc) * Hv + hv) * Dv + dv0 + lr;
+        in.vb[r] = static_cast<const uint32_t*>(v)[e >> 1];
+        in.mC[r] = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
     }
     const size_t frag = ((16u * w + lr) * kC + 4u * lg) * 2;
 #pragma unroll
@@ -360,13 +390,48 @@ __global__ __launch_bounds__(256, 1) void gdn_prefill_scan_kernel(
     ScanIn cur, nxt;
     scan_load<IO>(nxt, q, k, v, mask, wsn, b, hv, hk, dv0, T, Hk, Hv, Dv, 0u, w, lr, lg);
 
+    // y and delta of a chunk are stored at the start of the next iteration,
+    // before its prefetch: the prefetched values are then awaited without also
+    // waiting for those (conditional, hence uncounted) stores to complete.
+    f32x4v y_prev = {0.f, 0.f, 0.f, 0.f}, d_prev = y_prev;
+    uint32_t act_prev = 0u;
+    auto store_outputs = [&](uint32_t tp) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (act_prev & (1u << r)) {
+                const size_t i = ((static_cast<size_t>(b) * T + tp + 16u * w + 4u * lg + r) * Hv + hv) * Dv + dv0 + lr;
+                static_cast<uint16_t*>(y)[i] = static_cast<uint16_t>(f32_to_bf16_bits(y_prev[r]));
+                if (delta_log)
+                    static_cast<uint16_t*>(delta_log)[i] = static_cast<uint16_t>(f32_to_bf16_bits(d_prev[r]));
+            }
+        }
+    };
+
     for (uint32_t c = 0; c < nchunks; ++c) {
         cur = nxt;
+        if (c > 0) store_outputs((c - 1) * kC);
         if (c + 1 < nchunks)
             scan_load<IO>(nxt, q, k, v, mask, wsn + (c + 1) * static_cast<size_t>(PrefillWs::kBytes),
                           b, hv, hk, dv0, T, Hk, Hv, Dv, (c + 1) * kC, w, lr, lg);
         const uint32_t t0 = c * kC;
         uint16_t* ktb = kt[c & 1u];
+        // Inactive steps (masked, or past T): zero keys, queries and values.
+        uint32_t act = 0u;
+        {
+            const bool a = t0 + 16u * w + lr < T && cur.mA > 0u;
+#pragma unroll
+            for (int ks = 0; ks < kDk / 16; ++ks) {
+                cur.kf[ks] = a ? cur.kf[ks] : zero2();
+                cur.qf[ks] = a ? cur.qf[ks] : zero2();
+            }
+        }
+        f32x4v vv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool a = t0 + 16u * w + 4u * lg + r < T && cur.mC[r] > 0u;
+            vv[r] = a ? bf16_bits_to_f32((cur.vb[r] >> (16u * (lr & 1u))) & 0xffffu) : 0.0f;
+            act |= a ? (1u << r) : 0u;
+        }
 
         // State tiles of this wave -> (hi, lo) fragments for every wave.
 #pragma unroll
@@ -399,7 +464,7 @@ __global__ __launch_bounds__(256, 1) void gdn_prefill_scan_kernel(
         }
         f32x4v R;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) R[r] = cur.v[r] - cur.gam[r] * (xk[r] + xk2[r]);
+        for (int r = 0; r < 4; ++r) R[r] = vv[r] - cur.gam[r] * (xk[r] + xk2[r]);
         {
             u32x2 hi, lo;
             split4(R, hi, lo);
@@ -431,16 +496,8 @@ __global__ __launch_bounds__(256, 1) void gdn_prefill_scan_kernel(
             split4(Dt, hi, lo);
             dtf[w][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
         }
-        if (delta_log) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (cur.act & (1u << r)) {
-                    const size_t i = ((static_cast<size_t>(b) * T + t0 + 16u * w + 4u * lg + r) * Hv + hv) * Dv +
-                                     dv0 + lr;
-                    static_cast<uint16_t*>(delta_log)[i] = static_cast<uint16_t>(f32_to_bf16_bits(D[r]));
-                }
-            }
-        }
+        d_prev = D;
+        act_prev = act;
         __syncthreads();
 
         // Y (step tile w) = gamma o X_Q + P Delta.
@@ -456,12 +513,7 @@ __global__ __launch_bounds__(256, 1) void gdn_prefill_scan_kernel(
             Y2 = mfma_bf16(cur.pl[ks], dh, Y2);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if (cur.act & (1u << r)) {
-                const size_t i = ((static_cast<size_t>(b) * T + t0 + 16u * w + 4u * lg + r) * Hv + hv) * Dv + dv0 + lr;
-                static_cast<uint16_t*>(y)[i] = static_cast<uint16_t>(f32_to_bf16_bits(Y[r] + Y2[r]));
-            }
-        }
+        for (int r = 0; r < 4; ++r) y_prev[r] = Y[r] + Y2[r];
 
         // S^T <- gamma_63 S^T + K^T (rho o Delta) for this wave's key tiles.
 #pragma unroll
@@ -487,6 +539,7 @@ __global__ __launch_bounds__(256, 1) void gdn_prefill_scan_kernel(
             for (int r = 0; r < 4; ++r) acc[u][r] += lo_acc[u][r];
     }
 
+    store_outputs((nchunks - 1) * kC);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
         *reinterpret_cast<float4*>(state_out + srow + 16 * u) = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
