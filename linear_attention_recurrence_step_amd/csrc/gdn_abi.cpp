@@ -188,7 +188,7 @@ int gdn_prefill(const void* q, const void* k, const void* v, const void* g, cons
     const uint64_t nchunks = (uint64_t(T) + 63) / 64;
     uint64_t prep_items, scan_items;
     if (!mul_u64(&prep_items, {B, Hv, nchunks, 256}) || prep_items > kMaxWorkItems ||
-        !mul_u64(&scan_items, {B, Hv, Dv / 16, 256}) || scan_items > kMaxWorkItems)
+        !mul_u64(&scan_items, {B, Hv, Dv / 16, 512}) || scan_items > kMaxWorkItems)
         return fail(GDN_ERR_OVERFLOW, "%s: launch grid too large (split the batch)", kFn);
     const uint64_t need = gdn::prefill_workspace_bytes(B, T, Hv);
     if (!workspace || workspace_bytes < need)

@@ -291,68 +291,67 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(
 
 // ------------------------------------------------------------------ scan
 //
-// One workgroup of four waves per (b, hv, 16 consecutive value rows).  The
+// One workgroup of eight waves per (b, hv, 16 consecutive value rows).  The
 // state is held transposed in MFMA accumulators: wave w owns key columns
-// 32w .. 32w+31 (two 16 x 16 tiles), lane l holding S[dv0 + l%16][16 tile +
-// 4 (l/16) + r] -- the layout in which a tile is also the B operand of
-// X = K S^T for the key step it covers.  Wave w computes the chunk's step
-// tile w (steps 16w .. 16w+15) of X, Delta and Y.
+// 16w .. 16w+15, lane l holding S[dv0 + l%16][16w + 4 (l/16) + r] -- the
+// layout in which the tile is also the B operand of X = K S^T for key step w.
+// Waves 0-3 (the K side) take step tile w of the chunk: X_K, R and Delta.
+// Waves 4-7 (the Q side) take step tile w-4: X_Q, and Y of the previous chunk
+// while the K side solves for Delta (Y is not on the state's dependency chain).
 struct ScanIn {
-    u32x2 kf[kDk / 16], qf[kDk / 16];   // K, Q [16w + lr][16 ks + 4 lg ..], as loaded
-    u32x2 th[4], tl[4], ph[4], pl[4];   // Tb and P [16w + lr][16 ks + 4 lg ..]
-    uint32_t vb[4];                     // word holding v at steps 16w + 4 lg + r, row lr
+    u32x2 af[kDk / 16];                 // K (K side) or Q (Q side) [16 tt + lr][16 ks + 4 lg ..], as loaded
+    u32x2 mh[4], ml[4];                 // Tb (K side) or P (Q side) [16 tt + lr][16 ks + 4 lg ..], hi and lo
+    uint32_t vb[4];                     // word holding v at steps 16 tt + 4 lg + r, row lr
     uint32_t mA, mC[4];                 // mask words of those steps (1 without a mask)
-    f32x4v gam, rho;                    // gamma, rho at steps 16w + 4 lg + r
+    f32x4v gam, rho;                    // gamma, rho at steps 16 tt + 4 lg + r
     float gC;                           // gamma_63
 };
 
 // Issue the loads of one chunk.  Nothing here consumes a loaded value, so the
 // loads stay in flight while the previous chunk is computed; steps past T
 // read step T-1 and are zeroed where the values are used.
-template <int IO>
-__device__ __forceinline__ void scan_load(ScanIn& in, const void* q, const void* k, const void* v,
-                                          const uint32_t* mask, const unsigned char* wsb,
-                                          uint32_t b, uint32_t hv, uint32_t hk, uint32_t dv0,
-                                          uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dv,
-                                          uint32_t t0, uint32_t w, uint32_t lr, uint32_t lg) {
+__device__ __forceinline__ void scan_load(ScanIn& in, const void* src, const uint32_t* mask,
+                                          const void* v, const unsigned char* wsb, int ws_hi,
+                                          int ws_lo, uint32_t b, uint32_t hv, uint32_t hk,
+                                          uint32_t dv0, uint32_t T, uint32_t Hk, uint32_t Hv,
+                                          uint32_t Dv, uint32_t t0, uint32_t tt, uint32_t lr,
+                                          uint32_t lg) {
     {
-        const uint32_t t = t0 + 16u * w + lr, tc = t < T ? t : T - 1;
+        const uint32_t t = t0 + 16u * tt + lr, tc = t < T ? t : T - 1;
         const size_t off = ((static_cast<size_t>(b) * T + tc) * Hk + hk) * kDk * 2 + lg * 8;
 #pragma unroll
-        for (int ks = 0; ks < kDk / 16; ++ks) {
-            in.kf[ks] = load8(k, off + ks * 32);
-            in.qf[ks] = load8(q, off + ks * 32);
-        }
+        for (int ks = 0; ks < kDk / 16; ++ks) in.af[ks] = load8(src, off + ks * 32);
         in.mA = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const uint32_t t = t0 + 16u * w + 4u * lg + r, tc = t < T ? t : T - 1;
+        const uint32_t t = t0 + 16u * tt + 4u * lg + r, tc = t < T ? t : T - 1;
         // The aligned 32-bit word holding the element (Dv is even, so it lies
         // inside v); the half is picked where the value is used.
         const size_t e = ((static_cast<size_t>(b) * T + tc) * Hv + hv) * Dv + dv0 + lr;
         in.vb[r] = static_cast<const uint32_t*>(v)[e >> 1];
         in.mC[r] = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
     }
-    const size_t frag = ((16u * w + lr) * kC + 4u * lg) * 2;
+    const size_t frag = ((16u * tt + lr) * kC + 4u * lg) * 2;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        in.th[ks] = load8(wsb, PrefillWs::kTbHi + frag + ks * 32);
-        in.tl[ks] = load8(wsb, PrefillWs::kTbLo + frag + ks * 32);
-        in.ph[ks] = load8(wsb, PrefillWs::kPHi + frag + ks * 32);
-        in.pl[ks] = load8(wsb, PrefillWs::kPLo + frag + ks * 32);
+        in.mh[ks] = load8(wsb, ws_hi + frag + ks * 32);
+        in.ml[ks] = load8(wsb, ws_lo + frag + ks * 32);
     }
     const float* gam = reinterpret_cast<const float*>(wsb + PrefillWs::kGamma);
     const float* rho = reinterpret_cast<const float*>(wsb + PrefillWs::kRho);
-    const float4 g4 = *reinterpret_cast<const float4*>(gam + 16u * w + 4u * lg);
-    const float4 r4 = *reinterpret_cast<const float4*>(rho + 16u * w + 4u * lg);
+    const float4 g4 = *reinterpret_cast<const float4*>(gam + 16u * tt + 4u * lg);
+    const float4 r4 = *reinterpret_cast<const float4*>(rho + 16u * tt + 4u * lg);
     in.gam = f32x4v{g4.x, g4.y, g4.z, g4.w};
     in.rho = f32x4v{r4.x, r4.y, r4.z, r4.w};
     in.gC = gam[kC - 1];
 }
 
+__device__ __forceinline__ u32x2 lo2(const u32x4& x) { return u32x2{x.x, x.y}; }
+__device__ __forceinline__ u32x2 hi2(const u32x4& x) { return u32x2{x.z, x.w}; }
+
 template <int IO>
-__global__ __launch_bounds__(256, 1) void gdn_prefill_scan_kernel(
+__global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* state_in, const uint32_t* __restrict__ mask,
     const unsigned char* __restrict__ ws, void* __restrict__ y, float* state_out,
@@ -364,12 +363,14 @@ __global__ __launch_bounds__(256, 1) void gdn_prefill_scan_kernel(
     // Fragments exchanged between the waves: lane-ordered 16-byte (hi, lo) pairs.
     __shared__ __align__(16) u32x4 sfr[kDk / 16][64];  // state, per key step
     __shared__ __align__(16) u32x4 rfr[4][64];         // R, per step tile
-    __shared__ __align__(16) u32x4 dfr[4][64];         // Delta
+    __shared__ __align__(16) u32x4 dfr[2][4][64];      // Delta, two chunks
     __shared__ __align__(16) u32x4 dtf[4][64];         // rho o Delta
     __shared__ __align__(16) uint16_t kt[2][kDk * KTS];   // K^T [dk][t], two chunks
 
     const uint32_t tid = threadIdx.x, l = tid & 63u, w = tid >> 6;
     const uint32_t lr = l & 15u, lg = l >> 4;
+    const uint32_t tt = w & 3u;                         // step tile
+    const bool qside = w >= 4u;
     const uint32_t slices = Dv / kRows;
     const uint32_t blk = xcd_contiguous_index(blockIdx.x, gridDim.x);
     const uint32_t n = blk / slices;                    // b * Hv + hv
@@ -377,172 +378,189 @@ __global__ __launch_bounds__(256, 1) void gdn_prefill_scan_kernel(
     const uint32_t b = n / Hv, hv = n - b * Hv;
     const uint32_t hk = tiled ? hv % Hk : hv / group;
 
-    // This lane's two 16-byte state pieces: row dv0 + lr, columns 32w + 16u + 4lg.
-    const size_t srow = (static_cast<size_t>(n) * Dv + dv0 + lr) * kDk + 32u * w + 4u * lg;
-    f32x4v acc[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const float4 s4 = *reinterpret_cast<const float4*>(state_in + srow + 16 * u);
-        acc[u] = f32x4v{s4.x, s4.y, s4.z, s4.w};
+    // This lane's 16-byte state piece: row dv0 + lr, columns 16w + 4lg .. +3.
+    const size_t srow = (static_cast<size_t>(n) * Dv + dv0 + lr) * kDk + 16u * w + 4u * lg;
+    f32x4v acc;
+    {
+        const float4 s4 = *reinterpret_cast<const float4*>(state_in + srow);
+        acc = f32x4v{s4.x, s4.y, s4.z, s4.w};
     }
 
+    const void* src = qside ? q : k;
+    const int ws_hi = qside ? PrefillWs::kPHi : PrefillWs::kTbHi;
+    const int ws_lo = qside ? PrefillWs::kPLo : PrefillWs::kTbLo;
+    void* out = qside ? y : delta_log;                  // what this wave writes (delta_log may be NULL)
     const unsigned char* wsn = ws + static_cast<size_t>(n) * nchunks * PrefillWs::kBytes;
     ScanIn cur, nxt;
-    scan_load<IO>(nxt, q, k, v, mask, wsn, b, hv, hk, dv0, T, Hk, Hv, Dv, 0u, w, lr, lg);
+    scan_load(nxt, src, mask, v, wsn, ws_hi, ws_lo, b, hv, hk, dv0, T, Hk, Hv, Dv, 0u, tt, lr, lg);
 
-    // y and delta of a chunk are stored at the start of the next iteration,
-    // before its prefetch: the prefetched values are then awaited without also
-    // waiting for those (conditional, hence uncounted) stores to complete.
-    f32x4v y_prev = {0.f, 0.f, 0.f, 0.f}, d_prev = y_prev;
-    uint32_t act_prev = 0u;
-    auto store_outputs = [&](uint32_t tp) {
+    // One pending output tile per wave (Delta of this chunk on the K side, Y of
+    // the previous chunk on the Q side), stored at the start of the next
+    // iteration before its prefetch: the prefetched values are then awaited
+    // without also waiting for those (conditional, hence uncounted) stores.
+    f32x4v pend = {0.f, 0.f, 0.f, 0.f};
+    uint32_t pend_act = 0u, pend_t0 = 0u;
+    auto flush = [&]() {
+        if (out == nullptr) return;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            if (act_prev & (1u << r)) {
-                const size_t i = ((static_cast<size_t>(b) * T + tp + 16u * w + 4u * lg + r) * Hv + hv) * Dv + dv0 + lr;
-                static_cast<uint16_t*>(y)[i] = static_cast<uint16_t>(f32_to_bf16_bits(y_prev[r]));
-                if (delta_log)
-                    static_cast<uint16_t*>(delta_log)[i] = static_cast<uint16_t>(f32_to_bf16_bits(d_prev[r]));
+            if (pend_act & (1u << r)) {
+                const size_t i = ((static_cast<size_t>(b) * T + pend_t0 + 16u * tt + 4u * lg + r) * Hv + hv) * Dv +
+                                 dv0 + lr;
+                static_cast<uint16_t*>(out)[i] = static_cast<uint16_t>(f32_to_bf16_bits(pend[r]));
             }
         }
+        pend_act = 0u;
+    };
+    // Q side: what Y of a chunk needs one iteration later.
+    f32x4v xq_prev = {0.f, 0.f, 0.f, 0.f}, gam_prev = xq_prev;
+    u32x2 ph_prev[4], pl_prev[4];
+    uint32_t act_prev = 0u;
+    auto y_tile = [&](const u32x4 (&dsrc)[4][64]) {
+        f32x4v Y, Y2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Y[r] = gam_prev[r] * xq_prev[r];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const u32x4 dd = dsrc[ks][l];
+            Y = mfma_bf16(ph_prev[ks], lo2(dd), Y);
+            Y2 = mfma_bf16(ph_prev[ks], hi2(dd), Y2);
+            Y2 = mfma_bf16(pl_prev[ks], lo2(dd), Y2);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pend[r] = Y[r] + Y2[r];
     };
 
     for (uint32_t c = 0; c < nchunks; ++c) {
         cur = nxt;
-        if (c > 0) store_outputs((c - 1) * kC);
+        flush();
         if (c + 1 < nchunks)
-            scan_load<IO>(nxt, q, k, v, mask, wsn + (c + 1) * static_cast<size_t>(PrefillWs::kBytes),
-                          b, hv, hk, dv0, T, Hk, Hv, Dv, (c + 1) * kC, w, lr, lg);
+            scan_load(nxt, src, mask, v, wsn + (c + 1) * static_cast<size_t>(PrefillWs::kBytes), ws_hi, ws_lo,
+                      b, hv, hk, dv0, T, Hk, Hv, Dv, (c + 1) * kC, tt, lr, lg);
         const uint32_t t0 = c * kC;
         uint16_t* ktb = kt[c & 1u];
         // Inactive steps (masked, or past T): zero keys, queries and values.
-        uint32_t act = 0u;
         {
-            const bool a = t0 + 16u * w + lr < T && cur.mA > 0u;
+            const bool a = t0 + 16u * tt + lr < T && cur.mA > 0u;
 #pragma unroll
-            for (int ks = 0; ks < kDk / 16; ++ks) {
-                cur.kf[ks] = a ? cur.kf[ks] : zero2();
-                cur.qf[ks] = a ? cur.qf[ks] : zero2();
-            }
+            for (int ks = 0; ks < kDk / 16; ++ks) cur.af[ks] = a ? cur.af[ks] : zero2();
         }
+        uint32_t act = 0u;
         f32x4v vv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const bool a = t0 + 16u * w + 4u * lg + r < T && cur.mC[r] > 0u;
+            const bool a = t0 + 16u * tt + 4u * lg + r < T && cur.mC[r] > 0u;
             vv[r] = a ? bf16_bits_to_f32((cur.vb[r] >> (16u * (lr & 1u))) & 0xffffu) : 0.0f;
             act |= a ? (1u << r) : 0u;
         }
 
-        // State tiles of this wave -> (hi, lo) fragments for every wave.
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        // State tile -> (hi, lo) fragment for every wave; the K side's key rows,
+        // transposed into K^T [dk][t].
+        {
             u32x2 hi, lo;
-            split4(acc[u], hi, lo);
-            sfr[2 * w + u][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
+            split4(acc, hi, lo);
+            sfr[w][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
         }
-        // This wave's 16 key rows, transposed into K^T [dk][t].
+        if (!qside) {
 #pragma unroll
-        for (int ks = 0; ks < kDk / 16; ++ks) {
-            const uint32_t dk = 16u * ks + 4u * lg, t = 16u * w + lr;
-            ktb[(dk + 0) * KTS + t] = static_cast<uint16_t>(cur.kf[ks].x);
-            ktb[(dk + 1) * KTS + t] = static_cast<uint16_t>(cur.kf[ks].x >> 16);
-            ktb[(dk + 2) * KTS + t] = static_cast<uint16_t>(cur.kf[ks].y);
-            ktb[(dk + 3) * KTS + t] = static_cast<uint16_t>(cur.kf[ks].y >> 16);
+            for (int ks = 0; ks < kDk / 16; ++ks) {
+                const uint32_t dk = 16u * ks + 4u * lg, t = 16u * tt + lr;
+                ktb[(dk + 0) * KTS + t] = static_cast<uint16_t>(cur.af[ks].x);
+                ktb[(dk + 1) * KTS + t] = static_cast<uint16_t>(cur.af[ks].x >> 16);
+                ktb[(dk + 2) * KTS + t] = static_cast<uint16_t>(cur.af[ks].y);
+                ktb[(dk + 3) * KTS + t] = static_cast<uint16_t>(cur.af[ks].y >> 16);
+            }
         }
         __syncthreads();
 
-        // X_K = K S0^T and X_Q = Q S0^T for step tile w (hi and lo parts apart).
-        f32x4v xk = {0.f, 0.f, 0.f, 0.f}, xq = xk, xk2 = xk, xq2 = xk;
+        // X = (K or Q) S0^T for step tile tt (hi and lo parts apart).
+        f32x4v x = {0.f, 0.f, 0.f, 0.f}, x2 = x;
 #pragma unroll
         for (int ks = 0; ks < kDk / 16; ++ks) {
-            const u32x4 s = sfr[ks][l];
-            const u32x2 sh = {s.x, s.y}, sl = {s.z, s.w};
-            xk = mfma_bf16(cur.kf[ks], sh, xk);
-            xq = mfma_bf16(cur.qf[ks], sh, xq);
-            xk2 = mfma_bf16(cur.kf[ks], sl, xk2);
-            xq2 = mfma_bf16(cur.qf[ks], sl, xq2);
+            const u32x4 sv = sfr[ks][l];
+            x = mfma_bf16(cur.af[ks], lo2(sv), x);
+            x2 = mfma_bf16(cur.af[ks], hi2(sv), x2);
         }
-        f32x4v R;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) R[r] = vv[r] - cur.gam[r] * (xk[r] + xk2[r]);
-        {
+        for (int r = 0; r < 4; ++r) x[r] += x2[r];
+        if (!qside) {
+            f32x4v R;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) R[r] = vv[r] - cur.gam[r] * x[r];
             u32x2 hi, lo;
             split4(R, hi, lo);
-            rfr[w][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
+            rfr[tt][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
         }
         __syncthreads();
 
-        // Delta (step tile w) = Tb R.  Tb and P are zero above the diagonal, so
-        // the tiles past w add exact zeros; every wave runs all four, which
-        // costs nothing on the critical path (wave 3 needs all four anyway).
-        f32x4v D = {0.f, 0.f, 0.f, 0.f}, D2 = D;
+        if (!qside) {
+            // Delta (step tile tt) = Tb R.  Tb is zero above the diagonal, so
+            // the tiles past tt add exact zeros.
+            f32x4v D = {0.f, 0.f, 0.f, 0.f}, D2 = D;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const u32x4 rr = rfr[ks][l];
-            const u32x2 rh = {rr.x, rr.y}, rl = {rr.z, rr.w};
-            D = mfma_bf16(cur.th[ks], rh, D);
-            D2 = mfma_bf16(cur.th[ks], rl, D2);
-            D2 = mfma_bf16(cur.tl[ks], rh, D2);
-        }
+            for (int ks = 0; ks < 4; ++ks) {
+                const u32x4 rr = rfr[ks][l];
+                D = mfma_bf16(cur.mh[ks], lo2(rr), D);
+                D2 = mfma_bf16(cur.mh[ks], hi2(rr), D2);
+                D2 = mfma_bf16(cur.ml[ks], lo2(rr), D2);
+            }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) D[r] += D2[r];
-        {
+            for (int r = 0; r < 4; ++r) D[r] += D2[r];
             u32x2 hi, lo;
             split4(D, hi, lo);
-            dfr[w][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
+            dfr[c & 1u][tt][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
             f32x4v Dt;
 #pragma unroll
             for (int r = 0; r < 4; ++r) Dt[r] = cur.rho[r] * D[r];
             split4(Dt, hi, lo);
-            dtf[w][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
+            dtf[tt][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
+            pend = D;
+            pend_act = act;
+            pend_t0 = t0;
+        } else if (c > 0) {
+            // Y of the previous chunk = gamma o X_Q + P Delta.
+            y_tile(dfr[(c - 1) & 1u]);
+            pend_act = act_prev;
+            pend_t0 = t0 - kC;
         }
-        d_prev = D;
-        act_prev = act;
+        if (qside) {
+            xq_prev = x;
+            gam_prev = cur.gam;
+            act_prev = act;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                ph_prev[ks] = cur.mh[ks];
+                pl_prev[ks] = cur.ml[ks];
+            }
+        }
         __syncthreads();
 
-        // Y (step tile w) = gamma o X_Q + P Delta.
-        f32x4v Y, Y2 = {0.f, 0.f, 0.f, 0.f};
+        // S^T <- gamma_63 S^T + K^T (rho o Delta) for this wave's key tile.
+        f32x4v lo_acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Y[r] = cur.gam[r] * (xq[r] + xq2[r]);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const u32x4 dd = dfr[ks][l];
-            const u32x2 dh = {dd.x, dd.y}, dl = {dd.z, dd.w};
-            Y = mfma_bf16(cur.ph[ks], dh, Y);
-            Y2 = mfma_bf16(cur.ph[ks], dl, Y2);
-            Y2 = mfma_bf16(cur.pl[ks], dh, Y2);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) y_prev[r] = Y[r] + Y2[r];
-
-        // S^T <- gamma_63 S^T + K^T (rho o Delta) for this wave's key tiles.
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[u][r] *= cur.gC;
-        f32x4v lo_acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        for (int r = 0; r < 4; ++r) acc[r] *= cur.gC;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const u32x4 dd = dtf[ks][l];
-            const u32x2 dh = {dd.x, dd.y}, dl = {dd.z, dd.w};
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const uint32_t dk = 16u * (2u * w + u) + lr;
-                const u32x2 a = *reinterpret_cast<const u32x2*>(&ktb[dk * KTS + 16 * ks + 4 * lg]);
-                acc[u] = mfma_bf16(a, dh, acc[u]);
-                lo_acc[u] = mfma_bf16(a, dl, lo_acc[u]);
-            }
+            const uint32_t dk = 16u * w + lr;
+            const u32x2 a = *reinterpret_cast<const u32x2*>(&ktb[dk * KTS + 16 * ks + 4 * lg]);
+            acc = mfma_bf16(a, lo2(dd), acc);
+            lo_acc = mfma_bf16(a, hi2(dd), lo_acc);
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[u][r] += lo_acc[u][r];
+        for (int r = 0; r < 4; ++r) acc[r] += lo_acc[r];
     }
 
-    store_outputs((nchunks - 1) * kC);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-        *reinterpret_cast<float4*>(state_out + srow + 16 * u) = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+    flush();
+    if (qside) {
+        // Y of the last chunk (its Delta fragments were written before the
+        // last iteration's final barrier).
+        y_tile(dfr[(nchunks - 1) & 1u]);
+        pend_act = act_prev;
+        pend_t0 = (nchunks - 1) * kC;
+        flush();
+    }
+    *reinterpret_cast<float4*>(state_out + srow) = make_float4(acc[0], acc[1], acc[2], acc[3]);
 }
 
 }  // namespace
@@ -565,7 +583,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
                        a.q, a.k, a.g, a.beta, a.mask, ws, a.T, a.Hk, a.Hv, nchunks, group, tiled);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gdn_prefill_scan_kernel<kBF16>, dim3(a.B * a.Hv * (a.Dv / kRows)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(gdn_prefill_scan_kernel<kBF16>, dim3(a.B * a.Hv * (a.Dv / kRows)), dim3(512), 0, stream,
                        a.q, a.k, a.v, a.state_in, a.mask, ws, a.y, a.state_out, a.delta_log, a.T, a.Hk, a.Hv,
                        a.Dv, nchunks, group, tiled);
     return hipGetLastError();
