@@ -37,6 +37,8 @@
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
+#include <atomic>
+
 namespace gdn {
 namespace {
 
@@ -298,57 +300,97 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(
 // Waves 0-3 (the K side) take step tile w of the chunk: X_K, R and Delta.
 // Waves 4-7 (the Q side) take step tile w-4: X_Q, and Y of the previous chunk
 // while the K side solves for Delta (Y is not on the state's dependency chain).
-struct ScanIn {
-    u32x2 af[kDk / 16];                 // K (K side) or Q (Q side) [16 tt + lr][16 ks + 4 lg ..], as loaded
-    u32x2 mh[4], ml[4];                 // Tb (K side) or P (Q side) [16 tt + lr][16 ks + 4 lg ..], hi and lo
-    uint32_t vb[4];                     // word holding v at steps 16 tt + 4 lg + r, row lr
-    uint32_t mA, mC[4];                 // mask words of those steps (1 without a mask)
-    f32x4v gam, rho;                    // gamma, rho at steps 16 tt + 4 lg + r
-    float gC;                           // gamma_63
+//
+// A chunk's inputs (its 64 key and query rows, Tb and P, v of this row block,
+// gamma and rho) are copied by all 512 threads with contiguous 16-byte loads
+// into registers while the previous chunk is computed, and into LDS at the
+// top of the iteration; the MFMA fragments are read from LDS.  Key, query and
+// value rows of inactive steps (masked, or past T) are written as zeros.
+struct ScanLds {
+    static constexpr int KS = kDk * 2 + 16;            // K / Q row stride in bytes (padded)
+    static constexpr int TS = kC * 2 + 16;             // Tb / P row stride in bytes (padded)
+    static constexpr int KTS = kC + 4;                 // K^T row stride in bf16 (136 bytes)
+    static constexpr int SFR = 0;                      // state fragments [8][64] x 16 B
+    static constexpr int RFR = SFR + 8 * 64 * 16;      // R fragments [4][64] x 16 B
+    static constexpr int DFR = RFR + 4 * 64 * 16;      // Delta fragments [2][4][64] x 16 B
+    static constexpr int DTF = DFR + 8 * 64 * 16;      // rho o Delta fragments [4][64] x 16 B
+    static constexpr int KT = DTF + 4 * 64 * 16;       // K^T [dk][t] bf16
+    static constexpr int KR = KT + kDk * KTS * 2;      // K rows [64] x KS
+    static constexpr int QR = KR + kC * KS;            // Q rows [64] x KS
+    static constexpr int TP = QR + kC * KS;            // Tb hi, Tb lo, P hi, P lo: [4][64] x TS
+    static constexpr int VR = TP + 4 * kC * TS;        // v rows [64] x 32 B (bf16, this row block)
+    static constexpr int GR = VR + kC * 32;            // gamma [64], rho [64] fp32
+    static constexpr int AF = GR + 2 * kC * 4;         // active flags [64] u32 (0 or 1)
+    static constexpr int BYTES = AF + kC * 4;
 };
 
-// Issue the loads of one chunk.  Nothing here consumes a loaded value, so the
-// loads stay in flight while the previous chunk is computed; steps past T
-// read step T-1 and are zeroed where the values are used.
-__device__ __forceinline__ void scan_load(ScanIn& in, const void* src, const uint32_t* mask,
-                                          const void* v, const unsigned char* wsb, int ws_hi,
-                                          int ws_lo, uint32_t b, uint32_t hv, uint32_t hk,
-                                          uint32_t dv0, uint32_t T, uint32_t Hk, uint32_t Hv,
-                                          uint32_t Dv, uint32_t t0, uint32_t tt, uint32_t lr,
-                                          uint32_t lg) {
-    {
-        const uint32_t t = t0 + 16u * tt + lr, tc = t < T ? t : T - 1;
-        const size_t off = ((static_cast<size_t>(b) * T + tc) * Hk + hk) * kDk * 2 + lg * 8;
+// Staging registers: this thread's pieces of the next chunk.
+struct ScanStage {
+    u32x4 kq[4];          // K pieces 0, 1 then Q pieces 0, 1 (rows tid/16 and tid/16 + 32)
+    u32x4 tp[4];          // pieces tid + 512 j of the 32 KiB Tb/P block
+    u32x4 gv;             // threads 0-31: gamma/rho piece; threads 32-159: v piece
+    uint32_t m0, m1, mv;  // mask words of those rows (1 without a mask)
+};
+
+__device__ __forceinline__ void stage_load(ScanStage& st, const void* q, const void* k, const void* v,
+                                           const uint32_t* mask, const unsigned char* wsb, uint32_t b,
+                                           uint32_t hv, uint32_t hk, uint32_t dv0, uint32_t T, uint32_t Hk,
+                                           uint32_t Hv, uint32_t Dv, uint32_t t0, uint32_t tid) {
+    const uint32_t row = tid >> 4, c16 = tid & 15u;
 #pragma unroll
-        for (int ks = 0; ks < kDk / 16; ++ks) in.af[ks] = load8(src, off + ks * 32);
-        in.mA = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t t = t0 + row + 32u * j, tc = t < T ? t : T - 1;
+        const size_t off = ((static_cast<size_t>(b) * T + tc) * Hk + hk) * (kDk * 2) + c16 * 16;
+        st.kq[j] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(k) + off);
+        st.kq[2 + j] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(q) + off);
+        const uint32_t m = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
+        if (j == 0) st.m0 = m; else st.m1 = m;
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint32_t t = t0 + 16u * tt + 4u * lg + r, tc = t < T ? t : T - 1;
-        // The aligned 32-bit word holding the element (Dv is even, so it lies
-        // inside v); the half is picked where the value is used.
-        const size_t e = ((static_cast<size_t>(b) * T + tc) * Hv + hv) * Dv + dv0 + lr;
-        in.vb[r] = static_cast<const uint32_t*>(v)[e >> 1];
-        in.mC[r] = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
+    for (int j = 0; j < 4; ++j)
+        st.tp[j] = *reinterpret_cast<const u32x4*>(wsb + (tid + 512u * j) * 16);
+    st.mv = 1u;
+    if (tid < 32u) {
+        st.gv = *reinterpret_cast<const u32x4*>(wsb + PrefillWs::kGamma + tid * 16);
+    } else if (tid < 160u) {
+        const uint32_t p = tid - 32u, vr = p >> 1, t = t0 + vr, tc = t < T ? t : T - 1;
+        const size_t e = ((static_cast<size_t>(b) * T + tc) * Hv + hv) * Dv + dv0 + (p & 1u) * 8;
+        st.gv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(v) + e);
+        st.mv = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
     }
-    const size_t frag = ((16u * tt + lr) * kC + 4u * lg) * 2;
+}
+
+__device__ __forceinline__ void stage_store(const ScanStage& st, unsigned char* lds, uint32_t T, uint32_t t0,
+                                            uint32_t tid) {
+    const uint32_t row = tid >> 4, c16 = tid & 15u;
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        in.mh[ks] = load8(wsb, ws_hi + frag + ks * 32);
-        in.ml[ks] = load8(wsb, ws_lo + frag + ks * 32);
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t r = row + 32u * j;
+        const bool act = t0 + r < T && (j == 0 ? st.m0 : st.m1) > 0u;
+        *reinterpret_cast<u32x4*>(lds + ScanLds::KR + r * ScanLds::KS + c16 * 16) = act ? st.kq[j] : z;
+        *reinterpret_cast<u32x4*>(lds + ScanLds::QR + r * ScanLds::KS + c16 * 16) = act ? st.kq[2 + j] : z;
+        if (c16 == 0u) reinterpret_cast<uint32_t*>(lds + ScanLds::AF)[r] = act ? 1u : 0u;
     }
-    const float* gam = reinterpret_cast<const float*>(wsb + PrefillWs::kGamma);
-    const float* rho = reinterpret_cast<const float*>(wsb + PrefillWs::kRho);
-    const float4 g4 = *reinterpret_cast<const float4*>(gam + 16u * tt + 4u * lg);
-    const float4 r4 = *reinterpret_cast<const float4*>(rho + 16u * tt + 4u * lg);
-    in.gam = f32x4v{g4.x, g4.y, g4.z, g4.w};
-    in.rho = f32x4v{r4.x, r4.y, r4.z, r4.w};
-    in.gC = gam[kC - 1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t p = tid + 512u * j;                 // matrix p >> 9, row (p >> 3) & 63, piece p & 7
+        *reinterpret_cast<u32x4*>(lds + ScanLds::TP + (p >> 9) * (kC * ScanLds::TS) +
+                                  ((p >> 3) & 63u) * ScanLds::TS + (p & 7u) * 16) = st.tp[j];
+    }
+    if (tid < 32u) {
+        *reinterpret_cast<u32x4*>(lds + ScanLds::GR + tid * 16) = st.gv;
+    } else if (tid < 160u) {
+        const uint32_t p = tid - 32u, vr = p >> 1;
+        const bool act = t0 + vr < T && st.mv > 0u;
+        *reinterpret_cast<u32x4*>(lds + ScanLds::VR + vr * 32 + (p & 1u) * 16) = act ? st.gv : z;
+    }
 }
 
 __device__ __forceinline__ u32x2 lo2(const u32x4& x) { return u32x2{x.x, x.y}; }
 __device__ __forceinline__ u32x2 hi2(const u32x4& x) { return u32x2{x.z, x.w}; }
+
+__device__ __forceinline__ u32x2 lds8(const unsigned char* p) { return *reinterpret_cast<const u32x2*>(p); }
 
 template <int IO>
 __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
@@ -359,13 +401,13 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     uint32_t nchunks, uint32_t group, int tiled)
 {
     static_assert(IO == kBF16, "the chunked prefill takes bf16 I/O");
-    constexpr int KTS = kC + 4;                        // K^T row stride in bf16 (136 bytes)
-    // Fragments exchanged between the waves: lane-ordered 16-byte (hi, lo) pairs.
-    __shared__ __align__(16) u32x4 sfr[kDk / 16][64];  // state, per key step
-    __shared__ __align__(16) u32x4 rfr[4][64];         // R, per step tile
-    __shared__ __align__(16) u32x4 dfr[2][4][64];      // Delta, two chunks
-    __shared__ __align__(16) u32x4 dtf[4][64];         // rho o Delta
-    __shared__ __align__(16) uint16_t kt[2][kDk * KTS];   // K^T [dk][t], two chunks
+    extern __shared__ __align__(16) unsigned char lds[];
+    u32x4 (*sfr)[64] = reinterpret_cast<u32x4 (*)[64]>(lds + ScanLds::SFR);
+    u32x4 (*rfr)[64] = reinterpret_cast<u32x4 (*)[64]>(lds + ScanLds::RFR);
+    u32x4 (*dfr)[4][64] = reinterpret_cast<u32x4 (*)[4][64]>(lds + ScanLds::DFR);
+    u32x4 (*dtf)[64] = reinterpret_cast<u32x4 (*)[64]>(lds + ScanLds::DTF);
+    uint16_t* kt = reinterpret_cast<uint16_t*>(lds + ScanLds::KT);
+    const float* gr = reinterpret_cast<const float*>(lds + ScanLds::GR);
 
     const uint32_t tid = threadIdx.x, l = tid & 63u, w = tid >> 6;
     const uint32_t lr = l & 15u, lg = l >> 4;
@@ -386,18 +428,21 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         acc = f32x4v{s4.x, s4.y, s4.z, s4.w};
     }
 
-    const void* src = qside ? q : k;
-    const int ws_hi = qside ? PrefillWs::kPHi : PrefillWs::kTbHi;
-    const int ws_lo = qside ? PrefillWs::kPLo : PrefillWs::kTbLo;
     void* out = qside ? y : delta_log;                  // what this wave writes (delta_log may be NULL)
     const unsigned char* wsn = ws + static_cast<size_t>(n) * nchunks * PrefillWs::kBytes;
-    ScanIn cur, nxt;
-    scan_load(nxt, src, mask, v, wsn, ws_hi, ws_lo, b, hv, hk, dv0, T, Hk, Hv, Dv, 0u, tt, lr, lg);
+    // The A-operand rows of this wave: K (K side) or Q (Q side) row 16 tt + lr.
+    const unsigned char* arow = lds + (qside ? ScanLds::QR : ScanLds::KR) + (16u * tt + lr) * ScanLds::KS + lg * 8;
+    // Tb (K side) or P (Q side) row 16 tt + lr, hi and lo.
+    const unsigned char* mrow_hi = lds + ScanLds::TP + (qside ? 2 : 0) * (kC * ScanLds::TS) +
+                                   (16u * tt + lr) * ScanLds::TS + lg * 8;
+    const unsigned char* mrow_lo = mrow_hi + kC * ScanLds::TS;
+
+    ScanStage stage;
+    stage_load(stage, q, k, v, mask, wsn, b, hv, hk, dv0, T, Hk, Hv, Dv, 0u, tid);
 
     // One pending output tile per wave (Delta of this chunk on the K side, Y of
     // the previous chunk on the Q side), stored at the start of the next
-    // iteration before its prefetch: the prefetched values are then awaited
-    // without also waiting for those (conditional, hence uncounted) stores.
+    // iteration before its loads are issued.
     f32x4v pend = {0.f, 0.f, 0.f, 0.f};
     uint32_t pend_act = 0u, pend_t0 = 0u;
     auto flush = [&]() {
@@ -432,64 +477,70 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     };
 
     for (uint32_t c = 0; c < nchunks; ++c) {
-        cur = nxt;
+        const uint32_t t0 = c * kC;
+        stage_store(stage, lds, T, t0, tid);
         flush();
         if (c + 1 < nchunks)
-            scan_load(nxt, src, mask, v, wsn + (c + 1) * static_cast<size_t>(PrefillWs::kBytes), ws_hi, ws_lo,
-                      b, hv, hk, dv0, T, Hk, Hv, Dv, (c + 1) * kC, tt, lr, lg);
-        const uint32_t t0 = c * kC;
-        uint16_t* ktb = kt[c & 1u];
-        // Inactive steps (masked, or past T): zero keys, queries and values.
-        {
-            const bool a = t0 + 16u * tt + lr < T && cur.mA > 0u;
-#pragma unroll
-            for (int ks = 0; ks < kDk / 16; ++ks) cur.af[ks] = a ? cur.af[ks] : zero2();
-        }
-        uint32_t act = 0u;
-        f32x4v vv;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const bool a = t0 + 16u * tt + 4u * lg + r < T && cur.mC[r] > 0u;
-            vv[r] = a ? bf16_bits_to_f32((cur.vb[r] >> (16u * (lr & 1u))) & 0xffffu) : 0.0f;
-            act |= a ? (1u << r) : 0u;
-        }
-
-        // State tile -> (hi, lo) fragment for every wave; the K side's key rows,
-        // transposed into K^T [dk][t].
+            stage_load(stage, q, k, v, mask, wsn + (c + 1) * static_cast<size_t>(PrefillWs::kBytes), b, hv, hk,
+                       dv0, T, Hk, Hv, Dv, (c + 1) * kC, tid);
         {
             u32x2 hi, lo;
             split4(acc, hi, lo);
             sfr[w][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
         }
-        if (!qside) {
-#pragma unroll
-            for (int ks = 0; ks < kDk / 16; ++ks) {
-                const uint32_t dk = 16u * ks + 4u * lg, t = 16u * tt + lr;
-                ktb[(dk + 0) * KTS + t] = static_cast<uint16_t>(cur.af[ks].x);
-                ktb[(dk + 1) * KTS + t] = static_cast<uint16_t>(cur.af[ks].x >> 16);
-                ktb[(dk + 2) * KTS + t] = static_cast<uint16_t>(cur.af[ks].y);
-                ktb[(dk + 3) * KTS + t] = static_cast<uint16_t>(cur.af[ks].y >> 16);
-            }
-        }
         __syncthreads();
 
+        uint32_t act;                                   // bit r: step 16 tt + 4 lg + r is active
+        {
+            const u32x4 f = *reinterpret_cast<const u32x4*>(lds + ScanLds::AF + (16u * tt + 4u * lg) * 4);
+            act = f.x | (f.y << 1) | (f.z << 2) | (f.w << 3);
+        }
+
         // X = (K or Q) S0^T for step tile tt (hi and lo parts apart).
+        u32x2 af[kDk / 16];
+#pragma unroll
+        for (int ks = 0; ks < kDk / 16; ++ks) af[ks] = lds8(arow + ks * 32);
         f32x4v x = {0.f, 0.f, 0.f, 0.f}, x2 = x;
 #pragma unroll
         for (int ks = 0; ks < kDk / 16; ++ks) {
             const u32x4 sv = sfr[ks][l];
-            x = mfma_bf16(cur.af[ks], lo2(sv), x);
-            x2 = mfma_bf16(cur.af[ks], hi2(sv), x2);
+            x = mfma_bf16(af[ks], lo2(sv), x);
+            x2 = mfma_bf16(af[ks], hi2(sv), x2);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] += x2[r];
+        f32x4v gam;
+        {
+            const float4 g4 = *reinterpret_cast<const float4*>(gr + 16u * tt + 4u * lg);
+            gam = f32x4v{g4.x, g4.y, g4.z, g4.w};
+        }
         if (!qside) {
+            // This wave's 16 key rows, transposed into K^T [dk][t] for the state update.
+#pragma unroll
+            for (int ks = 0; ks < kDk / 16; ++ks) {
+                const uint32_t dk = 16u * ks + 4u * lg, t = 16u * tt + lr;
+                kt[(dk + 0) * ScanLds::KTS + t] = static_cast<uint16_t>(af[ks].x);
+                kt[(dk + 1) * ScanLds::KTS + t] = static_cast<uint16_t>(af[ks].x >> 16);
+                kt[(dk + 2) * ScanLds::KTS + t] = static_cast<uint16_t>(af[ks].y);
+                kt[(dk + 3) * ScanLds::KTS + t] = static_cast<uint16_t>(af[ks].y >> 16);
+            }
+            const uint16_t* vr = reinterpret_cast<const uint16_t*>(lds + ScanLds::VR);
             f32x4v R;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) R[r] = vv[r] - cur.gam[r] * x[r];
+            for (int r = 0; r < 4; ++r)
+                R[r] = bf16_bits_to_f32(vr[(16u * tt + 4u * lg + r) * 16 + lr]) - gam[r] * x[r];
             u32x2 hi, lo;
             split4(R, hi, lo);
             rfr[tt][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
+        }
+        // Q side: P fragments of this chunk (read now, used next iteration).
+        u32x2 ph_cur[4], pl_cur[4];
+        if (qside) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                ph_cur[ks] = lds8(mrow_hi + ks * 32);
+                pl_cur[ks] = lds8(mrow_lo + ks * 32);
+            }
         }
         __syncthreads();
 
@@ -500,9 +551,10 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const u32x4 rr = rfr[ks][l];
-                D = mfma_bf16(cur.mh[ks], lo2(rr), D);
-                D2 = mfma_bf16(cur.mh[ks], hi2(rr), D2);
-                D2 = mfma_bf16(cur.ml[ks], lo2(rr), D2);
+                const u32x2 th = lds8(mrow_hi + ks * 32), tl = lds8(mrow_lo + ks * 32);
+                D = mfma_bf16(th, lo2(rr), D);
+                D2 = mfma_bf16(th, hi2(rr), D2);
+                D2 = mfma_bf16(tl, lo2(rr), D2);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) D[r] += D2[r];
@@ -510,40 +562,41 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
             split4(D, hi, lo);
             dfr[c & 1u][tt][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
             f32x4v Dt;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Dt[r] = cur.rho[r] * D[r];
+            const float4 r4 = *reinterpret_cast<const float4*>(gr + kC + 16u * tt + 4u * lg);
+            Dt[0] = r4.x * D[0]; Dt[1] = r4.y * D[1]; Dt[2] = r4.z * D[2]; Dt[3] = r4.w * D[3];
             split4(Dt, hi, lo);
             dtf[tt][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
             pend = D;
             pend_act = act;
             pend_t0 = t0;
-        } else if (c > 0) {
-            // Y of the previous chunk = gamma o X_Q + P Delta.
-            y_tile(dfr[(c - 1) & 1u]);
-            pend_act = act_prev;
-            pend_t0 = t0 - kC;
-        }
-        if (qside) {
+        } else {
+            if (c > 0) {
+                // Y of the previous chunk = gamma o X_Q + P Delta.
+                y_tile(dfr[(c - 1) & 1u]);
+                pend_act = act_prev;
+                pend_t0 = t0 - kC;
+            }
             xq_prev = x;
-            gam_prev = cur.gam;
+            gam_prev = gam;
             act_prev = act;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                ph_prev[ks] = cur.mh[ks];
-                pl_prev[ks] = cur.ml[ks];
+                ph_prev[ks] = ph_cur[ks];
+                pl_prev[ks] = pl_cur[ks];
             }
         }
+        const float gC = gr[kC - 1];
         __syncthreads();
 
         // S^T <- gamma_63 S^T + K^T (rho o Delta) for this wave's key tile.
         f32x4v lo_acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] *= cur.gC;
+        for (int r = 0; r < 4; ++r) acc[r] *= gC;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const u32x4 dd = dtf[ks][l];
             const uint32_t dk = 16u * w + lr;
-            const u32x2 a = *reinterpret_cast<const u32x2*>(&ktb[dk * KTS + 16 * ks + 4 * lg]);
+            const u32x2 a = *reinterpret_cast<const u32x2*>(&kt[dk * ScanLds::KTS + 16 * ks + 4 * lg]);
             acc = mfma_bf16(a, lo2(dd), acc);
             lo_acc = mfma_bf16(a, hi2(dd), lo_acc);
         }
@@ -583,7 +636,21 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
                        a.q, a.k, a.g, a.beta, a.mask, ws, a.T, a.Hk, a.Hv, nchunks, group, tiled);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gdn_prefill_scan_kernel<kBF16>, dim3(a.B * a.Hv * (a.Dv / kRows)), dim3(512), 0, stream,
+    // The scan kernel takes more than the default 64 KiB of LDS: raise its
+    // limit once per device.
+    static std::atomic<uint64_t> lds_set{0};
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
+    if (bit == 0 || !(lds_set.load(std::memory_order_acquire) & bit)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gdn_prefill_scan_kernel<kBF16>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, ScanLds::BYTES);
+        if (e != hipSuccess) return e;
+        lds_set.fetch_or(bit, std::memory_order_release);
+    }
+    hipLaunchKernelGGL(gdn_prefill_scan_kernel<kBF16>, dim3(a.B * a.Hv * (a.Dv / kRows)), dim3(512), ScanLds::BYTES,
+                       stream,
                        a.q, a.k, a.v, a.state_in, a.mask, ws, a.y, a.state_out, a.delta_log, a.T, a.Hk, a.Hv,
                        a.Dv, nchunks, group, tiled);
     return hipGetLastError();
