@@ -143,19 +143,37 @@ __device__ __forceinline__ void forward_quad_row(float (&mine)[16], const float*
 //
 // One workgroup of four waves per (b, hv, chunk).  Wave w owns row tile w
 // (steps 16w .. 16w+15) of the 64 x 64 matrices.
+// LDS of the prep kernel.  The chunk's key and query rows (padded rows) are
+// dead once the Gram tiles are formed; the output block (Tb hi, Tb lo, P hi,
+// P lo, row-major 64 x 64 bf16, the workspace's own layout) reuses their space.
+struct PrepLds {
+    static constexpr int KS = kDk * 2 + 16;            // K / Q row stride in bytes (padded)
+    static constexpr int MS = kC + 1;                  // M row stride in floats
+    static constexpr int KR = 0;                       // K rows [64] x KS
+    static constexpr int QR = KR + kC * KS;            // Q rows [64] x KS
+    static constexpr int OUT = 0;                      // output block, 4 x 8 KiB (aliases K, Q)
+    static constexpr int ML = QR + kC * KS;            // M [64][65] fp32
+    static constexpr int AQ = ML + kC * MS * 4;        // A in the quad layout
+    static constexpr int GS = AQ + kC * 4 * kAqRow * 4;   // gates [64] fp32
+    static constexpr int BS = GS + kC * 4;             // betas [64] fp32
+    static constexpr int BYTES = BS + kC * 4;
+    static_assert(4 * kC * kC * 2 <= 2 * kC * KS, "output block fits in the key/query area");
+};
+
 template <int IO>
-__global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(
+__global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ g,
     const void* __restrict__ beta, const uint32_t* __restrict__ mask,
     unsigned char* __restrict__ ws, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t nchunks,
     uint32_t group, int tiled)
 {
     static_assert(IO == kBF16, "the chunked prefill takes bf16 I/O");
-    constexpr int MS = kC + 1;       // row stride of M in floats
-    __shared__ __align__(16) float gs[kC];
-    __shared__ float bs[kC];
-    __shared__ float Ml[kC * MS];
-    __shared__ __align__(16) float Aq[kC * 4 * kAqRow];
+    extern __shared__ __align__(16) unsigned char lds[];
+    constexpr int MS = PrepLds::MS;
+    float* gs = reinterpret_cast<float*>(lds + PrepLds::GS);
+    float* bs = reinterpret_cast<float*>(lds + PrepLds::BS);
+    float* Ml = reinterpret_cast<float*>(lds + PrepLds::ML);
+    float* Aq = reinterpret_cast<float*>(lds + PrepLds::AQ);
 
     const uint32_t tid = threadIdx.x, l = tid & 63u, w = tid >> 6;
     const uint32_t lr = l & 15u, lg = l >> 4;
@@ -166,54 +184,38 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(
     const uint32_t t0 = c * kC;
     unsigned char* wsb = ws + (static_cast<size_t>(n) * nchunks + c) * PrefillWs::kBytes;
 
-    // Key fragments of all four row tiles, and key and query fragments of
-    // this wave's tile: lane holds x[16 tile + lr][16 ks + 4 lg .. +3].  All
-    // loads are issued first (steps past T read row T-1); rows of inactive
-    // steps are then replaced by zeros (a select, so a NaN there cannot enter
-    // a product).
-    u32x2 kf[4][kDk / 16], kw[kDk / 16], qf[kDk / 16];
-    uint32_t mt[4], mw;
-    const size_t kq_row = static_cast<size_t>(Hk) * kDk * 2;   // bytes per step
-    const size_t kq_base = (static_cast<size_t>(b) * T * Hk + hk) * kDk * 2 + lg * 8;
-#pragma unroll
-    for (int tile = 0; tile < 4; ++tile) {
-        const uint32_t t = t0 + 16u * tile + lr, tc = t < T ? t : T - 1;
-        const size_t off = kq_base + static_cast<size_t>(tc) * kq_row;
-#pragma unroll
-        for (int ks = 0; ks < kDk / 16; ++ks) kf[tile][ks] = load8(k, off + ks * 32);
-        mt[tile] = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
-    }
+    // The chunk's key and query rows, 16-byte pieces: thread tid takes piece
+    // tid & 15 of rows (tid >> 4) + 16 j.  Steps past T read step T-1; rows of
+    // inactive steps are stored as zeros (a select, so a NaN there cannot
+    // enter a product).
     {
-        const uint32_t t = t0 + 16u * w + lr, tc = t < T ? t : T - 1;
-        const size_t off = kq_base + static_cast<size_t>(tc) * kq_row;
+        u32x4 kp[4], qp[4];
+        uint32_t mw[4];
+        const uint32_t row = tid >> 4, c16 = tid & 15u;
 #pragma unroll
-        for (int ks = 0; ks < kDk / 16; ++ks) {
-            kw[ks] = load8(k, off + ks * 32);
-            qf[ks] = load8(q, off + ks * 32);
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t t = t0 + row + 16u * j, tc = t < T ? t : T - 1;
+            const size_t off = ((static_cast<size_t>(b) * T + tc) * Hk + hk) * (kDk * 2) + c16 * 16;
+            kp[j] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(k) + off);
+            qp[j] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(q) + off);
+            mw[j] = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
         }
-        mw = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
-    }
-    if (tid < kC) {
-        const uint32_t t = t0 + tid, tc = t < T ? t : T - 1;
-        const size_t i = (static_cast<size_t>(b) * T + tc) * Hv + hv;
-        const float gl = io_load1<IO>(g, i), bl = io_load1<IO>(beta, i);
-        const uint32_t m = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
-        const bool act = t < T && m > 0u;
-        gs[tid] = act ? gl : 1.0f;
-        bs[tid] = act ? bl : 0.0f;
-    }
+        if (tid < kC) {
+            const uint32_t t = t0 + tid, tc = t < T ? t : T - 1;
+            const size_t i = (static_cast<size_t>(b) * T + tc) * Hv + hv;
+            const float gl = io_load1<IO>(g, i), bl = io_load1<IO>(beta, i);
+            const uint32_t m = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
+            const bool act = t < T && m > 0u;
+            gs[tid] = act ? gl : 1.0f;
+            bs[tid] = act ? bl : 0.0f;
+        }
+        const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int tile = 0; tile < 4; ++tile) {
-        const bool act = t0 + 16u * tile + lr < T && mt[tile] > 0u;
-#pragma unroll
-        for (int ks = 0; ks < kDk / 16; ++ks) kf[tile][ks] = act ? kf[tile][ks] : zero2();
-    }
-    {
-        const bool act = t0 + 16u * w + lr < T && mw > 0u;
-#pragma unroll
-        for (int ks = 0; ks < kDk / 16; ++ks) {
-            kw[ks] = act ? kw[ks] : zero2();
-            qf[ks] = act ? qf[ks] : zero2();
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t r = row + 16u * j;
+            const bool act = t0 + r < T && mw[j] > 0u;
+            *reinterpret_cast<u32x4*>(lds + PrepLds::KR + r * PrepLds::KS + c16 * 16) = act ? kp[j] : z;
+            *reinterpret_cast<u32x4*>(lds + PrepLds::QR + r * PrepLds::KS + c16 * 16) = act ? qp[j] : z;
         }
     }
     __syncthreads();
@@ -236,35 +238,58 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(
         }
         reinterpret_cast<float*>(wsb + PrefillWs::kGamma)[t] = p;   // gamma_t = g_0 .. g_t
     }
-    __syncthreads();
-    if (tid < kC) reinterpret_cast<float*>(wsb + PrefillWs::kRho)[tid] = Ml[(kC - 1) * MS + tid];
 
     // Gram tiles G = K K^T and H = Q K^T of row tile w (all four column tiles;
     // above the diagonal the s <= t masks below make A and P exact zeros).
-    // Products of bf16 values are exact in fp32.
-    uint16_t* phi = reinterpret_cast<uint16_t*>(wsb + PrefillWs::kPHi);
-    uint16_t* plo = reinterpret_cast<uint16_t*>(wsb + PrefillWs::kPLo);
+    // Products of bf16 values are exact in fp32.  Fragment: lane holds
+    // x[16 tile + lr][16 ks + 4 lg .. +3].
+    f32x4v G[4], H[4];
+    {
+        u32x2 kw[kDk / 16], qf[kDk / 16];
+        const unsigned char* kwr = lds + PrepLds::KR + (16u * w + lr) * PrepLds::KS + lg * 8;
+        const unsigned char* qwr = lds + PrepLds::QR + (16u * w + lr) * PrepLds::KS + lg * 8;
+#pragma unroll
+        for (int ks = 0; ks < kDk / 16; ++ks) {
+            kw[ks] = *reinterpret_cast<const u32x2*>(kwr + ks * 32);
+            qf[ks] = *reinterpret_cast<const u32x2*>(qwr + ks * 32);
+        }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const unsigned char* kr = lds + PrepLds::KR + (16u * st + lr) * PrepLds::KS + lg * 8;
+            f32x4v g0 = {0.f, 0.f, 0.f, 0.f}, h0 = g0, g1 = g0, h1 = g0;
+#pragma unroll
+            for (int ks = 0; ks < kDk / 16; ks += 2) {
+                const u32x2 b0 = *reinterpret_cast<const u32x2*>(kr + ks * 32);
+                const u32x2 b1 = *reinterpret_cast<const u32x2*>(kr + ks * 32 + 32);
+                g0 = mfma_bf16(kw[ks], b0, g0);
+                g1 = mfma_bf16(kw[ks + 1], b1, g1);
+                h0 = mfma_bf16(qf[ks], b0, h0);
+                h1 = mfma_bf16(qf[ks + 1], b1, h1);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                G[st][r] = g0[r] + g1[r];
+                H[st][r] = h0[r] + h1[r];
+            }
+        }
+    }
+    __syncthreads();       // M is complete; the key and query rows are dead
+
+    if (tid < kC) reinterpret_cast<float*>(wsb + PrefillWs::kRho)[tid] = Ml[(kC - 1) * MS + tid];
+    uint16_t* ophi = reinterpret_cast<uint16_t*>(lds + PrepLds::OUT + 2 * PrefillWs::kMat);
+    uint16_t* oplo = reinterpret_cast<uint16_t*>(lds + PrepLds::OUT + 3 * PrefillWs::kMat);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-        f32x4v G = {0.f, 0.f, 0.f, 0.f}, H = {0.f, 0.f, 0.f, 0.f};
-        f32x4v G2 = G, H2 = H;
-#pragma unroll
-        for (int ks = 0; ks < kDk / 16; ks += 2) {
-            G = mfma_bf16(kw[ks], kf[st][ks], G);
-            G2 = mfma_bf16(kw[ks + 1], kf[st][ks + 1], G2);
-            H = mfma_bf16(qf[ks], kf[st][ks], H);
-            H2 = mfma_bf16(qf[ks + 1], kf[st][ks + 1], H2);
-        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * static_cast<int>(w) + 4 * static_cast<int>(lg) + r;
             const int s = 16 * st + static_cast<int>(lr);
             const float m = Ml[t * MS + s];
-            Aq[(t * 4 + (s & 3)) * kAqRow + (s >> 2)] = s < t ? bs[t] * (m * (G[r] + G2[r])) : 0.0f;
+            Aq[(t * 4 + (s & 3)) * kAqRow + (s >> 2)] = s < t ? bs[t] * (m * G[st][r]) : 0.0f;
             uint16_t hi, lo;
-            split1(s <= t ? m * (H[r] + H2[r]) : 0.0f, hi, lo);
-            phi[t * kC + s] = hi;
-            plo[t * kC + s] = lo;
+            split1(s <= t ? m * H[st][r] : 0.0f, hi, lo);
+            ophi[t * kC + s] = hi;
+            oplo[t * kC + s] = lo;
         }
     }
     __syncthreads();
@@ -278,8 +303,8 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(
         for (int m = 0; m < 16; ++m) mine[m] = 0.0f;
         forward_quad_row<0>(mine, Aq, col, qq);
         const float bc = bs[col];
-        uint16_t* thi = reinterpret_cast<uint16_t*>(wsb + PrefillWs::kTbHi);
-        uint16_t* tlo = reinterpret_cast<uint16_t*>(wsb + PrefillWs::kTbLo);
+        uint16_t* thi = reinterpret_cast<uint16_t*>(lds + PrepLds::OUT);
+        uint16_t* tlo = reinterpret_cast<uint16_t*>(lds + PrepLds::OUT + PrefillWs::kMat);
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             const int i = 4 * m + qq;
@@ -288,6 +313,14 @@ __global__ __launch_bounds__(256) void gdn_prefill_prep_kernel(
             thi[i * kC + col] = hi;
             tlo[i * kC + col] = lo;
         }
+    }
+    __syncthreads();
+
+    // The 32 KiB block to the workspace in contiguous 16-byte pieces.
+#pragma unroll
+    for (int j = 0; j < 4 * PrefillWs::kMat / 16 / 256; ++j) {
+        const uint32_t p = tid + 256u * j;
+        *reinterpret_cast<u32x4*>(wsb + p * 16) = *reinterpret_cast<const u32x4*>(lds + PrepLds::OUT + p * 16);
     }
 }
 
@@ -632,23 +665,26 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     const uint32_t group = a.Hv / a.Hk;
     const int tiled = a.map == 1;
     auto* ws = static_cast<unsigned char*>(a.workspace);
-    hipLaunchKernelGGL(gdn_prefill_prep_kernel<kBF16>, dim3(a.B * a.Hv * nchunks), dim3(256), 0, stream,
-                       a.q, a.k, a.g, a.beta, a.mask, ws, a.T, a.Hk, a.Hv, nchunks, group, tiled);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // The scan kernel takes more than the default 64 KiB of LDS: raise its
-    // limit once per device.
+    // Both kernels take more than the default 64 KiB of LDS: raise their
+    // limits once per device.
     static std::atomic<uint64_t> lds_set{0};
     int dev = 0;
-    e = hipGetDevice(&dev);
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
     if (bit == 0 || !(lds_set.load(std::memory_order_acquire) & bit)) {
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gdn_prefill_scan_kernel<kBF16>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, ScanLds::BYTES);
         if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gdn_prefill_prep_kernel<kBF16>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, PrepLds::BYTES);
+        if (e != hipSuccess) return e;
         lds_set.fetch_or(bit, std::memory_order_release);
     }
+    hipLaunchKernelGGL(gdn_prefill_prep_kernel<kBF16>, dim3(a.B * a.Hv * nchunks), dim3(256), PrepLds::BYTES, stream,
+                       a.q, a.k, a.g, a.beta, a.mask, ws, a.T, a.Hk, a.Hv, nchunks, group, tiled);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gdn_prefill_scan_kernel<kBF16>, dim3(a.B * a.Hv * (a.Dv / kRows)), dim3(512), ScanLds::BYTES,
                        stream,
                        a.q, a.k, a.v, a.state_in, a.mask, ws, a.y, a.state_out, a.delta_log, a.T, a.Hk, a.Hv,
