@@ -474,8 +474,8 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     stage_load(stage, q, k, v, mask, wsn, b, hv, hk, dv0, T, Hk, Hv, Dv, 0u, tid);
 
     // One pending output tile per wave (Delta of this chunk on the K side, Y of
-    // the previous chunk on the Q side), stored at the start of the next
-    // iteration before its loads are issued.
+    // the previous chunk on the Q side), stored in the next iteration just
+    // before its loads are issued.
     f32x4v pend = {0.f, 0.f, 0.f, 0.f};
     uint32_t pend_act = 0u, pend_t0 = 0u;
     auto flush = [&]() {
@@ -512,10 +512,6 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     for (uint32_t c = 0; c < nchunks; ++c) {
         const uint32_t t0 = c * kC;
         stage_store(stage, lds, T, t0, tid);
-        flush();
-        if (c + 1 < nchunks)
-            stage_load(stage, q, k, v, mask, wsn + (c + 1) * static_cast<size_t>(PrefillWs::kBytes), b, hv, hk,
-                       dv0, T, Hk, Hv, Dv, (c + 1) * kC, tid);
         {
             u32x2 hi, lo;
             split4(acc, hi, lo);
@@ -540,6 +536,12 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
             x = mfma_bf16(af[ks], lo2(sv), x);
             x2 = mfma_bf16(af[ks], hi2(sv), x2);
         }
+        // The previous chunk's outputs and the next chunk's loads are issued
+        // here, behind the first barrier, while the products above run.
+        flush();
+        if (c + 1 < nchunks)
+            stage_load(stage, q, k, v, mask, wsn + (c + 1) * static_cast<size_t>(PrefillWs::kBytes), b, hv, hk,
+                       dv0, T, Hk, Hv, Dv, (c + 1) * kC, tid);
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] += x2[r];
         f32x4v gam;
