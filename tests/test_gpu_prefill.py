@@ -61,6 +61,8 @@ CASES = [
     (1, 130, 1, 2, 48, "trailing", "block"),
     (3, 127, 4, 4, 16, "bernoulli", "block"),
     (2, 256, 2, 6, 64, "none", "tiled"),
+    (1, 100, 1, 1, 1024, "bernoulli", "block"),     # the widest head the ABI takes
+    (16, 33, 4, 8, 32, "trailing", "tiled"),        # many heads, one ragged chunk each
 ]
 
 
