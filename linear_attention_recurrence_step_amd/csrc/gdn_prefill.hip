@@ -79,21 +79,6 @@ __device__ __forceinline__ void split1(float x, uint16_t& hi, uint16_t& lo) {
     lo = static_cast<uint16_t>(cvt_pk_bf16(x - bf16_bits_to_f32(h), 0.0f));
 }
 
-__device__ __forceinline__ u32x2 zero2() {
-    u32x2 z;
-    z.x = 0u;
-    z.y = 0u;
-    return z;
-}
-
-__device__ __forceinline__ u32x2 load8(const void* base, size_t byte_off) {
-    return *reinterpret_cast<const u32x2*>(static_cast<const char*>(base) + byte_off);
-}
-
-__device__ __forceinline__ bool step_active(const uint32_t* mask, uint32_t b, uint32_t T, uint32_t t) {
-    return t < T && (mask == nullptr || mask[static_cast<size_t>(b) * T + t] > 0u);
-}
-
 }  // namespace
 
 // Per (b, hv, chunk) block of the workspace, written by prep and read by scan.
@@ -143,6 +128,7 @@ __device__ __forceinline__ void forward_quad_row(float (&mine)[16], const float*
 //
 // One workgroup of four waves per (b, hv, chunk).  Wave w owns row tile w
 // (steps 16w .. 16w+15) of the 64 x 64 matrices.
+//
 // LDS of the prep kernel.  The chunk's key and query rows (padded rows) are
 // dead once the Gram tiles are formed; the output block (Tb hi, Tb lo, P hi,
 // P lo, row-major 64 x 64 bf16, the workspace's own layout) reuses their space.
