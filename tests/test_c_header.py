@@ -40,3 +40,21 @@ def test_c_caller_runs_record_and_replay_on_the_gpu(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
     assert "c gpu ok" in r.stdout
+
+
+@pytest.mark.gpu
+def test_c_caller_runs_the_chunked_prefill_on_the_gpu(tmp_path):
+    """A C program builds bf16 inputs, allocates the workspace with hipMalloc and
+    calls gdn_prefill: a short workspace is refused, and the result agrees with
+    gdn_record on the same inputs."""
+    exe = str(tmp_path / "prefill_c")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                    os.path.join(ROOT, "tests", "c", "prefill_c.c"),
+                    "-L", PKG, "-lgdn", "-L", "/opt/rocm/lib", "-lamdhip64", "-lm",
+                    "-Wl,-rpath," + PKG, "-Wl,-rpath,/opt/rocm/lib", "-o", exe], check=True)
+    sys.stderr.write("[gpu case] C caller of gdn_prefill\n")
+    sys.stderr.flush()
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert "c prefill ok" in r.stdout
