@@ -152,3 +152,31 @@ def test_prefill_nan_at_inactive_steps_never_reaches_an_output():
     inp = dict(inp, **poisoned)
     y, s, dl = _check(inp, "tiled", "NaN at inactive steps")
     assert not torch.isnan(s).any()
+
+
+def _sweep_cases(n=24, seed=4242):
+    """A fixed, seeded list of mixed configurations for the chunked prefill:
+    lengths from one step to several chunks with ragged last chunks, batch
+    rows, GQA ratios 1-3, value widths 16-256, both maps and every mask kind
+    (an all-zero mask included)."""
+    r = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        Dv = int(r.choice([16, 32, 48, 64, 96, 128, 256]))
+        Hk = int(r.integers(1, 4))
+        Hv = Hk * int(r.integers(1, 4))
+        B = int(r.integers(1, 4))
+        T = int(r.choice([1, 3, 17, 63, 64, 65, 100, 128, 129, 191, 256, 300]))
+        while B * Hv * Dv * 128 * T > 12_000_000 and T > 1:   # keep the oracle to about a second
+            T //= 2
+        gmap = str(r.choice(["block", "tiled"]))
+        mask = str(r.choice(["none", "ones", "trailing", "bernoulli", "zeros"]))
+        cases.append((B, T, Hk, Hv, Dv, gmap, mask, seed + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: "B%d_T%d_Hk%d_Hv%d_Dv%d_%s_%s_s%d" % c)
+def test_prefill_seeded_sweep(case):
+    B, T, Hk, Hv, Dv, gmap, mask, seed = case
+    inp = gi.record_inputs(B, T, Hk, Hv, 128, Dv, io="bf16", seed=seed, mask=mask)
+    _check(inp, gmap, "sweep %s" % (case,))
