@@ -82,15 +82,25 @@ __device__ __forceinline__ void split1(float x, uint16_t& hi, uint16_t& lo) {
 }  // namespace
 
 // Per (b, hv, chunk) block of the workspace, written by prep and read by scan.
+// Tb and P are stored in MFMA A-operand fragment order: the 16-byte slot
+// ((tt * 4 + ks) * 64 + l) holds, for lane l = 16 lg + lr, the hi and then the
+// lo bf16 parts of M[16 tt + lr][16 ks + 4 lg .. +3], so a wave reads one step
+// tile's four key-step fragments with four fully coalesced 1 KiB loads.
 struct PrefillWs {
     static constexpr int kMat = kC * kC * 2;             // one 64 x 64 bf16 matrix
-    static constexpr int kTbHi = 0, kTbLo = kMat, kPHi = 2 * kMat, kPLo = 3 * kMat;
+    static constexpr int kTb = 0, kP = 2 * kMat;         // Tb, P: hi/lo fragment slots, 16 KiB each
     static constexpr int kGamma = 4 * kMat;              // gamma_t, fp32 [64]
     static constexpr int kRho = kGamma + kC * 4;         // rho_t = M[63, t], fp32 [64]
     static constexpr int kBytes = kRho + kC * 4;         // 33280
 };
 
 namespace {
+
+// Byte offset of element [t][s] of a 64 x 64 matrix in the fragment order of
+// PrefillWs (its hi part; the lo part is 8 bytes further).
+__device__ __forceinline__ uint32_t frag_offset(uint32_t t, uint32_t s) {
+    return (((t >> 4) * 4u + (s >> 4)) * 64u + 16u * ((s & 15u) >> 2) + (t & 15u)) * 16u + (s & 3u) * 2u;
+}
 
 // Row I of the forward substitution (I + A) T = identity, then the rows after
 // it.  Four consecutive lanes share column c of T; lane q of the four keeps
@@ -130,8 +140,8 @@ __device__ __forceinline__ void forward_quad_row(float (&mine)[16], const float*
 // (steps 16w .. 16w+15) of the 64 x 64 matrices.
 //
 // LDS of the prep kernel.  The chunk's key and query rows (padded rows) are
-// dead once the Gram tiles are formed; the output block (Tb hi, Tb lo, P hi,
-// P lo, row-major 64 x 64 bf16, the workspace's own layout) reuses their space.
+// dead once the Gram tiles are formed; the output block (Tb and P in the
+// workspace's fragment order) reuses their space.
 struct PrepLds {
     static constexpr int KS = kDk * 2 + 16;            // K / Q row stride in bytes (padded)
     static constexpr int MS = kC + 1;                  // M row stride in floats
@@ -262,8 +272,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
     __syncthreads();       // M is complete; the key and query rows are dead
 
     if (tid < kC) reinterpret_cast<float*>(wsb + PrefillWs::kRho)[tid] = Ml[(kC - 1) * MS + tid];
-    uint16_t* ophi = reinterpret_cast<uint16_t*>(lds + PrepLds::OUT + 2 * PrefillWs::kMat);
-    uint16_t* oplo = reinterpret_cast<uint16_t*>(lds + PrepLds::OUT + 3 * PrefillWs::kMat);
+    unsigned char* op = lds + PrepLds::OUT + PrefillWs::kP;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
 #pragma unroll
@@ -274,8 +283,9 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
             Aq[(t * 4 + (s & 3)) * kAqRow + (s >> 2)] = s < t ? bs[t] * (m * G[st][r]) : 0.0f;
             uint16_t hi, lo;
             split1(s <= t ? m * H[st][r] : 0.0f, hi, lo);
-            ophi[t * kC + s] = hi;
-            oplo[t * kC + s] = lo;
+            const uint32_t o = frag_offset(static_cast<uint32_t>(t), static_cast<uint32_t>(s));
+            *reinterpret_cast<uint16_t*>(op + o) = hi;
+            *reinterpret_cast<uint16_t*>(op + o + 8) = lo;
         }
     }
     __syncthreads();
@@ -289,20 +299,21 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
         for (int m = 0; m < 16; ++m) mine[m] = 0.0f;
         forward_quad_row<0>(mine, Aq, col, qq);
         const float bc = bs[col];
-        uint16_t* thi = reinterpret_cast<uint16_t*>(lds + PrepLds::OUT);
-        uint16_t* tlo = reinterpret_cast<uint16_t*>(lds + PrepLds::OUT + PrefillWs::kMat);
+        unsigned char* otb = lds + PrepLds::OUT + PrefillWs::kTb;
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             const int i = 4 * m + qq;
             uint16_t hi, lo;
             split1(mine[m] * bc, hi, lo);
-            thi[i * kC + col] = hi;
-            tlo[i * kC + col] = lo;
+            const uint32_t o = frag_offset(static_cast<uint32_t>(i), static_cast<uint32_t>(col));
+            *reinterpret_cast<uint16_t*>(otb + o) = hi;
+            *reinterpret_cast<uint16_t*>(otb + o + 8) = lo;
         }
     }
     __syncthreads();
 
-    // The 32 KiB block to the workspace in contiguous 16-byte pieces.
+    // The 32 KiB of Tb and P (already in fragment order) to the workspace in
+    // contiguous 16-byte pieces.
 #pragma unroll
     for (int j = 0; j < 4 * PrefillWs::kMat / 16 / 256; ++j) {
         const uint32_t p = tid + 256u * j;
@@ -320,14 +331,14 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
 // Waves 4-7 (the Q side) take step tile w-4: X_Q, and Y of the previous chunk
 // while the K side solves for Delta (Y is not on the state's dependency chain).
 //
-// A chunk's inputs (its 64 key and query rows, Tb and P, v of this row block,
-// gamma and rho) are copied by all 512 threads with contiguous 16-byte loads
-// into registers while the previous chunk is computed, and into LDS at the
-// top of the iteration; the MFMA fragments are read from LDS.  Key, query and
+// A chunk's key and query rows, v of this row block, gamma and rho are copied
+// by all 512 threads with contiguous 16-byte loads into registers while the
+// previous chunk is computed, and into LDS at the top of the iteration; their
+// MFMA fragments are read from LDS.  Tb and P are already in fragment order in
+// the workspace and go straight to registers, one chunk ahead.  Key, query and
 // value rows of inactive steps (masked, or past T) are written as zeros.
 struct ScanLds {
     static constexpr int KS = kDk * 2 + 16;            // K / Q row stride in bytes (padded)
-    static constexpr int TS = kC * 2 + 16;             // Tb / P row stride in bytes (padded)
     static constexpr int KTS = kC + 4;                 // K^T row stride in bf16 (136 bytes)
     static constexpr int SFR = 0;                      // state fragments [8][64] x 16 B
     static constexpr int RFR = SFR + 8 * 64 * 16;      // R fragments [4][64] x 16 B
@@ -336,8 +347,7 @@ struct ScanLds {
     static constexpr int KT = DTF + 4 * 64 * 16;       // K^T [dk][t] bf16
     static constexpr int KR = KT + kDk * KTS * 2;      // K rows [64] x KS
     static constexpr int QR = KR + kC * KS;            // Q rows [64] x KS
-    static constexpr int TP = QR + kC * KS;            // Tb hi, Tb lo, P hi, P lo: [4][64] x TS
-    static constexpr int VR = TP + 4 * kC * TS;        // v rows [64] x 32 B (bf16, this row block)
+    static constexpr int VR = QR + kC * KS;            // v rows [64] x 32 B (bf16, this row block)
     static constexpr int GR = VR + kC * 32;            // gamma [64], rho [64] fp32
     static constexpr int AF = GR + 2 * kC * 4;         // active flags [64] u32 (0 or 1)
     static constexpr int BYTES = AF + kC * 4;
@@ -346,7 +356,6 @@ struct ScanLds {
 // Staging registers: this thread's pieces of the next chunk.
 struct ScanStage {
     u32x4 kq[4];          // K pieces 0, 1 then Q pieces 0, 1 (rows tid/16 and tid/16 + 32)
-    u32x4 tp[4];          // pieces tid + 512 j of the 32 KiB Tb/P block
     u32x4 gv;             // threads 0-31: gamma/rho piece; threads 32-159: v piece
     uint32_t m0, m1, mv;  // mask words of those rows (1 without a mask)
 };
@@ -365,9 +374,6 @@ __device__ __forceinline__ void stage_load(ScanStage& st, const void* q, const v
         const uint32_t m = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
         if (j == 0) st.m0 = m; else st.m1 = m;
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        st.tp[j] = *reinterpret_cast<const u32x4*>(wsb + (tid + 512u * j) * 16);
     st.mv = 1u;
     if (tid < 32u) {
         st.gv = *reinterpret_cast<const u32x4*>(wsb + PrefillWs::kGamma + tid * 16);
@@ -390,12 +396,6 @@ __device__ __forceinline__ void stage_store(const ScanStage& st, unsigned char* 
         *reinterpret_cast<u32x4*>(lds + ScanLds::KR + r * ScanLds::KS + c16 * 16) = act ? st.kq[j] : z;
         *reinterpret_cast<u32x4*>(lds + ScanLds::QR + r * ScanLds::KS + c16 * 16) = act ? st.kq[2 + j] : z;
         if (c16 == 0u) reinterpret_cast<uint32_t*>(lds + ScanLds::AF)[r] = act ? 1u : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t p = tid + 512u * j;                 // matrix p >> 9, row (p >> 3) & 63, piece p & 7
-        *reinterpret_cast<u32x4*>(lds + ScanLds::TP + (p >> 9) * (kC * ScanLds::TS) +
-                                  ((p >> 3) & 63u) * ScanLds::TS + (p & 7u) * 16) = st.tp[j];
     }
     if (tid < 32u) {
         *reinterpret_cast<u32x4*>(lds + ScanLds::GR + tid * 16) = st.gv;
@@ -451,13 +451,19 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     const unsigned char* wsn = ws + static_cast<size_t>(n) * nchunks * PrefillWs::kBytes;
     // The A-operand rows of this wave: K (K side) or Q (Q side) row 16 tt + lr.
     const unsigned char* arow = lds + (qside ? ScanLds::QR : ScanLds::KR) + (16u * tt + lr) * ScanLds::KS + lg * 8;
-    // Tb (K side) or P (Q side) row 16 tt + lr, hi and lo.
-    const unsigned char* mrow_hi = lds + ScanLds::TP + (qside ? 2 : 0) * (kC * ScanLds::TS) +
-                                   (16u * tt + lr) * ScanLds::TS + lg * 8;
-    const unsigned char* mrow_lo = mrow_hi + kC * ScanLds::TS;
+    // Tb (K side) or P (Q side) fragments of step tile tt: four 16-byte slots
+    // per lane (hi, lo), loaded from the workspace one chunk ahead.
+    const size_t mfrag = (qside ? PrefillWs::kP : PrefillWs::kTb) + (static_cast<size_t>(tt) * 4 * 64 + l) * 16;
+    auto mload = [&](u32x4 (&m)[4], uint32_t cc) {
+        const unsigned char* base = wsn + cc * static_cast<size_t>(PrefillWs::kBytes) + mfrag;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) m[ks] = *reinterpret_cast<const u32x4*>(base + ks * 64 * 16);
+    };
+    u32x4 mf[4], mf_next[4];
 
     ScanStage stage;
     stage_load(stage, q, k, v, mask, wsn, b, hv, hk, dv0, T, Hk, Hv, Dv, 0u, tid);
+    mload(mf_next, 0u);
 
     // One pending output tile per wave (Delta of this chunk on the K side, Y of
     // the previous chunk on the Q side), stored in the next iteration just
@@ -498,6 +504,8 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     for (uint32_t c = 0; c < nchunks; ++c) {
         const uint32_t t0 = c * kC;
         stage_store(stage, lds, T, t0, tid);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) mf[ks] = mf_next[ks];
         {
             u32x2 hi, lo;
             split4(acc, hi, lo);
@@ -525,9 +533,11 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         // The previous chunk's outputs and the next chunk's loads are issued
         // here, behind the first barrier, while the products above run.
         flush();
-        if (c + 1 < nchunks)
+        if (c + 1 < nchunks) {
             stage_load(stage, q, k, v, mask, wsn + (c + 1) * static_cast<size_t>(PrefillWs::kBytes), b, hv, hk,
                        dv0, T, Hk, Hv, Dv, (c + 1) * kC, tid);
+            mload(mf_next, c + 1);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] += x2[r];
         f32x4v gam;
@@ -559,8 +569,8 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         if (qside) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                ph_cur[ks] = lds8(mrow_hi + ks * 32);
-                pl_cur[ks] = lds8(mrow_lo + ks * 32);
+                ph_cur[ks] = lo2(mf[ks]);
+                pl_cur[ks] = hi2(mf[ks]);
             }
         }
         __syncthreads();
@@ -572,7 +582,7 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const u32x4 rr = rfr[ks][l];
-                const u32x2 th = lds8(mrow_hi + ks * 32), tl = lds8(mrow_lo + ks * 32);
+                const u32x2 th = lo2(mf[ks]), tl = hi2(mf[ks]);
                 D = mfma_bf16(th, lo2(rr), D);
                 D2 = mfma_bf16(th, hi2(rr), D2);
                 D2 = mfma_bf16(tl, lo2(rr), D2);
