@@ -562,6 +562,11 @@ def main():
                 "traffic": measured_traffic(dk["kernel"], args.workload, dk["name"]),
                 "kernel": dk["name"], "bytes_per_launch": dk["algorithmic_bytes"],
                 "us_per_launch": dk["us"]}
+    if args.workload == "chunk_prefill":
+        # the long record is a chain of dependent steps, not an HBM stream
+        roofline["note"] = ("latency-bound: 64 dependent chunk steps per 16-row block (gdn_prefill)"
+                            if step.chunked else
+                            "issue-bound: 4096 dependent steps per state row (gdn_record)")
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
