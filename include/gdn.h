@@ -212,6 +212,8 @@ int gqa_expand(const void* src, void* dst, uint32_t seq, uint32_t hg, uint32_t h
  * GDN_ERR_UNSUPPORTED_SHAPE for another dtype or head size, GDN_ERR_WORKSPACE
  * for a missing or short workspace.
  */
+/* Bytes of workspace gdn_prefill needs for these sizes: 33280 per (batch row, value head, chunk
+ * of 64 steps); UINT64_MAX if that does not fit in 64 bits. */
 uint64_t gdn_prefill_workspace_size(uint32_t B, uint32_t T, uint32_t Hv);
 
 int gdn_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,

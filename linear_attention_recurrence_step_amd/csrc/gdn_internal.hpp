@@ -76,7 +76,7 @@ struct PrefillArgs {
     int io;
     int map;      // 0 block, 1 tiled
 };
-size_t prefill_workspace_bytes(uint32_t B, uint32_t T, uint32_t Hv);
+uint64_t prefill_workspace_bytes(uint32_t B, uint32_t T, uint32_t Hv);   // UINT64_MAX if it overflows
 bool prefill_supported(uint32_t Dk, uint32_t Dv, int io);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

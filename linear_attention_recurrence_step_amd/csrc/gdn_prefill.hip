@@ -649,9 +649,12 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
 
 }  // namespace
 
-size_t prefill_workspace_bytes(uint32_t B, uint32_t T, uint32_t Hv) {
-    const size_t nchunks = (static_cast<size_t>(T) + kC - 1) / kC;
-    return static_cast<size_t>(B) * Hv * nchunks * PrefillWs::kBytes;
+uint64_t prefill_workspace_bytes(uint32_t B, uint32_t T, uint32_t Hv) {
+    const uint64_t nchunks = (static_cast<uint64_t>(T) + kC - 1) / kC;
+    uint64_t n = static_cast<uint64_t>(B) * Hv, bytes;    // B * Hv fits in 64 bits
+    if (__builtin_mul_overflow(n, nchunks, &n) || __builtin_mul_overflow(n, uint64_t(PrefillWs::kBytes), &bytes))
+        return ~uint64_t(0);
+    return bytes;
 }
 
 bool prefill_supported(uint32_t Dk, uint32_t Dv, int io) {

@@ -65,7 +65,8 @@ for c in cases:
 out.append({"id": "strerror", "rc": 0,
             "msg": json.dumps({str(s): lib.gdn_strerror(s).decode() for s in range(-11, 1)})})
 out.append({"id": "ws_size", "rc": 0,
-            "msg": json.dumps([lib.gdn_prefill_workspace_size(*x) for x in ([1, 4096, 32], [2, 65, 3], [1, 1, 1])])})
+            "msg": json.dumps([lib.gdn_prefill_workspace_size(*x) for x in ([1, 4096, 32], [2, 65, 3], [1, 1, 1],
+                                                                             [0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF])])})
 print(json.dumps(out))
 """
 
@@ -241,7 +242,8 @@ def test_strerror_covers_every_status(results):
 
 def test_prefill_workspace_size(results):
     """33280 bytes per (batch row, value head, chunk of 64 steps)."""
-    assert json.loads(results["ws_size"]["msg"]) == [32 * 64 * 33280, 2 * 3 * 2 * 33280, 33280]
+    assert json.loads(results["ws_size"]["msg"]) == [32 * 64 * 33280, 2 * 3 * 2 * 33280, 33280,
+                                                     2 ** 64 - 1]   # saturates instead of wrapping
 
 
 def test_python_binding_names_match_the_abi():
