@@ -331,23 +331,22 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
 // Waves 4-7 (the Q side) take step tile w-4: X_Q, and Y of the previous chunk
 // while the K side solves for Delta (Y is not on the state's dependency chain).
 //
-// A chunk's key and query rows, v of this row block, gamma and rho are copied
-// by all 512 threads with contiguous 16-byte loads into registers while the
-// previous chunk is computed, and into LDS at the top of the iteration; their
-// MFMA fragments are read from LDS.  Tb and P are already in fragment order in
-// the workspace and go straight to registers, one chunk ahead.  Key, query and
-// value rows of inactive steps (masked, or past T) are written as zeros.
+// Each lane loads its key or query fragments of the next chunk straight from
+// the input while the current chunk is computed: with the key index permuted
+// (kcol), the fragments of two key steps are one contiguous 16-byte piece of a
+// row.  v of this row block, gamma, rho and the step flags are copied into
+// registers the same way and into LDS at the top of the iteration.  Tb and P
+// are already in fragment order in the workspace and go straight to
+// registers, one chunk ahead.  Key, query and value rows of inactive steps
+// (masked, or past T) are replaced by zeros.
 struct ScanLds {
-    static constexpr int KS = kDk * 2 + 16;            // K / Q row stride in bytes (padded)
     static constexpr int KTS = kC + 4;                 // K^T row stride in bf16 (136 bytes)
     static constexpr int SFR = 0;                      // state fragments [8][64] x 16 B
     static constexpr int RFR = SFR + 8 * 64 * 16;      // R fragments [4][64] x 16 B
     static constexpr int DFR = RFR + 4 * 64 * 16;      // Delta fragments [2][4][64] x 16 B
     static constexpr int DTF = DFR + 8 * 64 * 16;      // rho o Delta fragments [4][64] x 16 B
     static constexpr int KT = DTF + 4 * 64 * 16;       // K^T [dk][t] bf16
-    static constexpr int KR = KT + kDk * KTS * 2;      // K rows [64] x KS
-    static constexpr int QR = KR + kC * KS;            // Q rows [64] x KS
-    static constexpr int VR = QR + kC * KS;            // v rows [64] x 32 B (bf16, this row block)
+    static constexpr int VR = KT + kDk * KTS * 2;      // v rows [64] x 32 B (bf16, this row block)
     static constexpr int GR = VR + kC * 32;            // gamma [64], rho [64] fp32
     static constexpr int AF = GR + 2 * kC * 4;         // active flags [64] u32 (0 or 1)
     static constexpr int BYTES = AF + kC * 4;
@@ -355,25 +354,14 @@ struct ScanLds {
 
 // Staging registers: this thread's pieces of the next chunk.
 struct ScanStage {
-    u32x4 kq[4];          // K pieces 0, 1 then Q pieces 0, 1 (rows tid/16 and tid/16 + 32)
     u32x4 gv;             // threads 0-31: gamma/rho piece; threads 32-159: v piece
-    uint32_t m0, m1, mv;  // mask words of those rows (1 without a mask)
+    uint32_t mv;          // threads 32-223: mask word of the v row / flag row (1 without a mask)
 };
 
 __device__ __forceinline__ void stage_load(ScanStage& st, const void* q, const void* k, const void* v,
                                            const uint32_t* mask, const unsigned char* wsb, uint32_t b,
                                            uint32_t hv, uint32_t hk, uint32_t dv0, uint32_t T, uint32_t Hk,
                                            uint32_t Hv, uint32_t Dv, uint32_t t0, uint32_t tid) {
-    const uint32_t row = tid >> 4, c16 = tid & 15u;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const uint32_t t = t0 + row + 32u * j, tc = t < T ? t : T - 1;
-        const size_t off = ((static_cast<size_t>(b) * T + tc) * Hk + hk) * (kDk * 2) + c16 * 16;
-        st.kq[j] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(k) + off);
-        st.kq[2 + j] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(q) + off);
-        const uint32_t m = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
-        if (j == 0) st.m0 = m; else st.m1 = m;
-    }
     st.mv = 1u;
     if (tid < 32u) {
         st.gv = *reinterpret_cast<const u32x4*>(wsb + PrefillWs::kGamma + tid * 16);
@@ -382,27 +370,24 @@ __device__ __forceinline__ void stage_load(ScanStage& st, const void* q, const v
         const size_t e = ((static_cast<size_t>(b) * T + tc) * Hv + hv) * Dv + dv0 + (p & 1u) * 8;
         st.gv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(v) + e);
         st.mv = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
+    } else if (tid < 224u) {
+        const uint32_t t = t0 + (tid - 160u), tc = t < T ? t : T - 1;
+        st.mv = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
     }
 }
 
 __device__ __forceinline__ void stage_store(const ScanStage& st, unsigned char* lds, uint32_t T, uint32_t t0,
                                             uint32_t tid) {
-    const uint32_t row = tid >> 4, c16 = tid & 15u;
     const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const uint32_t r = row + 32u * j;
-        const bool act = t0 + r < T && (j == 0 ? st.m0 : st.m1) > 0u;
-        *reinterpret_cast<u32x4*>(lds + ScanLds::KR + r * ScanLds::KS + c16 * 16) = act ? st.kq[j] : z;
-        *reinterpret_cast<u32x4*>(lds + ScanLds::QR + r * ScanLds::KS + c16 * 16) = act ? st.kq[2 + j] : z;
-        if (c16 == 0u) reinterpret_cast<uint32_t*>(lds + ScanLds::AF)[r] = act ? 1u : 0u;
-    }
     if (tid < 32u) {
         *reinterpret_cast<u32x4*>(lds + ScanLds::GR + tid * 16) = st.gv;
     } else if (tid < 160u) {
         const uint32_t p = tid - 32u, vr = p >> 1;
         const bool act = t0 + vr < T && st.mv > 0u;
         *reinterpret_cast<u32x4*>(lds + ScanLds::VR + vr * 32 + (p & 1u) * 16) = act ? st.gv : z;
+    } else if (tid < 224u) {
+        const uint32_t r = tid - 160u;
+        reinterpret_cast<uint32_t*>(lds + ScanLds::AF)[r] = t0 + r < T && st.mv > 0u ? 1u : 0u;
     }
 }
 
@@ -410,6 +395,17 @@ __device__ __forceinline__ u32x2 lo2(const u32x4& x) { return u32x2{x.x, x.y}; }
 __device__ __forceinline__ u32x2 hi2(const u32x4& x) { return u32x2{x.z, x.w}; }
 
 __device__ __forceinline__ u32x2 lds8(const unsigned char* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+// Key column of index i (0..15) of key step ks: the key steps are a
+// permutation of the key columns in which steps 2m and 2m+1 take, for each
+// group g of four indices, the eight consecutive columns 32m + 8g .. 32m + 8g + 7
+// (step 2m the first four, 2m+1 the last four).  Each lane's fragments of two
+// key steps are then one contiguous 16-byte piece of a key row, and each
+// lane's state piece stays contiguous too.  The contractions run over all
+// key columns either way.
+__device__ __forceinline__ uint32_t kcol(uint32_t ks, uint32_t i) {
+    return 32u * (ks >> 1) + 8u * (i >> 2) + 4u * (ks & 1u) + (i & 3u);
+}
 
 template <int IO>
 __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
@@ -439,8 +435,9 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     const uint32_t b = n / Hv, hv = n - b * Hv;
     const uint32_t hk = tiled ? hv % Hk : hv / group;
 
-    // This lane's 16-byte state piece: row dv0 + lr, columns 16w + 4lg .. +3.
-    const size_t srow = (static_cast<size_t>(n) * Dv + dv0 + lr) * kDk + 16u * w + 4u * lg;
+    // This lane's 16-byte state piece: row dv0 + lr, columns kcol(w, 4 lg) .. +3
+    // (the key index is permuted, see kcol).
+    const size_t srow = (static_cast<size_t>(n) * Dv + dv0 + lr) * kDk + kcol(w, 4u * lg);
     f32x4v acc;
     {
         const float4 s4 = *reinterpret_cast<const float4*>(state_in + srow);
@@ -449,8 +446,18 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
 
     void* out = qside ? y : delta_log;                  // what this wave writes (delta_log may be NULL)
     const unsigned char* wsn = ws + static_cast<size_t>(n) * nchunks * PrefillWs::kBytes;
-    // The A-operand rows of this wave: K (K side) or Q (Q side) row 16 tt + lr.
-    const unsigned char* arow = lds + (qside ? ScanLds::QR : ScanLds::KR) + (16u * tt + lr) * ScanLds::KS + lg * 8;
+    // This lane's row of the A operand of X (K on the K side, Q on the Q side):
+    // step 16 tt + lr, key columns 32 m + 8 lg .. +7 for m = 0..3, i.e. the
+    // fragments of key steps 2m and 2m+1, read straight from the input.
+    const char* arow = static_cast<const char*>(qside ? q : k) + (static_cast<size_t>(b) * T * Hk + hk) * (kDk * 2) +
+                       lg * 16;
+    const size_t arow_step = static_cast<size_t>(Hk) * kDk * 2;     // bytes per step
+    auto aload = [&](u32x4 (&a)[4], uint32_t t0n) {
+        const uint32_t t = t0n + 16u * tt + lr, tc = t < T ? t : T - 1;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[m] = *reinterpret_cast<const u32x4*>(arow + tc * arow_step + m * 64);
+    };
+    u32x4 ak[4], ak_next[4];
     // Tb (K side) or P (Q side) fragments of step tile tt: four 16-byte slots
     // per lane (hi, lo), loaded from the workspace one chunk ahead.
     const size_t mfrag = (qside ? PrefillWs::kP : PrefillWs::kTb) + (static_cast<size_t>(tt) * 4 * 64 + l) * 16;
@@ -464,6 +471,7 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     ScanStage stage;
     stage_load(stage, q, k, v, mask, wsn, b, hv, hk, dv0, T, Hk, Hv, Dv, 0u, tid);
     mload(mf_next, 0u);
+    aload(ak_next, 0u);
 
     // One pending output tile per wave (Delta of this chunk on the K side, Y of
     // the previous chunk on the Q side), stored in the next iteration just
@@ -505,7 +513,10 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         const uint32_t t0 = c * kC;
         stage_store(stage, lds, T, t0, tid);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) mf[ks] = mf_next[ks];
+        for (int ks = 0; ks < 4; ++ks) {
+            mf[ks] = mf_next[ks];
+            ak[ks] = ak_next[ks];
+        }
         {
             u32x2 hi, lo;
             split4(acc, hi, lo);
@@ -519,10 +530,19 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
             act = f.x | (f.y << 1) | (f.z << 2) | (f.w << 3);
         }
 
-        // X = (K or Q) S0^T for step tile tt (hi and lo parts apart).
+        // X = (K or Q) S0^T for step tile tt (hi and lo parts apart).  The row
+        // of an inactive step is zero (a select, so a NaN there cannot enter).
         u32x2 af[kDk / 16];
+        {
+            const bool ra = reinterpret_cast<const uint32_t*>(lds + ScanLds::AF)[16u * tt + lr] != 0u;
+            const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int ks = 0; ks < kDk / 16; ++ks) af[ks] = lds8(arow + ks * 32);
+            for (int m = 0; m < 4; ++m) {
+                const u32x4 a = ra ? ak[m] : z;
+                af[2 * m] = lo2(a);
+                af[2 * m + 1] = hi2(a);
+            }
+        }
         f32x4v x = {0.f, 0.f, 0.f, 0.f}, x2 = x;
 #pragma unroll
         for (int ks = 0; ks < kDk / 16; ++ks) {
@@ -537,6 +557,7 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
             stage_load(stage, q, k, v, mask, wsn + (c + 1) * static_cast<size_t>(PrefillWs::kBytes), b, hv, hk,
                        dv0, T, Hk, Hv, Dv, (c + 1) * kC, tid);
             mload(mf_next, c + 1);
+            aload(ak_next, (c + 1) * kC);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] += x2[r];
@@ -549,7 +570,7 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
             // This wave's 16 key rows, transposed into K^T [dk][t] for the state update.
 #pragma unroll
             for (int ks = 0; ks < kDk / 16; ++ks) {
-                const uint32_t dk = 16u * ks + 4u * lg, t = 16u * tt + lr;
+                const uint32_t dk = kcol(ks, 4u * lg), t = 16u * tt + lr;
                 kt[(dk + 0) * ScanLds::KTS + t] = static_cast<uint16_t>(af[ks].x);
                 kt[(dk + 1) * ScanLds::KTS + t] = static_cast<uint16_t>(af[ks].x >> 16);
                 kt[(dk + 2) * ScanLds::KTS + t] = static_cast<uint16_t>(af[ks].y);
@@ -626,7 +647,7 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const u32x4 dd = dtf[ks][l];
-            const uint32_t dk = 16u * w + lr;
+            const uint32_t dk = kcol(w, lr);
             const u32x2 a = *reinterpret_cast<const u32x2*>(&kt[dk * ScanLds::KTS + 16 * ks + 4 * lg]);
             acc = mfma_bf16(a, lo2(dd), acc);
             lo_acc = mfma_bf16(a, hi2(dd), lo_acc);
