@@ -362,18 +362,21 @@ __device__ __forceinline__ void stage_load(ScanStage& st, const void* q, const v
                                            const uint32_t* mask, const unsigned char* wsb, uint32_t b,
                                            uint32_t hv, uint32_t hk, uint32_t dv0, uint32_t T, uint32_t Hk,
                                            uint32_t Hv, uint32_t Dv, uint32_t t0, uint32_t tid) {
-    st.mv = 1u;
-    if (tid < 32u) {
-        st.gv = *reinterpret_cast<const u32x4*>(wsb + PrefillWs::kGamma + tid * 16);
-    } else if (tid < 160u) {
-        const uint32_t p = tid - 32u, vr = p >> 1, t = t0 + vr, tc = t < T ? t : T - 1;
-        const size_t e = ((static_cast<size_t>(b) * T + tc) * Hv + hv) * Dv + dv0 + (p & 1u) * 8;
-        st.gv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(v) + e);
-        st.mv = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
-    } else if (tid < 224u) {
-        const uint32_t t = t0 + (tid - 160u), tc = t < T ? t : T - 1;
-        st.mv = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
-    }
+    // Every thread issues the same two loads (threads with nothing to fetch
+    // read a valid address and drop the value), so that the number of memory
+    // operations in flight does not depend on the lane and the waits for them
+    // can be placed exactly where the data is used.
+    const unsigned char* gsrc = wsb + PrefillWs::kGamma + (tid & 31u) * 16;
+    const uint32_t p = tid - 32u, vr = p >> 1;
+    const uint32_t row = tid < 160u ? vr : tid - 160u;              // step row of the mask word
+    const uint32_t t = t0 + (tid < 224u ? row : 0u), tc = t < T ? t : T - 1;
+    const size_t e = ((static_cast<size_t>(b) * T + tc) * Hv + hv) * Dv + dv0 + (p & 1u) * 8;
+    const bool vthread = tid >= 32u && tid < 160u;
+    const unsigned char* src = vthread ? reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(v) + e) : gsrc;
+    st.gv = *reinterpret_cast<const u32x4*>(src);
+    const uint32_t* mp = mask ? mask + static_cast<size_t>(b) * T + tc : reinterpret_cast<const uint32_t*>(gsrc);
+    const uint32_t mw = *mp;
+    st.mv = mask ? mw : 1u;
 }
 
 __device__ __forceinline__ void stage_store(const ScanStage& st, unsigned char* lds, uint32_t T, uint32_t t0,
@@ -457,7 +460,6 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
 #pragma unroll
         for (int m = 0; m < 4; ++m) a[m] = *reinterpret_cast<const u32x4*>(arow + tc * arow_step + m * 64);
     };
-    u32x4 ak[4], ak_next[4];
     // Tb (K side) or P (Q side) fragments of step tile tt: four 16-byte slots
     // per lane (hi, lo), loaded from the workspace one chunk ahead.
     const size_t mfrag = (qside ? PrefillWs::kP : PrefillWs::kTb) + (static_cast<size_t>(tt) * 4 * 64 + l) * 16;
@@ -466,13 +468,13 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) m[ks] = *reinterpret_cast<const u32x4*>(base + ks * 64 * 16);
     };
-    u32x4 mf[4], mf_next[4];
 
     ScanStage stage;
     stage_load(stage, q, k, v, mask, wsn, b, hv, hk, dv0, T, Hk, Hv, Dv, 0u, tid);
-    mload(mf_next, 0u);
-    aload(ak_next, 0u);
-
+    u32x4 mfa[4], mfb[4], aka[4], akb[4];
+    mload(mfa, 0u);
+    aload(aka, 0u);
+    aload(akb, (nchunks > 1u ? 1u : 0u) * kC);
     // One pending output tile per wave (Delta of this chunk on the K side, Y of
     // the previous chunk on the Q side), stored in the next iteration just
     // before its loads are issued.
@@ -509,14 +511,15 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         for (int r = 0; r < 4; ++r) pend[r] = Y[r] + Y2[r];
     };
 
-    for (uint32_t c = 0; c < nchunks; ++c) {
+    // One chunk.  mf holds its Tb or P fragments and mf_nxt receives the next
+    // chunk's; ak holds its key or query fragments and then receives those of
+    // the chunk after next.  The loop below runs two chunks per iteration with
+    // the buffers swapped, so that no register still being loaded is copied
+    // (a copy would wait for the load).
+    auto chunk = [&](uint32_t c, const u32x4 (&mf)[4], u32x4 (&mf_nxt)[4], u32x4 (&ak)[4])
+                     __attribute__((always_inline)) {
         const uint32_t t0 = c * kC;
         stage_store(stage, lds, T, t0, tid);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            mf[ks] = mf_next[ks];
-            ak[ks] = ak_next[ks];
-        }
         {
             u32x2 hi, lo;
             split4(acc, hi, lo);
@@ -553,11 +556,14 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         // The previous chunk's outputs and the next chunk's loads are issued
         // here, behind the first barrier, while the products above run.
         flush();
-        if (c + 1 < nchunks) {
-            stage_load(stage, q, k, v, mask, wsn + (c + 1) * static_cast<size_t>(PrefillWs::kBytes), b, hv, hk,
-                       dv0, T, Hk, Hv, Dv, (c + 1) * kC, tid);
-            mload(mf_next, c + 1);
-            aload(ak_next, (c + 1) * kC);
+        // (Past the last chunk the loads repeat it and go unused, so that
+        // every iteration issues the same memory operations.)
+        {
+            const uint32_t c1 = c + 1 < nchunks ? c + 1 : c, c2 = c + 2 < nchunks ? c + 2 : c1;
+            stage_load(stage, q, k, v, mask, wsn + c1 * static_cast<size_t>(PrefillWs::kBytes), b, hv, hk, dv0, T,
+                       Hk, Hv, Dv, c1 * kC, tid);
+            mload(mf_nxt, c1);
+            aload(ak, c2 * kC);                         // ak is free again: its selects are done
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] += x2[r];
@@ -654,7 +660,13 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] += lo_acc[r];
+    };
+    uint32_t c = 0;
+    for (; c + 1 < nchunks; c += 2) {
+        chunk(c, mfa, mfb, aka);
+        chunk(c + 1, mfb, mfa, akb);
     }
+    if (c < nchunks) chunk(c, mfa, mfb, aka);          // an odd chunk count's last chunk
 
     flush();
     if (qside) {
