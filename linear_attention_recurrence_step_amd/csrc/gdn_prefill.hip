@@ -184,7 +184,11 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
     // tid & 15 of rows (tid >> 4) + 16 j.  Steps past T read step T-1; rows of
     // inactive steps are stored as zeros (a select, so a NaN there cannot
     // enter a product).
+    // Mask words are loaded whether or not there is a mask (from k, whose
+    // B*T*Hk*Dk/2 words cover every index, when there is none) and then
+    // selected, so the loads are not serialised behind branches.
     {
+        const uint32_t* mwords = mask ? mask : static_cast<const uint32_t*>(k);
         u32x4 kp[4], qp[4];
         uint32_t mw[4];
         const uint32_t row = tid >> 4, c16 = tid & 15u;
@@ -194,14 +198,15 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
             const size_t off = ((static_cast<size_t>(b) * T + tc) * Hk + hk) * (kDk * 2) + c16 * 16;
             kp[j] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(k) + off);
             qp[j] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(q) + off);
-            mw[j] = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
+            const uint32_t m = mwords[static_cast<size_t>(b) * T + tc];
+            mw[j] = mask ? m : 1u;
         }
         if (tid < kC) {
             const uint32_t t = t0 + tid, tc = t < T ? t : T - 1;
             const size_t i = (static_cast<size_t>(b) * T + tc) * Hv + hv;
             const float gl = io_load1<IO>(g, i), bl = io_load1<IO>(beta, i);
-            const uint32_t m = mask ? mask[static_cast<size_t>(b) * T + tc] : 1u;
-            const bool act = t < T && m > 0u;
+            const uint32_t mword = mwords[static_cast<size_t>(b) * T + tc];
+            const bool act = t < T && (mask ? mword : 1u) > 0u;
             gs[tid] = act ? gl : 1.0f;
             bs[tid] = act ? bl : 0.0f;
         }
