@@ -363,27 +363,6 @@ struct ScanStage {
     uint32_t mv;          // threads 32-223: mask word of the v row / flag row (1 without a mask)
 };
 
-__device__ __forceinline__ void stage_load(ScanStage& st, const void* q, const void* k, const void* v,
-                                           const uint32_t* mask, const unsigned char* wsb, uint32_t b,
-                                           uint32_t hv, uint32_t hk, uint32_t dv0, uint32_t T, uint32_t Hk,
-                                           uint32_t Hv, uint32_t Dv, uint32_t t0, uint32_t tid) {
-    // Every thread issues the same two loads (threads with nothing to fetch
-    // read a valid address and drop the value), so that the number of memory
-    // operations in flight does not depend on the lane and the waits for them
-    // can be placed exactly where the data is used.
-    const unsigned char* gsrc = wsb + PrefillWs::kGamma + (tid & 31u) * 16;
-    const uint32_t p = tid - 32u, vr = p >> 1;
-    const uint32_t row = tid < 160u ? vr : tid - 160u;              // step row of the mask word
-    const uint32_t t = t0 + (tid < 224u ? row : 0u), tc = t < T ? t : T - 1;
-    const size_t e = ((static_cast<size_t>(b) * T + tc) * Hv + hv) * Dv + dv0 + (p & 1u) * 8;
-    const bool vthread = tid >= 32u && tid < 160u;
-    const unsigned char* src = vthread ? reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(v) + e) : gsrc;
-    st.gv = *reinterpret_cast<const u32x4*>(src);
-    const uint32_t* mp = mask ? mask + static_cast<size_t>(b) * T + tc : reinterpret_cast<const uint32_t*>(gsrc);
-    const uint32_t mw = *mp;
-    st.mv = mask ? mw : 1u;
-}
-
 __device__ __forceinline__ void stage_store(const ScanStage& st, unsigned char* lds, uint32_t T, uint32_t t0,
                                             uint32_t tid) {
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -432,7 +411,9 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     uint16_t* kt = reinterpret_cast<uint16_t*>(lds + ScanLds::KT);
     const float* gr = reinterpret_cast<const float*>(lds + ScanLds::GR);
 
-    const uint32_t tid = threadIdx.x, l = tid & 63u, w = tid >> 6;
+    // The wave index is read from lane 0 so that the compiler treats it, and
+    // what derives from it (the side, the step tile), as wave-uniform.
+    const uint32_t tid = threadIdx.x, l = tid & 63u, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t lr = l & 15u, lg = l >> 4;
     const uint32_t tt = w & 3u;                         // step tile
     const bool qside = w >= 4u;
@@ -460,10 +441,12 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     const char* arow = static_cast<const char*>(qside ? q : k) + (static_cast<size_t>(b) * T * Hk + hk) * (kDk * 2) +
                        lg * 16;
     const size_t arow_step = static_cast<size_t>(Hk) * kDk * 2;     // bytes per step
+    const char* a_lane = arow + (16u * tt + lr) * arow_step;
+    const char* a_last = arow + static_cast<size_t>(T - 1) * arow_step;
     auto aload = [&](u32x4 (&a)[4], uint32_t t0n) {
-        const uint32_t t = t0n + 16u * tt + lr, tc = t < T ? t : T - 1;
+        const char* src = t0n + 16u * tt + lr < T ? a_lane + t0n * arow_step : a_last;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) a[m] = *reinterpret_cast<const u32x4*>(arow + tc * arow_step + m * 64);
+        for (int m = 0; m < 4; ++m) a[m] = *reinterpret_cast<const u32x4*>(src + m * 64);
     };
     // Tb (K side) or P (Q side) fragments of step tile tt: four 16-byte slots
     // per lane (hi, lo), loaded from the workspace one chunk ahead.
@@ -474,8 +457,33 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         for (int ks = 0; ks < 4; ++ks) m[ks] = *reinterpret_cast<const u32x4*>(base + ks * 64 * 16);
     };
 
+    // Staging loads.  Every thread issues the same two loads (threads with
+    // nothing to fetch read a valid address and drop the value), so that the
+    // number of memory operations in flight does not depend on the lane and
+    // the waits for them can be placed exactly where the data is used.
+    // Per-lane base pointers are formed once; a chunk adds a wave-uniform
+    // offset, and a row past T reads row T-1 instead.  Without a mask the
+    // mask word is read from k (B*T*Hk*Dk/2 words cover every index).
+    const size_t rs = static_cast<size_t>(Hv) * Dv;                 // elements per step of v, y, delta
+    const bool vthread = tid >= 32u && tid < 160u;
+    const uint32_t vhalf = (tid - 32u) & 1u;
+    const uint32_t mrow = vthread ? (tid - 32u) >> 1 : (tid >= 160u && tid < 224u ? tid - 160u : 0u);
+    const size_t vhead = (static_cast<size_t>(b) * T * Hv + hv) * Dv + dv0 + vhalf * 8;
+    const uint16_t* v_lane = static_cast<const uint16_t*>(v) + vhead + mrow * rs;
+    const uint16_t* v_last = static_cast<const uint16_t*>(v) + vhead + static_cast<size_t>(T - 1) * rs;
+    const uint32_t* mwords = (mask ? mask : static_cast<const uint32_t*>(k)) + static_cast<size_t>(b) * T;
+    const unsigned char* g_lane = wsn + PrefillWs::kGamma + (tid & 31u) * 16;
+    auto sload = [&](ScanStage& st, uint32_t cc) {
+        const uint32_t t0n = cc * kC;
+        const bool in = t0n + mrow < T;
+        const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(in ? v_lane + t0n * rs : v_last);
+        const unsigned char* src = vthread ? vsrc : g_lane + cc * static_cast<size_t>(PrefillWs::kBytes);
+        st.gv = *reinterpret_cast<const u32x4*>(src);
+        const uint32_t mw = mwords[in ? t0n + mrow : T - 1];
+        st.mv = mask ? mw : 1u;
+    };
     ScanStage stage;
-    stage_load(stage, q, k, v, mask, wsn, b, hv, hk, dv0, T, Hk, Hv, Dv, 0u, tid);
+    sload(stage, 0u);
     u32x4 mfa[4], mfb[4], aka[4], akb[4];
     mload(mfa, 0u);
     aload(aka, 0u);
@@ -485,16 +493,17 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     // before its loads are issued.
     f32x4v pend = {0.f, 0.f, 0.f, 0.f};
     uint32_t pend_act = 0u, pend_t0 = 0u;
+    // This lane's output element of step 16 tt + 4 lg of a chunk starting at
+    // step 0; a chunk adds a wave-uniform offset, row r adds r steps.
+    uint16_t* const out_lane = out == nullptr ? nullptr
+        : static_cast<uint16_t*>(out) + (static_cast<size_t>(b) * T * Hv + hv) * Dv + dv0 + lr +
+              (16u * tt + 4u * lg) * rs;
     auto flush = [&]() {
         if (out == nullptr) return;
+        uint16_t* const o = out_lane + pend_t0 * rs;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if (pend_act & (1u << r)) {
-                const size_t i = ((static_cast<size_t>(b) * T + pend_t0 + 16u * tt + 4u * lg + r) * Hv + hv) * Dv +
-                                 dv0 + lr;
-                static_cast<uint16_t*>(out)[i] = static_cast<uint16_t>(f32_to_bf16_bits(pend[r]));
-            }
-        }
+        for (int r = 0; r < 4; ++r)
+            if (pend_act & (1u << r)) o[r * rs] = static_cast<uint16_t>(f32_to_bf16_bits(pend[r]));
         pend_act = 0u;
     };
     // Q side: what Y of a chunk needs one iteration later.
@@ -565,8 +574,7 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         // every iteration issues the same memory operations.)
         {
             const uint32_t c1 = c + 1 < nchunks ? c + 1 : c, c2 = c + 2 < nchunks ? c + 2 : c1;
-            stage_load(stage, q, k, v, mask, wsn + c1 * static_cast<size_t>(PrefillWs::kBytes), b, hv, hk, dv0, T,
-                       Hk, Hv, Dv, c1 * kC, tid);
+            sload(stage, c1);
             mload(mf_nxt, c1);
             aload(ak, c2 * kC);                         // ak is free again: its selects are done
         }
