@@ -57,6 +57,16 @@ __device__ __forceinline__ f32x4v mfma_bf16(u32x2 a, u32x2 b, f32x4v acc) {
                                                      __builtin_bit_cast(i16x4, b), acc, 0, 0, 0);
 }
 
+// D += A B on gfx950's double-depth bf16 tile: 16 x 16 x 32, eight bf16 of
+// A (row l % 16) and of B (column l % 16) per lane, over the same eight
+// positions of the 32-deep sum in both, so that any operands whose lanes
+// pair the same summation index give the full product.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4v mfma_bf16_k32(u32x4 a, u32x4 b, f32x4v acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
+                                                   0, 0, 0);
+}
+
 // Two floats rounded to nearest-even bf16 and packed (v_cvt_pk_bf16_f32),
 // the first in the low half.  Used only for the internal hi/lo operands.
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
@@ -346,7 +356,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
 // (masked, or past T) are replaced by zeros.
 struct ScanLds {
     static constexpr int KTS = kC + 4;                 // K^T row stride in bf16 (136 bytes)
-    static constexpr int SFR = 0;                      // state fragments [8][64] x 16 B
+    static constexpr int SFR = 0;                      // state fragments [8][64] x 16 B (hi [4], lo [4])
     static constexpr int RFR = SFR + 8 * 64 * 16;      // R fragments [4][64] x 16 B
     static constexpr int DFR = RFR + 4 * 64 * 16;      // Delta fragments [2][4][64] x 16 B
     static constexpr int DTF = DFR + 8 * 64 * 16;      // rho o Delta fragments [4][64] x 16 B
@@ -537,7 +547,11 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         {
             u32x2 hi, lo;
             split4(acc, hi, lo);
-            sfr[w][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
+            // hi parts of key steps 2m and 2m+1 side by side in slot m, lo
+            // parts in slot 4 + m: one 16-byte read is then a B operand of
+            // the 32-deep product over key columns 32m .. 32m + 31.
+            *reinterpret_cast<u32x2*>(reinterpret_cast<unsigned char*>(&sfr[w >> 1][l]) + (w & 1u) * 8) = hi;
+            *reinterpret_cast<u32x2*>(reinterpret_cast<unsigned char*>(&sfr[4 + (w >> 1)][l]) + (w & 1u) * 8) = lo;
         }
         __syncthreads();
 
@@ -549,23 +563,20 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
 
         // X = (K or Q) S0^T for step tile tt (hi and lo parts apart).  The row
         // of an inactive step is zero (a select, so a NaN there cannot enter).
-        u32x2 af[kDk / 16];
+        // Lane (lr, lg) holds key columns 32m + 8lg .. +7 of its row for each
+        // m: the A operand of the 32-deep product over columns 32m .. 32m + 31.
+        u32x4 a8[4];
         {
             const bool ra = reinterpret_cast<const uint32_t*>(lds + ScanLds::AF)[16u * tt + lr] != 0u;
             const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const u32x4 a = ra ? ak[m] : z;
-                af[2 * m] = lo2(a);
-                af[2 * m + 1] = hi2(a);
-            }
+            for (int m = 0; m < 4; ++m) a8[m] = ra ? ak[m] : z;
         }
         f32x4v x = {0.f, 0.f, 0.f, 0.f}, x2 = x;
 #pragma unroll
-        for (int ks = 0; ks < kDk / 16; ++ks) {
-            const u32x4 sv = sfr[ks][l];
-            x = mfma_bf16(af[ks], lo2(sv), x);
-            x2 = mfma_bf16(af[ks], hi2(sv), x2);
+        for (int m = 0; m < 4; ++m) {
+            x = mfma_bf16_k32(a8[m], sfr[m][l], x);
+            x2 = mfma_bf16_k32(a8[m], sfr[4 + m][l], x2);
         }
         // The previous chunk's outputs and the next chunk's loads are issued
         // here, behind the first barrier, while the products above run.
@@ -590,10 +601,11 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
 #pragma unroll
             for (int ks = 0; ks < kDk / 16; ++ks) {
                 const uint32_t dk = kcol(ks, 4u * lg), t = 16u * tt + lr;
-                kt[(dk + 0) * ScanLds::KTS + t] = static_cast<uint16_t>(af[ks].x);
-                kt[(dk + 1) * ScanLds::KTS + t] = static_cast<uint16_t>(af[ks].x >> 16);
-                kt[(dk + 2) * ScanLds::KTS + t] = static_cast<uint16_t>(af[ks].y);
-                kt[(dk + 3) * ScanLds::KTS + t] = static_cast<uint16_t>(af[ks].y >> 16);
+                const u32x2 a = (ks & 1) ? hi2(a8[ks >> 1]) : lo2(a8[ks >> 1]);
+                kt[(dk + 0) * ScanLds::KTS + t] = static_cast<uint16_t>(a.x);
+                kt[(dk + 1) * ScanLds::KTS + t] = static_cast<uint16_t>(a.x >> 16);
+                kt[(dk + 2) * ScanLds::KTS + t] = static_cast<uint16_t>(a.y);
+                kt[(dk + 3) * ScanLds::KTS + t] = static_cast<uint16_t>(a.y >> 16);
             }
             const uint16_t* vr = reinterpret_cast<const uint16_t*>(lds + ScanLds::VR);
             f32x4v R;
