@@ -92,10 +92,11 @@ __device__ __forceinline__ void split1(float x, uint16_t& hi, uint16_t& lo) {
 }  // namespace
 
 // Per (b, hv, chunk) block of the workspace, written by prep and read by scan.
-// Tb and P are stored in MFMA A-operand fragment order: the 16-byte slot
-// ((tt * 4 + ks) * 64 + l) holds, for lane l = 16 lg + lr, the hi and then the
-// lo bf16 parts of M[16 tt + lr][16 ks + 4 lg .. +3], so a wave reads one step
-// tile's four key-step fragments with four fully coalesced 1 KiB loads.
+// Tb and P are stored in the A-operand order of the 16 x 16 x 32 matrix
+// instruction: the 32-byte slot ((tt * 2 + kb) * 64 + l) holds, for lane
+// l = 16 lg + lr, the hi and then the lo bf16 parts of
+// M[16 tt + lr][32 kb + 8 lg .. +7], so a wave reads one step tile's
+// operands with four fully coalesced 1 KiB loads.
 struct PrefillWs {
     static constexpr int kMat = kC * kC * 2;             // one 64 x 64 bf16 matrix
     static constexpr int kTb = 0, kP = 2 * kMat;         // Tb, P: hi/lo fragment slots, 16 KiB each
@@ -107,9 +108,10 @@ struct PrefillWs {
 namespace {
 
 // Byte offset of element [t][s] of a 64 x 64 matrix in the fragment order of
-// PrefillWs (its hi part; the lo part is 8 bytes further).
+// PrefillWs (its hi part; the lo part is kFragLo bytes further).
+constexpr uint32_t kFragLo = 16;
 __device__ __forceinline__ uint32_t frag_offset(uint32_t t, uint32_t s) {
-    return (((t >> 4) * 4u + (s >> 4)) * 64u + 16u * ((s & 15u) >> 2) + (t & 15u)) * 16u + (s & 3u) * 2u;
+    return (((t >> 4) * 2u + (s >> 5)) * 64u + 16u * ((s & 31u) >> 3) + (t & 15u)) * 32u + (s & 7u) * 2u;
 }
 
 // Row I of the forward substitution (I + A) T = identity, then the rows after
@@ -300,7 +302,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
             split1(s <= t ? m * H[st][r] : 0.0f, hi, lo);
             const uint32_t o = frag_offset(static_cast<uint32_t>(t), static_cast<uint32_t>(s));
             *reinterpret_cast<uint16_t*>(op + o) = hi;
-            *reinterpret_cast<uint16_t*>(op + o + 8) = lo;
+            *reinterpret_cast<uint16_t*>(op + o + kFragLo) = lo;
         }
     }
     __syncthreads();
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
             split1(mine[m] * bc, hi, lo);
             const uint32_t o = frag_offset(static_cast<uint32_t>(i), static_cast<uint32_t>(col));
             *reinterpret_cast<uint16_t*>(otb + o) = hi;
-            *reinterpret_cast<uint16_t*>(otb + o + 8) = lo;
+            *reinterpret_cast<uint16_t*>(otb + o + kFragLo) = lo;
         }
     }
     __syncthreads();
@@ -355,11 +357,12 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
 // registers, one chunk ahead.  Key, query and value rows of inactive steps
 // (masked, or past T) are replaced by zeros.
 struct ScanLds {
-    static constexpr int KTS = kC + 4;                 // K^T row stride in bf16 (136 bytes)
+    static constexpr int KTS = kC + 8;                 // K^T row stride in bf16 (144 bytes, 16-byte aligned)
     static constexpr int SFR = 0;                      // state fragments [8][64] x 16 B (hi [4], lo [4])
-    static constexpr int RFR = SFR + 8 * 64 * 16;      // R fragments [4][64] x 16 B
-    static constexpr int DFR = RFR + 4 * 64 * 16;      // Delta fragments [2][4][64] x 16 B
-    static constexpr int DTF = DFR + 8 * 64 * 16;      // rho o Delta fragments [4][64] x 16 B
+    static constexpr int BOP = 4 * 64 * 16;            // one step-indexed B operand (see bop_store)
+    static constexpr int RFR = SFR + 8 * 64 * 16;      // R
+    static constexpr int DFR = RFR + BOP;              // Delta, two chunks
+    static constexpr int DTF = DFR + 2 * BOP;          // rho o Delta
     static constexpr int KT = DTF + 4 * 64 * 16;       // K^T [dk][t] bf16
     static constexpr int VR = KT + kDk * KTS * 2;      // v rows [64] x 32 B (bf16, this row block)
     static constexpr int GR = VR + kC * 32;            // gamma [64], rho [64] fp32
@@ -404,6 +407,24 @@ __device__ __forceinline__ uint32_t kcol(uint32_t ks, uint32_t i) {
     return 32u * (ks >> 1) + 8u * (i >> 2) + 4u * (ks & 1u) + (i & 3u);
 }
 
+// A [64 steps][16 columns] operand split into hi and lo bf16 parts, written
+// by the wave that holds step tile tt as an accumulator (lane 16 lg + lr:
+// rows 16 tt + 4 lg .. +3 of column lr) and read as the B operand of 32-deep
+// products over steps: hi of block kb at 16-byte slot kb * 64 + l, lo 2 KiB
+// further, lane 16 lg' + lr holding rows 32 kb + 8 lg' .. +7 of column lr.
+__device__ __forceinline__ void bop_store(unsigned char* base, uint32_t tt, uint32_t lr, uint32_t lg, u32x2 hi,
+                                          u32x2 lo) {
+    const uint32_t o = ((tt >> 1) * 64u + 16u * (2u * (tt & 1u) + (lg >> 1)) + lr) * 16u + (lg & 1u) * 8u;
+    *reinterpret_cast<u32x2*>(base + o) = hi;
+    *reinterpret_cast<u32x2*>(base + 2048 + o) = lo;
+}
+__device__ __forceinline__ u32x4 bop_hi(const unsigned char* base, uint32_t kb, uint32_t l) {
+    return *reinterpret_cast<const u32x4*>(base + (kb * 64u + l) * 16u);
+}
+__device__ __forceinline__ u32x4 bop_lo(const unsigned char* base, uint32_t kb, uint32_t l) {
+    return *reinterpret_cast<const u32x4*>(base + 2048 + (kb * 64u + l) * 16u);
+}
+
 template <int IO>
 __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
@@ -415,9 +436,9 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     static_assert(IO == kBF16, "the chunked prefill takes bf16 I/O");
     extern __shared__ __align__(16) unsigned char lds[];
     u32x4 (*sfr)[64] = reinterpret_cast<u32x4 (*)[64]>(lds + ScanLds::SFR);
-    u32x4 (*rfr)[64] = reinterpret_cast<u32x4 (*)[64]>(lds + ScanLds::RFR);
-    u32x4 (*dfr)[4][64] = reinterpret_cast<u32x4 (*)[4][64]>(lds + ScanLds::DFR);
-    u32x4 (*dtf)[64] = reinterpret_cast<u32x4 (*)[64]>(lds + ScanLds::DTF);
+    unsigned char* const rfr = lds + ScanLds::RFR;
+    unsigned char* const dfr = lds + ScanLds::DFR;      // chunk c at dfr + (c & 1) * BOP
+    unsigned char* const dtf = lds + ScanLds::DTF;
     uint16_t* kt = reinterpret_cast<uint16_t*>(lds + ScanLds::KT);
     const float* gr = reinterpret_cast<const float*>(lds + ScanLds::GR);
 
@@ -460,11 +481,15 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     };
     // Tb (K side) or P (Q side) fragments of step tile tt: four 16-byte slots
     // per lane (hi, lo), loaded from the workspace one chunk ahead.
-    const size_t mfrag = (qside ? PrefillWs::kP : PrefillWs::kTb) + (static_cast<size_t>(tt) * 4 * 64 + l) * 16;
+    // m[2 kb] = hi, m[2 kb + 1] = lo part of step block kb.
+    const size_t mfrag = (qside ? PrefillWs::kP : PrefillWs::kTb) + (static_cast<size_t>(tt) * 2 * 64 + l) * 32;
     auto mload = [&](u32x4 (&m)[4], uint32_t cc) {
         const unsigned char* base = wsn + cc * static_cast<size_t>(PrefillWs::kBytes) + mfrag;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) m[ks] = *reinterpret_cast<const u32x4*>(base + ks * 64 * 16);
+        for (int kb = 0; kb < 2; ++kb) {
+            m[2 * kb] = *reinterpret_cast<const u32x4*>(base + kb * 64 * 32);
+            m[2 * kb + 1] = *reinterpret_cast<const u32x4*>(base + kb * 64 * 32 + kFragLo);
+        }
     };
 
     // Staging loads.  Every thread issues the same two loads (threads with
@@ -518,18 +543,18 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     };
     // Q side: what Y of a chunk needs one iteration later.
     f32x4v xq_prev = {0.f, 0.f, 0.f, 0.f}, gam_prev = xq_prev;
-    u32x2 ph_prev[4], pl_prev[4];
+    u32x4 p_prev[4];
     uint32_t act_prev = 0u;
-    auto y_tile = [&](const u32x4 (&dsrc)[4][64]) {
+    auto y_tile = [&](const unsigned char* dsrc) {
         f32x4v Y, Y2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < 4; ++r) Y[r] = gam_prev[r] * xq_prev[r];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const u32x4 dd = dsrc[ks][l];
-            Y = mfma_bf16(ph_prev[ks], lo2(dd), Y);
-            Y2 = mfma_bf16(ph_prev[ks], hi2(dd), Y2);
-            Y2 = mfma_bf16(pl_prev[ks], lo2(dd), Y2);
+        for (int kb = 0; kb < 2; ++kb) {
+            const u32x4 dh = bop_hi(dsrc, kb, l), dl = bop_lo(dsrc, kb, l);
+            Y = mfma_bf16_k32(p_prev[2 * kb], dh, Y);
+            Y2 = mfma_bf16_k32(p_prev[2 * kb], dl, Y2);
+            Y2 = mfma_bf16_k32(p_prev[2 * kb + 1], dh, Y2);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) pend[r] = Y[r] + Y2[r];
@@ -614,16 +639,7 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
                 R[r] = bf16_bits_to_f32(vr[(16u * tt + 4u * lg + r) * 16 + lr]) - gam[r] * x[r];
             u32x2 hi, lo;
             split4(R, hi, lo);
-            rfr[tt][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
-        }
-        // Q side: P fragments of this chunk (read now, used next iteration).
-        u32x2 ph_cur[4], pl_cur[4];
-        if (qside) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                ph_cur[ks] = lo2(mf[ks]);
-                pl_cur[ks] = hi2(mf[ks]);
-            }
+            bop_store(rfr, tt, lr, lg, hi, lo);
         }
         __syncthreads();
 
@@ -632,30 +648,29 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
             // the tiles past tt add exact zeros.
             f32x4v D = {0.f, 0.f, 0.f, 0.f}, D2 = D;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const u32x4 rr = rfr[ks][l];
-                const u32x2 th = lo2(mf[ks]), tl = hi2(mf[ks]);
-                D = mfma_bf16(th, lo2(rr), D);
-                D2 = mfma_bf16(th, hi2(rr), D2);
-                D2 = mfma_bf16(tl, lo2(rr), D2);
+            for (int kb = 0; kb < 2; ++kb) {
+                const u32x4 rh = bop_hi(rfr, kb, l), rl = bop_lo(rfr, kb, l);
+                D = mfma_bf16_k32(mf[2 * kb], rh, D);
+                D2 = mfma_bf16_k32(mf[2 * kb], rl, D2);
+                D2 = mfma_bf16_k32(mf[2 * kb + 1], rh, D2);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) D[r] += D2[r];
             u32x2 hi, lo;
             split4(D, hi, lo);
-            dfr[c & 1u][tt][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
+            bop_store(dfr + (c & 1u) * ScanLds::BOP, tt, lr, lg, hi, lo);
             f32x4v Dt;
             const float4 r4 = *reinterpret_cast<const float4*>(gr + kC + 16u * tt + 4u * lg);
             Dt[0] = r4.x * D[0]; Dt[1] = r4.y * D[1]; Dt[2] = r4.z * D[2]; Dt[3] = r4.w * D[3];
             split4(Dt, hi, lo);
-            dtf[tt][l] = u32x4{hi.x, hi.y, lo.x, lo.y};
+            bop_store(dtf, tt, lr, lg, hi, lo);
             pend = D;
             pend_act = act;
             pend_t0 = t0;
         } else {
             if (c > 0) {
                 // Y of the previous chunk = gamma o X_Q + P Delta.
-                y_tile(dfr[(c - 1) & 1u]);
+                y_tile(dfr + ((c - 1) & 1u) * ScanLds::BOP);
                 pend_act = act_prev;
                 pend_t0 = t0 - kC;
             }
@@ -663,10 +678,7 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
             gam_prev = gam;
             act_prev = act;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                ph_prev[ks] = ph_cur[ks];
-                pl_prev[ks] = pl_cur[ks];
-            }
+            for (int i = 0; i < 4; ++i) p_prev[i] = mf[i];      // P of this chunk, for its Y next iteration
         }
         const float gC = gr[kC - 1];
         __syncthreads();
@@ -676,12 +688,11 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] *= gC;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const u32x4 dd = dtf[ks][l];
+        for (int kb = 0; kb < 2; ++kb) {
             const uint32_t dk = kcol(w, lr);
-            const u32x2 a = *reinterpret_cast<const u32x2*>(&kt[dk * ScanLds::KTS + 16 * ks + 4 * lg]);
-            acc = mfma_bf16(a, lo2(dd), acc);
-            lo_acc = mfma_bf16(a, hi2(dd), lo_acc);
+            const u32x4 a = *reinterpret_cast<const u32x4*>(&kt[dk * ScanLds::KTS + 32 * kb + 8 * lg]);
+            acc = mfma_bf16_k32(a, bop_hi(dtf, kb, l), acc);
+            lo_acc = mfma_bf16_k32(a, bop_lo(dtf, kb, l), lo_acc);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] += lo_acc[r];
@@ -697,7 +708,7 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     if (qside) {
         // Y of the last chunk (its Delta fragments were written before the
         // last iteration's final barrier).
-        y_tile(dfr[(nchunks - 1) & 1u]);
+        y_tile(dfr + ((nchunks - 1) & 1u) * ScanLds::BOP);
         pend_act = act_prev;
         pend_t0 = (nchunks - 1) * kC;
         flush();
