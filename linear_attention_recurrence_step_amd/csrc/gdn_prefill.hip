@@ -254,36 +254,30 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
 
     // Gram tiles G = K K^T and H = Q K^T of row tile w (all four column tiles;
     // above the diagonal the s <= t masks below make A and P exact zeros).
-    // Products of bf16 values are exact in fp32.  Fragment: lane holds
-    // x[16 tile + lr][16 ks + 4 lg .. +3].
+    // Products of bf16 values are exact in fp32.  32-deep products over key
+    // columns: lane holds x[16 tile + lr][32 m + 8 lg .. +7] as A and B.
     f32x4v G[4], H[4];
     {
-        u32x2 kw[kDk / 16], qf[kDk / 16];
-        const unsigned char* kwr = lds + PrepLds::KR + (16u * w + lr) * PrepLds::KS + lg * 8;
-        const unsigned char* qwr = lds + PrepLds::QR + (16u * w + lr) * PrepLds::KS + lg * 8;
+        u32x4 kw[kDk / 32], qf[kDk / 32];
+        const unsigned char* kwr = lds + PrepLds::KR + (16u * w + lr) * PrepLds::KS + lg * 16;
+        const unsigned char* qwr = lds + PrepLds::QR + (16u * w + lr) * PrepLds::KS + lg * 16;
 #pragma unroll
-        for (int ks = 0; ks < kDk / 16; ++ks) {
-            kw[ks] = *reinterpret_cast<const u32x2*>(kwr + ks * 32);
-            qf[ks] = *reinterpret_cast<const u32x2*>(qwr + ks * 32);
+        for (int m = 0; m < kDk / 32; ++m) {
+            kw[m] = *reinterpret_cast<const u32x4*>(kwr + m * 64);
+            qf[m] = *reinterpret_cast<const u32x4*>(qwr + m * 64);
         }
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            const unsigned char* kr = lds + PrepLds::KR + (16u * st + lr) * PrepLds::KS + lg * 8;
-            f32x4v g0 = {0.f, 0.f, 0.f, 0.f}, h0 = g0, g1 = g0, h1 = g0;
+            const unsigned char* kr = lds + PrepLds::KR + (16u * st + lr) * PrepLds::KS + lg * 16;
+            f32x4v g = {0.f, 0.f, 0.f, 0.f}, h = g;
 #pragma unroll
-            for (int ks = 0; ks < kDk / 16; ks += 2) {
-                const u32x2 b0 = *reinterpret_cast<const u32x2*>(kr + ks * 32);
-                const u32x2 b1 = *reinterpret_cast<const u32x2*>(kr + ks * 32 + 32);
-                g0 = mfma_bf16(kw[ks], b0, g0);
-                g1 = mfma_bf16(kw[ks + 1], b1, g1);
-                h0 = mfma_bf16(qf[ks], b0, h0);
-                h1 = mfma_bf16(qf[ks + 1], b1, h1);
+            for (int m = 0; m < kDk / 32; ++m) {
+                const u32x4 bk = *reinterpret_cast<const u32x4*>(kr + m * 64);
+                g = mfma_bf16_k32(kw[m], bk, g);
+                h = mfma_bf16_k32(qf[m], bk, h);
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                G[st][r] = g0[r] + g1[r];
-                H[st][r] = h0[r] + h1[r];
-            }
+            G[st] = g;
+            H[st] = h;
         }
     }
     __syncthreads();       // M is complete; the key and query rows are dead
