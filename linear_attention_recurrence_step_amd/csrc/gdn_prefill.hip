@@ -367,21 +367,22 @@ struct ScanLds {
 // Staging registers: this thread's pieces of the next chunk.
 struct ScanStage {
     u32x4 gv;             // threads 0-31: gamma/rho piece; threads 32-159: v piece
-    uint32_t mv;          // threads 32-223: mask word of the v row / flag row (1 without a mask)
+    uint32_t mv;          // threads 32-223: mask word of the v row / flag row (any word without a mask)
 };
 
-__device__ __forceinline__ void stage_store(const ScanStage& st, unsigned char* lds, uint32_t T, uint32_t t0,
+__device__ __forceinline__ void stage_store(const ScanStage& st, bool has_mask, unsigned char* lds, uint32_t T,
+                                            uint32_t t0,
                                             uint32_t tid) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     if (tid < 32u) {
         *reinterpret_cast<u32x4*>(lds + ScanLds::GR + tid * 16) = st.gv;
     } else if (tid < 160u) {
         const uint32_t p = tid - 32u, vr = p >> 1;
-        const bool act = t0 + vr < T && st.mv > 0u;
+        const bool act = t0 + vr < T && (!has_mask || st.mv > 0u);
         *reinterpret_cast<u32x4*>(lds + ScanLds::VR + vr * 32 + (p & 1u) * 16) = act ? st.gv : z;
     } else if (tid < 224u) {
         const uint32_t r = tid - 160u;
-        reinterpret_cast<uint32_t*>(lds + ScanLds::AF)[r] = t0 + r < T && st.mv > 0u ? 1u : 0u;
+        reinterpret_cast<uint32_t*>(lds + ScanLds::AF)[r] = t0 + r < T && (!has_mask || st.mv > 0u) ? 1u : 0u;
     }
 }
 
@@ -508,13 +509,19 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         const unsigned char* vsrc = reinterpret_cast<const unsigned char*>(in ? v_lane + t0n * rs : v_last);
         const unsigned char* src = vthread ? vsrc : g_lane + cc * static_cast<size_t>(PrefillWs::kBytes);
         st.gv = *reinterpret_cast<const u32x4*>(src);
-        const uint32_t mw = mwords[in ? t0n + mrow : T - 1];
-        st.mv = mask ? mw : 1u;
+        // The raw word: selecting on it here would wait for the load (the
+        // select is made where the word is used, in stage_store).
+        st.mv = mwords[in ? t0n + mrow : T - 1];
     };
-    ScanStage stage;
-    sload(stage, 0u);
+    ScanStage sta, stb;
     u32x4 mfa[4], mfb[4], aka[4], akb[4];
-    mload(mfa, 0u);
+    {
+        const uint32_t c1 = nchunks > 1u ? 1u : 0u;
+        sload(sta, 0u);
+        sload(stb, c1);
+        mload(mfa, 0u);
+        mload(mfb, c1);
+    }
     aload(aka, 0u);
     aload(akb, (nchunks > 1u ? 1u : 0u) * kC);
     // One pending output tile per wave (Delta of this chunk on the K side, Y of
@@ -554,15 +561,19 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         for (int r = 0; r < 4; ++r) pend[r] = Y[r] + Y2[r];
     };
 
-    // One chunk.  mf holds its Tb or P fragments and mf_nxt receives the next
-    // chunk's; ak holds its key or query fragments and then receives those of
-    // the chunk after next.  The loop below runs two chunks per iteration with
-    // the buffers swapped, so that no register still being loaded is copied
-    // (a copy would wait for the load).
-    auto chunk = [&](uint32_t c, const u32x4 (&mf)[4], u32x4 (&mf_nxt)[4], u32x4 (&ak)[4])
+    // One chunk.  st, mf and ak hold its staged rows, its Tb or P fragments
+    // and its key or query fragments; each then receives those of the chunk
+    // after next, once this chunk is done with it.  The loop below runs two
+    // chunks per iteration with the buffers swapped, so that no register still
+    // being loaded is copied (a copy would wait for the load) and every load
+    // has one to two chunks of compute to arrive in.
+    auto chunk = [&](uint32_t c, ScanStage& st, u32x4 (&mf)[4], u32x4 (&ak)[4])
                      __attribute__((always_inline)) {
         const uint32_t t0 = c * kC;
-        stage_store(stage, lds, T, t0, tid);
+        // (Past the last chunk the loads repeat it and go unused, so that
+        // every iteration issues the same memory operations.)
+        const uint32_t c2 = c + 2 < nchunks ? c + 2 : nchunks - 1;
+        stage_store(st, mask != nullptr, lds, T, t0, tid);
         {
             u32x2 hi, lo;
             split4(acc, hi, lo);
@@ -597,17 +608,11 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
             x = mfma_bf16_k32(a8[m], sfr[m][l], x);
             x2 = mfma_bf16_k32(a8[m], sfr[4 + m][l], x2);
         }
-        // The previous chunk's outputs and the next chunk's loads are issued
-        // here, behind the first barrier, while the products above run.
+        // The previous chunk's outputs and loads for the chunk after next are
+        // issued here, behind the first barrier, while the products above run.
         flush();
-        // (Past the last chunk the loads repeat it and go unused, so that
-        // every iteration issues the same memory operations.)
-        {
-            const uint32_t c1 = c + 1 < nchunks ? c + 1 : c, c2 = c + 2 < nchunks ? c + 2 : c1;
-            sload(stage, c1);
-            mload(mf_nxt, c1);
-            aload(ak, c2 * kC);                         // ak is free again: its selects are done
-        }
+        sload(st, c2);                                  // st was stored into LDS at the top
+        aload(ak, c2 * kC);                             // ak is free again: its selects are done
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] += x2[r];
         f32x4v gam;
@@ -690,13 +695,14 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] += lo_acc[r];
+        mload(mf, c2);                                  // mf's last use was before the third barrier
     };
     uint32_t c = 0;
     for (; c + 1 < nchunks; c += 2) {
-        chunk(c, mfa, mfb, aka);
-        chunk(c + 1, mfb, mfa, akb);
+        chunk(c, sta, mfa, aka);
+        chunk(c + 1, stb, mfb, akb);
     }
-    if (c < nchunks) chunk(c, mfa, mfb, aka);          // an odd chunk count's last chunk
+    if (c < nchunks) chunk(c, sta, mfa, aka);          // an odd chunk count's last chunk
 
     flush();
     if (qside) {
