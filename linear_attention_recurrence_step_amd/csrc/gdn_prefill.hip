@@ -361,7 +361,9 @@ struct ScanLds {
     static constexpr int VR = KT + kDk * KTS * 2;      // v rows [64] x 32 B (bf16, this row block)
     static constexpr int GR = VR + kC * 32;            // gamma [64], rho [64] fp32
     static constexpr int AF = GR + 2 * kC * 4;         // active flags [64] u32 (0 or 1)
-    static constexpr int BYTES = AF + kC * 4;
+    static constexpr int OT = AF + kC * 4;             // per wave: its pending output tile [16][16] bf16
+    static constexpr int OTF = OT + 8 * 16 * 16 * 2;   // per wave: that tile's row flags [16] u32
+    static constexpr int BYTES = OTF + 8 * 16 * 4;
 };
 
 // Staging registers: this thread's pieces of the next chunk.
@@ -526,27 +528,40 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     aload(akb, (nchunks > 1u ? 1u : 0u) * kC);
     // One pending output tile per wave (Delta of this chunk on the K side, Y of
     // the previous chunk on the Q side), stored in the next iteration just
-    // before its loads are issued.
-    f32x4v pend = {0.f, 0.f, 0.f, 0.f};
-    uint32_t pend_act = 0u, pend_t0 = 0u;
-    // This lane's output element of step 16 tt + 4 lg of a chunk starting at
-    // step 0; a chunk adds a wave-uniform offset, row r adds r steps.
-    uint16_t* const out_lane = out == nullptr ? nullptr
-        : static_cast<uint16_t*>(out) + (static_cast<size_t>(b) * T * Hv + hv) * Dv + dv0 + lr +
-              (16u * tt + 4u * lg) * rs;
-    auto flush = [&]() {
-        if (out == nullptr) return;
-        uint16_t* const o = out_lane + pend_t0 * rs;
+    // before its loads are issued.  The tile goes through this wave's own LDS
+    // area as bf16 with a flag per row, so that each lane stores one 8-byte
+    // piece (four consecutive values of one step) instead of four 2-byte
+    // values of four steps.  Only this wave touches its area, in program order.
+    uint16_t* const ot = reinterpret_cast<uint16_t*>(lds + ScanLds::OT) + w * 256;
+    uint32_t* const otf = reinterpret_cast<uint32_t*>(lds + ScanLds::OTF) + w * 16;
+    bool pend_valid = false;
+    uint32_t pend_t0 = 0u;
+    auto produce = [&](const f32x4v& vals, uint32_t actbits, uint32_t t0p) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (pend_act & (1u << r)) o[r * rs] = static_cast<uint16_t>(f32_to_bf16_bits(pend[r]));
-        pend_act = 0u;
+        for (int r = 0; r < 4; ++r) ot[(4u * lg + r) * 16 + lr] = static_cast<uint16_t>(f32_to_bf16_bits(vals[r]));
+        if (lr == 0u) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) otf[4u * lg + r] = (actbits >> r) & 1u;
+        }
+        pend_valid = true;
+        pend_t0 = t0p;
+    };
+    // This lane's 8-byte piece: step 16 tt + l / 4 of a chunk starting at step
+    // 0, values dv0 + 4 (l % 4) .. +3; a chunk adds a wave-uniform offset.
+    uint16_t* const out_lane = out == nullptr ? nullptr
+        : static_cast<uint16_t*>(out) + (static_cast<size_t>(b) * T * Hv + hv) * Dv + dv0 + 4u * (l & 3u) +
+              (16u * tt + (l >> 2)) * rs;
+    auto flush = [&]() {
+        if (out == nullptr || !pend_valid) return;
+        const u32x2 piece = *reinterpret_cast<const u32x2*>(ot + (l >> 2) * 16 + 4u * (l & 3u));
+        if (otf[l >> 2] != 0u) *reinterpret_cast<u32x2*>(out_lane + pend_t0 * rs) = piece;
+        pend_valid = false;
     };
     // Q side: what Y of a chunk needs one iteration later.
     f32x4v xq_prev = {0.f, 0.f, 0.f, 0.f}, gam_prev = xq_prev;
     u32x4 p_prev[4];
     uint32_t act_prev = 0u;
-    auto y_tile = [&](const unsigned char* dsrc) {
+    auto y_tile = [&](const unsigned char* dsrc) -> f32x4v {
         f32x4v Y, Y2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < 4; ++r) Y[r] = gam_prev[r] * xq_prev[r];
@@ -558,7 +573,8 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
             Y2 = mfma_bf16_k32(p_prev[2 * kb + 1], dh, Y2);
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pend[r] = Y[r] + Y2[r];
+        for (int r = 0; r < 4; ++r) Y[r] += Y2[r];
+        return Y;
     };
 
     // One chunk.  st, mf and ak hold its staged rows, its Tb or P fragments
@@ -663,15 +679,11 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
             Dt[0] = r4.x * D[0]; Dt[1] = r4.y * D[1]; Dt[2] = r4.z * D[2]; Dt[3] = r4.w * D[3];
             split4(Dt, hi, lo);
             bop_store(dtf, tt, lr, lg, hi, lo);
-            pend = D;
-            pend_act = act;
-            pend_t0 = t0;
+            produce(D, act, t0);
         } else {
             if (c > 0) {
                 // Y of the previous chunk = gamma o X_Q + P Delta.
-                y_tile(dfr + ((c - 1) & 1u) * ScanLds::BOP);
-                pend_act = act_prev;
-                pend_t0 = t0 - kC;
+                produce(y_tile(dfr + ((c - 1) & 1u) * ScanLds::BOP), act_prev, t0 - kC);
             }
             xq_prev = x;
             gam_prev = gam;
@@ -708,9 +720,7 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     if (qside) {
         // Y of the last chunk (its Delta fragments were written before the
         // last iteration's final barrier).
-        y_tile(dfr + ((nchunks - 1) & 1u) * ScanLds::BOP);
-        pend_act = act_prev;
-        pend_t0 = (nchunks - 1) * kC;
+        produce(y_tile(dfr + ((nchunks - 1) & 1u) * ScanLds::BOP), act_prev, (nchunks - 1) * kC);
         flush();
     }
     *reinterpret_cast<float4*>(state_out + srow) = make_float4(acc[0], acc[1], acc[2], acc[3]);
