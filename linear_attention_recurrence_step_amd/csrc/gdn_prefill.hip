@@ -46,21 +46,13 @@ constexpr int kC = 64;            // steps per chunk
 constexpr int kDk = 128;          // key width this path is built for
 constexpr int kRows = 16;         // state rows per scan workgroup
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
-
-// acc += A (16 x 16) * B (16 x 16) with bf16 operands.  Lane l holds
-// A[l % 16][4 (l / 16) + 0..3], B[4 (l / 16) + 0..3][l % 16] and returns
-// D[4 (l / 16) + r][l % 16], r = 0..3.
-__device__ __forceinline__ f32x4v mfma_bf16(u32x2 a, u32x2 b, f32x4v acc) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
-                                                     __builtin_bit_cast(i16x4, b), acc, 0, 0, 0);
-}
 
 // D += A B on gfx950's double-depth bf16 tile: 16 x 16 x 32, eight bf16 of
 // A (row l % 16) and of B (column l % 16) per lane, over the same eight
 // positions of the 32-deep sum in both, so that any operands whose lanes
-// pair the same summation index give the full product.
+// pair the same summation index give the full product.  D comes back as
+// D[4 (l / 16) + r][l % 16], r = 0..3.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ f32x4v mfma_bf16_k32(u32x4 a, u32x4 b, f32x4v acc) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc,
@@ -335,21 +327,22 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
 // ------------------------------------------------------------------ scan
 //
 // One workgroup of eight waves per (b, hv, 16 consecutive value rows).  The
-// state is held transposed in MFMA accumulators: wave w owns key columns
-// 16w .. 16w+15, lane l holding S[dv0 + l%16][16w + 4 (l/16) + r] -- the
-// layout in which the tile is also the B operand of X = K S^T for key step w.
+// state is held transposed in MFMA accumulators: wave w owns the sixteen key
+// columns kcol(w, 0..15), lane l holding S[dv0 + l%16][kcol(w, 4 (l/16) + r)];
+// the hi and lo parts of tiles 2m and 2m+1 side by side are the B operand of
+// the 32-deep product X = K S^T over key columns 32m .. 32m + 31.
 // Waves 0-3 (the K side) take step tile w of the chunk: X_K, R and Delta.
 // Waves 4-7 (the Q side) take step tile w-4: X_Q, and Y of the previous chunk
 // while the K side solves for Delta (Y is not on the state's dependency chain).
 //
-// Each lane loads its key or query fragments of the next chunk straight from
-// the input while the current chunk is computed: with the key index permuted
-// (kcol), the fragments of two key steps are one contiguous 16-byte piece of a
-// row.  v of this row block, gamma, rho and the step flags are copied into
-// registers the same way and into LDS at the top of the iteration.  Tb and P
-// are already in fragment order in the workspace and go straight to
-// registers, one chunk ahead.  Key, query and value rows of inactive steps
-// (masked, or past T) are replaced by zeros.
+// Each lane loads its key or query pieces straight from the input two chunks
+// ahead: with the key index permuted (kcol), the eight key columns a lane
+// multiplies are one contiguous 16-byte piece of a row.  v of this row block,
+// gamma, rho and the step flags come into registers two chunks ahead too and
+// into LDS at the top of their chunk.  Tb and P are already in operand order
+// in the workspace and go straight to registers, two chunks ahead.  Key,
+// query and value rows of inactive steps (masked, or past T) are replaced by
+// zeros.
 struct ScanLds {
     static constexpr int KTS = kC + 8;                 // K^T row stride in bf16 (144 bytes, 16-byte aligned)
     static constexpr int SFR = 0;                      // state fragments [8][64] x 16 B (hi [4], lo [4])
@@ -390,8 +383,6 @@ __device__ __forceinline__ void stage_store(const ScanStage& st, bool has_mask, 
 
 __device__ __forceinline__ u32x2 lo2(const u32x4& x) { return u32x2{x.x, x.y}; }
 __device__ __forceinline__ u32x2 hi2(const u32x4& x) { return u32x2{x.z, x.w}; }
-
-__device__ __forceinline__ u32x2 lds8(const unsigned char* p) { return *reinterpret_cast<const u32x2*>(p); }
 
 // Key column of index i (0..15) of key step ks: the key steps are a
 // permutation of the key columns in which steps 2m and 2m+1 take, for each
