@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum gdn_dtype {
     GDN_F32 = 0,
@@ -123,8 +123,9 @@ int gdn_record(const void* q, const void* k, const void* v, const void* g, const
                int io_dtype, int gqa_map, void* stream);
 
 /*
- * gdn_replay -- re-fold the accepted prefix of an innovation tape onto a
- * pre-record state snapshot (speculative-decode rollback).
+ * gdn_replay -- speculative-decode rollback: starting again from the state
+ * saved before gdn_record ran, apply only the tape positions that were
+ * accepted.
  *
  * Defined by the replay kernel (macro `state_replay!`) and the module
  * documentation ("Two kernels", "Tape layout") on the metaltile-std 0.1.0 page
@@ -247,6 +248,56 @@ int gdn_prefill(const void* q, const void* k, const void* v, const void* g, cons
  */
 int rms_norm_bf16(const float* x, const uint16_t* weight, float* out, uint32_t n_tokens,
                   uint32_t dim, float eps, void* stream);
+
+/*
+ * Launch choices, for tests and launch-shape sweeps.
+ *
+ * gdn_record and gdn_replay pick their kernel and launch shape from the sizes
+ * alone; nothing else (no environment, no state) changes what they run.
+ * gdn_record_debug and gdn_replay_debug take the same arguments after a
+ * gdn_launch_choice that forces those picks, so that tests can check every
+ * kernel configuration against the others and sweeps can time each one.  A
+ * NULL or all-zero choice leaves every pick to the library: the call is then
+ * exactly gdn_record / gdn_replay.  Every configuration computes the same
+ * function: row tilings change no bit of any output, and the two replay folds
+ * agree within the stated tolerance (they round differently).
+ *
+ * Errors, besides those of the plain calls: a (rows_per_thread, threads) pair
+ * that is not one of the five below, an unknown fold or a wave count other
+ * than 0, 2 or 4 -> GDN_ERR_BAD_ENUM; a tiling whose rows per workgroup
+ * (rows_per_thread * threads / 16) do not divide Dv, that would keep more than
+ * 64 state values per lane (rows_per_thread * Dk / 16), or, for a record of
+ * more than one step, covers more than 64 rows; or the matrix-core fold on a
+ * float32 tape or with Dv not a multiple of 64 -> GDN_ERR_UNSUPPORTED_SHAPE.
+ */
+typedef enum gdn_replay_fold {
+    GDN_FOLD_AUTO = 0,    /* the matrix cores for 16+ positions of a 16-bit tape with Dv % 64 == 0 */
+    GDN_FOLD_VALU = 1,    /* the vector-ALU fold (any tape)                                        */
+    GDN_FOLD_MATRIX = 2   /* the matrix-core fold (16-bit tape, Dv a multiple of 64)               */
+} gdn_replay_fold;
+
+typedef struct gdn_launch_choice {
+    /* State rows per thread and threads per workgroup of the vector-ALU
+     * kernels: (8,256), (4,256), (2,256), (1,256) or (1,64); both 0 for the
+     * library's choice.  Ignored by a replay that runs on the matrix cores. */
+    uint32_t rows_per_thread;
+    uint32_t threads;
+    int32_t replay_fold;      /* gdn_replay_fold; gdn_replay_debug only (0 for gdn_record_debug) */
+    uint32_t matrix_waves;    /* matrix-core fold: waves per workgroup, 2 or 4; 0 for the library's (4) */
+} gdn_launch_choice;
+
+int gdn_record_debug(const gdn_launch_choice* choice,
+                     const void* q, const void* k, const void* v, const void* g, const void* beta,
+                     const float* state_in, const uint32_t* mask,
+                     void* y, float* state_out, void* delta_log, void* k_log, void* g_log,
+                     uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+                     int io_dtype, int gqa_map, void* stream);
+
+int gdn_replay_debug(const gdn_launch_choice* choice,
+                     const void* delta_log, const void* k_log, const void* g_log,
+                     const float* state_in, const uint32_t* mask, float* state_out,
+                     uint32_t B, uint32_t T_log, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+                     uint32_t accepted, int io_dtype, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* gdn_strerror(int status);

@@ -23,9 +23,17 @@ STATUS = {
     -7: "GDN_ERR_BAD_ENUM", -8: "GDN_ERR_LAUNCH", -9: "GDN_ERR_MISALIGNED",
     -10: "GDN_ERR_WORKSPACE",
 }
+GDN_FOLD_AUTO, GDN_FOLD_VALU, GDN_FOLD_MATRIX = 0, 1, 2
 EXPORTS = ("gdn_record", "gdn_replay", "gqa_expand", "gdn_prefill", "gdn_prefill_workspace_size",
-           "rms_norm_bf16", "gdn_strerror", "gdn_last_error", "gdn_abi_version")
-ABI_VERSION = 4
+           "rms_norm_bf16", "gdn_record_debug", "gdn_replay_debug", "gdn_strerror", "gdn_last_error",
+           "gdn_abi_version")
+ABI_VERSION = 5
+
+
+class LaunchChoice(ctypes.Structure):
+    """gdn_launch_choice of include/gdn.h."""
+    _fields_ = [("rows_per_thread", ctypes.c_uint32), ("threads", ctypes.c_uint32),
+                ("replay_fold", ctypes.c_int32), ("matrix_waves", ctypes.c_uint32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -39,6 +47,11 @@ def _load() -> ctypes.CDLL:
     lib.gdn_record.restype = i32
     lib.gdn_replay.argtypes = [vp] * 6 + [u32] * 6 + [i32, vp]
     lib.gdn_replay.restype = i32
+    lc = ctypes.POINTER(LaunchChoice)
+    lib.gdn_record_debug.argtypes = [lc] + lib.gdn_record.argtypes
+    lib.gdn_record_debug.restype = i32
+    lib.gdn_replay_debug.argtypes = [lc] + lib.gdn_replay.argtypes
+    lib.gdn_replay_debug.restype = i32
     lib.gqa_expand.argtypes = [vp, vp] + [u32] * 4 + [i32, i32, vp]
     lib.gqa_expand.restype = i32
     lib.gdn_prefill.argtypes = [vp] * 11 + [ctypes.c_uint64] + [u32] * 6 + [i32, i32, vp]

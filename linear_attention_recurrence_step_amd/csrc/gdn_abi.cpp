@@ -91,24 +91,56 @@ const char* gdn_strerror(int status) {
     }
 }
 
-int gdn_record(const void* q, const void* k, const void* v, const void* g, const void* beta,
-               const float* state_in, const uint32_t* mask,
-               void* y, float* state_out, void* delta_log, void* k_log, void* g_log,
-               uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
-               int io_dtype, int gqa_map, void* stream) {
-    static const char* kFn = "gdn_record";
+}  // extern "C"
+
+namespace {
+
+// The tiling a launch choice forces ({0, 0}: none), after checking it against
+// the shape; returns GDN_OK or the status to fail with (message set).
+int forced_tiling(const gdn_launch_choice* c, const char* fn, uint32_t Dk, uint32_t Dv,
+                  uint32_t max_rows, gdn::RowTiling* out) {
+    *out = gdn::RowTiling{0, 0};
+    if (c == nullptr || (c->rows_per_thread == 0 && c->threads == 0)) return GDN_OK;
+    const int rpt = static_cast<int>(c->rows_per_thread), nt = static_cast<int>(c->threads);
+    if (c->rows_per_thread > 8 || c->threads > 256 || !gdn::tiling_known(rpt, nt))
+        return fail(GDN_ERR_BAD_ENUM, "%s: no row tiling of %u rows per thread over %u threads", fn,
+                    c->rows_per_thread, c->threads);
+    const gdn::RowTiling t{rpt, nt};
+    if (!gdn::tiling_fits(t, Dk, Dv) || static_cast<uint32_t>(t.rows()) > max_rows)
+        return fail(GDN_ERR_UNSUPPORTED_SHAPE,
+                    "%s: a tiling of %d rows per thread over %d threads does not fit Dk=%u, Dv=%u "
+                    "(at most %u rows per workgroup here)", fn, rpt, nt, Dk, Dv, max_rows);
+    *out = t;
+    return GDN_OK;
+}
+
+int record_impl(const gdn_launch_choice* choice,
+                const void* q, const void* k, const void* v, const void* g, const void* beta,
+                const float* state_in, const uint32_t* mask,
+                void* y, float* state_out, void* delta_log, void* k_log, void* g_log,
+                uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+                int io_dtype, int gqa_map, void* stream, const char* kFn) {
     if (!valid_dtype(io_dtype)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown io_dtype %d", kFn, io_dtype);
     if (!valid_map(gqa_map)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown gqa_map %d", kFn, gqa_map);
     if (!q || !k || !v || !g || !beta || !state_in || !y || !state_out)
-        return fail(GDN_ERR_NULL, "%s: q, k, v, g, beta, state_in, y and state_out must be non-NULL", kFn);
+        return fail(GDN_ERR_NULL, "%s: one of q, k, v, g, beta, state_in, y, state_out is NULL", kFn);
     if (B == 0 || T == 0 || Hk == 0 || Hv == 0 || Dk == 0 || Dv == 0)
-        return fail(GDN_ERR_ZERO_DIM, "%s: B, T, Hk, Hv, Dk, Dv must all be > 0 (got %u,%u,%u,%u,%u,%u)",
+        return fail(GDN_ERR_ZERO_DIM, "%s: zero-sized dimension in B=%u T=%u Hk=%u Hv=%u Dk=%u Dv=%u",
                     kFn, B, T, Hk, Hv, Dk, Dv);
-    if (Hv % Hk != 0) return fail(GDN_ERR_GQA_RATIO, "%s: Hv (%u) must be a multiple of Hk (%u)", kFn, Hv, Hk);
+    if (Hv % Hk != 0)
+        return fail(GDN_ERR_GQA_RATIO, "%s: %u value heads cannot share %u key heads evenly", kFn, Hv, Hk);
     if (!gdn::dk_supported(Dk) || Dv % 16 != 0 || Dv > 1024)
         return fail(GDN_ERR_UNSUPPORTED_SHAPE,
-                    "%s: Dk must be one of 32, 64, 128, 192, 256 and Dv a multiple of 16 up to 1024 "
-                    "(got Dk=%u, Dv=%u)", kFn, Dk, Dv);
+                    "%s: no kernel for Dk=%u, Dv=%u (Dk in {32, 64, 128, 192, 256}; Dv a multiple "
+                    "of 16, at most 1024)", kFn, Dk, Dv);
+    if (choice != nullptr && (choice->replay_fold != 0 || choice->matrix_waves != 0))
+        return fail(GDN_ERR_BAD_ENUM, "%s: replay_fold and matrix_waves apply to the replay only", kFn);
+    gdn::RowTiling forced;
+    {
+        const uint32_t max_rows = T == 1 ? 1024u : static_cast<uint32_t>(gdn::kStagedMaxRows);
+        const int st = forced_tiling(choice, kFn, Dk, Dv, max_rows, &forced);
+        if (st != GDN_OK) return st;
+    }
 
     const uint64_t e = io_bytes(io_dtype);
     uint64_t n_qk, n_v, n_g, n_s, n_m, n_kl;
@@ -119,7 +151,7 @@ int gdn_record(const void* q, const void* k, const void* v, const void* g, const
         return fail(GDN_ERR_OVERFLOW, "%s: tensor sizes overflow", kFn);
 
     gdn::RecordArgs a{q, k, v, g, beta, state_in, mask, y, state_out, delta_log, k_log, g_log,
-                      B, T, Hk, Hv, Dk, Dv, io_dtype, gqa_map};
+                      B, T, Hk, Hv, Dk, Dv, io_dtype, gqa_map, forced};
     const gdn::RowTiling til = gdn::record_tiling(a);
     uint64_t items;
     if (!mul_u64(&items, {B, Hv, Dv / static_cast<uint32_t>(til.rows()), static_cast<uint32_t>(til.threads)}) ||
@@ -155,6 +187,113 @@ int gdn_record(const void* q, const void* k, const void* v, const void* g, const
     return launch_status(gdn::launch_record(a, static_cast<hipStream_t>(stream)), kFn);
 }
 
+int replay_impl(const gdn_launch_choice* choice,
+                const void* delta_log, const void* k_log, const void* g_log,
+                const float* state_in, const uint32_t* mask, float* state_out,
+                uint32_t B, uint32_t T_log, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+                uint32_t accepted, int io_dtype, void* stream, const char* kFn) {
+    if (!valid_dtype(io_dtype)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown io_dtype %d", kFn, io_dtype);
+    if (!delta_log || !k_log || !g_log || !state_in || !state_out)
+        return fail(GDN_ERR_NULL, "%s: one of delta_log, k_log, g_log, state_in, state_out is NULL", kFn);
+    if (B == 0 || T_log == 0 || Hv == 0 || Dk == 0 || Dv == 0)
+        return fail(GDN_ERR_ZERO_DIM, "%s: zero-sized dimension in B=%u T_log=%u Hv=%u Dk=%u Dv=%u",
+                    kFn, B, T_log, Hv, Dk, Dv);
+    if (!gdn::dk_supported(Dk) || Dv % 16 != 0 || Dv > 1024)
+        return fail(GDN_ERR_UNSUPPORTED_SHAPE,
+                    "%s: no kernel for Dk=%u, Dv=%u (Dk in {32, 64, 128, 192, 256}; Dv a multiple "
+                    "of 16, at most 1024)", kFn, Dk, Dv);
+    gdn::RowTiling forced;
+    {
+        const int st = forced_tiling(choice, kFn, Dk, Dv, 1024u, &forced);
+        if (st != GDN_OK) return st;
+    }
+    const int fold = choice ? choice->replay_fold : GDN_FOLD_AUTO;
+    const uint32_t waves = choice ? choice->matrix_waves : 0u;
+    if (fold != GDN_FOLD_AUTO && fold != GDN_FOLD_VALU && fold != GDN_FOLD_MATRIX)
+        return fail(GDN_ERR_BAD_ENUM, "%s: unknown replay_fold %d", kFn, fold);
+    if (waves != 0 && waves != 2 && waves != 4)
+        return fail(GDN_ERR_BAD_ENUM, "%s: matrix_waves must be 0, 2 or 4 (got %u)", kFn, waves);
+
+    const uint64_t e = io_bytes(io_dtype);
+    uint64_t n_d, n_k, n_g, n_s, n_m;
+    if (!mul_u64(&n_d, {B, T_log, Hv, Dv, e}) || !mul_u64(&n_k, {B, T_log, Hv, Dk, e}) ||
+        !mul_u64(&n_g, {B, T_log, Hv, e}) || !mul_u64(&n_s, {B, Hv, Dv, Dk, 4}) ||
+        !mul_u64(&n_m, {B, T_log, 4}) || n_d > kMaxBytes || n_k > kMaxBytes || n_s > kMaxBytes)
+        return fail(GDN_ERR_OVERFLOW, "%s: tensor sizes overflow", kFn);
+
+    gdn::ReplayArgs a{delta_log, k_log, g_log, state_in, mask, state_out,
+                      B, T_log, Hv, Dk, Dv, accepted < T_log ? accepted : T_log, io_dtype,
+                      forced, fold, waves};
+    if (fold == GDN_FOLD_MATRIX && !gdn::replay_mfma_possible(a))
+        return fail(GDN_ERR_UNSUPPORTED_SHAPE,
+                    "%s: the matrix-core fold needs a 16-bit tape, Dv a multiple of 64 and at most "
+                    "2^32 - 1 work-items (4 per state row)", kFn);
+    if (!gdn::replay_mfma_applies(a)) {
+        const gdn::RowTiling til = gdn::replay_tiling(a);
+        uint64_t items;
+        if (!mul_u64(&items, {B, Hv, Dv / static_cast<uint32_t>(til.rows()), static_cast<uint32_t>(til.threads)}) ||
+            items > kMaxWorkItems)
+            return fail(GDN_ERR_OVERFLOW, "%s: launch grid too large (B*Hv*Dv too large for one launch)", kFn);
+    }
+
+    const void* a16[] = {delta_log, k_log, state_in, state_out};
+    const char* a16n[] = {"delta_log", "k_log", "state_in", "state_out"};
+    for (int i = 0; i < 4; ++i)
+        if (!aligned(a16[i], 16)) return fail(GDN_ERR_MISALIGNED, "%s: %s must be 16-byte aligned", kFn, a16n[i]);
+    if (mask && !aligned(mask, 4)) return fail(GDN_ERR_MISALIGNED, "%s: mask must be 4-byte aligned", kFn);
+    if (!aligned(g_log, e)) return fail(GDN_ERR_MISALIGNED, "%s: g_log must be element-aligned", kFn);
+
+    const Span out{state_out, n_s, "state_out"};
+    const Span ins[] = {{delta_log, n_d, "delta_log"}, {k_log, n_k, "k_log"}, {g_log, n_g, "g_log"},
+                        {state_in, n_s, "state_in"}, {mask, mask ? n_m : 0, "mask"}};
+    for (const Span& i : ins) {
+        if (i.p == state_in && out.p == state_in) continue;                   // exact in-place state
+        if (overlaps(out, i)) return fail(GDN_ERR_ALIAS, "%s: state_out overlaps %s", kFn, i.name);
+    }
+
+    return launch_status(gdn::launch_replay(a, static_cast<hipStream_t>(stream)), kFn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_record(const void* q, const void* k, const void* v, const void* g, const void* beta,
+               const float* state_in, const uint32_t* mask,
+               void* y, float* state_out, void* delta_log, void* k_log, void* g_log,
+               uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+               int io_dtype, int gqa_map, void* stream) {
+    return record_impl(nullptr, q, k, v, g, beta, state_in, mask, y, state_out, delta_log, k_log, g_log,
+                       B, T, Hk, Hv, Dk, Dv, io_dtype, gqa_map, stream, "gdn_record");
+}
+
+int gdn_record_debug(const gdn_launch_choice* choice,
+                     const void* q, const void* k, const void* v, const void* g, const void* beta,
+                     const float* state_in, const uint32_t* mask,
+                     void* y, float* state_out, void* delta_log, void* k_log, void* g_log,
+                     uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+                     int io_dtype, int gqa_map, void* stream) {
+    return record_impl(choice, q, k, v, g, beta, state_in, mask, y, state_out, delta_log, k_log, g_log,
+                       B, T, Hk, Hv, Dk, Dv, io_dtype, gqa_map, stream, "gdn_record_debug");
+}
+
+int gdn_replay(const void* delta_log, const void* k_log, const void* g_log,
+               const float* state_in, const uint32_t* mask, float* state_out,
+               uint32_t B, uint32_t T_log, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+               uint32_t accepted, int io_dtype, void* stream) {
+    return replay_impl(nullptr, delta_log, k_log, g_log, state_in, mask, state_out, B, T_log, Hv, Dk, Dv,
+                       accepted, io_dtype, stream, "gdn_replay");
+}
+
+int gdn_replay_debug(const gdn_launch_choice* choice,
+                     const void* delta_log, const void* k_log, const void* g_log,
+                     const float* state_in, const uint32_t* mask, float* state_out,
+                     uint32_t B, uint32_t T_log, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+                     uint32_t accepted, int io_dtype, void* stream) {
+    return replay_impl(choice, delta_log, k_log, g_log, state_in, mask, state_out, B, T_log, Hv, Dk, Dv,
+                       accepted, io_dtype, stream, "gdn_replay_debug");
+}
+
 uint64_t gdn_prefill_workspace_size(uint32_t B, uint32_t T, uint32_t Hv) {
     return gdn::prefill_workspace_bytes(B, T, Hv);
 }
@@ -169,11 +308,12 @@ int gdn_prefill(const void* q, const void* k, const void* v, const void* g, cons
     if (!valid_dtype(io_dtype)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown io_dtype %d", kFn, io_dtype);
     if (!valid_map(gqa_map)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown gqa_map %d", kFn, gqa_map);
     if (!q || !k || !v || !g || !beta || !state_in || !y || !state_out)
-        return fail(GDN_ERR_NULL, "%s: q, k, v, g, beta, state_in, y and state_out must be non-NULL", kFn);
+        return fail(GDN_ERR_NULL, "%s: one of q, k, v, g, beta, state_in, y, state_out is NULL", kFn);
     if (B == 0 || T == 0 || Hk == 0 || Hv == 0 || Dk == 0 || Dv == 0)
-        return fail(GDN_ERR_ZERO_DIM, "%s: B, T, Hk, Hv, Dk, Dv must all be > 0 (got %u,%u,%u,%u,%u,%u)",
+        return fail(GDN_ERR_ZERO_DIM, "%s: zero-sized dimension in B=%u T=%u Hk=%u Hv=%u Dk=%u Dv=%u",
                     kFn, B, T, Hk, Hv, Dk, Dv);
-    if (Hv % Hk != 0) return fail(GDN_ERR_GQA_RATIO, "%s: Hv (%u) must be a multiple of Hk (%u)", kFn, Hv, Hk);
+    if (Hv % Hk != 0)
+        return fail(GDN_ERR_GQA_RATIO, "%s: %u value heads cannot share %u key heads evenly", kFn, Hv, Hk);
     if (!gdn::prefill_supported(Dk, Dv, io_dtype) || Dv > 1024)
         return fail(GDN_ERR_UNSUPPORTED_SHAPE,
                     "%s: needs bf16 I/O, Dk = 128 and Dv a multiple of 16 up to 1024 "
@@ -227,64 +367,17 @@ int gdn_prefill(const void* q, const void* k, const void* v, const void* g, cons
     return launch_status(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)), kFn);
 }
 
-int gdn_replay(const void* delta_log, const void* k_log, const void* g_log,
-               const float* state_in, const uint32_t* mask, float* state_out,
-               uint32_t B, uint32_t T_log, uint32_t Hv, uint32_t Dk, uint32_t Dv,
-               uint32_t accepted, int io_dtype, void* stream) {
-    static const char* kFn = "gdn_replay";
-    if (!valid_dtype(io_dtype)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown io_dtype %d", kFn, io_dtype);
-    if (!delta_log || !k_log || !g_log || !state_in || !state_out)
-        return fail(GDN_ERR_NULL, "%s: delta_log, k_log, g_log, state_in and state_out must be non-NULL", kFn);
-    if (B == 0 || T_log == 0 || Hv == 0 || Dk == 0 || Dv == 0)
-        return fail(GDN_ERR_ZERO_DIM, "%s: B, T_log, Hv, Dk, Dv must all be > 0 (got %u,%u,%u,%u,%u)",
-                    kFn, B, T_log, Hv, Dk, Dv);
-    if (!gdn::dk_supported(Dk) || Dv % 16 != 0 || Dv > 1024)
-        return fail(GDN_ERR_UNSUPPORTED_SHAPE,
-                    "%s: Dk must be one of 32, 64, 128, 192, 256 and Dv a multiple of 16 up to 1024 "
-                    "(got Dk=%u, Dv=%u)", kFn, Dk, Dv);
-
-    const uint64_t e = io_bytes(io_dtype);
-    uint64_t n_d, n_k, n_g, n_s, n_m;
-    if (!mul_u64(&n_d, {B, T_log, Hv, Dv, e}) || !mul_u64(&n_k, {B, T_log, Hv, Dk, e}) ||
-        !mul_u64(&n_g, {B, T_log, Hv, e}) || !mul_u64(&n_s, {B, Hv, Dv, Dk, 4}) ||
-        !mul_u64(&n_m, {B, T_log, 4}) || n_d > kMaxBytes || n_k > kMaxBytes || n_s > kMaxBytes)
-        return fail(GDN_ERR_OVERFLOW, "%s: tensor sizes overflow", kFn);
-
-    gdn::ReplayArgs a{delta_log, k_log, g_log, state_in, mask, state_out,
-                      B, T_log, Hv, Dk, Dv, accepted < T_log ? accepted : T_log, io_dtype};
-    const gdn::RowTiling til = gdn::replay_tiling(a);
-    uint64_t items;
-    if (!mul_u64(&items, {B, Hv, Dv / static_cast<uint32_t>(til.rows()), static_cast<uint32_t>(til.threads)}) ||
-        items > kMaxWorkItems)
-        return fail(GDN_ERR_OVERFLOW, "%s: launch grid too large (B*Hv*Dv too large for one launch)", kFn);
-
-    const void* a16[] = {delta_log, k_log, state_in, state_out};
-    const char* a16n[] = {"delta_log", "k_log", "state_in", "state_out"};
-    for (int i = 0; i < 4; ++i)
-        if (!aligned(a16[i], 16)) return fail(GDN_ERR_MISALIGNED, "%s: %s must be 16-byte aligned", kFn, a16n[i]);
-    if (mask && !aligned(mask, 4)) return fail(GDN_ERR_MISALIGNED, "%s: mask must be 4-byte aligned", kFn);
-    if (!aligned(g_log, e)) return fail(GDN_ERR_MISALIGNED, "%s: g_log must be element-aligned", kFn);
-
-    const Span out{state_out, n_s, "state_out"};
-    const Span ins[] = {{delta_log, n_d, "delta_log"}, {k_log, n_k, "k_log"}, {g_log, n_g, "g_log"},
-                        {state_in, n_s, "state_in"}, {mask, mask ? n_m : 0, "mask"}};
-    for (const Span& i : ins) {
-        if (i.p == state_in && out.p == state_in) continue;                   // exact in-place state
-        if (overlaps(out, i)) return fail(GDN_ERR_ALIAS, "%s: state_out overlaps %s", kFn, i.name);
-    }
-
-    return launch_status(gdn::launch_replay(a, static_cast<hipStream_t>(stream)), kFn);
-}
-
 int gqa_expand(const void* src, void* dst, uint32_t seq, uint32_t hg, uint32_t h, uint32_t k,
                int dtype, int gqa_map, void* stream) {
     static const char* kFn = "gqa_expand";
     if (!valid_dtype(dtype)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown dtype %d", kFn, dtype);
     if (!valid_map(gqa_map)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown gqa_map %d", kFn, gqa_map);
-    if (!src || !dst) return fail(GDN_ERR_NULL, "%s: src and dst must be non-NULL", kFn);
+    if (!src || !dst) return fail(GDN_ERR_NULL, "%s: src or dst is NULL", kFn);
     if (seq == 0 || hg == 0 || h == 0 || k == 0)
-        return fail(GDN_ERR_ZERO_DIM, "%s: seq, hg, h, k must all be > 0", kFn);
-    if (h % hg != 0) return fail(GDN_ERR_GQA_RATIO, "%s: h (%u) must be a multiple of hg (%u)", kFn, h, hg);
+        return fail(GDN_ERR_ZERO_DIM, "%s: zero-sized dimension in seq=%u hg=%u h=%u k=%u", kFn, seq, hg, h, k);
+    if (h % hg != 0)
+        return fail(GDN_ERR_GQA_RATIO, "%s: %u destination heads cannot be spread evenly over %u source heads",
+                    kFn, h, hg);
     const uint64_t e = io_bytes(dtype);
     uint64_t n_src, n_dst;
     if (!mul_u64(&n_src, {seq, hg, k, e}) || !mul_u64(&n_dst, {seq, h, k, e}) || n_dst > kMaxBytes)

@@ -9,6 +9,18 @@
 
 namespace gdn {
 
+// Row blocking of a head: a workgroup of `threads` threads covers
+// rows_per_thread * threads / 16 consecutive value rows of one head.
+// rows_per_thread == 0 stands for "not forced" in the argument structs.
+struct RowTiling {
+    int rows_per_thread;
+    int threads;
+    int rows() const { return rows_per_thread * threads / 16; }
+};
+
+// Which kernel folds a replay (same values as gdn_replay_fold in gdn.h).
+enum ReplayFold : int { kFoldAuto = 0, kFoldValu = 1, kFoldMatrix = 2 };
+
 struct RecordArgs {
     const void* q; const void* k; const void* v; const void* g; const void* beta;
     const float* state_in; const uint32_t* mask;
@@ -17,6 +29,7 @@ struct RecordArgs {
     uint32_t B, T, Hk, Hv, Dk, Dv;
     int io;       // IoType
     int map;      // 0 block, 1 tiled
+    RowTiling forced;                     // {0, 0}: the launcher picks
 };
 
 struct ReplayArgs {
@@ -24,6 +37,9 @@ struct ReplayArgs {
     const float* state_in; const uint32_t* mask; float* state_out;
     uint32_t B, T_log, Hv, Dk, Dv, steps;   // steps = min(accepted, T_log)
     int io;
+    RowTiling forced;                     // VALU folds; {0, 0}: the launcher picks
+    int fold;                             // ReplayFold
+    uint32_t matrix_waves;                // matrix-core fold: 2 or 4 waves; 0: the launcher picks
 };
 
 struct ExpandArgs {
@@ -31,14 +47,6 @@ struct ExpandArgs {
     uint32_t seq, hg, h, k;
     uint32_t elem_bytes;
     int map;
-};
-
-// Row blocking of a head: a workgroup of `threads` threads covers
-// rows_per_thread * threads / 16 consecutive value rows of one head.
-struct RowTiling {
-    int rows_per_thread;
-    int threads;
-    int rows() const { return rows_per_thread * threads / 16; }
 };
 
 // Does a kernel exist for this key width?
@@ -61,6 +69,10 @@ hipError_t launch_rms_norm(const RmsNormArgs& a, hipStream_t stream);
 // Folds of at least this many positions of a 16-bit tape run as matrix
 // products on the matrix cores (gdn_replay_mfma.hip).
 inline constexpr uint32_t kReplayMfmaFromSteps = 16;
+// Whether the matrix-core fold can take this replay at all (16-bit tape,
+// whole 64-row workgroups, grid within one launch), and whether the launcher
+// sends it there (that, and the fold chosen or the length rule above).
+bool replay_mfma_possible(const ReplayArgs& a);
 bool replay_mfma_applies(const ReplayArgs& a);
 hipError_t launch_replay_mfma(const ReplayArgs& a, hipStream_t stream);
 hipError_t launch_expand(const ExpandArgs& a, hipStream_t stream);
@@ -113,10 +125,11 @@ inline RowTiling pick_tiling(uint64_t heads, uint32_t Dk, uint32_t Dv, uint64_t 
 // bounds that kernel's LDS below 64 KiB.
 inline constexpr int kStagedMaxRows = 64;
 
-// Optional tiling forced through an environment variable ("rows_per_thread,threads"),
-// used for launch-shape sweeps; ignored unless it names a known tiling that fits
-// and covers at most max_rows rows.
-bool tiling_override(const char* env_name, uint32_t Dk, uint32_t Dv, uint32_t max_rows,
-                     RowTiling* out);
+// Whether (rows_per_thread, threads) is one of kTilings.
+inline bool tiling_known(int rows_per_thread, int threads) {
+    for (int i = 0; i < kNumTilings; ++i)
+        if (kTilings[i].rows_per_thread == rows_per_thread && kTilings[i].threads == threads) return true;
+    return false;
+}
 
 }  // namespace gdn

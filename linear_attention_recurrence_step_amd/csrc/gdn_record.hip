@@ -36,8 +36,6 @@
 #include "gdn_internal.hpp"
 
 #include <atomic>
-#include <cstdlib>
-#include <cstdio>
 
 namespace gdn {
 namespace {
@@ -539,26 +537,8 @@ bool dk_supported(uint32_t Dk) {
     return Dk == 32 || Dk == 64 || Dk == 128 || Dk == 192 || Dk == 256;
 }
 
-bool tiling_override(const char* env_name, uint32_t Dk, uint32_t Dv, uint32_t max_rows,
-                     RowTiling* out) {
-    const char* s = std::getenv(env_name);
-    if (s == nullptr || *s == '\0') return false;
-    int rpt = 0, nt = 0;
-    if (std::sscanf(s, "%d,%d", &rpt, &nt) != 2) return false;
-    for (int i = 0; i < kNumTilings; ++i) {
-        if (kTilings[i].rows_per_thread == rpt && kTilings[i].threads == nt &&
-            tiling_fits(kTilings[i], Dk, Dv) && static_cast<uint32_t>(kTilings[i].rows()) <= max_rows) {
-            *out = kTilings[i];
-            return true;
-        }
-    }
-    return false;
-}
-
 RowTiling record_tiling(const RecordArgs& a) {
-    RowTiling t;
-    const uint32_t max_rows = a.T == 1 ? 1024u : static_cast<uint32_t>(kStagedMaxRows);
-    if (tiling_override("GDN_RECORD_TILING", a.Dk, a.Dv, max_rows, &t)) return t;
+    if (a.forced.rows_per_thread != 0) return a.forced;      // checked by the caller
     // Up to 16 steps (decode, speculative decode): two rows per thread over
     // 256-thread groups measured fastest while that still gives 1024 groups
     // (2% faster than one row per thread at a 512 MiB decode step, 20% at an

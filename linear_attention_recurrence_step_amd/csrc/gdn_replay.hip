@@ -383,8 +383,7 @@ hipError_t launch_io(const ReplayArgs& a, const RowTiling& t, hipStream_t stream
 }  // namespace
 
 RowTiling replay_tiling(const ReplayArgs& a) {
-    RowTiling t;
-    if (tiling_override("GDN_REPLAY_TILING", a.Dk, a.Dv, 1024u, &t)) return t;
+    if (a.forced.rows_per_thread != 0) return a.forced;      // checked by the caller
     // One or two taken positions: a pure state stream, fastest with one row
     // per thread.  Longer folds share each position's tape data over more
     // rows per workgroup; four rows per thread measured fastest (eight cost

@@ -20,19 +20,20 @@
 // MFMAs), keeping about 22 significant bits for fp16 tapes and 16 for bf16.
 // With every taken gate of the chunk in [0, 1], |w_t| <= 1, so w_t delta_t
 // stays within the tape dtype's range; a chunk with any other taken gate (or a
-// NaN gate) runs the exact sequential update instead, one position per MFMA.
-// Untaken positions and positions past `accepted` are never loaded: their
-// rows of A and B are zeros, so a NaN in an untaken slot cannot reach S.
+// NaN gate) runs the exact sequential update instead, one position per MFMA,
+// on the state itself (see the fold below).
+// Positions past `accepted` are never loaded.  Masked positions below it are
+// loaded with the rest of their chunk (unconditional loads keep the
+// compiler's memory waits exact) but their rows of A and B are zeroed before
+// they reach an operand, so a NaN in an untaken slot cannot reach S.
 //
-// Mapping.  A workgroup of NW waves takes 16*TPW*NW consecutive value rows of
-// one head; each wave owns TPW 16-row tiles across all Dk/16 column tiles
-// (4*TPW*Dk/16 fp32 accumulators per lane).  A chunk of 16 positions of k_log
-// and delta_log is staged through LDS transposed ([column][position]), so each
-// MFMA operand fragment (four consecutive positions) is one 8-byte LDS read.
+// Mapping.  A workgroup of NW waves takes 16*NW consecutive value rows of one
+// head; each wave owns 16 rows across all Dk/16 column tiles (4*Dk/16 fp32
+// accumulators per lane).  A chunk of 32 positions of k_log and delta_log is
+// staged through LDS transposed ([column][position pair]), so each MFMA
+// operand fragment (four consecutive positions) is one 8-byte LDS read.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
-
-#include <cstdlib>
 
 namespace gdn {
 namespace {
@@ -203,17 +204,20 @@ __global__ __launch_bounds__(64 * NW, DK <= 128 ? 4 : 2) void gdn_replay_mfma_ke
     // The fold is accumulated apart from the state, U = sum over chunks of
     // (later gammas) * (chunk's w-weighted products), starting from zero, and
     // S = Gamma * S0 + U at the end (Gamma = product of every taken gate).  So
-    // the state loads, issued after the first chunk's, stay in flight while
-    // the tape is folded.  acc[i] is the 16x16 tile of U^T for columns 16i..
-    // and the wave's 16 rows; lane l holds columns 16i + 4*lg + 0..3 of row lr.
-    // The fold is accumulated apart from the state, U = sum over chunks of
-    // (later gammas) * (chunk's w-weighted products), starting from zero, and
-    // S = Gamma * S0 + U at the end (Gamma = product of every taken gate).  So
     // the state loads (issued with a single chunk, or while the last chunk of
     // a longer fold is folded) are in flight during the fold, and they never
     // hold registers at the same time as a prefetched chunk.  acc[i] is the
     // 16x16 tile of U^T for columns 16i.. and the wave's 16 rows; lane l holds
     // columns 16i + 4*lg + 0..3 of row lr.
+    //
+    // Gamma and U apart are only safe while every taken gate lies in [0, 1]
+    // (Gamma then stays in [0, 1]).  The first chunk with any other gate
+    // first folds the snapshot in, acc = Gamma * S0 + U, read straight from
+    // memory in the accumulator layout, and from then on the accumulators
+    // hold the state itself (`absorbed`): a long run of gates above 1 grows
+    // the state step by step as the sequential fold does, instead of
+    // overflowing a separate Gamma, and an infinite gate meets the state,
+    // not an accumulator of zeros.
     f32x4 sreg[NI];
     auto load_state = [&]() {
 #pragma unroll
@@ -224,6 +228,7 @@ __global__ __launch_bounds__(64 * NW, DK <= 128 ? 4 : 2) void gdn_replay_mfma_ke
 #pragma unroll
     for (int i = 0; i < NI; ++i) acc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
     float Gamma = 1.f;
+    bool absorbed = false;                                    // acc holds S itself (uniform)
 
     auto chunk = [&](uint32_t t0, auto prefetch) {
         const int valid = static_cast<int>(steps - t0 < kPos ? steps - t0 : kPos);
@@ -285,6 +290,16 @@ __global__ __launch_bounds__(64 * NW, DK <= 128 ? 4 : 2) void gdn_replay_mfma_ke
         // every other position's operand lanes zeroed), which is the exact
         // sequential update: each product then rounds like fma(k, delta, S * g).
         const bool whole = misc[1] != 0.f;
+        if (!whole && !absorbed) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const f32x4 s0 = *reinterpret_cast<const f32x4*>(sin + lr * DK + 16 * i + 4 * lg);
+                acc[i] = f32x4v{fmaf(Gamma, s0.x, acc[i][0]), fmaf(Gamma, s0.y, acc[i][1]),
+                                fmaf(Gamma, s0.z, acc[i][2]), fmaf(Gamma, s0.w, acc[i][3])};
+            }
+            Gamma = 1.f;
+            absorbed = true;
+        }
         int tt = 0;
         for (;;) {
             float gamma = misc[0];
@@ -345,6 +360,7 @@ __global__ __launch_bounds__(64 * NW, DK <= 128 ? 4 : 2) void gdn_replay_mfma_ke
 
 
     // U: accumulator layout -> LDS -> row layout; S = Gamma * S0 + U -> HBM
+    // (or S = acc once the snapshot has been folded in)
 #pragma unroll
     for (int i = 0; i < NI; ++i)
         *reinterpret_cast<f32x4*>(frag_lds(i)) = f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
@@ -352,8 +368,9 @@ __global__ __launch_bounds__(64 * NW, DK <= 128 ? 4 : 2) void gdn_replay_mfma_ke
 #pragma unroll
     for (int u = 0; u < NI; ++u) {
         const f32x4 uu = *reinterpret_cast<const f32x4*>(piece_lds(u));
-        const f32x4 r = {fmaf(Gamma, sreg[u].x, uu.x), fmaf(Gamma, sreg[u].y, uu.y),
-                         fmaf(Gamma, sreg[u].z, uu.z), fmaf(Gamma, sreg[u].w, uu.w)};
+        const f32x4 r = absorbed ? uu
+                                 : f32x4{fmaf(Gamma, sreg[u].x, uu.x), fmaf(Gamma, sreg[u].y, uu.y),
+                                         fmaf(Gamma, sreg[u].z, uu.z), fmaf(Gamma, sreg[u].w, uu.w)};
         __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(sout + (l + 64 * u) * 4));
     }
 }
@@ -374,12 +391,10 @@ hipError_t launch_nw(const ReplayArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Four waves (64 value rows) per workgroup; GDN_REPLAY_MFMA_WAVES=2 selects
-// two (launch-shape sweeps).
+// Four waves (64 value rows) per workgroup, unless the caller chose two.
 template <int IO, int DK>
 hipError_t launch_dk(const ReplayArgs& a, hipStream_t stream) {
-    const char* e = std::getenv("GDN_REPLAY_MFMA_WAVES");
-    if (e != nullptr && std::strtoul(e, nullptr, 10) == 2) return launch_nw<IO, DK, 2>(a, stream);
+    if (a.matrix_waves == 2) return launch_nw<IO, DK, 2>(a, stream);
     return launch_nw<IO, DK, 4>(a, stream);
 }
 
@@ -397,18 +412,16 @@ hipError_t launch_io(const ReplayArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-bool replay_mfma_applies(const ReplayArgs& a) {
+bool replay_mfma_possible(const ReplayArgs& a) {
     if (a.io != kF16 && a.io != kBF16) return false;
-    const char* e = std::getenv("GDN_REPLAY_MFMA");
-    uint32_t from = kReplayMfmaFromSteps;
-    if (e != nullptr && *e != '\0') {
-        const long v = std::strtol(e, nullptr, 10);
-        if (v <= 0) return false;
-        from = static_cast<uint32_t>(v);
-    }
-    if (a.steps < from || a.Dv % 64 != 0) return false;       // whole 64-row workgroups
+    if (a.Dv % 64 != 0) return false;                         // whole 64-row workgroups
     // four work-items per state row (64 per 16-row wave), 2^32 - 1 at most per launch
     return static_cast<uint64_t>(a.B) * a.Hv * a.Dv * 4 <= 0xffffffffull;
+}
+
+bool replay_mfma_applies(const ReplayArgs& a) {
+    if (a.fold == kFoldValu || !replay_mfma_possible(a)) return false;
+    return a.fold == kFoldMatrix || a.steps >= kReplayMfmaFromSteps;
 }
 
 hipError_t launch_replay_mfma(const ReplayArgs& a, hipStream_t stream) {

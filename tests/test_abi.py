@@ -28,7 +28,7 @@ def _declared_functions():
 def test_header_declares_the_three_entry_points():
     fns = _declared_functions()
     for name in ("gdn_record", "gdn_replay", "gqa_expand", "gdn_prefill", "gdn_prefill_workspace_size",
-                 "rms_norm_bf16", "gdn_strerror",
+                 "rms_norm_bf16", "gdn_record_debug", "gdn_replay_debug", "gdn_strerror",
                  "gdn_last_error", "gdn_abi_version"):
         assert name in fns, fns
 
@@ -53,6 +53,11 @@ lib.rms_norm_bf16.argtypes = [vp, vp, vp, u32, u32, ctypes.c_float, vp]
 lib.gdn_prefill.argtypes = [vp] * 11 + [ctypes.c_uint64] + [u32] * 6 + [i32, i32, vp]
 lib.gdn_prefill_workspace_size.argtypes = [u32] * 3
 lib.gdn_prefill_workspace_size.restype = ctypes.c_uint64
+class Choice(ctypes.Structure):
+    _fields_ = [("rows_per_thread", ctypes.c_uint32), ("threads", ctypes.c_uint32),
+                ("replay_fold", ctypes.c_int32), ("matrix_waves", ctypes.c_uint32)]
+lib.gdn_record_debug.argtypes = [ctypes.POINTER(Choice)] + lib.gdn_record.argtypes
+lib.gdn_replay_debug.argtypes = [ctypes.POINTER(Choice)] + lib.gdn_replay.argtypes
 lib.gdn_strerror.restype = ctypes.c_char_p
 lib.gdn_last_error.restype = ctypes.c_char_p
 cases = json.loads(sys.argv[2])
@@ -60,6 +65,9 @@ out = []
 for c in cases:
     fn = getattr(lib, c["fn"])
     args = [None if a is None else a for a in c["args"]]
+    if c["fn"].endswith("_debug"):
+        ch = c["args"][0]
+        args[0] = None if ch is None else ctypes.byref(Choice(*ch))
     rc = fn(*args)
     out.append({"id": c["id"], "rc": rc, "msg": lib.gdn_last_error().decode()})
 out.append({"id": "strerror", "rc": 0,
@@ -125,6 +133,16 @@ def pre(**kw):
     return [a["q"], a["k"], a["v"], a["g"], a["beta"], a["s_in"], a["mask"], a["y"], a["s_out"],
             a["dl"], a["ws"], a["wsb"], a["B"], a["T"], a["Hk"], a["Hv"], a["Dk"], a["Dv"], a["io"],
             a["map"], None]
+
+
+# gdn_record_debug / gdn_replay_debug: the launch choice first, as
+# [rows_per_thread, threads, replay_fold, matrix_waves] (None: NULL)
+def recd(choice, **kw):
+    return [choice] + rec(**kw)
+
+
+def repd(choice, **kw):
+    return [choice] + rep(**kw)
 
 
 NULL, ZERO, RATIO, SHAPE, OVER, ALIAS, ENUM, LAUNCH, ALIGN = -1, -2, -3, -4, -5, -6, -7, -8, -9
@@ -202,6 +220,23 @@ CASES = [
     ("pre_y_over_v", "gdn_prefill", pre(y=P(2, 512)), ALIAS),
     ("pre_state_partial_alias", "gdn_prefill", pre(s_out=P(5, 4096)), ALIAS),
     ("pre_grid_overflow", "gdn_prefill", pre(B=1 << 16, T=1 << 15, Hk=1, Hv=1 << 8, Dv=16), OVER),
+    ("recd_unknown_tiling", "gdn_record_debug", recd([3, 256, 0, 0]), ENUM),
+    ("recd_half_tiling", "gdn_record_debug", recd([2, 0, 0, 0]), ENUM),
+    ("recd_huge_tiling", "gdn_record_debug", recd([1 << 31, 256, 0, 0]), ENUM),
+    ("recd_replay_fold_on_record", "gdn_record_debug", recd([0, 0, 1, 0]), ENUM),
+    ("recd_waves_on_record", "gdn_record_debug", recd([0, 0, 0, 4]), ENUM),
+    # 128 rows per workgroup: fine for one step, too many for the staged kernel
+    ("recd_staged_too_many_rows", "gdn_record_debug", recd([8, 256, 0, 0], T=3), SHAPE),
+    ("recd_rows_not_dividing_dv", "gdn_record_debug", recd([2, 256, 0, 0], T=1, Dv=48), SHAPE),
+    ("recd_too_many_state_values", "gdn_record_debug", recd([8, 256, 0, 0], T=1, Dk=192), SHAPE),
+    ("recd_null_choice_still_validates", "gdn_record_debug", recd(None, q=None), NULL),
+    ("repd_bad_fold", "gdn_replay_debug", repd([0, 0, 3, 0]), ENUM),
+    ("repd_bad_waves", "gdn_replay_debug", repd([0, 0, 2, 3]), ENUM),
+    ("repd_matrix_on_f32", "gdn_replay_debug", repd([0, 0, 2, 0], io=0), SHAPE),
+    ("repd_matrix_dv48", "gdn_replay_debug", repd([0, 0, 2, 0], Dv=48), SHAPE),
+    ("repd_tiling_not_fitting", "gdn_replay_debug", repd([8, 256, 1, 0], Dv=64), SHAPE),
+    ("repd_unknown_tiling", "gdn_replay_debug", repd([4, 64, 1, 0]), ENUM),
+    ("repd_null_state_out", "gdn_replay_debug", repd([0, 0, 1, 0], s_out=None), NULL),
     ("exp_bad_dtype", "gqa_expand", exp(dt=7), ENUM),
     ("exp_bad_map", "gqa_expand", exp(map=-1), ENUM),
     ("exp_null_dst", "gqa_expand", exp(dst=None), NULL),
@@ -250,7 +285,7 @@ def test_python_binding_names_match_the_abi():
     import linear_attention_recurrence_step_amd as gdn
     from linear_attention_recurrence_step_amd import _native
     for name in ("gdn_record", "gdn_replay", "gqa_expand", "gdn_prefill", "gdn_prefill_workspace_size",
-                 "rms_norm_bf16"):
+                 "rms_norm_bf16", "gdn_record_debug", "gdn_replay_debug"):
         assert callable(getattr(gdn, name))
         assert hasattr(_native.lib, name)
     assert _native.lib.gdn_abi_version() == _native.ABI_VERSION
@@ -276,3 +311,12 @@ def test_python_binding_rejects_host_tensors_before_the_library():
         gdn.gqa_expand(torch.zeros(2, 1, 32), 2)
     with pytest.raises(ValueError, match="HIP device"):
         gdn.rms_norm_bf16(torch.zeros(2, 32), torch.zeros(32, dtype=torch.bfloat16), 1e-6)
+
+
+def test_library_reads_no_environment():
+    """What a call runs depends on its arguments only: the library's sources
+    read no environment variable."""
+    import glob
+    for path in glob.glob(os.path.join(ROOT, "linear_attention_recurrence_step_amd", "csrc", "*")):
+        text = open(path).read()
+        assert "getenv" not in text and "environ" not in text, path

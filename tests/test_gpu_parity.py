@@ -265,8 +265,20 @@ MFMA_REPLAY = [
 ]
 
 
+def _replay_fold(tape, accepted, fold, state_out=None, waves=0):
+    """gdn_replay_debug with the fold forced ("valu" or "matrix")."""
+    d = to_dev(tape)
+    so = None
+    if state_out == "in_place":
+        so = d["state_in"]
+    s = gdn.gdn_replay_debug({"fold": fold, "matrix_waves": waves}, d["delta_log"], d["k_log"],
+                             d["g_log"], d["state_in"], d["mask"], accepted, state_out=so)
+    torch.cuda.synchronize()
+    return s
+
+
 @pytest.mark.parametrize("case", MFMA_REPLAY, ids=lambda c: "B%d_T%d_Hv%d_Dk%d_Dv%d_%s_%s" % c[:7])
-def test_replay_long_fold_on_matrix_cores(case, monkeypatch):
+def test_replay_long_fold_on_matrix_cores(case):
     """Folds of 16+ positions of a 16-bit tape run as MFMA products over
     chunks of positions; against the oracle at the I/O tolerance, untaken
     slots NaN-poisoned, and against the VALU fold of the same tape."""
@@ -274,14 +286,111 @@ def test_replay_long_fold_on_matrix_cores(case, monkeypatch):
     tape = gi.tape_inputs(B, T, Hv, Dk, Dv, io, seed=111 + Dk + T, mask=mask)
     for a in accepted:
         pt = gi.poison_untaken(tape, a)
-        monkeypatch.delenv("GDN_REPLAY_MFMA", raising=False)
-        s_mfma = _check_replay(pt, a, "matrix-core fold %s" % (case[:7],))
-        monkeypatch.setenv("GDN_REPLAY_MFMA", "0")
+        s_auto = _check_replay(pt, a, "matrix-core fold %s" % (case[:7],))
         note("VALU fold of the same tape, accepted=%d" % a)
-        d = to_dev(pt)
-        s_valu = gdn.gdn_replay(d["delta_log"], d["k_log"], d["g_log"], d["state_in"], d["mask"], a)
-        torch.cuda.synchronize()
-        assert_close(s_mfma, f64(s_valu), torch.float32, "matrix-core vs VALU fold")
+        s_valu = _replay_fold(pt, a, "valu")
+        assert_close(s_auto, f64(s_valu), torch.float32, "matrix-core vs VALU fold")
+        if Dv % 64 == 0:
+            note("forced matrix-core fold, accepted=%d" % a)
+            s_mat = _replay_fold(pt, a, "matrix")
+            assert torch.equal(_bit_view(s_auto), _bit_view(s_mat)), "automatic fold is not the matrix one"
+
+
+def _gate_case(B, T, Hv, Dk, Dv, io, seed, gates):
+    """A NaN-poisoned Bernoulli tape whose taken gates are overwritten at
+    given (t0, t1, value) ranges (all heads)."""
+    tape = gi.tape_inputs(B, T, Hv, Dk, Dv, io, seed=seed, mask="bernoulli", mask_p=0.8)
+    g = tape["g_log"].float().clone()
+    for t0, t1, val in gates:
+        g[:, t0:t1] = val
+    tape["g_log"] = g.to(gi.IO_DTYPES[io])
+    return tape
+
+
+# Chunks of 32 positions whose taken gates leave [0, 1] (or are NaN or
+# infinite) run the matrix-core fold's per-position path on the state itself;
+# the neighbouring chunks keep the one-pass contraction.
+GATE_CASES = [
+    # name, Dv, io, T, gate ranges (t0, t1, value)
+    ("above_one_then_whole", 64, "f16", 48, [(5, 6, 1.5), (9, 10, 1.9), (20, 21, -0.5)]),
+    ("whole_then_above_one", 128, "bf16", 70, [(40, 41, 1.5), (50, 51, 1.9), (60, 61, -0.5)]),
+    ("negative_gates", 128, "f16", 40, [(0, 3, -0.5), (33, 34, -1.0)]),
+    ("run_of_four_64", 64, "f16", 64, [(0, 64, 4.0)]),
+    ("run_of_four_bf16", 128, "bf16", 64, [(0, 64, 4.0)]),
+    ("large_then_tiny", 64, "bf16", 96, [(0, 30, 3.0), (64, 96, 1e-3)]),
+]
+
+
+@pytest.mark.parametrize("case", GATE_CASES, ids=[c[0] for c in GATE_CASES])
+def test_matrix_core_fold_with_gates_outside_unit_interval(case):
+    """Taken gates of 1.5, 1.9, -0.5, runs of 3 and 4 (the state grows by 2^128
+    over 64 positions without overflowing) in some chunks but not others:
+    the matrix-core fold against the oracle and against the VALU fold."""
+    name, Dv, io, T, gates = case
+    B, Hv, Dk = 2, 2, 128
+    tape = _gate_case(B, T, Hv, Dk, Dv, io, seed=131 + T, gates=gates)
+    if name.startswith("run_of_four"):
+        tape["mask"] = None                         # every one of the 64 gates is taken
+    for a in sorted({T, T - 7, 40}):
+        pt = gi.poison_untaken(tape, a)
+        note("matrix-core fold with gates outside [0, 1]: %s accepted=%d" % (name, a))
+        s_mat = _replay_fold(pt, a, "matrix")
+        rs = oracle.gdn_replay(pt["delta_log"], pt["k_log"], pt["g_log"], pt["state_in"], pt["mask"], a)
+        assert np.isfinite(rs).all()
+        assert_close(s_mat, rs, tape["delta_log"].dtype, "%s matrix fold a=%d" % (name, a))
+        s_valu = _replay_fold(pt, a, "valu")
+        assert_close(s_mat, f64(s_valu), tape["delta_log"].dtype, "%s matrix vs VALU a=%d" % (name, a))
+
+
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+@pytest.mark.parametrize("bad", ["nan", "inf", "-inf"])
+def test_matrix_core_fold_with_non_finite_gates(io, bad):
+    """A NaN or infinite gate at one taken position: the oracle's state holds
+    NaN or infinities there on, and the matrix-core fold must put NaN exactly
+    where the oracle does (other values within tolerance)."""
+    B, T, Hv, Dk, Dv = 2, 48, 2, 64, 64
+    val = {"nan": float("nan"), "inf": float("inf"), "-inf": float("-inf")}[bad]
+    tape = gi.tape_inputs(B, T, Hv, Dk, Dv, io, seed=141, mask="none")
+    g = tape["g_log"].float().clone()
+    g[0, 37, 1] = val                               # second chunk, batch row 0, head 1 only
+    tape["g_log"] = g.to(gi.IO_DTYPES[io])
+    for a in (T, 30):
+        note("matrix-core fold with a %s gate, %s, accepted=%d" % (bad, io, a))
+        s_mat = _replay_fold(tape, a, "matrix")
+        rs = oracle.gdn_replay(tape["delta_log"], tape["k_log"], tape["g_log"], tape["state_in"],
+                               None, a)
+        got = f64(s_mat)
+        assert np.array_equal(np.isnan(got), np.isnan(rs)), "NaN positions differ"
+        assert np.array_equal(np.isinf(got), np.isinf(rs)), "infinite positions differ"
+        fin = np.isfinite(rs)
+        assert_close(got[fin], rs[fin], tape["delta_log"].dtype, "%s gate, finite part" % bad)
+        if a == 30:                                 # the bad gate lies past `accepted`
+            assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("gates", ["unit", "outside"])
+@pytest.mark.parametrize("waves", [2, 4])
+def test_matrix_core_fold_in_place(gates, waves):
+    """state_out == state_in on the matrix-core fold (both workgroup shapes),
+    with whole-chunk contractions and with the per-position path, equals the
+    out-of-place result bit for bit."""
+    B, T, Hv, Dk, Dv = 3, 45, 2, 128, 128
+    if gates == "unit":
+        tape = gi.tape_inputs(B, T, Hv, Dk, Dv, "bf16", seed=151, mask="bernoulli")
+    else:
+        tape = _gate_case(B, T, Hv, Dk, Dv, "bf16", 152, [(3, 4, 1.7), (35, 36, -0.25)])
+    note("matrix-core fold out of place, %s gates, %d waves" % (gates, waves))
+    ref = _replay_fold(tape, T, "matrix", waves=waves)
+    d = to_dev(tape)
+    st = d["state_in"].clone()
+    note("matrix-core fold in place, %s gates, %d waves" % (gates, waves))
+    gdn.gdn_replay_debug({"fold": "matrix", "matrix_waves": waves}, d["delta_log"], d["k_log"],
+                         d["g_log"], st, d["mask"], T, state_out=st)
+    torch.cuda.synchronize()
+    assert torch.equal(_bit_view(st), _bit_view(ref))
+    rs = oracle.gdn_replay(tape["delta_log"], tape["k_log"], tape["g_log"], tape["state_in"],
+                           tape["mask"], T)
+    assert_close(st, rs, torch.bfloat16, "in-place matrix fold")
 
 
 @pytest.mark.parametrize("case", [(3, 5, 2, 32, 16, "f32"), (2, 6, 3, 64, 48, "bf16"),
@@ -409,27 +518,67 @@ def test_batch_permutation_permutes_outputs_bitwise():
     assert torch.equal(_bit_view(r_a[pd]), _bit_view(r_b))
 
 
-@pytest.mark.parametrize("T", [3, 12, 40])
-def test_every_tiling_gives_identical_bits(monkeypatch, T):
+TILINGS = [(8, 256), (4, 256), (2, 256), (1, 256), (1, 64)]
+
+
+def _record_tiled(inp, gqa_map, tiling):
+    d = to_dev(inp)
+    io = d["q"].dtype
+    y = torch.full(d["v"].shape, Y_SENTINEL, dtype=io, device=dev())
+    dl = torch.full(d["v"].shape, D_SENTINEL, dtype=io, device=dev())
+    out = gdn.gdn_record_debug({"tiling": tiling}, d["q"], d["k"], d["v"], d["g"], d["beta"],
+                               d["state_in"], d["mask"], gqa_map=gqa_map, y=y, delta_log=dl)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("T", [1, 3, 12, 40])
+def test_every_tiling_gives_identical_bits(T):
     """Row tilings (and with them the staged kernel's chunk lengths: one row
     per thread over few heads takes 64-step chunks, more rows per thread 32)
-    change no bit of any output."""
+    change no bit of any output; the first tiling's outputs also match the
+    oracle."""
     inp = gi.record_inputs(2, T, 2, 4, 128, 128, "bf16", seed=51, mask="bernoulli")
     tape = gi.tape_inputs(2, 3, 4, 128, 128, "bf16", seed=52)
+    d = to_dev(tape)
     ref = None
-    for til in ("8,256", "4,256", "2,256", "1,256", "1,64"):
-        monkeypatch.setenv("GDN_RECORD_TILING", til)
-        monkeypatch.setenv("GDN_REPLAY_TILING", til)
-        note("tiling %s" % til)
-        out = _record_gpu(inp, "tiled")
-        d = to_dev(tape)
-        rs = gdn.gdn_replay(d["delta_log"], d["k_log"], d["g_log"], d["state_in"], d["mask"], 2)
+    for til in TILINGS:
+        if T > 1 and til[0] * til[1] // 16 > 64:       # the staged record takes at most 64 rows
+            continue
+        note("tiling %s T=%d" % (til, T))
+        out = _record_tiled(inp, "tiled", til)
+        rs = gdn.gdn_replay_debug({"tiling": til, "fold": "valu"}, d["delta_log"], d["k_log"],
+                                  d["g_log"], d["state_in"], d["mask"], 2)
         torch.cuda.synchronize()
         cur = [t.cpu() for t in out] + [rs.cpu()]
         if ref is None:
             ref = cur
+            ry, rs_, rd = oracle.gdn_record(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                            inp["state_in"], inp["mask"], gqa_map="tiled")
+            assert_close(cur[1], rs_, torch.bfloat16, "tiling %s state" % (til,))
         else:
             assert all(torch.equal(a, b) for a, b in zip(ref, cur)), til
+
+
+def test_launch_choice_none_is_the_plain_call():
+    """gdn_record_debug / gdn_replay_debug with nothing forced give the plain
+    calls' bits."""
+    inp = gi.record_inputs(2, 5, 2, 4, 128, 128, "bf16", seed=53, mask="bernoulli")
+    tape = gi.tape_inputs(2, 20, 4, 128, 128, "f16", seed=54)
+    d, t = to_dev(inp), to_dev(tape)
+    note("launch choice {} against the plain calls")
+    # masked positions of y and delta_log are never written: start both from sentinels
+    outs = [dict(y=torch.full(d["v"].shape, Y_SENTINEL, dtype=d["v"].dtype, device=dev()),
+                 delta_log=torch.full(d["v"].shape, D_SENTINEL, dtype=d["v"].dtype, device=dev()))
+            for _ in range(2)]
+    a = gdn.gdn_record(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"], d["mask"], **outs[0])
+    b = gdn.gdn_record_debug({}, d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"], d["mask"],
+                             **outs[1])
+    r1 = gdn.gdn_replay(t["delta_log"], t["k_log"], t["g_log"], t["state_in"], t["mask"], 18)
+    r2 = gdn.gdn_replay_debug(None, t["delta_log"], t["k_log"], t["g_log"], t["state_in"], t["mask"], 18)
+    torch.cuda.synchronize()
+    assert all(torch.equal(_bit_view(x), _bit_view(z)) for x, z in zip(a, b))
+    assert torch.equal(_bit_view(r1), _bit_view(r2))
 
 
 def test_in_place_state_and_tapeless_step():
@@ -470,7 +619,7 @@ def _bits(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int32 if t.element_size() == 4 else torch.int16).numpy()
 
 
-def _record_capture(inp, gqa_map, want_k=True, want_g=True):
+def _record_capture(inp, gqa_map, want_k=True, want_g=True, tiling=None):
     d = to_dev(inp)
     B, T, Hk, Dk = d["k"].shape
     Hv = d["v"].shape[2]
@@ -479,8 +628,9 @@ def _record_capture(inp, gqa_map, want_k=True, want_g=True):
     dl = torch.full(d["v"].shape, D_SENTINEL, dtype=io, device=dev())
     kl = torch.full((B, T, Hv, Dk), K_SENTINEL, dtype=io, device=dev()) if want_k else None
     gl = torch.full((B, T, Hv), G_SENTINEL, dtype=io, device=dev()) if want_g else None
-    y, s, dl = gdn.gdn_record(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"], d["mask"],
-                              gqa_map=gqa_map, y=y, delta_log=dl, k_log=kl, g_log=gl)
+    y, s, dl = gdn.gdn_record_debug({"tiling": tiling} if tiling else None, d["q"], d["k"], d["v"],
+                                    d["g"], d["beta"], d["state_in"], d["mask"], gqa_map=gqa_map,
+                                    y=y, delta_log=dl, k_log=kl, g_log=gl)
     torch.cuda.synchronize()
     return y, s, dl, kl, gl
 
@@ -542,13 +692,15 @@ def test_record_captures_one_log_alone(want_k, want_g):
         assert kl is None and torch.equal(gl, ref[4])
 
 
-def test_capture_identical_under_every_tiling(monkeypatch):
-    inp = gi.record_inputs(2, 11, 2, 4, 128, 128, "bf16", seed=93, mask="bernoulli")
+@pytest.mark.parametrize("T", [1, 11])
+def test_capture_identical_under_every_tiling(T):
+    inp = gi.record_inputs(2, T, 2, 4, 128, 128, "bf16", seed=93, mask="bernoulli")
     ref = None
-    for til in ("8,256", "4,256", "2,256", "1,256", "1,64"):
-        monkeypatch.setenv("GDN_RECORD_TILING", til)
-        note("capture under tiling %s" % til)
-        cur = [t.cpu() for t in _record_capture(inp, "block")]
+    for til in TILINGS:
+        if T > 1 and til[0] * til[1] // 16 > 64:
+            continue
+        note("capture under tiling %s T=%d" % (til, T))
+        cur = [t.cpu() for t in _record_capture(inp, "block", tiling=til)]
         if ref is None:
             ref = cur
         else:
