@@ -252,147 +252,194 @@ class Step:
 
 # ------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(name: str, budget_s: float):
-    """Time the CPU oracle on a bounded sample of the workload: batch rows
-    (independent recurrences) processed by a pool of threads, one slice each."""
-    from concurrent.futures import ThreadPoolExecutor
+CPU_THREADS_MAX = 16
 
+
+def _host_threads(requested=None):
+    """(cores in this process's affinity mask, threads the oracle timing uses):
+    every core of the mask, at most CPU_THREADS_MAX, unless requested."""
+    aff = len(os.sched_getaffinity(0))
+    if requested:
+        return aff, max(1, int(requested))
+    return aff, max(1, min(aff, CPU_THREADS_MAX))
+
+
+def _timed_threads(work_lists, budget_s):
+    """Run each list of prepared oracle calls in its own thread, over and over
+    until the budget is spent; returns (bytes done, seconds).  A list is
+    [(callable, algorithmic bytes of one call), ...].  Only the oracle's C
+    calls run inside the loops (ctypes releases the GIL around them)."""
+    import threading
+    done = [0] * len(work_lists)
+    ends = [0.0] * len(work_lists)
+    start = threading.Barrier(len(work_lists) + 1)
+    holder = {}
+
+    def loop(i):
+        calls = work_lists[i]
+        for f, _ in calls:                       # one untimed pass
+            f()
+        start.wait()
+        deadline = holder["t0"] + budget_s
+        n = 0
+        while True:
+            for f, nb in calls:
+                f()
+                n += nb
+            if time.perf_counter() >= deadline:
+                break
+        done[i] = n
+        ends[i] = time.perf_counter()
+
+    threads = [threading.Thread(target=loop, args=(i,)) for i in range(len(work_lists))]
+    for t in threads:
+        t.start()
+    holder["t0"] = time.perf_counter()
+    start.wait()
+    for t in threads:
+        t.join()
+    return sum(done), max(ends) - holder["t0"]
+
+
+def _unit_calls(name, w, sl, e):
+    """Prepared oracle calls for one slice of the sample (dict of CPU tensors)
+    and their algorithmic bytes, in the order a step runs them."""
     import torch
-
-    import gdn_inputs as gi
     import oracle
+    calls = []
+    if name == "long_tape_replay":
+        nb = sl["delta_log"].shape[0]
+        for a in w.accepted:
+            f, _ = oracle.prepare_replay(sl["delta_log"], sl["k_log"], sl["g_log"], sl["state_in"],
+                                         sl["mask"], a)
+            taken = _active(sl["mask"], nb, w.T, a)
+            calls.append((f, replay_bytes(nb, w.T, w.Hv, w.Dk, w.Dv, e, a, taken, True)))
+        return calls
+    if name == "chunk_prefill":
+        heads = sl["v"].shape[2]
+        f, _ = oracle.prepare_record(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["state_in"],
+                                     None, gqa_map="block")
+        return [(f, record_bytes(1, w.T, heads, heads, w.Dk, w.Dv, e, w.T, False))]
+    nb = sl["q"].shape[0]
+    bits = torch.int32 if e == 4 else torch.int16
+    kbits = sl["k"].contiguous().view(bits).numpy().reshape(nb * w.T, w.Hk, w.Dk)
+    fx, k_log_bits = oracle.prepare_expand(kbits, w.Hv, w.gqa_map)
+    fx()
+    fr, (_, _, dlt) = oracle.prepare_record(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"],
+                                            sl["state_in"], sl["mask"], gqa_map=w.gqa_map)
+    fr()
+    # the replay's tape: the record's delta in the I/O dtype, the expanded keys, g
+    tape_d = torch.from_numpy(dlt).to(sl["q"].dtype)
+    k_log = torch.from_numpy(k_log_bits).view(sl["k"].dtype).reshape(nb, w.T, w.Hv, w.Dk)
+    a = w.accepted[0] if name != "spec_decode" else w.T
+    fp, _ = oracle.prepare_replay(tape_d, k_log, sl["g"], sl["state_in"], sl["mask"], a)
+    U = _active(sl["mask"], nb, w.T)
+    taken = _active(sl["mask"], nb, w.T, a)
+    has_mask = sl["mask"] is not None
+    return [(fx, expand_bytes(nb * w.T, w.Hk, w.Hv, w.Dk, e)),
+            (fr, record_bytes(nb, w.T, w.Hk, w.Hv, w.Dk, w.Dv, e, U, has_mask)),
+            (fp, replay_bytes(nb, w.T, w.Hv, w.Dk, w.Dv, e, a, taken, has_mask))]
+
+
+def cpu_baseline(name: str, budget_s: float, threads_req=None):
+    """Time the CPU oracle on a bounded sample of the workload on this host.
+
+    The sample (batch rows, or value heads of the one-sequence prefill, or
+    tokens) is split into one contiguous slice per thread; each thread runs
+    its slice's oracle calls (prepared once: inputs widened to float64 and
+    outputs allocated outside the timed loop) until the budget is spent.
+    Then one slice of one unit runs alone on one thread for the per-core
+    figure.  Bytes are the same algorithmic bytes as the GPU figures."""
+    import gdn_inputs as gi
 
     if name in gi.NORM_WORKLOADS:
-        return _cpu_baseline_norm(name, budget_s)
+        return _cpu_baseline_norm(name, budget_s, threads_req)
     w = gi.WORKLOADS[name]
-    bits_dtype = torch.int32 if w.io == "f32" else torch.int16
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    aff, threads = _host_threads(threads_req)
     e = 4 if w.io == "f32" else 2
-    # batch rows per sample: about 32 MiB of state (16 rows of the 128x128x32-head
-    # shape), so that small heads are not timed as Python call overhead
-    per_row = w.Hv * w.Dv * w.Dk * 4
-    b_sample = min(w.B, max(cores, (32 << 20) // per_row if w.T <= 16 else 1))
-    if name == "chunk_prefill":
-        heads = min(w.Hv, max(cores, 4))     # value heads of the single batch row
     seed = 123
-    if name == "long_tape_replay":
-        tape = gi.tape_inputs(b_sample, w.T, w.Hv, w.Dk, w.Dv, w.io, seed=seed, mask=w.mask, mask_p=w.mask_p)
+    if name == "chunk_prefill":
+        units = min(w.Hv, threads)                     # value heads of the single batch row
+        inp = gi.record_inputs(1, w.T, w.Hk, w.Hv, w.Dk, w.Dv, w.io, seed, w.mask, w.mask_p)
+
+        def slice_of(lo, hi):
+            hk = [hv % w.Hk for hv in range(lo, hi)]   # the tiled map, as keys pre-expanded
+            return dict(q=inp["q"][:, :, hk], k=inp["k"][:, :, hk], v=inp["v"][:, :, lo:hi],
+                        g=inp["g"][:, :, lo:hi], beta=inp["beta"][:, :, lo:hi],
+                        state_in=inp["state_in"][:, lo:hi])
     else:
-        inp = gi.record_inputs(b_sample, w.T, w.Hk, w.Hv, w.Dk, w.Dv, w.io, seed, w.mask, w.mask_p)
-
-    def work(lo, hi):
-        nbytes = 0
+        # batch rows: at least one per thread, and about 32 MiB of state
+        per_row = w.Hv * w.Dv * w.Dk * 4
+        units = min(w.B, max(threads, (32 << 20) // per_row))
         if name == "long_tape_replay":
-            sl = {k: (v[lo:hi] if v is not None else None) for k, v in tape.items()}
-            for a in w.accepted:
-                oracle.gdn_replay(sl["delta_log"], sl["k_log"], sl["g_log"], sl["state_in"], sl["mask"], a)
-                taken = _active(sl["mask"], hi - lo, w.T, a)
-                nbytes += replay_bytes(hi - lo, w.T, w.Hv, w.Dk, w.Dv, e, a, taken, True)
-            return nbytes
-        if name == "chunk_prefill":
-            hk = [hv % w.Hk for hv in range(lo, hi)]
-            sub = dict(q=inp["q"][:, :, hk], k=inp["k"][:, :, hk], v=inp["v"][:, :, lo:hi],
-                       g=inp["g"][:, :, lo:hi], beta=inp["beta"][:, :, lo:hi],
-                       state_in=inp["state_in"][:, lo:hi])
-            oracle.gdn_record(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], sub["state_in"], None,
-                              gqa_map="block")
-            return record_bytes(1, w.T, hi - lo, hi - lo, w.Dk, w.Dv, e, w.T, False)
-        sl = {k: (v[lo:hi] if v is not None else None) for k, v in inp.items()}
-        nb = hi - lo
-        y, s, dlt = oracle.gdn_record(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["state_in"],
-                                      sl["mask"], gqa_map=w.gqa_map)
-        kbits = sl["k"].contiguous().view(bits_dtype).numpy().reshape(nb * w.T, w.Hk, w.Dk)
-        k_log = torch.from_numpy(oracle.gqa_expand(kbits, w.Hv, w.gqa_map)).view(sl["k"].dtype)
-        a = w.accepted[0] if name != "spec_decode" else w.T
-        oracle.gdn_replay(dlt, k_log.reshape(nb, w.T, w.Hv, w.Dk), sl["g"],
-                          sl["state_in"], sl["mask"], a)
-        U = _active(sl["mask"], nb, w.T)
-        taken = _active(sl["mask"], nb, w.T, a)
-        has_mask = sl["mask"] is not None
-        return (expand_bytes(nb * w.T, w.Hk, w.Hv, w.Dk, e)
-                + record_bytes(nb, w.T, w.Hk, w.Hv, w.Dk, w.Dv, e, U, has_mask)
-                + replay_bytes(nb, w.T, w.Hv, w.Dk, w.Dv, e, a, taken, has_mask))
+            inp = gi.tape_inputs(units, w.T, w.Hv, w.Dk, w.Dv, w.io, seed=seed, mask=w.mask,
+                                 mask_p=w.mask_p)
+        else:
+            inp = gi.record_inputs(units, w.T, w.Hk, w.Hv, w.Dk, w.Dv, w.io, seed, w.mask, w.mask_p)
 
-    units = heads if name == "chunk_prefill" else b_sample
-    per = max(1, units // cores)
-    chunks = [(lo, min(units, lo + per)) for lo in range(0, units, per)]
-    total_bytes, passes = 0, 0
-    t0 = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=cores) as ex:
-        while True:
-            total_bytes += sum(ex.map(lambda c: work(*c), chunks))
-            passes += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-    dt = time.perf_counter() - t0
-    # one thread over one unit, for the per-core figure
-    one_bytes, t1 = 0, time.perf_counter()
-    while True:
-        one_bytes += work(0, 1)
-        if time.perf_counter() - t1 >= budget_s / 4:
-            break
-    dt1 = time.perf_counter() - t1
+        def slice_of(lo, hi):
+            return {k: (v[lo:hi] if v is not None else None) for k, v in inp.items()}
+    threads = min(threads, units)
+    bounds = [(i * units // threads, (i + 1) * units // threads) for i in range(threads)]
+    work = [_unit_calls(name, w, slice_of(lo, hi), e) for lo, hi in bounds]
+    total, dt = _timed_threads(work, budget_s)
+    one_total, dt1 = _timed_threads([_unit_calls(name, w, slice_of(0, 1), e)], budget_s / 4)
     unit_name = "value heads" if name == "chunk_prefill" else "batch rows"
-    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": min(cores, len(chunks)),
+    return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": "%d of %d %s of %s, %d pass(es), %.1f s, threads over %s"
-                      % (units, w.Hv if name == "chunk_prefill" else w.B, unit_name, name, passes, dt,
-                         unit_name),
-            "single_thread_value": round(one_bytes / dt1 / 1e9, 4),
-            "cpu_model": _cpu_model(),
+            "sample": "%d of %d %s of %s, one slice per thread, %.1f s"
+                      % (units, w.Hv if name == "chunk_prefill" else w.B, unit_name, name, dt),
+            "single_thread_value": round(one_total / dt1 / 1e9, 4),
+            "affinity_cores": aff, "cpu_model": _cpu_model(),
             "label": "CPU baseline, not the target"}
 
 
-def _cpu_baseline_norm(name: str, budget_s: float):
-    """The RMSNorm oracle on a sample of 1024 tokens, threads over token slices."""
-    from concurrent.futures import ThreadPoolExecutor
-
+def _cpu_baseline_norm(name: str, budget_s: float, threads_req=None):
+    """The RMSNorm oracle on a sample of 1024 tokens, one token slice per thread."""
     import gdn_inputs as gi
     import oracle
 
     w = gi.NORM_WORKLOADS[name]
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    aff, threads = _host_threads(threads_req)
     n = min(w["n_tokens"], 1024)
     x, wt = gi.norm_inputs(n, w["dim"], 123)
     xn = x.numpy()
-    per = max(1, n // cores)
-    chunks = [(lo, min(n, lo + per)) for lo in range(0, n, per)]
 
-    def work(lo, hi):
-        oracle.rms_norm_bf16(xn[lo:hi], wt, w["eps"])
-        return rms_norm_bytes(hi - lo, w["dim"])
+    def calls(lo, hi):
+        f, _ = oracle.prepare_rms_norm_bf16(xn[lo:hi], wt, w["eps"])
+        return [(f, rms_norm_bytes(hi - lo, w["dim"]))]
 
-    total, passes, t0 = 0, 0, time.perf_counter()
-    with ThreadPoolExecutor(max_workers=cores) as ex:
-        while True:
-            total += sum(ex.map(lambda c: work(*c), chunks))
-            passes += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-    dt = time.perf_counter() - t0
-    one, t1 = 0, time.perf_counter()
-    while True:
-        one += work(0, min(n, 16))
-        if time.perf_counter() - t1 >= budget_s / 4:
-            break
-    dt1 = time.perf_counter() - t1
-    return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": min(cores, len(chunks)),
-            "kind": "oracle",
-            "sample": "%d of %d tokens of %s, %d pass(es), %.1f s, threads over tokens"
-                      % (n, w["n_tokens"], name, passes, dt),
-            "single_thread_value": round(one / dt1 / 1e9, 4), "cpu_model": _cpu_model(),
-            "label": "CPU baseline, not the target"}
+    bounds = [(i * n // threads, (i + 1) * n // threads) for i in range(threads)]
+    total, dt = _timed_threads([calls(lo, hi) for lo, hi in bounds], budget_s)
+    one, dt1 = _timed_threads([calls(0, n // threads)], budget_s / 4)
+    return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d tokens of %s, one slice per thread, %.1f s" % (n, w["n_tokens"], name, dt),
+            "single_thread_value": round(one / dt1 / 1e9, 4), "affinity_cores": aff,
+            "cpu_model": _cpu_model(), "label": "CPU baseline, not the target"}
 
 
 def _cpu_model() -> str:
+    """The host CPU's model name as lscpu prints it (the longer of its
+    "Model name" and "BIOS Model name" lines), else /proc/cpuinfo's."""
+    import subprocess
+    names = []
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            key, _, val = line.partition(":")
+            if key.strip() in ("Model name", "BIOS Model name") and val.strip():
+                names.append(val.strip())
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                    names.append(line.split(":", 1)[1].strip())
+                    break
     except OSError:
         pass
-    return "unknown"
+    return max(names, key=len) if names else "unknown"
 
 
 # ------------------------------------------------------- counter calibration
@@ -480,9 +527,13 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
-    ap.add_argument("--scrub", choices=("auto", "on", "off"), default="auto",
-                    help="overwrite a 1 GiB buffer before every timed step so no input is left in "
-                         "the L2 / 256 MB MALL (auto: on unless the step moves >= 1 GB anyway)")
+    ap.add_argument("--scrub", choices=("on", "off"), default="on",
+                    help="before every timed step, write and then read back a 1 GiB buffer, so "
+                         "that no input is left in the L2 / 256 MB MALL and no dirty line of the "
+                         "scrub is left to write back during the step")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the CPU baseline (default: the affinity mask's cores, at most %d)"
+                         % CPU_THREADS_MAX)
     ap.add_argument("--capture", choices=("separate", "fused"), default="separate",
                     help="separate: k_log by a gqa_expand launch and g_log = g; fused: the record "
                          "writes k_log and g_log itself")
@@ -516,8 +567,9 @@ def main():
     torch.cuda.synchronize()
 
     step_bytes = sum(k[2] for k in step.kernels)
-    scrub = args.scrub == "on" or (args.scrub == "auto" and step_bytes < (1 << 30))
+    scrub = args.scrub == "on"
     scrub_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if scrub else None
+    scrub_sum = torch.empty((), dtype=torch.float32, device=dev) if scrub else None
 
     stream = torch.cuda.current_stream(dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
@@ -526,7 +578,10 @@ def main():
     t0 = time.perf_counter()
     for s in range(args.steps):
         if scrub:
-            scrub_buf.fill_(float(s))          # outside the events: evicts L2 and MALL
+            # outside the events: the write evicts the L2 and the MALL, the read
+            # back leaves them holding clean lines of the scrub buffer only
+            scrub_buf.fill_(float(s))
+            torch.sum(scrub_buf, dim=0, out=scrub_sum)
         ev[s][0].record(stream)
         for i, f in enumerate(launches):
             f()
@@ -598,7 +653,7 @@ def main():
                                  "copy_bytes_each_way": COPY_BYTES,
                                  "reported": reported_hbm_figure()}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_budget, args.cpu_threads or None)
     print(json.dumps(out), flush=True)
 
 

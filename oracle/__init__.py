@@ -204,3 +204,92 @@ def rms_norm_bf16(x, weight, eps: float) -> np.ndarray:
     if _load().oracle_rms_norm_bf16(xa.ctypes.data, wa.ctypes.data, _dp(out), n, dim, float(eps)) != 0:
         raise ValueError("oracle_rms_norm_bf16 rejected its arguments")
     return out
+
+
+# ------------------------------------------------------------ prepared calls
+#
+# For timing the oracle itself (the CPU-baseline leg of the benchmark): the
+# inputs are widened to float64 and the outputs allocated once, and the
+# returned callable makes only the C call (ctypes releases the GIL around
+# it, so threads run the oracle in parallel).  Same functions as above.
+
+def prepare_record(q, k, v, g, beta, state_in, mask=None, gqa_map="block"):
+    """A callable running oracle_gdn_record on fixed inputs; returns it and
+    the output arrays (y, state_out, delta_log) it writes."""
+    q, k, v, g, beta, s0 = (_f64(a) for a in (q, k, v, g, beta, state_in))
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    m = _u32(mask)
+    y = np.full(v.shape, np.nan)
+    d = np.full(v.shape, np.nan)
+    s1 = np.empty_like(s0)
+    lib = _load()
+    args = (_dp(q), _dp(k), _dp(v), _dp(g), _dp(beta), _dp(s0), _up(m), _dp(y), _dp(s1), _dp(d),
+            B, T, Hk, Hv, Dk, Dv, _MAPS[gqa_map])
+    keep = (q, k, v, g, beta, s0, m, y, d, s1)    # every array the pointers in args refer to
+
+    def run():
+        if lib.oracle_gdn_record(*args) != 0:
+            raise ValueError("oracle_gdn_record rejected its arguments")
+        return keep is not None
+    return run, (y, s1, d)
+
+
+def prepare_replay(delta_log, k_log, g_log, state_in, mask=None, accepted=None):
+    """A callable running oracle_gdn_replay on fixed inputs; returns it and
+    the state_out array it writes."""
+    d, kl, gl, s0 = (_f64(a) for a in (delta_log, k_log, g_log, state_in))
+    B, T, Hv, Dv = d.shape
+    Dk = kl.shape[3]
+    m = _u32(mask)
+    s1 = np.empty_like(s0)
+    lib = _load()
+    args = (_dp(d), _dp(kl), _dp(gl), _dp(s0), _up(m), _dp(s1), B, T, Hv, Dk, Dv,
+            T if accepted is None else int(accepted))
+    keep = (d, kl, gl, s0, m, s1)
+
+    def run():
+        if lib.oracle_gdn_replay(*args) != 0:
+            raise ValueError("oracle_gdn_replay rejected its arguments")
+        return keep is not None
+    return run, s1
+
+
+def prepare_expand(src: np.ndarray, h: int, gqa_map="tiled"):
+    """A callable running oracle_gqa_expand on a fixed [seq, hg, k] source;
+    returns it and the destination array."""
+    a = np.ascontiguousarray(src)
+    seq, hg, kk = a.shape
+    out = np.empty((seq, h, kk), dtype=a.dtype)
+    lib = _load()
+    args = (a.ctypes.data, out.ctypes.data, seq, hg, h, kk, a.dtype.itemsize, _MAPS[gqa_map])
+    keep = (a, out)
+
+    def run():
+        if lib.oracle_gqa_expand(*args) != 0:
+            raise ValueError("oracle_gqa_expand rejected its arguments")
+        return keep is not None
+    return run, out
+
+
+def prepare_rms_norm_bf16(x, weight, eps: float):
+    """A callable running oracle_rms_norm_bf16 on fixed inputs; returns it and
+    the output array."""
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    xa = np.ascontiguousarray(x, dtype=np.float32)
+    if hasattr(weight, "detach"):
+        import torch  # only reached when the caller already holds torch tensors
+        weight = weight.detach().cpu().contiguous().view(torch.int16).numpy()
+    wa = np.ascontiguousarray(np.asarray(weight).view(np.uint16))
+    n, dim = xa.shape
+    out = np.empty((n, dim), dtype=np.float64)
+    lib = _load()
+    args = (xa.ctypes.data, wa.ctypes.data, _dp(out), n, dim, float(eps))
+    keep = (xa, wa, out)
+
+    def run():
+        if lib.oracle_rms_norm_bf16(*args) != 0:
+            raise ValueError("oracle_rms_norm_bf16 rejected its arguments")
+        return keep is not None
+    return run, out
