@@ -225,6 +225,34 @@ int gdn_prefill(const void* q, const void* k, const void* v, const void* g, cons
                 int io_dtype, int gqa_map, void* stream);
 
 /*
+ * gdn_prefill_noalloc -- gdn_prefill without a workspace argument, allocating
+ * nothing.  For callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops that must not allocate, harnesses that forbid
+ * hipMalloc.
+ *
+ * Same arguments (less workspace and workspace_bytes), results and errors as
+ * gdn_prefill; it runs the same kernels.  Its workspace is a scratch area of
+ * GDN_PREFILL_SCRATCH_BYTES bytes inside the library: each GPU it runs on
+ * holds its own copy from the first call until the process ends.  The call
+ * allocates and frees nothing.  Sizes that need more (gdn_prefill_workspace_size
+ * (B, T, Hv) > GDN_PREFILL_SCRATCH_BYTES, i.e. B * Hv * ceil(T / 64) > 2048,
+ * e.g. past a 4096-step prefill over 32 value heads) fail with
+ * GDN_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU uses
+ * that one area, whose contents the previous call left: two calls whose
+ * kernels overlap in time on one GPU (on different streams, or from threads
+ * that do not order them) race and corrupt each other's results; calls
+ * ordered on one stream are safe.  `stream` must belong to the current device
+ * (GDN_ERR_LAUNCH otherwise).
+ */
+#define GDN_PREFILL_SCRATCH_BYTES 68157440ull
+
+int gdn_prefill_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                        const float* state_in, const uint32_t* mask,
+                        void* y, float* state_out, void* delta_log,
+                        uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+                        int io_dtype, int gqa_map, void* stream);
+
+/*
  * rms_norm_bf16 -- RMSNorm with bf16 weights over a batch of tokens.
  *
  * Defined on the moeflux 0.1.0-pre.3 page src/riir/backend/gpu/gpu_norm.rs

@@ -22,7 +22,10 @@ from . import _native
 from ._native import GdnError, lib
 
 __all__ = ["gdn_record", "gdn_replay", "gqa_expand", "gdn_prefill", "gdn_prefill_workspace_size",
-           "rms_norm_bf16", "gdn_record_debug", "gdn_replay_debug", "GdnError", "IO_DTYPES"]
+           "rms_norm_bf16", "gdn_record_debug", "gdn_replay_debug", "gdn_prefill_noalloc", "GdnError",
+           "IO_DTYPES", "PREFILL_SCRATCH_BYTES"]
+
+PREFILL_SCRATCH_BYTES = _native.PREFILL_SCRATCH_BYTES
 
 IO_DTYPES = {torch.float32: _native.GDN_F32, torch.float16: _native.GDN_F16,
              torch.bfloat16: _native.GDN_BF16}
@@ -176,20 +179,8 @@ def gdn_prefill_workspace_size(B: int, T: int, Hv: int) -> int:
     return int(lib.gdn_prefill_workspace_size(B, T, Hv))
 
 
-def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
-                beta: torch.Tensor, state_in: torch.Tensor, mask: Optional[torch.Tensor] = None,
-                *, gqa_map: str = "block", y: Optional[torch.Tensor] = None,
-                state_out: Optional[torch.Tensor] = None,
-                delta_log: Optional[torch.Tensor] = None, write_tape: bool = True,
-                workspace: Optional[torch.Tensor] = None,
-                stream=None) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
-    """The record step over a long sequence, 64 steps at a time on the matrix
-    cores; returns (y, state_out, delta_log) as gdn_record does.
-
-    bf16 I/O, Dk = 128, Dv a multiple of 16.  ``workspace`` (a uint8 device
-    tensor of at least gdn_prefill_workspace_size(B, T, Hv) bytes) is allocated
-    when not given; pass one to reuse it across calls on one stream.
-    """
+def _prefill(noalloc, q, k, v, g, beta, state_in, mask, gqa_map, y, state_out, delta_log,
+             write_tape, workspace, stream):
     if gqa_map not in _MAPS:
         raise ValueError("gqa_map must be 'block' or 'tiled'")
     dev = _device_of(q)
@@ -214,7 +205,7 @@ def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
             state_out = torch.empty_like(state_in)
         if delta_log is None and write_tape:
             delta_log = torch.empty((B, T, Hv, Dv), dtype=io, device=dev)
-        if workspace is None:
+        if workspace is None and not noalloc:
             # freed when this call returns: allocated on the kernels' stream, so
             # its memory is not reused before they have finished with it
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -222,6 +213,12 @@ def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     _want("state_out", state_out, (B, Hv, Dv, Dk), torch.float32, dev)
     if delta_log is not None:
         _want("delta_log", delta_log, (B, T, Hv, Dv), io, dev)
+    if noalloc:
+        rc = lib.gdn_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+                                     _ptr(mask), _ptr(y), _ptr(state_out), _ptr(delta_log), B, T, Hk,
+                                     Hv, Dk, Dv, _io_code(q), _MAPS[gqa_map], st.cuda_stream)
+        _native.check("gdn_prefill_noalloc", rc)
+        return y, state_out, delta_log
     _want("workspace", workspace, (workspace.numel(),), torch.uint8, dev)
     rc = lib.gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
                          _ptr(mask), _ptr(y), _ptr(state_out), _ptr(delta_log), _ptr(workspace),
@@ -229,6 +226,40 @@ def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
                          st.cuda_stream)
     _native.check("gdn_prefill", rc)
     return y, state_out, delta_log
+
+
+def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                beta: torch.Tensor, state_in: torch.Tensor, mask: Optional[torch.Tensor] = None,
+                *, gqa_map: str = "block", y: Optional[torch.Tensor] = None,
+                state_out: Optional[torch.Tensor] = None,
+                delta_log: Optional[torch.Tensor] = None, write_tape: bool = True,
+                workspace: Optional[torch.Tensor] = None,
+                stream=None) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """The record step over a long sequence, 64 steps at a time on the matrix
+    cores; returns (y, state_out, delta_log) as gdn_record does.
+
+    bf16 I/O, Dk = 128, Dv a multiple of 16.  ``workspace`` (a uint8 device
+    tensor of at least gdn_prefill_workspace_size(B, T, Hv) bytes) is allocated
+    when not given; pass one to reuse it across calls on one stream.
+    """
+    return _prefill(False, q, k, v, g, beta, state_in, mask, gqa_map, y, state_out, delta_log,
+                    write_tape, workspace, stream)
+
+
+def gdn_prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                        beta: torch.Tensor, state_in: torch.Tensor,
+                        mask: Optional[torch.Tensor] = None, *, gqa_map: str = "block",
+                        y: Optional[torch.Tensor] = None, state_out: Optional[torch.Tensor] = None,
+                        delta_log: Optional[torch.Tensor] = None, write_tape: bool = True,
+                        stream=None) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """gdn_prefill with its workspace in the library's own scratch area
+    (PREFILL_SCRATCH_BYTES per GPU, shared by every such call on that GPU):
+    the library call allocates nothing.  Pass y, state_out and delta_log (or
+    write_tape=False) so that this binding allocates nothing either.  Calls
+    whose kernels overlap in time on one GPU race; calls on one stream are
+    ordered."""
+    return _prefill(True, q, k, v, g, beta, state_in, mask, gqa_map, y, state_out, delta_log,
+                    write_tape, None, stream)
 
 
 def _replay(choice, delta_log, k_log, g_log, state_in, mask, accepted, state_out, stream):

@@ -25,8 +25,9 @@ STATUS = {
 }
 GDN_FOLD_AUTO, GDN_FOLD_VALU, GDN_FOLD_MATRIX = 0, 1, 2
 EXPORTS = ("gdn_record", "gdn_replay", "gqa_expand", "gdn_prefill", "gdn_prefill_workspace_size",
-           "rms_norm_bf16", "gdn_record_debug", "gdn_replay_debug", "gdn_strerror", "gdn_last_error",
-           "gdn_abi_version")
+           "rms_norm_bf16", "gdn_record_debug", "gdn_replay_debug", "gdn_prefill_noalloc",
+           "gdn_strerror", "gdn_last_error", "gdn_abi_version")
+PREFILL_SCRATCH_BYTES = 68157440     # GDN_PREFILL_SCRATCH_BYTES
 ABI_VERSION = 5
 
 
@@ -56,6 +57,8 @@ def _load() -> ctypes.CDLL:
     lib.gqa_expand.restype = i32
     lib.gdn_prefill.argtypes = [vp] * 11 + [ctypes.c_uint64] + [u32] * 6 + [i32, i32, vp]
     lib.gdn_prefill.restype = i32
+    lib.gdn_prefill_noalloc.argtypes = [vp] * 10 + [u32] * 6 + [i32, i32, vp]
+    lib.gdn_prefill_noalloc.restype = i32
     lib.gdn_prefill_workspace_size.argtypes = [u32] * 3
     lib.gdn_prefill_workspace_size.restype = ctypes.c_uint64
     lib.rms_norm_bf16.argtypes = [vp, vp, vp, u32, u32, ctypes.c_float, vp]

@@ -42,6 +42,8 @@ constexpr uint64_t kMaxBytes = uint64_t(1) << 48;   // 256 TiB: far beyond any d
 // size is 32 bits wide).
 constexpr uint64_t kMaxWorkItems = 0xffffffffull;
 
+static_assert(GDN_PREFILL_SCRATCH_BYTES == gdn::kPrefillScratchBytes, "gdn.h and the library disagree");
+
 struct Span {
     const void* p;
     uint64_t bytes;
@@ -298,13 +300,18 @@ uint64_t gdn_prefill_workspace_size(uint32_t B, uint32_t T, uint32_t Hv) {
     return gdn::prefill_workspace_bytes(B, T, Hv);
 }
 
-int gdn_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                const float* state_in, const uint32_t* mask,
-                void* y, float* state_out, void* delta_log,
-                void* workspace, uint64_t workspace_bytes,
-                uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
-                int io_dtype, int gqa_map, void* stream) {
-    static const char* kFn = "gdn_prefill";
+}  // extern "C"
+
+namespace {
+
+// noalloc: the workspace is the library's own scratch area (workspace and
+// workspace_bytes are ignored), looked up after validation.
+int prefill_impl(bool noalloc, const void* q, const void* k, const void* v, const void* g, const void* beta,
+                 const float* state_in, const uint32_t* mask,
+                 void* y, float* state_out, void* delta_log,
+                 void* workspace, uint64_t workspace_bytes,
+                 uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+                 int io_dtype, int gqa_map, void* stream, const char* kFn) {
     if (!valid_dtype(io_dtype)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown io_dtype %d", kFn, io_dtype);
     if (!valid_map(gqa_map)) return fail(GDN_ERR_BAD_ENUM, "%s: unknown gqa_map %d", kFn, gqa_map);
     if (!q || !k || !v || !g || !beta || !state_in || !y || !state_out)
@@ -331,17 +338,29 @@ int gdn_prefill(const void* q, const void* k, const void* v, const void* g, cons
         !mul_u64(&scan_items, {B, Hv, Dv / 16, 512}) || scan_items > kMaxWorkItems)
         return fail(GDN_ERR_OVERFLOW, "%s: launch grid too large (split the batch)", kFn);
     const uint64_t need = gdn::prefill_workspace_bytes(B, T, Hv);
-    if (!workspace || workspace_bytes < need)
+    if (noalloc) {
+        if (need > gdn::kPrefillScratchBytes)
+            return fail(GDN_ERR_WORKSPACE,
+                        "%s: these sizes need %llu bytes of workspace; the library's scratch area holds "
+                        "%llu (B*Hv*ceil(T/64) = %llu blocks, at most 2048): split the batch or the "
+                        "heads, or call gdn_prefill with a workspace", kFn,
+                        static_cast<unsigned long long>(need),
+                        static_cast<unsigned long long>(gdn::kPrefillScratchBytes),
+                        static_cast<unsigned long long>(need / 33280u));
+        workspace = nullptr;
+    } else if (!workspace || workspace_bytes < need) {
         return fail(GDN_ERR_WORKSPACE, "%s: workspace of %llu bytes needed, %llu given%s", kFn,
                     static_cast<unsigned long long>(need), static_cast<unsigned long long>(workspace_bytes),
                     workspace ? "" : " (NULL)");
+    }
 
     const void* a16[] = {q, k, v, state_in, y, state_out, delta_log};
     const char* a16n[] = {"q", "k", "v", "state_in", "y", "state_out", "delta_log"};
     for (int i = 0; i < 7; ++i)
         if (a16[i] && !aligned(a16[i], 16))
             return fail(GDN_ERR_MISALIGNED, "%s: %s must be 16-byte aligned", kFn, a16n[i]);
-    if (!aligned(workspace, 256)) return fail(GDN_ERR_MISALIGNED, "%s: workspace must be 256-byte aligned", kFn);
+    if (!noalloc && !aligned(workspace, 256))
+        return fail(GDN_ERR_MISALIGNED, "%s: workspace must be 256-byte aligned", kFn);
     if (mask && !aligned(mask, 4)) return fail(GDN_ERR_MISALIGNED, "%s: mask must be 4-byte aligned", kFn);
     if (!aligned(g, e) || !aligned(beta, e))
         return fail(GDN_ERR_MISALIGNED, "%s: g and beta must be element-aligned", kFn);
@@ -349,7 +368,8 @@ int gdn_prefill(const void* q, const void* k, const void* v, const void* g, cons
     const Span ins[] = {{q, n_qk, "q"}, {k, n_qk, "k"}, {v, n_v, "v"}, {g, n_g, "g"},
                         {beta, n_g, "beta"}, {state_in, n_s, "state_in"}, {mask, mask ? n_m : 0, "mask"}};
     const Span outs[] = {{y, n_v, "y"}, {state_out, n_s, "state_out"},
-                         {delta_log, delta_log ? n_v : 0, "delta_log"}, {workspace, need, "workspace"}};
+                         {delta_log, delta_log ? n_v : 0, "delta_log"},
+                         {workspace, noalloc ? 0 : need, "workspace"}};
     constexpr int kOuts = 4;
     for (const Span& o : outs) {
         for (const Span& i : ins) {
@@ -362,9 +382,39 @@ int gdn_prefill(const void* q, const void* k, const void* v, const void* g, cons
             if (overlaps(outs[i], outs[j]))
                 return fail(GDN_ERR_ALIAS, "%s: %s overlaps %s", kFn, outs[i].name, outs[j].name);
 
+    if (noalloc) {
+        const hipError_t e = gdn::prefill_scratch(static_cast<hipStream_t>(stream), &workspace);
+        if (e == hipErrorInvalidDevice)
+            return fail(GDN_ERR_LAUNCH, "%s: the stream does not belong to the current device", kFn);
+        if (e != hipSuccess)
+            return fail(GDN_ERR_LAUNCH, "%s: cannot find the scratch area: %s", kFn, hipGetErrorString(e));
+    }
     gdn::PrefillArgs a{q, k, v, g, beta, state_in, mask, y, state_out, delta_log, workspace,
                        B, T, Hk, Hv, Dk, Dv, io_dtype, gqa_map};
     return launch_status(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)), kFn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                const float* state_in, const uint32_t* mask,
+                void* y, float* state_out, void* delta_log,
+                void* workspace, uint64_t workspace_bytes,
+                uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+                int io_dtype, int gqa_map, void* stream) {
+    return prefill_impl(false, q, k, v, g, beta, state_in, mask, y, state_out, delta_log, workspace,
+                        workspace_bytes, B, T, Hk, Hv, Dk, Dv, io_dtype, gqa_map, stream, "gdn_prefill");
+}
+
+int gdn_prefill_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                        const float* state_in, const uint32_t* mask,
+                        void* y, float* state_out, void* delta_log,
+                        uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
+                        int io_dtype, int gqa_map, void* stream) {
+    return prefill_impl(true, q, k, v, g, beta, state_in, mask, y, state_out, delta_log, nullptr, 0,
+                        B, T, Hk, Hv, Dk, Dv, io_dtype, gqa_map, stream, "gdn_prefill_noalloc");
 }
 
 int gqa_expand(const void* src, void* dst, uint32_t seq, uint32_t hg, uint32_t h, uint32_t k,

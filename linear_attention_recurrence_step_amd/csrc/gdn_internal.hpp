@@ -92,6 +92,14 @@ uint64_t prefill_workspace_bytes(uint32_t B, uint32_t T, uint32_t Hv);   // UINT
 bool prefill_supported(uint32_t Dk, uint32_t Dv, int io);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
+// The allocation-free prefill's workspace: a file-scope device array of this
+// many bytes in gdn_prefill.hip (2048 blocks of 33280 bytes: a 4096-step
+// prefill over 32 value heads).  prefill_scratch() gives its address on the
+// device `stream` runs on, looked up once per device; that device must be
+// the current one (hipErrorInvalidDevice otherwise).
+inline constexpr uint64_t kPrefillScratchBytes = 68157440ull;
+hipError_t prefill_scratch(hipStream_t stream, void** out);
+
 }  // namespace gdn
 
 namespace gdn {

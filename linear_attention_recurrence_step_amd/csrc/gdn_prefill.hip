@@ -727,6 +727,42 @@ uint64_t prefill_workspace_bytes(uint32_t B, uint32_t T, uint32_t Hv) {
     return bytes;
 }
 
+// ------------------------------------------------ allocation-free variant
+
+// The workspace of gdn_prefill_noalloc.  Each GPU the library runs on holds
+// its own copy from the first call until the process ends, and every call of
+// that entry point on a GPU shares it.  prep writes every byte of a block
+// that scan reads, so nothing here has to start at zero.  In host code the
+// name `scratch` is only a stand-in for the symbol, not a device address:
+// kernels get the address prefill_scratch() looked up.
+static_assert(kPrefillScratchBytes == 2048ull * PrefillWs::kBytes, "scratch size");
+static __device__ __align__(256) unsigned char scratch[kPrefillScratchBytes];
+
+hipError_t prefill_scratch(hipStream_t stream, void** out) {
+    constexpr int kDevices = 64;
+    static std::atomic<void*> addr[kDevices];
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    hipDevice_t sdev = cur;
+    if (stream != nullptr) {
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess) return e;
+    }
+    if (sdev != cur || cur < 0 || cur >= kDevices) return hipErrorInvalidDevice;
+    void* p = addr[cur].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        // once per device, with that device current (two threads racing here
+        // both store the same address)
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[cur].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return hipSuccess;
+}
+
 bool prefill_supported(uint32_t Dk, uint32_t Dv, int io) {
     return io == kBF16 && Dk == static_cast<uint32_t>(kDk) && Dv % kRows == 0;
 }

@@ -28,8 +28,8 @@ def _declared_functions():
 def test_header_declares_the_three_entry_points():
     fns = _declared_functions()
     for name in ("gdn_record", "gdn_replay", "gqa_expand", "gdn_prefill", "gdn_prefill_workspace_size",
-                 "rms_norm_bf16", "gdn_record_debug", "gdn_replay_debug", "gdn_strerror",
-                 "gdn_last_error", "gdn_abi_version"):
+                 "rms_norm_bf16", "gdn_record_debug", "gdn_replay_debug", "gdn_prefill_noalloc",
+                 "gdn_strerror", "gdn_last_error", "gdn_abi_version"):
         assert name in fns, fns
 
 
@@ -51,6 +51,7 @@ lib.gdn_replay.argtypes = [vp] * 6 + [u32] * 6 + [i32, vp]
 lib.gqa_expand.argtypes = [vp, vp] + [u32] * 4 + [i32, i32, vp]
 lib.rms_norm_bf16.argtypes = [vp, vp, vp, u32, u32, ctypes.c_float, vp]
 lib.gdn_prefill.argtypes = [vp] * 11 + [ctypes.c_uint64] + [u32] * 6 + [i32, i32, vp]
+lib.gdn_prefill_noalloc.argtypes = [vp] * 10 + [u32] * 6 + [i32, i32, vp]
 lib.gdn_prefill_workspace_size.argtypes = [u32] * 3
 lib.gdn_prefill_workspace_size.restype = ctypes.c_uint64
 class Choice(ctypes.Structure):
@@ -145,6 +146,12 @@ def repd(choice, **kw):
     return [choice] + rep(**kw)
 
 
+# gdn_prefill_noalloc: gdn_prefill's arguments less workspace and workspace_bytes
+def prena(**kw):
+    a = pre(**kw)
+    return a[:10] + a[12:]
+
+
 NULL, ZERO, RATIO, SHAPE, OVER, ALIAS, ENUM, LAUNCH, ALIGN = -1, -2, -3, -4, -5, -6, -7, -8, -9
 WORKSPACE = -10
 
@@ -237,6 +244,13 @@ CASES = [
     ("repd_tiling_not_fitting", "gdn_replay_debug", repd([8, 256, 1, 0], Dv=64), SHAPE),
     ("repd_unknown_tiling", "gdn_replay_debug", repd([4, 64, 1, 0]), ENUM),
     ("repd_null_state_out", "gdn_replay_debug", repd([0, 0, 1, 0], s_out=None), NULL),
+    ("prena_bad_dtype", "gdn_prefill_noalloc", prena(io=5), ENUM),
+    ("prena_null_q", "gdn_prefill_noalloc", prena(q=None), NULL),
+    ("prena_f16", "gdn_prefill_noalloc", prena(io=1), SHAPE),
+    ("prena_y_over_v", "gdn_prefill_noalloc", prena(y=P(2, 512)), ALIAS),
+    # one chunk block past the 2048 the scratch area holds
+    ("prena_past_scratch", "gdn_prefill_noalloc", prena(B=1, T=64 * 65, Hk=1, Hv=32), WORKSPACE),
+    ("prena_past_scratch_batch", "gdn_prefill_noalloc", prena(B=2049, T=1, Hk=1, Hv=1), WORKSPACE),
     ("exp_bad_dtype", "gqa_expand", exp(dt=7), ENUM),
     ("exp_bad_map", "gqa_expand", exp(map=-1), ENUM),
     ("exp_null_dst", "gqa_expand", exp(dst=None), NULL),
@@ -285,7 +299,7 @@ def test_python_binding_names_match_the_abi():
     import linear_attention_recurrence_step_amd as gdn
     from linear_attention_recurrence_step_amd import _native
     for name in ("gdn_record", "gdn_replay", "gqa_expand", "gdn_prefill", "gdn_prefill_workspace_size",
-                 "rms_norm_bf16", "gdn_record_debug", "gdn_replay_debug"):
+                 "rms_norm_bf16", "gdn_record_debug", "gdn_replay_debug", "gdn_prefill_noalloc"):
         assert callable(getattr(gdn, name))
         assert hasattr(_native.lib, name)
     assert _native.lib.gdn_abi_version() == _native.ABI_VERSION
