@@ -6,8 +6,8 @@
  * of the benchmark use it.  It shares no code, header, table or helper with the
  * HIP library.
  *
- * Every operation is written as the straightforward loop that the source page
- * describes, in double precision, with floating-point contraction disabled at
+ * Every operation is written from the equations of the method, one pass per
+ * equation, in double precision, with floating-point contraction disabled at
  * build time (-ffp-contract=off) so that each product and sum is rounded once,
  * in the order written here.  Inputs arrive already widened to double; the
  * widening of fp32 / fp16 / bf16 to double is exact, so the oracle sees the
@@ -64,6 +64,14 @@ static uint32_t oracle_key_head(uint32_t hv, uint32_t Hk, uint32_t Hv, int map)
     return hv % Hk;
 }
 
+/* sum_i a[i] * b[i], in index order. */
+static double oracle_dot(const double* a, const double* b, uint32_t n)
+{
+    double acc = 0.0;
+    for (uint32_t i = 0; i < n; ++i) acc = acc + a[i] * b[i];
+    return acc;
+}
+
 static int oracle_step_active(const uint32_t* mask, uint32_t T, uint32_t b, uint32_t t)
 {
     /* [P1] record kernel: with has_mask == 0 every step is active, otherwise
@@ -78,13 +86,13 @@ static int oracle_step_active(const uint32_t* mask, uint32_t T, uint32_t b, uint
  * description of `gated_delta_step_record`).
  *
  * For every (b, hv) and every value row dv of S, for t = 0 .. T-1 with the step
- * active:
- *     S[dv, :] <- g_t * S[dv, :]                         (decay first)
- *     kv       <- sum_dk S[dv, dk] * k_t[dk]             (read-out of the decayed row)
- *     delta    <- (v_t[dv] - kv) * beta_t
- *     delta_log[b, t, hv, dv] <- delta                   (tape write)
- *     S[dv, :] <- S[dv, :] + k_t[:] * delta              (rank-1 write)
- *     y[b, t, hv, dv] <- sum_dk S[dv, dk] * q_t[dk]      (read-out of the updated row)
+ * active, the gated delta rule on row dv:
+ *     (1) S[dv, :] <- g_t S[dv, :]                       (the gate decays the row first)
+ *     (2) kv = S[dv, :] . k_t                            (prediction of the decayed row)
+ *     (3) delta = beta_t (v_t[dv] - kv)                  (innovation)
+ *     (4) delta_log[b, t, hv, dv] = delta                (tape)
+ *     (5) S[dv, :] <- S[dv, :] + delta k_t               (rank-one correction)
+ *     (6) y[b, t, hv, dv] = S[dv, :] . q_t               (output from the corrected row)
  * Inactive steps change nothing and write nothing.  The final S goes to
  * state_out.  delta_log may be NULL (the plain forward step without a tape).
  *
@@ -121,20 +129,18 @@ int oracle_gdn_record(const double* q, const double* k, const double* v,
                     double bet = beta[bt * Hv + hv];
                     size_t vo = (bt * Hv + hv) * Dv + dv;
 
-                    double kv = 0.0;
-                    for (uint32_t i = 0; i < Dk; ++i) {
-                        S[i] = S[i] * gt;
-                        kv = kv + S[i] * kt[i];
-                    }
-                    double delta = (v[vo] - kv) * bet;
+                    /* (1) decay the row by the step's gate */
+                    for (uint32_t i = 0; i < Dk; ++i) S[i] = gt * S[i];
+                    /* (2) what the decayed row predicts for this key */
+                    double kv = oracle_dot(S, kt, Dk);
+                    /* (3) innovation: the prediction error, scaled by beta */
+                    double delta = bet * (v[vo] - kv);
+                    /* (4) the tape keeps the innovation */
                     if (delta_log != NULL) delta_log[vo] = delta;
-
-                    double out = 0.0;
-                    for (uint32_t i = 0; i < Dk; ++i) {
-                        S[i] = S[i] + kt[i] * delta;
-                        out = out + S[i] * qt[i];
-                    }
-                    y[vo] = out;
+                    /* (5) rank-one correction along the key */
+                    for (uint32_t i = 0; i < Dk; ++i) S[i] = S[i] + delta * kt[i];
+                    /* (6) output: the corrected row read against the query */
+                    y[vo] = oracle_dot(S, qt, Dk);
                 }
             }
         }

@@ -18,15 +18,22 @@ SRC = os.path.join(ROOT, "oracle", "gdn_oracle.c")
 
 MUTANTS = {
     "decay_after_readout": (
-        "S[i] = S[i] * gt;\n                        kv = kv + S[i] * kt[i];",
-        "kv = kv + S[i] * kt[i];\n                        S[i] = S[i] * gt;"),
-    "innovation_sign": ("(v[vo] - kv) * bet", "(kv - v[vo]) * bet"),
-    "beta_on_value_only": ("(v[vo] - kv) * bet", "(v[vo] * bet - kv)"),
+        "for (uint32_t i = 0; i < Dk; ++i) S[i] = gt * S[i];\n"
+        "                    /* (2) what the decayed row predicts for this key */\n"
+        "                    double kv = oracle_dot(S, kt, Dk);",
+        "double kv = oracle_dot(S, kt, Dk);\n"
+        "                    for (uint32_t i = 0; i < Dk; ++i) S[i] = gt * S[i];"),
+    "innovation_sign": ("bet * (v[vo] - kv)", "bet * (kv - v[vo])"),
+    "beta_on_value_only": ("bet * (v[vo] - kv)", "(bet * v[vo] - kv)"),
     "query_readout_before_write": (
-        "S[i] = S[i] + kt[i] * delta;\n                        out = out + S[i] * qt[i];",
-        "out = out + S[i] * qt[i];\n                        S[i] = S[i] + kt[i] * delta;"),
-    "readout_with_key": ("out = out + S[i] * qt[i];", "out = out + S[i] * kt[i];"),
-    "no_decay_in_record": ("S[i] = S[i] * gt;", "S[i] = S[i];"),
+        "for (uint32_t i = 0; i < Dk; ++i) S[i] = S[i] + delta * kt[i];\n"
+        "                    /* (6) output: the corrected row read against the query */\n"
+        "                    y[vo] = oracle_dot(S, qt, Dk);",
+        "y[vo] = oracle_dot(S, qt, Dk);\n"
+        "                    for (uint32_t i = 0; i < Dk; ++i) S[i] = S[i] + delta * kt[i];"),
+    "readout_with_key": ("y[vo] = oracle_dot(S, qt, Dk);", "y[vo] = oracle_dot(S, kt, Dk);"),
+    "no_decay_in_record": ("S[i] = gt * S[i];", "S[i] = S[i];"),
+    "rank_one_along_query": ("S[i] = S[i] + delta * kt[i];", "S[i] = S[i] + delta * qt[i];"),
     "block_map_as_tiled": ("return hv / group;", "return hv % Hk;"),
     "tiled_map_as_block": ("    return hv % Hk;\n}", "    return hv / (Hv / Hk);\n}"),
     "mask_ignored": ("return mask[(size_t)b * T + t] > 0u;", "return 1;"),
