@@ -52,7 +52,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 METRIC = "GDN record+replay effective HBM GB/s (% of peak) and head-steps/sec"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
-    "gdn_record": ["gdn_record.hip", "gdn_device.hpp"],
+    "gdn_record": ["gdn_record.hip", "gdn_record_mfma.hip", "gdn_device.hpp"],
     "gdn_replay": ["gdn_replay.hip", "gdn_replay_mfma.hip", "gdn_device.hpp"],
     "gqa_expand": ["gqa_expand.hip", "gdn_device.hpp"],
     "rms_norm_bf16": ["rms_norm.hip", "gdn_device.hpp"],

@@ -16,8 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["gdn_abi.cpp", "gdn_record.hip", "gdn_replay.hip", "gdn_replay_mfma.hip", "gqa_expand.hip",
-           "rms_norm.hip", "gdn_prefill.hip"]
+SOURCES = ["gdn_abi.cpp", "gdn_record.hip", "gdn_record_mfma.hip", "gdn_replay.hip", "gdn_replay_mfma.hip",
+           "gqa_expand.hip", "rms_norm.hip", "gdn_prefill.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -34,6 +34,7 @@ FLAGS = [
 # ordinary VGPRs (gfx950 allows either file): it also scales them with VALU
 # instructions, and one register file instead of two doubles its occupancy.
 SOURCE_FLAGS = {"gdn_replay_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "gdn_record_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                 "gdn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
@@ -51,7 +52,7 @@ def _compile(src: str, extra) -> str:
 def build(resource_usage: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs

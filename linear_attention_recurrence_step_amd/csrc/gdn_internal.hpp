@@ -52,11 +52,21 @@ struct ExpandArgs {
 // Does a kernel exist for this key width?
 bool dk_supported(uint32_t Dk);
 
+// Compute units of the current device (cached per device; 256, the MI355X
+// count, if the runtime cannot say).
+uint32_t compute_units();
+
 // Tiling the launchers will use (also used by the ABI for its grid-size check).
 RowTiling record_tiling(const RecordArgs& a);
 RowTiling replay_tiling(const ReplayArgs& a);
 
 hipError_t launch_record(const RecordArgs& a, hipStream_t stream);
+
+// Records of 2..4 steps of bf16 I/O with whole 64-row workgroups (and no
+// forced tiling) run their dense products on the matrix cores
+// (gdn_record_mfma.hip).
+bool record_mfma_applies(const RecordArgs& a);
+hipError_t launch_record_mfma(const RecordArgs& a, hipStream_t stream);
 hipError_t launch_replay(const ReplayArgs& a, hipStream_t stream);
 
 struct RmsNormArgs {

@@ -194,6 +194,145 @@ __global__ __launch_bounds__(NT) void gdn_record_kernel(
     for (int r = 0; r < RPT; ++r) store_state_row<W, NC, E>(state_out + srow + r * DK, lane, s[r]);
 }
 
+// ------------------------------------------------------ short-tape kernel
+
+// N consecutive I/O elements held as their raw bits (N * element size <= 16
+// bytes), widened only where they are used, so that a load is never waited
+// for where it is issued.
+template <int IO, int N>
+struct RawIo {
+    static constexpr int EB = IoTraits<IO>::kBytes;
+    using V = typename RawVec<N * EB>::T;
+    static_assert(N * EB <= 16, "one vector access");
+    V raw;
+    __device__ __forceinline__ void load(const void* base, size_t idx) {
+        raw = *reinterpret_cast<const V*>(static_cast<const char*>(base) + idx * EB);
+    }
+    __device__ __forceinline__ void store(void* base, size_t idx) const {
+        *reinterpret_cast<V*>(static_cast<char*>(base) + idx * EB) = raw;
+    }
+    __device__ __forceinline__ float at(int e) const {
+        if constexpr (N * EB >= 4) {
+            uint32_t w[(N * EB) / 4];
+            __builtin_memcpy(w, &raw, N * EB);
+            if constexpr (IO == kF32) return __uint_as_float(w[e]);
+            const uint32_t bits = (w[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+            return IO == kBF16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
+        } else {
+            const uint32_t bits = raw;
+            return IO == kBF16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
+        }
+    }
+};
+
+// Tapes of at most this many steps run the short-tape kernel.
+constexpr uint32_t kShortDirectSteps = 4;
+
+// Record of a short tape (2 <= T <= TMAX), the speculative-decode case: the
+// direct kernel's layout, with every step's inputs loaded right after the
+// state (step indices past T clamped to T - 1, so every load is valid and
+// unconditional) and the steps then run from registers: no LDS, no barrier,
+// and a single round trip to memory before the first step.  k . q of every
+// step is reduced once up front, off the state's chain.  Same arithmetic as
+// the other record kernels (record_step), so the same bits.
+template <int IO, int DK, int RPT, int NT, int TMAX>
+__global__ __launch_bounds__(NT) void gdn_record_short_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const void* __restrict__ g, const void* __restrict__ beta,
+    const float* state_in, const uint32_t* __restrict__ mask,
+    void* __restrict__ y, float* state_out, void* __restrict__ delta_log,
+    void* __restrict__ k_log, void* __restrict__ g_log,
+    uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dv, uint32_t row_blocks, int tiled)
+{
+    constexpr int L = 16;
+    constexpr int E = DK / L;
+    constexpr int W = E < 4 ? E : 4;
+    constexpr int NC = E / W;
+    constexpr int SLOTS = NT / L;
+    constexpr int R = SLOTS * RPT;
+    static_assert(DK % (L * W) == 0 && NC * W == E, "unsupported Dk");
+
+    const uint32_t lane = threadIdx.x & (L - 1);
+    const uint32_t slot = threadIdx.x / L;
+    const uint32_t blk = xcd_contiguous_index(blockIdx.x, gridDim.x);
+    const size_t srow = (static_cast<size_t>(blk) * R + slot * RPT) * DK;
+
+    float s[RPT][E];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) load_state_row<W, NC, E>(state_in + srow + r * DK, lane, s[r]);
+
+    const uint32_t n = blk / row_blocks;                      // b * Hv + hv
+    const uint32_t row0 = (blk - n * row_blocks) * R + slot * RPT;
+    const uint32_t b = n / Hv;
+    const uint32_t hv = n - b * Hv;
+    const uint32_t hk = tiled ? hv % Hk : hv / (Hv / Hk);
+
+    RawIo<IO, W> kr[TMAX][NC], qr[TMAX][NC];
+    RawIo<IO, RPT> vr[TMAX];
+    RawIo<IO, 1> gr[TMAX], br[TMAX];
+    uint32_t mk[TMAX];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+        const uint32_t tc = static_cast<uint32_t>(t) < T ? static_cast<uint32_t>(t) : T - 1;
+        const size_t bt = static_cast<size_t>(b) * T + tc;
+        const size_t kq = (bt * Hk + hk) * DK;
+        const size_t gi = bt * Hv + hv;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            kr[t][c].load(k, kq + (c * L + lane) * W);
+            qr[t][c].load(q, kq + (c * L + lane) * W);
+        }
+        vr[t].load(v, gi * Dv + row0);
+        gr[t].load(g, gi);
+        br[t].load(beta, gi);
+        mk[t] = mask != nullptr ? mask[bt] : 1u;
+    }
+
+    auto widen = [&](const RawIo<IO, W> (&raw)[NC], float (&out)[E]) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int w = 0; w < W; ++w) out[c * W + w] = raw[c].at(w);
+    };
+    float kq[TMAX];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+        float kk[E], qq[E];
+        widen(kr[t], kk);
+        widen(qr[t], qq);
+        kq[t] = lane_dot<E>(kk, qq);
+    }
+    row16_sum_n<TMAX>(kq);
+
+    const bool capture = row0 == 0;                           // first row group of the head
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+        if (static_cast<uint32_t>(t) >= T) break;
+        if (mk[t] == 0u) continue;                            // inactive step: no decay, no writes
+        const size_t bt = static_cast<size_t>(b) * T + t;
+        const size_t gi = bt * Hv + hv;
+        const size_t vo = gi * Dv + row0;
+        if (capture) {                                        // tape capture: bit copies
+            if (k_log != nullptr)
+#pragma unroll
+                for (int c = 0; c < NC; ++c) kr[t][c].store(k_log, gi * DK + (c * L + lane) * W);
+            if (g_log != nullptr && lane == 0) gr[t].store(g_log, gi);
+        }
+        float kk[E], qq[E], vv[RPT];
+        widen(kr[t], kk);
+        widen(qr[t], qq);
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) vv[r] = vr[t].at(r);
+        float d[RPT], out[RPT];
+        record_step<RPT, E>(s, kk, qq, vv, gr[t].at(0), br[t].at(0), kq[t], d, out);
+        if (delta_log != nullptr && lane == 0) io_store_vec<IO, RPT>(delta_log, vo, d);
+        if (lane == 0) io_store_vec<IO, RPT>(y, vo, out);
+    }
+
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) store_state_row<W, NC, E>(state_out + srow + r * DK, lane, s[r]);
+}
+
 // ------------------------------------------------------------ staged kernel
 
 // Chunk lengths of the staged kernel: the inputs of up to TC steps sit in LDS
@@ -437,24 +576,6 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
     for (int r = 0; r < RPT; ++r) store_state_row<W, NC, E>(state_out + srow + r * DK, lane, s[r]);
 }
 
-// Compute units of the current device (cached per device; 256, the MI355X
-// count, if the runtime cannot say).
-uint32_t compute_units() {
-    constexpr int kDevices = 64;
-    static std::atomic<uint32_t> cache[kDevices];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 256;
-    uint32_t c = cache[dev].load(std::memory_order_relaxed);
-    if (c == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        c = static_cast<uint32_t>(n);
-        cache[dev].store(c, std::memory_order_relaxed);
-    }
-    return c;
-}
-
 template <int IO, int DK, int RPT, int NT>
 hipError_t launch_cfg(const RecordArgs& a, hipStream_t stream) {
     constexpr int R = RPT * NT / 16;
@@ -466,6 +587,15 @@ hipError_t launch_cfg(const RecordArgs& a, hipStream_t stream) {
                            a.state_out, a.delta_log, a.k_log, a.g_log, a.T, a.Hk, a.Hv, a.Dv,
                            row_blocks, a.map);
         return hipGetLastError();
+    }
+    if constexpr (RPT <= 2) {
+        if (a.T <= kShortDirectSteps) {
+            hipLaunchKernelGGL((gdn_record_short_kernel<IO, DK, RPT, NT, kShortDirectSteps>),
+                               dim3(static_cast<uint32_t>(grid)), dim3(NT), 0, stream, a.q, a.k, a.v, a.g,
+                               a.beta, a.state_in, a.mask, a.y, a.state_out, a.delta_log, a.k_log, a.g_log,
+                               a.T, a.Hk, a.Hv, a.Dv, row_blocks, a.map);
+            return hipGetLastError();
+        }
     }
     if constexpr (R <= kStagedMaxRows) {
         const bool masked = a.mask != nullptr;
@@ -533,6 +663,24 @@ hipError_t launch_io(const RecordArgs& a, const RowTiling& t, hipStream_t stream
 
 }  // namespace
 
+// Compute units of the current device (cached per device; 256, the MI355X
+// count, if the runtime cannot say).
+uint32_t compute_units() {
+    constexpr int kDevices = 64;
+    static std::atomic<uint32_t> cache[kDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 256;
+    uint32_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        c = static_cast<uint32_t>(n);
+        cache[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
+
 bool dk_supported(uint32_t Dk) {
     return Dk == 32 || Dk == 64 || Dk == 128 || Dk == 192 || Dk == 256;
 }
@@ -558,6 +706,7 @@ RowTiling record_tiling(const RecordArgs& a) {
 }
 
 hipError_t launch_record(const RecordArgs& a, hipStream_t stream) {
+    if (record_mfma_applies(a)) return launch_record_mfma(a, stream);
     const RowTiling t = record_tiling(a);
     switch (a.io) {
         case kF32: return launch_io<kF32>(a, t, stream);

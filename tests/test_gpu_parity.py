@@ -560,6 +560,54 @@ def test_every_tiling_gives_identical_bits(T):
             assert all(torch.equal(a, b) for a, b in zip(ref, cur)), til
 
 
+# Records of 2..4 steps of bf16 I/O with Dv a multiple of 64 run their dense
+# products on the matrix cores; a forced tiling runs the VALU kernels.
+MFMA_RECORD = [
+    # B, T, Hk, Hv, Dk, Dv, map, mask
+    (8, 4, 16, 32, 128, 128, "block", "trailing"),     # the speculative-decode shape
+    (3, 2, 2, 4, 64, 64, "tiled", "bernoulli"),
+    (2, 3, 1, 3, 192, 128, "block", "none"),
+    (4, 4, 2, 2, 32, 256, "tiled", "ones"),
+    (2, 4, 2, 4, 128, 64, "block", "zeros"),
+    (1, 2, 4, 8, 64, 192, "tiled", "bernoulli"),
+    (5, 3, 3, 6, 128, 128, "tiled", "trailing"),
+]
+
+
+@pytest.mark.parametrize("case", MFMA_RECORD, ids=lambda c: "B%d_T%d_Hk%d_Hv%d_Dk%d_Dv%d_%s_%s" % c)
+def test_short_record_on_matrix_cores(case):
+    """Against the oracle (sentinels at inactive steps) and against the VALU
+    kernels (a forced tiling) at the bf16 tolerance."""
+    B, T, Hk, Hv, Dk, Dv, gqa_map, mask = case
+    inp = gi.record_inputs(B, T, Hk, Hv, Dk, Dv, "bf16", seed=171 + T + Dk, mask=mask)
+    _check_record(inp, gqa_map, "matrix-core record %s" % (case,))
+    note("matrix-core record against the VALU kernels %s" % (case,))
+    y0, s0, d0 = _record_gpu(inp, gqa_map)
+    y1, s1, d1 = _record_tiled(inp, gqa_map, (1, 64))
+    act = np.broadcast_to(step_mask(inp["mask"], B, T)[:, :, None, None], y0.shape)
+    assert_close(y0, f64(y1), torch.bfloat16, "y, matrix cores vs VALU", where=act)
+    assert_close(d0, f64(d1), torch.bfloat16, "delta, matrix cores vs VALU", where=act)
+    assert_close(s0, f64(s1), torch.bfloat16, "state, matrix cores vs VALU")
+
+
+@pytest.mark.parametrize("T", [2, 4])
+def test_short_record_on_matrix_cores_with_extreme_gates_and_betas(T):
+    """Gates of exactly 0, 1, 1e-6 and 1.25 and beta of exactly 0 and 1."""
+    B, Hk, Hv, Dk, Dv = 3, 2, 4, 128, 64
+    inp = gi.record_inputs(B, T, Hk, Hv, Dk, Dv, "bf16", seed=181 + T, mask="bernoulli")
+    g = inp["g"].float().clone()
+    beta = inp["beta"].float().clone()
+    g[:, 0, 0] = 0.0
+    g[:, 1, 1] = 1.0
+    g[:, T - 1, 2] = 1e-6
+    g[:, 1:, 3] = 1.25
+    beta[:, 0, 1] = 0.0
+    beta[:, T - 1, 0] = 1.0
+    inp["g"] = g.to(torch.bfloat16)
+    inp["beta"] = beta.to(torch.bfloat16)
+    _check_record(inp, "block", "matrix-core record, extreme gates T=%d" % T)
+
+
 def test_launch_choice_none_is_the_plain_call():
     """gdn_record_debug / gdn_replay_debug with nothing forced give the plain
     calls' bits."""
