@@ -799,6 +799,32 @@ def test_gqa_expand_unaligned_views_and_batch_dims():
     assert out.cpu().view(torch.int16).numpy().reshape(15, 6, 24).tobytes() == want.tobytes()
 
 
+def test_gqa_expand_past_32_bit_indices():
+    """More than 2^32 source vectors (2-byte elements at a 2-byte offset, so
+    one element per vector) take the kernel's 64-bit index path: 8.8 GB
+    expanded into 17.6 GB on the device, with rows sampled around the 2^32
+    vector boundary, at both ends and at random checked against the oracle's
+    expansion of the same rows."""
+    seq, hg, h, kk = 22_000_000, 2, 4, 100                   # 4.4e9 source elements
+    assert seq * hg * kk > 2 ** 32
+    note("gqa_expand with 64-bit indices: %d x %d x %d bf16 -> %d heads" % (seq, hg, kk, h))
+    raw = torch.empty(seq * hg * kk + 1, dtype=torch.int16, device=dev())
+    raw.random_(-32768, 32767, generator=torch.Generator(device=dev()).manual_seed(7))
+    src = raw[1:].view(torch.bfloat16).view(seq, hg, kk)      # 2-byte offset: 2-byte vectors
+    out = gdn.gqa_expand(src, h, "block")
+    torch.cuda.synchronize()
+    boundary = (2 ** 32) // (hg * kk)                         # the seq row holding vector 2^32
+    rows = sorted({0, 1, seq - 1, boundary - 1, boundary, boundary + 1} |
+                  set(np.random.Generator(np.random.PCG64(3)).integers(0, seq, size=12).tolist()))
+    assert max(rows) < seq
+    idx = torch.tensor(rows, device=dev())
+    got = out.index_select(0, idx).view(torch.int16).cpu().numpy()
+    want = oracle.gqa_expand(src.index_select(0, idx).view(torch.int16).cpu().numpy(), h, "block")
+    assert got.tobytes() == want.tobytes()
+    del out, raw, src
+    torch.cuda.empty_cache()
+
+
 def test_tolerances_are_the_stated_ones():
     assert TOL[torch.float32] == 1e-3 and TOL[torch.bfloat16] == 2e-2 and TOL[torch.float16] == 2e-2
 
