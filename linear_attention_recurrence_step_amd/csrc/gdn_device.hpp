@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace gdn {
 
 // I/O dtype codes (same values as gdn_dtype in include/gdn.h).
@@ -146,34 +148,129 @@ __device__ __forceinline__ void io_copy_vec(const void* src, size_t si, void* ds
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Non-temporal load of N consecutive float32 values (the recurrent state,
-// read exactly once per launch); 8- or 16-byte aligned.  The streaming hint
-// keeps the state from evicting reusable lines and measurably raises read
-// bandwidth on this part.
+// N consecutive I/O elements held as their raw bits (in pieces of at most 16
+// bytes), widened only where they are used, so that a load is never waited
+// for where it is issued.
+template <int IO, int N>
+struct RawIo {
+    static constexpr int EB = IoTraits<IO>::kBytes;
+    static constexpr int BYTES = N * EB;
+    static constexpr int PB = BYTES < 16 ? BYTES : 16;       // bytes per piece
+    static constexpr int NP = BYTES / PB;
+    static constexpr int PER = PB / EB;                      // elements per piece
+    using V = typename RawVec<PB>::T;
+    V raw[NP];
+    __device__ __forceinline__ void load(const void* base, size_t idx) {
+        const char* p = static_cast<const char*>(base) + idx * EB;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) raw[i] = *reinterpret_cast<const V*>(p + i * PB);
+    }
+    __device__ __forceinline__ void store(void* base, size_t idx) const {
+        char* p = static_cast<char*>(base) + idx * EB;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) *reinterpret_cast<V*>(p + i * PB) = raw[i];
+    }
+    __device__ __forceinline__ float at(int e) const {
+        const V& piece = raw[e / PER];
+        const int j = e % PER;
+        if constexpr (PB >= 4) {
+            uint32_t w[PB / 4];
+            __builtin_memcpy(w, &piece, PB);
+            if constexpr (IO == kF32) return __uint_as_float(w[j]);
+            const uint32_t bits = (w[j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+            return IO == kBF16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
+        } else {
+            const uint32_t bits = piece;
+            return IO == kBF16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
+        }
+    }
+};
+
+
+// Streaming accesses: data that one launch reads once (the recurrent state,
+// a tape, a source to copy) or writes once, with the non-temporal hint both
+// ways.  Non-temporal stores measured faster than plain ones where it counts:
+// back-to-back decode steps over inputs too large to stay in the caches
+// (every write-back paid inside the timing) ran 355 us a step with them and
+// 372 us with plain stores (380 us with plain loads too).  Timed in
+// isolation after a cache scrub, plain stores look faster, because up to a
+// cache's worth of their write-backs is left for whatever runs next.
+template <typename V>
+__device__ __forceinline__ V stream_load(const V* p) {
+    return __builtin_nontemporal_load(p);
+}
+template <typename V>
+__device__ __forceinline__ void stream_store(V v, V* p) {
+    __builtin_nontemporal_store(v, p);
+}
+
+// N consecutive float32 values of the state (read once per launch); 8- or
+// 16-byte aligned.
 template <int N>
 __device__ __forceinline__ void f32_load_vec(const float* p, float (&out)[N]) {
     static_assert(N == 2 || N == 4, "state chunks are 2 or 4 floats");
     if constexpr (N == 4) {
-        f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        f32x4 v = stream_load(reinterpret_cast<const f32x4*>(p));
         out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
     } else {
-        f32x2 v = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+        f32x2 v = stream_load(reinterpret_cast<const f32x2*>(p));
         out[0] = v.x; out[1] = v.y;
     }
 }
 
-// Non-temporal store of N floats: the state written back is not re-read by
-// this launch, so it should not displace reusable lines from the caches.
+// N floats of the state, written once per launch.
 template <int N>
-__device__ __forceinline__ void f32_store_vec_nt(float* p, const float (&in)[N]) {
+__device__ __forceinline__ void f32_store_vec(float* p, const float (&in)[N]) {
     static_assert(N == 2 || N == 4, "state chunks are 2 or 4 floats");
     if constexpr (N == 4) {
-        f32x4 v = {in[0], in[1], in[2], in[3]};
-        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+        stream_store(f32x4{in[0], in[1], in[2], in[3]}, reinterpret_cast<f32x4*>(p));
     } else {
-        f32x2 v = {in[0], in[1]};
-        __builtin_nontemporal_store(v, reinterpret_cast<f32x2*>(p));
+        stream_store(f32x2{in[0], in[1]}, reinterpret_cast<f32x2*>(p));
     }
+}
+
+// A thread's RPT consecutive state rows (row r at p + r * 16 * E floats),
+// lane `lane` holding the columns {(c * 16 + lane) * W + w} of each.  The
+// rows are visited by a fold, not a loop: a one-trip loop over the rows (one
+// row per thread) survived until the backend's loop-invariant code motion,
+// which rewrote its stores without the non-temporal hint.
+template <int E, size_t... R>
+__device__ __forceinline__ void load_rows_impl(const float* p, uint32_t lane, float (&s)[sizeof...(R)][E],
+                                               std::index_sequence<R...>) {
+    constexpr int W = E < 4 ? E : 4;
+    auto one = [&](const float* row, float (&dst)[E]) {
+#pragma unroll
+        for (int c = 0; c < E / W; ++c) {
+            float t[W];
+            f32_load_vec<W>(row + (c * 16 + lane) * W, t);
+#pragma unroll
+            for (int w = 0; w < W; ++w) dst[c * W + w] = t[w];
+        }
+    };
+    (one(p + R * 16 * E, s[R]), ...);
+}
+template <int E, size_t... R>
+__device__ __forceinline__ void store_rows_impl(float* p, uint32_t lane, const float (&s)[sizeof...(R)][E],
+                                                std::index_sequence<R...>) {
+    constexpr int W = E < 4 ? E : 4;
+    auto one = [&](float* row, const float (&src)[E]) {
+#pragma unroll
+        for (int c = 0; c < E / W; ++c) {
+            float t[W];
+#pragma unroll
+            for (int w = 0; w < W; ++w) t[w] = src[c * W + w];
+            f32_store_vec<W>(row + (c * 16 + lane) * W, t);
+        }
+    };
+    (one(p + R * 16 * E, s[R]), ...);
+}
+template <int RPT, int E>
+__device__ __forceinline__ void load_state_rows(const float* p, uint32_t lane, float (&s)[RPT][E]) {
+    load_rows_impl<E>(p, lane, s, std::make_index_sequence<RPT>{});
+}
+template <int RPT, int E>
+__device__ __forceinline__ void store_state_rows(float* p, uint32_t lane, const float (&s)[RPT][E]) {
+    store_rows_impl<E>(p, lane, s, std::make_index_sequence<RPT>{});
 }
 
 // Wait until every vector memory load and store issued so far has completed

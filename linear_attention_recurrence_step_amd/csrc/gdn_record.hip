@@ -92,30 +92,14 @@ __device__ __forceinline__ void record_step(float (&s)[RPT][E], const float (&kk
         for (int e = 0; e < E; ++e) s[r][e] = fmaf(kk[e], d[r], s[r][e]);   // rank-1 write
 }
 
-template <int W, int NC, int E>
-__device__ __forceinline__ void load_state_row(const float* p, uint32_t lane, float (&row)[E]) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        float t4[W];
-        f32_load_vec<W>(p + (c * 16 + lane) * W, t4);
-#pragma unroll
-        for (int w = 0; w < W; ++w) row[c * W + w] = t4[w];
-    }
-}
-
-template <int W, int NC, int E>
-__device__ __forceinline__ void store_state_row(float* p, uint32_t lane, const float (&row)[E]) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        float t4[W];
-#pragma unroll
-        for (int w = 0; w < W; ++w) t4[w] = row[c * W + w];
-        f32_store_vec_nt<W>(p + (c * 16 + lane) * W, t4);
-    }
-}
-
 // ------------------------------------------------------------ direct kernel
 
+// One step (T = 1, decode).  Every input of the step (k, q, v, g, beta and
+// the mask word) is issued right behind the state loads, so the kernel
+// waits for memory once; there is no step loop, whose loop-carried state
+// registers had made the compiler wait for the state before issuing the
+// step's loads.  An inactive step leaves the state as loaded and writes
+// nothing.
 template <int IO, int DK, int RPT, int NT>
 __global__ __launch_bounds__(NT) void gdn_record_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
@@ -123,7 +107,7 @@ __global__ __launch_bounds__(NT) void gdn_record_kernel(
     const float* state_in, const uint32_t* __restrict__ mask,
     void* __restrict__ y, float* state_out, void* __restrict__ delta_log,
     void* __restrict__ k_log, void* __restrict__ g_log,
-    uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dv, uint32_t row_blocks, int tiled)
+    uint32_t Hk, uint32_t Hv, uint32_t Dv, uint32_t row_blocks, int tiled)
 {
     constexpr int L = 16;                 // lanes per state row
     constexpr int E = DK / L;             // state values per lane per row
@@ -144,86 +128,62 @@ __global__ __launch_bounds__(NT) void gdn_record_kernel(
     const size_t srow = (static_cast<size_t>(blk) * R + slot * RPT) * DK;
 
     float s[RPT][E];
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) load_state_row<W, NC, E>(state_in + srow + r * DK, lane, s[r]);
+    load_state_rows<RPT, E>(state_in + srow, lane, s);
 
-    const uint32_t n = blk / row_blocks;                      // b * Hv + hv
+    const uint32_t n = blk / row_blocks;                      // b * Hv + hv (= bt * Hv + hv: T = 1)
     const uint32_t row0 = (blk - n * row_blocks) * R + slot * RPT;  // first row within the head
     const uint32_t b = n / Hv;
     const uint32_t hv = n - b * Hv;
     const uint32_t hk = tiled ? hv % Hk : hv / (Hv / Hk);
-    const bool capture = row0 == 0;                           // first row group of the head
+    const size_t kq = (static_cast<size_t>(b) * Hk + hk) * DK;
+    const size_t vo = static_cast<size_t>(n) * Dv + row0;
 
-    for (uint32_t t = 0; t < T; ++t) {
-        const size_t bt = static_cast<size_t>(b) * T + t;
-        if (mask != nullptr && mask[bt] == 0u) continue;      // inactive step: no decay, no writes
+    RawIo<IO, W> kr[NC], qr[NC];
+    RawIo<IO, RPT> vr;
+    RawIo<IO, 1> gr, br;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        kr[c].load(k, kq + (c * L + lane) * W);
+        qr[c].load(q, kq + (c * L + lane) * W);
+    }
+    vr.load(v, vo);
+    gr.load(g, n);
+    br.load(beta, n);
+    const bool active = mask == nullptr || mask[b] != 0u;
 
-        const size_t gi = bt * Hv + hv;
-        const float gt = io_load1<IO>(g, gi);
-        const float bt_beta = io_load1<IO>(beta, gi);
-        const size_t kq = (bt * Hk + hk) * DK;
-        const size_t vo = gi * Dv + row0;
-        if (capture) {                                        // tape capture: bit copies
+    // One exit: an inactive step (no decay, no writes) falls through to the
+    // state store.  (An early return there was structurized into a cycle
+    // whose loop-invariant code motion dropped the non-temporal hint from
+    // the state stores.)
+    if (active) {
+        if (row0 == 0) {                                      // tape capture: bit copies
             if (k_log != nullptr)
 #pragma unroll
-                for (int c = 0; c < NC; ++c)
-                    io_copy_vec<IO, W>(k, kq + (c * L + lane) * W, k_log, gi * DK + (c * L + lane) * W);
-            if (g_log != nullptr && lane == 0) io_copy_vec<IO, 1>(g, gi, g_log, gi);
+                for (int c = 0; c < NC; ++c) kr[c].store(k_log, static_cast<size_t>(n) * DK + (c * L + lane) * W);
+            if (g_log != nullptr && lane == 0) gr.store(g_log, n);
         }
-
         float kk[E], qq[E], vv[RPT];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            float tk[W], tq[W];
-            io_load_vec<IO, W>(k, kq + (c * L + lane) * W, tk);
-            io_load_vec<IO, W>(q, kq + (c * L + lane) * W, tq);
+        for (int c = 0; c < NC; ++c)
 #pragma unroll
-            for (int w = 0; w < W; ++w) { kk[c * W + w] = tk[w]; qq[c * W + w] = tq[w]; }
-        }
-        io_load_vec<IO, RPT>(v, vo, vv);
-
+            for (int w = 0; w < W; ++w) {
+                kk[c * W + w] = kr[c].at(w);
+                qq[c * W + w] = qr[c].at(w);
+            }
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) vv[r] = vr.at(r);
         float kqs[1] = {lane_dot<E>(kk, qq)};
         row16_sum_n<1>(kqs);
         float d[RPT], out[RPT];
-        record_step<RPT, E>(s, kk, qq, vv, gt, bt_beta, kqs[0], d, out);
+        record_step<RPT, E>(s, kk, qq, vv, gr.at(0), br.at(0), kqs[0], d, out);
         if (delta_log != nullptr && lane == 0) io_store_vec<IO, RPT>(delta_log, vo, d);
         if (lane == 0) io_store_vec<IO, RPT>(y, vo, out);
     }
 
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) store_state_row<W, NC, E>(state_out + srow + r * DK, lane, s[r]);
+    store_state_rows<RPT, E>(state_out + srow, lane, s);
 }
 
 // ------------------------------------------------------ short-tape kernel
-
-// N consecutive I/O elements held as their raw bits (N * element size <= 16
-// bytes), widened only where they are used, so that a load is never waited
-// for where it is issued.
-template <int IO, int N>
-struct RawIo {
-    static constexpr int EB = IoTraits<IO>::kBytes;
-    using V = typename RawVec<N * EB>::T;
-    static_assert(N * EB <= 16, "one vector access");
-    V raw;
-    __device__ __forceinline__ void load(const void* base, size_t idx) {
-        raw = *reinterpret_cast<const V*>(static_cast<const char*>(base) + idx * EB);
-    }
-    __device__ __forceinline__ void store(void* base, size_t idx) const {
-        *reinterpret_cast<V*>(static_cast<char*>(base) + idx * EB) = raw;
-    }
-    __device__ __forceinline__ float at(int e) const {
-        if constexpr (N * EB >= 4) {
-            uint32_t w[(N * EB) / 4];
-            __builtin_memcpy(w, &raw, N * EB);
-            if constexpr (IO == kF32) return __uint_as_float(w[e]);
-            const uint32_t bits = (w[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-            return IO == kBF16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
-        } else {
-            const uint32_t bits = raw;
-            return IO == kBF16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
-        }
-    }
-};
 
 // Tapes of at most this many steps run the short-tape kernel.
 constexpr uint32_t kShortDirectSteps = 4;
@@ -258,8 +218,7 @@ __global__ __launch_bounds__(NT) void gdn_record_short_kernel(
     const size_t srow = (static_cast<size_t>(blk) * R + slot * RPT) * DK;
 
     float s[RPT][E];
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) load_state_row<W, NC, E>(state_in + srow + r * DK, lane, s[r]);
+    load_state_rows<RPT, E>(state_in + srow, lane, s);
 
     const uint32_t n = blk / row_blocks;                      // b * Hv + hv
     const uint32_t row0 = (blk - n * row_blocks) * R + slot * RPT;
@@ -329,8 +288,7 @@ __global__ __launch_bounds__(NT) void gdn_record_short_kernel(
         if (lane == 0) io_store_vec<IO, RPT>(y, vo, out);
     }
 
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) store_state_row<W, NC, E>(state_out + srow + r * DK, lane, s[r]);
+    store_state_rows<RPT, E>(state_out + srow, lane, s);
 }
 
 // ------------------------------------------------------------ staged kernel
@@ -457,8 +415,7 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
     const size_t srow = ((static_cast<size_t>(b) * Hv + hv) * Dv + wrow0 + slot * RPT) * DK;
 
     float s[RPT][E];
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) load_state_row<W, NC, E>(state_in + srow + r * DK, lane, s[r]);
+    load_state_rows<RPT, E>(state_in + srow, lane, s);
 
     ChunkStager<IO, TC, DK, piece_elems<IO, DK>(), NT> stk, stq;
     ChunkStager<IO, TC, R, PR, NT> stv;
@@ -572,8 +529,7 @@ __global__ __launch_bounds__(NT) void gdn_record_staged_kernel(
     __syncthreads();
     flush_chunk(((T - 1) / TC) * TC);
 
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) store_state_row<W, NC, E>(state_out + srow + r * DK, lane, s[r]);
+    store_state_rows<RPT, E>(state_out + srow, lane, s);
 }
 
 template <int IO, int DK, int RPT, int NT>
@@ -584,7 +540,7 @@ hipError_t launch_cfg(const RecordArgs& a, hipStream_t stream) {
     if (a.T == 1) {
         hipLaunchKernelGGL((gdn_record_kernel<IO, DK, RPT, NT>), dim3(static_cast<uint32_t>(grid)),
                            dim3(NT), 0, stream, a.q, a.k, a.v, a.g, a.beta, a.state_in, a.mask, a.y,
-                           a.state_out, a.delta_log, a.k_log, a.g_log, a.T, a.Hk, a.Hv, a.Dv,
+                           a.state_out, a.delta_log, a.k_log, a.g_log, a.Hk, a.Hv, a.Dv,
                            row_blocks, a.map);
         return hipGetLastError();
     }
@@ -687,16 +643,20 @@ bool dk_supported(uint32_t Dk) {
 
 RowTiling record_tiling(const RecordArgs& a) {
     if (a.forced.rows_per_thread != 0) return a.forced;      // checked by the caller
-    // Up to 16 steps (decode, speculative decode): two rows per thread over
-    // 256-thread groups measured fastest while that still gives 1024 groups
-    // (2% faster than one row per thread at a 512 MiB decode step, 20% at an
-    // 8-sequence speculative step, where each thread's two rows keep twice the
-    // loads in flight); then one row per thread, then one-wave groups.  Long
-    // tapes take 16-row groups (one per CU at a 32-head prefill), or one-wave
-    // groups when even that leaves CUs idle.
+    // Up to 16 steps (speculative decode, and decode at Dk below 128): two
+    // rows per thread over 256-thread groups measured fastest while that still
+    // gives 1024 groups (20% faster than one row per thread at an 8-sequence
+    // speculative step, where each thread's two rows keep twice the loads in
+    // flight); then one row per thread, then one-wave groups.  Long tapes take
+    // 16-row groups (one per CU at a 32-head prefill), or one-wave groups when
+    // even that leaves CUs idle.
     static const int kShort[] = {3, 4};             // (1,256), (1,64)
     static const int kLong[] = {3, 4};              // (1,256), (1,64)
     const uint64_t heads = static_cast<uint64_t>(a.B) * a.Hv;
+    // One step at Dk >= 128: one row per thread (two 16-byte state pieces or
+    // more per lane already), 352 against 357 us a decode step of 512 MiB
+    // of state run back to back, every write-back paid.
+    if (a.T == 1 && a.Dk >= 128) return pick_tiling(heads, a.Dk, a.Dv, 2048, kShort, 2);
     if (a.T <= 16) {
         const RowTiling& wide = kTilings[2];                  // (2,256)
         if (tiling_fits(wide, a.Dk, a.Dv) && heads * (a.Dv / wide.rows()) >= 1024) return wide;

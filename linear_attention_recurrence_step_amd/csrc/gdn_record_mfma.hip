@@ -146,7 +146,7 @@ __global__ __launch_bounds__(64) void gdn_record_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const size_t off = ROWS_IN ? (l + 64u * i) * 4 : lr * DK + 16 * i + 4 * lg;
-        sreg[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sin + off));
+        sreg[i] = stream_load(reinterpret_cast<const f32x4*>(sin + off));
     }
 
     // staged key / query pieces of this lane, piece p = l + 64 j: which (0
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(64) void gdn_record_mfma_kernel(
     for (int i = 0; i < NI; ++i) {
         const int p = static_cast<int>(l) + 64 * i;
         const f32x4 r = *reinterpret_cast<const f32x4*>(sbuf + (p / (DK / 4)) * Lds::SROW + (p % (DK / 4)) * 16);
-        __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(sout + (l + 64u * i) * 4));
+        stream_store(r, reinterpret_cast<f32x4*>(sout + (l + 64u * i) * 4));
     }
 }
 

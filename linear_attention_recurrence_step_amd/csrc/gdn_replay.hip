@@ -28,6 +28,11 @@
 namespace gdn {
 namespace {
 
+// At most one taken position (steps <= 1, so only position 0 can be taken):
+// the state loads and position 0's tape loads go out together, the fold
+// runs at most once, and there is no position loop (its loop-carried state
+// registers had made the compiler wait for the state before issuing the
+// tape's loads).
 template <int IO, int DK, int RPT, int NT>
 __global__ __launch_bounds__(NT) void gdn_replay_kernel(
     const void* __restrict__ delta_log, const void* __restrict__ k_log,
@@ -52,52 +57,38 @@ __global__ __launch_bounds__(NT) void gdn_replay_kernel(
     const size_t srow = (static_cast<size_t>(blk) * R + slot * RPT) * DK;
 
     float s[RPT][E];
-#pragma unroll
-    for (int r = 0; r < RPT; ++r)
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            float t4[W];
-            f32_load_vec<W>(state_in + srow + r * DK + (c * L + lane) * W, t4);
-#pragma unroll
-            for (int w = 0; w < W; ++w) s[r][c * W + w] = t4[w];
-        }
+    load_state_rows<RPT, E>(state_in + srow, lane, s);
 
     const uint32_t n = blk / row_blocks;          // b * Hv + hv
     const uint32_t row0 = (blk - n * row_blocks) * R + slot * RPT;
     const uint32_t b = n / Hv;
     const uint32_t hv = n - b * Hv;
+    const size_t bt = static_cast<size_t>(b) * T_log;         // position 0
+    const size_t gi = bt * Hv + hv;
 
-    for (uint32_t t = 0; t < steps; ++t) {
-        const size_t bt = static_cast<size_t>(b) * T_log + t;
-        if (mask != nullptr && mask[bt] == 0u) continue;     // untaken position
+    RawIo<IO, W> kr[NC];
+    RawIo<IO, RPT> dr;
+    RawIo<IO, 1> gr;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kr[c].load(k_log, gi * DK + (c * L + lane) * W);
+    dr.load(delta_log, gi * Dv + row0);
+    gr.load(g_log, gi);
+    const bool take = steps > 0u && (mask == nullptr || mask[bt] != 0u);
 
-        const size_t gi = bt * Hv + hv;
-        const float gt = io_load1<IO>(g_log, gi);
-        float kk[E], dd[RPT];
+    if (take) {
+        const float gt = gr.at(0);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            float tk[W];
-            io_load_vec<IO, W>(k_log, gi * DK + (c * L + lane) * W, tk);
+        for (int r = 0; r < RPT; ++r) {
+            const float dd = dr.at(r);
 #pragma unroll
-            for (int w = 0; w < W; ++w) kk[c * W + w] = tk[w];
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int w = 0; w < W; ++w)
+                    s[r][c * W + w] = fmaf(kr[c].at(w), dd, s[r][c * W + w] * gt);
         }
-        io_load_vec<IO, RPT>(delta_log, gi * Dv + row0, dd);
-
-#pragma unroll
-        for (int r = 0; r < RPT; ++r)
-#pragma unroll
-            for (int e = 0; e < E; ++e) s[r][e] = fmaf(kk[e], dd[r], s[r][e] * gt);
     }
 
-#pragma unroll
-    for (int r = 0; r < RPT; ++r)
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            float t4[W];
-#pragma unroll
-            for (int w = 0; w < W; ++w) t4[w] = s[r][c * W + w];
-            f32_store_vec_nt<W>(state_out + srow + r * DK + (c * L + lane) * W, t4);
-        }
+    store_state_rows<RPT, E>(state_out + srow, lane, s);
 }
 
 // The LDS operands of one tape position for one lane: its E columns of k_log,
@@ -200,15 +191,7 @@ __global__ __launch_bounds__(NT) void gdn_replay_staged_kernel(
     const size_t srow = (static_cast<size_t>(blk) * R + slot * RPT) * DK;
 
     float s[RPT][E];
-#pragma unroll
-    for (int r = 0; r < RPT; ++r)
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            float t4[W];
-            f32_load_vec<W>(state_in + srow + r * DK + (c * L + lane) * W, t4);
-#pragma unroll
-            for (int w = 0; w < W; ++w) s[r][c * W + w] = t4[w];
-        }
+    load_state_rows<RPT, E>(state_in + srow, lane, s);
 
     const uint32_t n = blk / row_blocks;          // b * Hv + hv
     const uint32_t wrow0 = (blk - n * row_blocks) * R;
@@ -312,15 +295,7 @@ __global__ __launch_bounds__(NT) void gdn_replay_staged_kernel(
             for (int e = 0; e < E; ++e) s[r][e] *= scale;
     }
 
-#pragma unroll
-    for (int r = 0; r < RPT; ++r)
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            float t4[W];
-#pragma unroll
-            for (int w = 0; w < W; ++w) t4[w] = s[r][c * W + w];
-            f32_store_vec_nt<W>(state_out + srow + r * DK + (c * L + lane) * W, t4);
-        }
+    store_state_rows<RPT, E>(state_out + srow, lane, s);
 }
 
 template <int IO, int DK, int RPT, int NT>

@@ -169,7 +169,7 @@ __global__ __launch_bounds__(64 * NW, DK <= 128 ? 4 : 2) void gdn_replay_mfma_ke
             for (int h = 0; h < 2; ++h) {
                 const int tt = 2 * q + h < last ? 2 * q + h : last;
                 const size_t bt = static_cast<size_t>(b) * T_log + t0 + tt;
-                kr[u][h] = __builtin_nontemporal_load(
+                kr[u][h] = stream_load(
                     reinterpret_cast<const u32x4*>(kb + ((bt * Hv + hv) * DK + cg * 8) * 2));
                 kmw[u][h] = mask_at(t0 + tt);
             }
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(64 * NW, DK <= 128 ? 4 : 2) void gdn_replay_mfma_ke
             for (int h = 0; h < 2; ++h) {
                 const int tt = 2 * q + h < last ? 2 * q + h : last;
                 const size_t bt = static_cast<size_t>(b) * T_log + t0 + tt;
-                dr[u][h] = __builtin_nontemporal_load(
+                dr[u][h] = stream_load(
                     reinterpret_cast<const u32x4*>(db + ((bt * Hv + hv) * Dv + dv0 + dg * 8) * 2));
                 dmw[u][h] = mask_at(t0 + tt);
             }
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(64 * NW, DK <= 128 ? 4 : 2) void gdn_replay_mfma_ke
     auto load_state = [&]() {
 #pragma unroll
         for (int u = 0; u < NI; ++u)
-            sreg[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sin + (l + 64 * u) * 4));
+            sreg[u] = stream_load(reinterpret_cast<const f32x4*>(sin + (l + 64 * u) * 4));
     };
     f32x4v acc[NI];
 #pragma unroll
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(64 * NW, DK <= 128 ? 4 : 2) void gdn_replay_mfma_ke
         const f32x4 r = absorbed ? uu
                                  : f32x4{fmaf(Gamma, sreg[u].x, uu.x), fmaf(Gamma, sreg[u].y, uu.y),
                                          fmaf(Gamma, sreg[u].z, uu.z), fmaf(Gamma, sreg[u].w, uu.w)};
-        __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(sout + (l + 64 * u) * 4));
+        stream_store(r, reinterpret_cast<f32x4*>(sout + (l + 64 * u) * 4));
     }
 }
 

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void gqa_expand_kernel(
     const uint32_t group = h / hg;
     const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
     for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < nvec; i += stride) {
-        const V val = __builtin_nontemporal_load(src + i);
+        const V val = stream_load(src + i);
         uint64_t s;
         uint32_t c, hs;
         if constexpr (WIDE) {
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void gqa_expand_kernel(
         }
         for (uint32_t j = 0; j < group; ++j) {
             const uint32_t hd = tiled ? j * hg + hs : hs * group + j;
-            __builtin_nontemporal_store(val, dst + (s * h + hd) * row_vecs + c);
+            stream_store(val, dst + (s * h + hd) * row_vecs + c);
         }
     }
 }

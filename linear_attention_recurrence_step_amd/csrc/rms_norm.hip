@@ -60,7 +60,7 @@ __global__ __launch_bounds__(NT) void rms_norm_vec_kernel(
         for (int j = 0; j < MAXV; ++j) {
             const uint32_t p = threadIdx.x + j * NT;
             v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (p < nv) v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x + row) + p);
+            if (p < nv) v[j] = stream_load(reinterpret_cast<const f32x4*>(x + row) + p);
         }
 #pragma unroll
         for (int j = 0; j < MAXV; ++j)
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(NT) void rms_norm_vec_kernel(
                                  v[j].y * r * bf16_bits_to_f32(wb.x >> 16),
                                  v[j].z * r * bf16_bits_to_f32(wb.y & 0xffffu),
                                  v[j].w * r * bf16_bits_to_f32(wb.y >> 16)};
-                __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(out + row) + p);
+                stream_store(o, reinterpret_cast<f32x4*>(out + row) + p);
             }
         }
         if constexpr (NT > 64) __syncthreads();               // red is reused by the next token
