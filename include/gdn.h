@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum gdn_dtype {
     GDN_F32 = 0,
@@ -196,7 +196,10 @@ int gqa_expand(const void* src, void* dst, uint32_t seq, uint32_t hg, uint32_t h
  * (mask entry 0) change nothing and write nothing, as in gdn_record.
  *
  * Arguments
- *   q .. delta_log    as for gdn_record (k_log and g_log capture is not offered).
+ *   q .. g_log        as for gdn_record, including the optional tape capture:
+ *                     k_log [B,T,Hv,Dk] receives at every active step the keys
+ *                     expanded to value heads, g_log [B,T,Hv] the gates, both
+ *                     as bit copies (NULL: not written).
  *   workspace         device scratch of at least gdn_prefill_workspace_size(B,
  *                     T, Hv) bytes, 256-byte aligned, owned by the caller and
  *                     overlapping no other argument.  Its contents on entry do
@@ -219,7 +222,7 @@ uint64_t gdn_prefill_workspace_size(uint32_t B, uint32_t T, uint32_t Hv);
 
 int gdn_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
                 const float* state_in, const uint32_t* mask,
-                void* y, float* state_out, void* delta_log,
+                void* y, float* state_out, void* delta_log, void* k_log, void* g_log,
                 void* workspace, uint64_t workspace_bytes,
                 uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
                 int io_dtype, int gqa_map, void* stream);
@@ -248,7 +251,7 @@ int gdn_prefill(const void* q, const void* k, const void* v, const void* g, cons
 
 int gdn_prefill_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
                         const float* state_in, const uint32_t* mask,
-                        void* y, float* state_out, void* delta_log,
+                        void* y, float* state_out, void* delta_log, void* k_log, void* g_log,
                         uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
                         int io_dtype, int gqa_map, void* stream);
 

@@ -180,7 +180,7 @@ def gdn_prefill_workspace_size(B: int, T: int, Hv: int) -> int:
 
 
 def _prefill(noalloc, q, k, v, g, beta, state_in, mask, gqa_map, y, state_out, delta_log,
-             write_tape, workspace, stream):
+             write_tape, k_log, g_log, workspace, stream):
     if gqa_map not in _MAPS:
         raise ValueError("gqa_map must be 'block' or 'tiled'")
     dev = _device_of(q)
@@ -213,17 +213,20 @@ def _prefill(noalloc, q, k, v, g, beta, state_in, mask, gqa_map, y, state_out, d
     _want("state_out", state_out, (B, Hv, Dv, Dk), torch.float32, dev)
     if delta_log is not None:
         _want("delta_log", delta_log, (B, T, Hv, Dv), io, dev)
+    if k_log is not None:
+        _want("k_log", k_log, (B, T, Hv, Dk), io, dev)
+    if g_log is not None:
+        _want("g_log", g_log, (B, T, Hv), io, dev)
+    outs = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in), _ptr(mask), _ptr(y),
+            _ptr(state_out), _ptr(delta_log), _ptr(k_log), _ptr(g_log))
     if noalloc:
-        rc = lib.gdn_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
-                                     _ptr(mask), _ptr(y), _ptr(state_out), _ptr(delta_log), B, T, Hk,
-                                     Hv, Dk, Dv, _io_code(q), _MAPS[gqa_map], st.cuda_stream)
+        rc = lib.gdn_prefill_noalloc(*outs, B, T, Hk, Hv, Dk, Dv, _io_code(q), _MAPS[gqa_map],
+                                     st.cuda_stream)
         _native.check("gdn_prefill_noalloc", rc)
         return y, state_out, delta_log
     _want("workspace", workspace, (workspace.numel(),), torch.uint8, dev)
-    rc = lib.gdn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
-                         _ptr(mask), _ptr(y), _ptr(state_out), _ptr(delta_log), _ptr(workspace),
-                         workspace.numel(), B, T, Hk, Hv, Dk, Dv, _io_code(q), _MAPS[gqa_map],
-                         st.cuda_stream)
+    rc = lib.gdn_prefill(*outs, _ptr(workspace), workspace.numel(), B, T, Hk, Hv, Dk, Dv,
+                         _io_code(q), _MAPS[gqa_map], st.cuda_stream)
     _native.check("gdn_prefill", rc)
     return y, state_out, delta_log
 
@@ -233,17 +236,19 @@ def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
                 *, gqa_map: str = "block", y: Optional[torch.Tensor] = None,
                 state_out: Optional[torch.Tensor] = None,
                 delta_log: Optional[torch.Tensor] = None, write_tape: bool = True,
+                k_log: Optional[torch.Tensor] = None, g_log: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None,
                 stream=None) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
     """The record step over a long sequence, 64 steps at a time on the matrix
     cores; returns (y, state_out, delta_log) as gdn_record does.
 
-    bf16 I/O, Dk = 128, Dv a multiple of 16.  ``workspace`` (a uint8 device
-    tensor of at least gdn_prefill_workspace_size(B, T, Hv) bytes) is allocated
-    when not given; pass one to reuse it across calls on one stream.
+    bf16 I/O, Dk = 128, Dv a multiple of 16.  ``k_log`` and ``g_log``, if given,
+    receive the rest of the tape as in gdn_record.  ``workspace`` (a uint8
+    device tensor of at least gdn_prefill_workspace_size(B, T, Hv) bytes) is
+    allocated when not given; pass one to reuse it across calls on one stream.
     """
     return _prefill(False, q, k, v, g, beta, state_in, mask, gqa_map, y, state_out, delta_log,
-                    write_tape, workspace, stream)
+                    write_tape, k_log, g_log, workspace, stream)
 
 
 def gdn_prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
@@ -251,6 +256,7 @@ def gdn_prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
                         mask: Optional[torch.Tensor] = None, *, gqa_map: str = "block",
                         y: Optional[torch.Tensor] = None, state_out: Optional[torch.Tensor] = None,
                         delta_log: Optional[torch.Tensor] = None, write_tape: bool = True,
+                        k_log: Optional[torch.Tensor] = None, g_log: Optional[torch.Tensor] = None,
                         stream=None) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
     """gdn_prefill with its workspace in the library's own scratch area
     (PREFILL_SCRATCH_BYTES per GPU, shared by every such call on that GPU):
@@ -259,7 +265,7 @@ def gdn_prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: to
     whose kernels overlap in time on one GPU race; calls on one stream are
     ordered."""
     return _prefill(True, q, k, v, g, beta, state_in, mask, gqa_map, y, state_out, delta_log,
-                    write_tape, None, stream)
+                    write_tape, k_log, g_log, None, stream)
 
 
 def _replay(choice, delta_log, k_log, g_log, state_in, mask, accepted, state_out, stream):

@@ -28,7 +28,7 @@ EXPORTS = ("gdn_record", "gdn_replay", "gqa_expand", "gdn_prefill", "gdn_prefill
            "rms_norm_bf16", "gdn_record_debug", "gdn_replay_debug", "gdn_prefill_noalloc",
            "gdn_strerror", "gdn_last_error", "gdn_abi_version")
 PREFILL_SCRATCH_BYTES = 68157440     # GDN_PREFILL_SCRATCH_BYTES
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class LaunchChoice(ctypes.Structure):
@@ -55,9 +55,9 @@ def _load() -> ctypes.CDLL:
     lib.gdn_replay_debug.restype = i32
     lib.gqa_expand.argtypes = [vp, vp] + [u32] * 4 + [i32, i32, vp]
     lib.gqa_expand.restype = i32
-    lib.gdn_prefill.argtypes = [vp] * 11 + [ctypes.c_uint64] + [u32] * 6 + [i32, i32, vp]
+    lib.gdn_prefill.argtypes = [vp] * 13 + [ctypes.c_uint64] + [u32] * 6 + [i32, i32, vp]
     lib.gdn_prefill.restype = i32
-    lib.gdn_prefill_noalloc.argtypes = [vp] * 10 + [u32] * 6 + [i32, i32, vp]
+    lib.gdn_prefill_noalloc.argtypes = [vp] * 12 + [u32] * 6 + [i32, i32, vp]
     lib.gdn_prefill_noalloc.restype = i32
     lib.gdn_prefill_workspace_size.argtypes = [u32] * 3
     lib.gdn_prefill_workspace_size.restype = ctypes.c_uint64

@@ -308,7 +308,7 @@ namespace {
 // workspace_bytes are ignored), looked up after validation.
 int prefill_impl(bool noalloc, const void* q, const void* k, const void* v, const void* g, const void* beta,
                  const float* state_in, const uint32_t* mask,
-                 void* y, float* state_out, void* delta_log,
+                 void* y, float* state_out, void* delta_log, void* k_log, void* g_log,
                  void* workspace, uint64_t workspace_bytes,
                  uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
                  int io_dtype, int gqa_map, void* stream, const char* kFn) {
@@ -327,10 +327,11 @@ int prefill_impl(bool noalloc, const void* q, const void* k, const void* v, cons
                     "(got io_dtype=%d, Dk=%u, Dv=%u)", kFn, io_dtype, Dk, Dv);
 
     const uint64_t e = io_bytes(io_dtype);
-    uint64_t n_qk, n_v, n_g, n_s, n_m;
+    uint64_t n_qk, n_v, n_g, n_s, n_m, n_kl;
     if (!mul_u64(&n_qk, {B, T, Hk, Dk, e}) || !mul_u64(&n_v, {B, T, Hv, Dv, e}) ||
         !mul_u64(&n_g, {B, T, Hv, e}) || !mul_u64(&n_s, {B, Hv, Dv, Dk, 4}) || !mul_u64(&n_m, {B, T, 4}) ||
-        n_qk > kMaxBytes || n_v > kMaxBytes || n_s > kMaxBytes)
+        !mul_u64(&n_kl, {B, T, Hv, Dk, e}) ||
+        n_qk > kMaxBytes || n_v > kMaxBytes || n_s > kMaxBytes || n_kl > kMaxBytes)
         return fail(GDN_ERR_OVERFLOW, "%s: tensor sizes overflow", kFn);
     const uint64_t nchunks = (uint64_t(T) + 63) / 64;
     uint64_t prep_items, scan_items;
@@ -354,23 +355,24 @@ int prefill_impl(bool noalloc, const void* q, const void* k, const void* v, cons
                     workspace ? "" : " (NULL)");
     }
 
-    const void* a16[] = {q, k, v, state_in, y, state_out, delta_log};
-    const char* a16n[] = {"q", "k", "v", "state_in", "y", "state_out", "delta_log"};
-    for (int i = 0; i < 7; ++i)
+    const void* a16[] = {q, k, v, state_in, y, state_out, delta_log, k_log};
+    const char* a16n[] = {"q", "k", "v", "state_in", "y", "state_out", "delta_log", "k_log"};
+    for (int i = 0; i < 8; ++i)
         if (a16[i] && !aligned(a16[i], 16))
             return fail(GDN_ERR_MISALIGNED, "%s: %s must be 16-byte aligned", kFn, a16n[i]);
     if (!noalloc && !aligned(workspace, 256))
         return fail(GDN_ERR_MISALIGNED, "%s: workspace must be 256-byte aligned", kFn);
     if (mask && !aligned(mask, 4)) return fail(GDN_ERR_MISALIGNED, "%s: mask must be 4-byte aligned", kFn);
-    if (!aligned(g, e) || !aligned(beta, e))
-        return fail(GDN_ERR_MISALIGNED, "%s: g and beta must be element-aligned", kFn);
+    if (!aligned(g, e) || !aligned(beta, e) || (g_log && !aligned(g_log, e)))
+        return fail(GDN_ERR_MISALIGNED, "%s: g, beta and g_log must be element-aligned", kFn);
 
     const Span ins[] = {{q, n_qk, "q"}, {k, n_qk, "k"}, {v, n_v, "v"}, {g, n_g, "g"},
                         {beta, n_g, "beta"}, {state_in, n_s, "state_in"}, {mask, mask ? n_m : 0, "mask"}};
     const Span outs[] = {{y, n_v, "y"}, {state_out, n_s, "state_out"},
                          {delta_log, delta_log ? n_v : 0, "delta_log"},
+                         {k_log, k_log ? n_kl : 0, "k_log"}, {g_log, g_log ? n_g : 0, "g_log"},
                          {workspace, noalloc ? 0 : need, "workspace"}};
-    constexpr int kOuts = 4;
+    constexpr int kOuts = 6;
     for (const Span& o : outs) {
         for (const Span& i : ins) {
             if (o.p == state_out && i.p == state_in && o.p == i.p) continue;   // exact in-place state
@@ -389,7 +391,7 @@ int prefill_impl(bool noalloc, const void* q, const void* k, const void* v, cons
         if (e != hipSuccess)
             return fail(GDN_ERR_LAUNCH, "%s: cannot find the scratch area: %s", kFn, hipGetErrorString(e));
     }
-    gdn::PrefillArgs a{q, k, v, g, beta, state_in, mask, y, state_out, delta_log, workspace,
+    gdn::PrefillArgs a{q, k, v, g, beta, state_in, mask, y, state_out, delta_log, k_log, g_log, workspace,
                        B, T, Hk, Hv, Dk, Dv, io_dtype, gqa_map};
     return launch_status(gdn::launch_prefill(a, static_cast<hipStream_t>(stream)), kFn);
 }
@@ -400,21 +402,22 @@ extern "C" {
 
 int gdn_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
                 const float* state_in, const uint32_t* mask,
-                void* y, float* state_out, void* delta_log,
+                void* y, float* state_out, void* delta_log, void* k_log, void* g_log,
                 void* workspace, uint64_t workspace_bytes,
                 uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
                 int io_dtype, int gqa_map, void* stream) {
-    return prefill_impl(false, q, k, v, g, beta, state_in, mask, y, state_out, delta_log, workspace,
-                        workspace_bytes, B, T, Hk, Hv, Dk, Dv, io_dtype, gqa_map, stream, "gdn_prefill");
+    return prefill_impl(false, q, k, v, g, beta, state_in, mask, y, state_out, delta_log, k_log, g_log,
+                        workspace, workspace_bytes, B, T, Hk, Hv, Dk, Dv, io_dtype, gqa_map, stream,
+                        "gdn_prefill");
 }
 
 int gdn_prefill_noalloc(const void* q, const void* k, const void* v, const void* g, const void* beta,
                         const float* state_in, const uint32_t* mask,
-                        void* y, float* state_out, void* delta_log,
+                        void* y, float* state_out, void* delta_log, void* k_log, void* g_log,
                         uint32_t B, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dk, uint32_t Dv,
                         int io_dtype, int gqa_map, void* stream) {
-    return prefill_impl(true, q, k, v, g, beta, state_in, mask, y, state_out, delta_log, nullptr, 0,
-                        B, T, Hk, Hv, Dk, Dv, io_dtype, gqa_map, stream, "gdn_prefill_noalloc");
+    return prefill_impl(true, q, k, v, g, beta, state_in, mask, y, state_out, delta_log, k_log, g_log,
+                        nullptr, 0, B, T, Hk, Hv, Dk, Dv, io_dtype, gqa_map, stream, "gdn_prefill_noalloc");
 }
 
 int gqa_expand(const void* src, void* dst, uint32_t seq, uint32_t hg, uint32_t h, uint32_t k,

@@ -93,6 +93,7 @@ struct PrefillArgs {
     const void* q; const void* k; const void* v; const void* g; const void* beta;
     const float* state_in; const uint32_t* mask;
     void* y; float* state_out; void* delta_log;
+    void* k_log; void* g_log;             // optional tape capture
     void* workspace;
     uint32_t B, T, Hk, Hv, Dk, Dv;
     int io;

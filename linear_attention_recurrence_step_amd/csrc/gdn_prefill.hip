@@ -164,8 +164,8 @@ template <int IO>
 __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ g,
     const void* __restrict__ beta, const uint32_t* __restrict__ mask,
-    unsigned char* __restrict__ ws, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t nchunks,
-    uint32_t group, int tiled)
+    unsigned char* __restrict__ ws, void* __restrict__ k_log, void* __restrict__ g_log,
+    uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t nchunks, uint32_t group, int tiled)
 {
     static_assert(IO == kBF16, "the chunked prefill takes bf16 I/O");
     extern __shared__ __align__(16) unsigned char lds[];
@@ -208,11 +208,15 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
         if (tid < kC) {
             const uint32_t t = t0 + tid, tc = t < T ? t : T - 1;
             const size_t i = (static_cast<size_t>(b) * T + tc) * Hv + hv;
-            const float gl = io_load1<IO>(g, i), bl = io_load1<IO>(beta, i);
+            const uint32_t graw = static_cast<const uint16_t*>(g)[i];
+            const float bl = io_load1<IO>(beta, i);
             const uint32_t mword = mwords[static_cast<size_t>(b) * T + tc];
             const bool act = t < T && (mask ? mword : 1u) > 0u;
-            gs[tid] = act ? gl : 1.0f;
+            gs[tid] = act ? bf16_bits_to_f32(graw) : 1.0f;
             bs[tid] = act ? bl : 0.0f;
+            if (g_log != nullptr && act)                         // tape capture: the gate's bits
+                static_cast<uint16_t*>(g_log)[(static_cast<size_t>(b) * T + t) * Hv + hv] =
+                    static_cast<uint16_t>(graw);
         }
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -221,6 +225,10 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
             const bool act = t0 + r < T && mw[j] > 0u;
             *reinterpret_cast<u32x4*>(lds + PrepLds::KR + r * PrepLds::KS + c16 * 16) = act ? kp[j] : z;
             *reinterpret_cast<u32x4*>(lds + PrepLds::QR + r * PrepLds::KS + c16 * 16) = act ? qp[j] : z;
+            if (k_log != nullptr && act)                         // tape capture: key row of this value head
+                *reinterpret_cast<u32x4*>(static_cast<char*>(k_log) +
+                                          ((static_cast<size_t>(b) * T + t0 + r) * Hv + hv) * (kDk * 2) +
+                                          c16 * 16) = kp[j];
         }
     }
     __syncthreads();
@@ -789,7 +797,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
         lds_set.fetch_or(bit, std::memory_order_release);
     }
     hipLaunchKernelGGL(gdn_prefill_prep_kernel<kBF16>, dim3(a.B * a.Hv * nchunks), dim3(256), PrepLds::BYTES, stream,
-                       a.q, a.k, a.g, a.beta, a.mask, ws, a.T, a.Hk, a.Hv, nchunks, group, tiled);
+                       a.q, a.k, a.g, a.beta, a.mask, ws, a.k_log, a.g_log, a.T, a.Hk, a.Hv, nchunks, group, tiled);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gdn_prefill_scan_kernel<kBF16>, dim3(a.B * a.Hv * (a.Dv / kRows)), dim3(512), ScanLds::BYTES,

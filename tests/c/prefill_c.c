@@ -65,10 +65,10 @@ int main(void) {
     CHECK(hipMemcpy(db, beta, ng * 2, hipMemcpyHostToDevice));
     CHECK(hipMemcpy(ds0, s0, ns * 4, hipMemcpyHostToDevice));
 
-    int rc = gdn_prefill(dq, dk, dv, dg, db, ds0, NULL, dy1, ds1, NULL, dws, wsb - 1,
+    int rc = gdn_prefill(dq, dk, dv, dg, db, ds0, NULL, dy1, ds1, NULL, NULL, NULL, dws, wsb - 1,
                          B, T, HK, HV, DK, DV, GDN_BF16, GDN_GQA_BLOCK, NULL);
     if (rc != GDN_ERR_WORKSPACE) { printf("short workspace accepted (%d)\n", rc); return 11; }
-    rc = gdn_prefill(dq, dk, dv, dg, db, ds0, NULL, dy1, ds1, NULL, dws, wsb,
+    rc = gdn_prefill(dq, dk, dv, dg, db, ds0, NULL, dy1, ds1, NULL, NULL, NULL, dws, wsb,
                      B, T, HK, HV, DK, DV, GDN_BF16, GDN_GQA_BLOCK, NULL);
     if (rc != GDN_OK) { printf("gdn_prefill: %s\n", gdn_last_error()); return 12; }
     rc = gdn_record(dq, dk, dv, dg, db, ds0, NULL, dy2, ds2, NULL, NULL, NULL,

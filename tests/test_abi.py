@@ -50,8 +50,8 @@ lib.gdn_record.argtypes = [vp] * 12 + [u32] * 6 + [i32, i32, vp]
 lib.gdn_replay.argtypes = [vp] * 6 + [u32] * 6 + [i32, vp]
 lib.gqa_expand.argtypes = [vp, vp] + [u32] * 4 + [i32, i32, vp]
 lib.rms_norm_bf16.argtypes = [vp, vp, vp, u32, u32, ctypes.c_float, vp]
-lib.gdn_prefill.argtypes = [vp] * 11 + [ctypes.c_uint64] + [u32] * 6 + [i32, i32, vp]
-lib.gdn_prefill_noalloc.argtypes = [vp] * 10 + [u32] * 6 + [i32, i32, vp]
+lib.gdn_prefill.argtypes = [vp] * 13 + [ctypes.c_uint64] + [u32] * 6 + [i32, i32, vp]
+lib.gdn_prefill_noalloc.argtypes = [vp] * 12 + [u32] * 6 + [i32, i32, vp]
 lib.gdn_prefill_workspace_size.argtypes = [u32] * 3
 lib.gdn_prefill_workspace_size.restype = ctypes.c_uint64
 class Choice(ctypes.Structure):
@@ -122,18 +122,19 @@ def rms(**kw):
     return [a["x"], a["w"], a["out"], a["n"], a["dim"], a["eps"], None]
 
 
-# gdn_prefill(q, k, v, g, beta, state_in, mask, y, state_out, delta_log, workspace, workspace_bytes,
-#             B, T, Hk, Hv, Dk, Dv, io, map, stream)
+# gdn_prefill(q, k, v, g, beta, state_in, mask, y, state_out, delta_log, k_log, g_log, workspace,
+#             workspace_bytes, B, T, Hk, Hv, Dk, Dv, io, map, stream)
 WS_NEED = 2 * 4 * 1 * 33280          # B=2, Hv=4, one chunk of 64 steps
 
 
 def pre(**kw):
     a = dict(q=P(0), k=P(1), v=P(2), g=P(3), beta=P(4), s_in=P(5), mask=P(6), y=P(7), s_out=P(8),
-             dl=P(9), ws=P(10), wsb=WS_NEED, B=2, T=3, Hk=2, Hv=4, Dk=128, Dv=128, io=2, map=1)
+             dl=P(9), kl=P(11), gl=P(12), ws=P(10), wsb=WS_NEED, B=2, T=3, Hk=2, Hv=4, Dk=128,
+             Dv=128, io=2, map=1)
     a.update(kw)
     return [a["q"], a["k"], a["v"], a["g"], a["beta"], a["s_in"], a["mask"], a["y"], a["s_out"],
-            a["dl"], a["ws"], a["wsb"], a["B"], a["T"], a["Hk"], a["Hv"], a["Dk"], a["Dv"], a["io"],
-            a["map"], None]
+            a["dl"], a["kl"], a["gl"], a["ws"], a["wsb"], a["B"], a["T"], a["Hk"], a["Hv"], a["Dk"],
+            a["Dv"], a["io"], a["map"], None]
 
 
 # gdn_record_debug / gdn_replay_debug: the launch choice first, as
@@ -149,7 +150,7 @@ def repd(choice, **kw):
 # gdn_prefill_noalloc: gdn_prefill's arguments less workspace and workspace_bytes
 def prena(**kw):
     a = pre(**kw)
-    return a[:10] + a[12:]
+    return a[:12] + a[14:]
 
 
 NULL, ZERO, RATIO, SHAPE, OVER, ALIAS, ENUM, LAUNCH, ALIGN = -1, -2, -3, -4, -5, -6, -7, -8, -9
@@ -227,6 +228,12 @@ CASES = [
     ("pre_y_over_v", "gdn_prefill", pre(y=P(2, 512)), ALIAS),
     ("pre_state_partial_alias", "gdn_prefill", pre(s_out=P(5, 4096)), ALIAS),
     ("pre_grid_overflow", "gdn_prefill", pre(B=1 << 16, T=1 << 15, Hk=1, Hv=1 << 8, Dv=16), OVER),
+    ("pre_k_log_over_k", "gdn_prefill", pre(kl=P(1, 512)), ALIAS),
+    ("pre_g_log_over_workspace", "gdn_prefill", pre(gl=P(10, 64)), ALIAS),
+    ("pre_k_log_over_g_log", "gdn_prefill", pre(gl=P(11, 256)), ALIAS),
+    ("pre_misaligned_k_log", "gdn_prefill", pre(kl=P(11, 8)), ALIGN),
+    ("pre_misaligned_g_log", "gdn_prefill", pre(gl=P(12, 1)), ALIGN),
+    ("pre_k_log_bytes_overflow", "gdn_prefill", pre(B=1 << 20, T=1 << 20, Hk=1, Hv=1 << 12), OVER),
     ("recd_unknown_tiling", "gdn_record_debug", recd([3, 256, 0, 0]), ENUM),
     ("recd_half_tiling", "gdn_record_debug", recd([2, 0, 0, 0]), ENUM),
     ("recd_huge_tiling", "gdn_record_debug", recd([1 << 31, 256, 0, 0]), ENUM),
@@ -248,6 +255,8 @@ CASES = [
     ("prena_null_q", "gdn_prefill_noalloc", prena(q=None), NULL),
     ("prena_f16", "gdn_prefill_noalloc", prena(io=1), SHAPE),
     ("prena_y_over_v", "gdn_prefill_noalloc", prena(y=P(2, 512)), ALIAS),
+    ("prena_k_log_over_q", "gdn_prefill_noalloc", prena(kl=P(0, 16)), ALIAS),
+    ("prena_misaligned_g_log", "gdn_prefill_noalloc", prena(gl=P(12, 1)), ALIGN),
     # one chunk block past the 2048 the scratch area holds
     ("prena_past_scratch", "gdn_prefill_noalloc", prena(B=1, T=64 * 65, Hk=1, Hv=32), WORKSPACE),
     ("prena_past_scratch_batch", "gdn_prefill_noalloc", prena(B=2049, T=1, Hk=1, Hv=1), WORKSPACE),

@@ -180,3 +180,57 @@ def test_prefill_seeded_sweep(case):
     B, T, Hk, Hv, Dv, gmap, mask, seed = case
     inp = gi.record_inputs(B, T, Hk, Hv, 128, Dv, io="bf16", seed=seed, mask=mask)
     _check(inp, gmap, "sweep %s" % (case,))
+
+
+K_SENTINEL = 5.5
+G_SENTINEL = -0.625
+
+
+def _bits(t):
+    t = t.detach().cpu().contiguous()
+    return t.view(torch.int16).numpy()
+
+
+CAPTURE = [
+    # B, T, Hk, Hv, Dv, map, mask: one step, ragged chunks, several chunks, both maps
+    (1, 1, 1, 2, 16, "block", "ones"),
+    (2, 70, 2, 4, 64, "tiled", "bernoulli"),
+    (1, 129, 1, 3, 32, "block", "trailing"),
+    (3, 64, 2, 2, 16, "tiled", "zeros"),
+]
+
+
+@pytest.mark.parametrize("case", CAPTURE, ids=lambda c: "B%d_T%d_Hk%d_Hv%d_Dv%d_%s_%s" % c)
+def test_prefill_captures_expanded_keys_and_gates(case):
+    """k_log holds the keys expanded to value heads and g_log the gates, bit
+    for bit, at active steps only; capturing changes no other output, and the
+    captured tape replays exactly like one expanded by a separate pass."""
+    B, T, Hk, Hv, Dv, gmap, mask = case
+    inp = gi.record_inputs(B, T, Hk, Hv, 128, Dv, io="bf16", seed=31 + T, mask=mask)
+    note("prefill with capture %s" % (case,))
+    d = to_dev(inp)
+    kl = torch.full((B, T, Hv, 128), K_SENTINEL, dtype=torch.bfloat16, device=dev())
+    gl = torch.full((B, T, Hv), G_SENTINEL, dtype=torch.bfloat16, device=dev())
+    y = torch.full(d["v"].shape, Y_SENTINEL, dtype=torch.bfloat16, device=dev())
+    dl = torch.full(d["v"].shape, D_SENTINEL, dtype=torch.bfloat16, device=dev())
+    y, s, dl = gdn.gdn_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"], d["mask"],
+                               gqa_map=gmap, y=y, delta_log=dl, k_log=kl, g_log=gl)
+    torch.cuda.synchronize()
+    y0, s0, dl0 = _prefill_gpu(inp, gmap)
+    assert torch.equal(y, y0) and torch.equal(s, s0) and torch.equal(dl, dl0)
+    act = step_mask(inp["mask"], B, T).reshape(B * T)
+    ref_k = oracle.gqa_expand(_bits(inp["k"]).reshape(B * T, Hk, 128), Hv, gmap)
+    got_k = _bits(kl).reshape(B * T, Hv, 128)
+    assert np.array_equal(got_k[act], ref_k[act]), "k_log differs from the expanded keys"
+    assert np.all(f64(kl).reshape(B * T, Hv, 128)[~act] == K_SENTINEL), "k_log written at an inactive step"
+    got_g, ref_g = _bits(gl).reshape(B * T, Hv), _bits(inp["g"]).reshape(B * T, Hv)
+    assert np.array_equal(got_g[act], ref_g[act]), "g_log differs from g"
+    assert np.all(f64(gl).reshape(B * T, Hv)[~act] == G_SENTINEL), "g_log written at an inactive step"
+    k_exp = gdn.gqa_expand(d["k"], Hv, gmap)
+    for acc in sorted({0, 1, min(T, 6)}):
+        note("replay of a prefill-captured tape, accepted=%d" % acc)
+        r1 = gdn.gdn_replay(dl, kl, gl, d["state_in"], d["mask"], acc)
+        r2 = gdn.gdn_replay(dl, k_exp, d["g"], d["state_in"], d["mask"], acc)
+        torch.cuda.synchronize()
+        assert torch.equal(r1, r2), acc
+

@@ -93,3 +93,18 @@ def test_noalloc_prefill_refuses_more_than_the_scratch():
     assert err.value.status_name == "GDN_ERR_WORKSPACE"
     torch.cuda.synchronize()
     assert torch.all(o["y"] == Y_SENTINEL)                          # nothing ran
+
+
+def test_prefill_noalloc_captures_like_prefill():
+    inp = gi.record_inputs(2, 90, 2, 4, 128, 32, io="bf16", seed=77, mask="bernoulli")
+    note("prefill_noalloc with capture")
+    d = to_dev(inp)
+    logs = []
+    for fn in (gdn.gdn_prefill, gdn.gdn_prefill_noalloc):
+        kl = torch.full((2, 90, 4, 128), 5.5, dtype=torch.bfloat16, device=dev())
+        gl = torch.full((2, 90, 4), -0.625, dtype=torch.bfloat16, device=dev())
+        fn(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"], d["mask"], gqa_map="tiled",
+           k_log=kl, g_log=gl)
+        torch.cuda.synchronize()
+        logs.append((kl, gl))
+    assert torch.equal(logs[0][0], logs[1][0]) and torch.equal(logs[0][1], logs[1][1])
