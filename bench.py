@@ -15,6 +15,8 @@ input already resident in HBM:
     tiny:             gdn_record + gdn_replay
     cell_d192_128, cell_d64_32: the page's other two head-shape cells as decode
                       steps (B=1024 / 16384), same launches as large_batch_decode
+    prefill_d192_128: the record over 4096 steps at the Dk=192, Dv=128, Hk=Hv=4 cell,
+                      by gdn_prefill (--prefill sequential: gdn_record)
     rms_norm_prefill: rms_norm_bf16 of 4096 fp32 hidden states of width 2048
 
 With --capture fused (decode workloads) the record writes k_log and g_log
@@ -130,7 +132,8 @@ class Step:
         self.name = name
         self.gi_norm = gi.NORM_WORKLOADS
         self.fused = capture == "fused"
-        self.chunked = prefill == "chunked" and name == "chunk_prefill"
+        self.prefill_step = name in gi.PREFILL_WORKLOADS
+        self.chunked = prefill == "chunked" and self.prefill_step
         self.kernels = []            # (label, kernel, algorithmic bytes, head-steps)
         self.touched = {}
         if name in gi.NORM_WORKLOADS:
@@ -144,7 +147,7 @@ class Step:
             self.kernels.append(("rms_norm", "rms_norm_bf16", rms_norm_bytes(w["n_tokens"], w["dim"]), 0))
             return
         self.w = w = gi.WORKLOADS[name]
-        if self.fused and name in ("long_tape_replay", "chunk_prefill"):
+        if self.fused and (name == "long_tape_replay" or self.prefill_step):
             raise SystemExit("--capture fused applies to workloads with a record and a replay")
         self.e = 4 if w.io == "f32" else 2
         self.kernels = []            # (label, kernel, algorithmic bytes, head-steps)
@@ -183,7 +186,7 @@ class Step:
             for i, what in enumerate(("q", "k")):
                 self.kernels.append(("expand_%s" % what, "gqa_expand",
                                      expand_bytes(w.B * T, w.Hk, w.Hv, w.Dk, eb), 0))
-        else:
+        elif not self.prefill_step:
             self.k_log = torch.empty((w.B, T, w.Hv, w.Dk), dtype=io, device=dev)
             self.g_log = torch.empty((w.B, T, w.Hv), dtype=io, device=dev) if self.fused else None
             if not self.fused:
@@ -201,7 +204,7 @@ class Step:
             self.kernels.append(("prefill", "gdn_prefill", rb, U * w.Hv))
         else:
             self.kernels.append(("record", "gdn_record", rb, U * w.Hv))
-        if name != "chunk_prefill":
+        if not self.prefill_step:
             if name == "spec_decode":
                 import numpy as np
                 self.accepted = int(np.random.Generator(np.random.PCG64(seed + 77)).integers(0, w.T + 1))
@@ -227,7 +230,7 @@ class Step:
         if self.name == "chunk_prefill":
             for i in range(2):
                 out.append(lambda i=i: gdn.gqa_expand(self.src[i], w.Hv, w.gqa_map, dst=self.dst[i]))
-        elif not self.fused:
+        elif not self.fused and not self.prefill_step:
             out.append(lambda: gdn.gqa_expand(d["k"], w.Hv, w.gqa_map, dst=self.k_log))
         if self.chunked:
             out.append(lambda: gdn.gdn_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
@@ -243,7 +246,7 @@ class Step:
             out.append(lambda: gdn.gdn_record(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"],
                                               d["mask"], gqa_map=w.gqa_map, y=self.y,
                                               state_out=self.s_rec, delta_log=self.dl))
-        if self.name != "chunk_prefill":
+        if not self.prefill_step:
             g_log = self.g_log if self.fused else d["g"]
             out.append(lambda: gdn.gdn_replay(self.dl, self.k_log, g_log, d["state_in"], d["mask"],
                                               self.accepted, state_out=self.s_rep))
@@ -305,6 +308,7 @@ def _unit_calls(name, w, sl, e):
     """Prepared oracle calls for one slice of the sample (dict of CPU tensors)
     and their algorithmic bytes, in the order a step runs them."""
     import torch
+    import gdn_inputs as gi
     import oracle
     calls = []
     if name == "long_tape_replay":
@@ -315,7 +319,7 @@ def _unit_calls(name, w, sl, e):
             taken = _active(sl["mask"], nb, w.T, a)
             calls.append((f, replay_bytes(nb, w.T, w.Hv, w.Dk, w.Dv, e, a, taken, True)))
         return calls
-    if name == "chunk_prefill":
+    if name in gi.PREFILL_WORKLOADS:
         heads = sl["v"].shape[2]
         f, _ = oracle.prepare_record(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], sl["state_in"],
                                      None, gqa_map="block")
@@ -358,7 +362,7 @@ def cpu_baseline(name: str, budget_s: float, threads_req=None):
     aff, threads = _host_threads(threads_req)
     e = 4 if w.io == "f32" else 2
     seed = 123
-    if name == "chunk_prefill":
+    if name in gi.PREFILL_WORKLOADS:
         units = min(w.Hv, threads)                     # value heads of the single batch row
         inp = gi.record_inputs(1, w.T, w.Hk, w.Hv, w.Dk, w.Dv, w.io, seed, w.mask, w.mask_p)
 
@@ -384,11 +388,11 @@ def cpu_baseline(name: str, budget_s: float, threads_req=None):
     work = [_unit_calls(name, w, slice_of(lo, hi), e) for lo, hi in bounds]
     total, dt = _timed_threads(work, budget_s)
     one_total, dt1 = _timed_threads([_unit_calls(name, w, slice_of(0, 1), e)], budget_s / 4)
-    unit_name = "value heads" if name == "chunk_prefill" else "batch rows"
+    unit_name = "value heads" if name in gi.PREFILL_WORKLOADS else "batch rows"
     return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": "%d of %d %s of %s, one slice per thread, %.1f s"
-                      % (units, w.Hv if name == "chunk_prefill" else w.B, unit_name, name, dt),
+                      % (units, w.Hv if name in gi.PREFILL_WORKLOADS else w.B, unit_name, name, dt),
             "single_thread_value": round(one_total / dt1 / 1e9, 4),
             "affinity_cores": aff, "cpu_model": _cpu_model(),
             "label": "CPU baseline, not the target"}
@@ -617,7 +621,7 @@ def main():
                 "traffic": measured_traffic(dk["kernel"], args.workload, dk["name"]),
                 "kernel": dk["name"], "bytes_per_launch": dk["algorithmic_bytes"],
                 "us_per_launch": dk["us"]}
-    if args.workload == "chunk_prefill":
+    if step.prefill_step:
         # the long record is a chain of dependent steps, not an HBM stream
         roofline["note"] = ("latency-bound: 64 dependent chunk steps per 16-row block (gdn_prefill)"
                             if step.chunked else
@@ -635,7 +639,7 @@ def main():
                    {"workload": args.workload, "B": w.B, "T": w.T, "Hk": w.Hk, "Hv": w.Hv,
                     "Dk": w.Dk, "Dv": w.Dv, "io_dtype": w.io, "state_dtype": "f32",
                     "gqa_map": w.gqa_map, "mask": w.mask, "capture": args.capture,
-                    **({"prefill": args.prefill} if args.workload == "chunk_prefill" else {}),
+                    **({"prefill": args.prefill} if step.prefill_step else {}),
                     "step": " + ".join(k[0] for k in step.kernels)}),
         "frac_of_peak": round(value / HBM_PEAK_GBPS, 4),
         "head_steps_per_s": round(head_steps / (ms_per_step * 1e-3), 1),
@@ -646,7 +650,7 @@ def main():
     }
     if isinstance(w, dict):
         out["tokens_per_s"] = round(w["n_tokens"] / (ms_per_step * 1e-3), 1)
-    if args.workload == "chunk_prefill":
+    if step.prefill_step:
         out["tokens_per_s"] = round(w.B * w.T / (ms_per_step * 1e-3), 1)
     if not args.no_peak_probe:
         out["practical_peak"] = {"copy_GB/s": round(copy_bandwidth(dev), 1),

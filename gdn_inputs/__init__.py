@@ -80,7 +80,15 @@ WORKLOADS = {
     "cell_d64_32": Workload("cell_d64_32", B=16384, T=1, Hk=2, Hv=2, Dk=64, Dv=32,
                             io="bf16", gqa_map="block", mask="ones", accepted=(1,),
                             note="Dk=64, Dv=32, Hk=Hv=2 decode step; 256 MiB of fp32 state"),
+    # The main cell's record over a 4096-step sequence (the prefill length of
+    # chunk_prefill), keys already one per value head.
+    "prefill_d192_128": Workload("prefill_d192_128", B=1, T=4096, Hk=4, Hv=4, Dk=192, Dv=128,
+                                 io="bf16", gqa_map="block", mask="none",
+                                 note="4096-step record at the Dk=192, Dv=128, Hk=Hv=4 cell"),
 }
+
+# Workloads whose step is one long record (a prefill), not a decode step.
+PREFILL_WORKLOADS = ("chunk_prefill", "prefill_d192_128")
 
 
 def rng(seed: int) -> np.random.Generator:

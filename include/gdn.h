@@ -192,8 +192,9 @@ int gqa_expand(const void* src, void* dst, uint32_t seq, uint32_t hg, uint32_t h
  * keys, gates and betas, and y and the state follow from matrix products.  The
  * arithmetic is reordered, so results agree with gdn_record to rounding (float32
  * accumulation; float32 operands enter the bf16 matrix cores as a sum of two
- * bf16 numbers, about 16 significant bits), not bit for bit.  Inactive steps
- * (mask entry 0) change nothing and write nothing, as in gdn_record.
+ * bf16 numbers, about 16 significant bits; fp16 keys and queries as an exact
+ * sum of two bf16 numbers), not bit for bit.  Inactive steps (mask entry 0)
+ * change nothing and write nothing, as in gdn_record.
  *
  * Arguments
  *   q .. g_log        as for gdn_record, including the optional tape capture:
@@ -207,9 +208,9 @@ int gqa_expand(const void* src, void* dst, uint32_t seq, uint32_t hg, uint32_t h
  *                     flight at once need two workspaces.
  *   workspace_bytes   its size.
  *   B, T, Hk, Hv      sizes; Hk must divide Hv.
- *   Dk, Dv            Dk must be 128 and Dv a multiple of 16 up to 1024.
- *   io_dtype          must be GDN_BF16 (keys and queries enter the matrix
- *                     cores exactly).
+ *   Dk, Dv            Dk must be 128 or 192 (the page's shape-cell key
+ *                     width), Dv a multiple of 16 up to 1024.
+ *   io_dtype          GDN_BF16 or GDN_F16 (not GDN_F32).
  *   gqa_map, stream   as for gdn_record.
  * The call enqueues two kernels on `stream`.
  * Returns GDN_OK or a negative gdn_status (nothing is enqueued on error):

@@ -242,7 +242,7 @@ def gdn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tens
     """The record step over a long sequence, 64 steps at a time on the matrix
     cores; returns (y, state_out, delta_log) as gdn_record does.
 
-    bf16 I/O, Dk = 128, Dv a multiple of 16.  ``k_log`` and ``g_log``, if given,
+    bf16 or fp16 I/O, Dk = 128 or 192, Dv a multiple of 16.  ``k_log`` and ``g_log``, if given,
     receive the rest of the tape as in gdn_record.  ``workspace`` (a uint8
     device tensor of at least gdn_prefill_workspace_size(B, T, Hv) bytes) is
     allocated when not given; pass one to reuse it across calls on one stream.

@@ -323,7 +323,7 @@ int prefill_impl(bool noalloc, const void* q, const void* k, const void* v, cons
         return fail(GDN_ERR_GQA_RATIO, "%s: %u value heads cannot share %u key heads evenly", kFn, Hv, Hk);
     if (!gdn::prefill_supported(Dk, Dv, io_dtype) || Dv > 1024)
         return fail(GDN_ERR_UNSUPPORTED_SHAPE,
-                    "%s: needs bf16 I/O, Dk = 128 and Dv a multiple of 16 up to 1024 "
+                    "%s: needs bf16 or fp16 I/O, Dk = 128 or 192 and Dv a multiple of 16 up to 1024 "
                     "(got io_dtype=%d, Dk=%u, Dv=%u)", kFn, io_dtype, Dk, Dv);
 
     const uint64_t e = io_bytes(io_dtype);

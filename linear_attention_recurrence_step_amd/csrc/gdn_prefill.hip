@@ -24,16 +24,21 @@
 //     S_C  = gamma_63 S0 + sum_s M[63,s] delta_s k_s^T.
 // Tb and P = M o H depend on the chunk's keys, queries and gates only, so a
 // first kernel (prep) forms them for every chunk in parallel; a second kernel
-// (scan) carries the state through the chunks in order, with every product a
-// 16x16x16 MFMA: X = [K; Q] S0^T, Delta = Tb R, Y = gamma o XQ + P Delta and
-// S^T <- gamma_63 S^T + K^T (rho o Delta), rho_s = M[63,s].
+// (scan) carries the state through the chunks in order, with every product on
+// the 16 x 16 x 32 bf16 matrix instruction: X = [K; Q] S0^T, Delta = Tb R,
+// Y = gamma o XQ + P Delta and S^T <- gamma_63 S^T + K^T (rho o Delta),
+// rho_s = M[63,s].  Key widths 128 and 192 (the 192-wide key heads of the
+// record page's shape-cell instances), bf16 or fp16 I/O.
 //
-// Precision.  Keys and queries are bf16 and enter the MFMAs exactly.  Every
-// fp32 operand (the state, R, Delta, Tb, P) enters as hi + lo, two bf16 numbers
-// with hi = round(x) and lo = round(x - hi) (about 16 significant bits); an
-// fp32 x fp32 product takes three MFMAs (hi.hi + hi.lo + lo.hi), a bf16 x fp32
-// product two.  Accumulation is fp32.  M is formed by running products of the
-// gates (no division), so zero or tiny gates are exact.
+// Precision.  bf16 keys and queries enter the MFMAs exactly.  An fp16 key or
+// query element (11 significant bits) is split exactly into two bf16 numbers
+// hi = round(x), lo = x - hi.  Every fp32 operand (the state, R, Delta, Tb, P)
+// enters as hi + lo, two bf16 numbers with hi = round(x) and lo = round(x - hi)
+// (about 16 significant bits).  A product of two split operands takes three
+// MFMAs (hi.hi + hi.lo + lo.hi), a bf16 x split product two; the Gram
+// matrices of fp16 keys and queries take all four.  Accumulation is fp32.  M
+// is formed by running products of the gates (no division), so zero or tiny
+// gates are exact.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
@@ -43,7 +48,6 @@ namespace gdn {
 namespace {
 
 constexpr int kC = 64;            // steps per chunk
-constexpr int kDk = 128;          // key width this path is built for
 constexpr int kRows = 16;         // state rows per scan workgroup
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
@@ -73,6 +77,35 @@ __device__ __forceinline__ void split4(const f32x4v& x, u32x2& hi, u32x2& lo) {
     hi.y = cvt_pk_bf16(x[2], x[3]);
     lo.x = cvt_pk_bf16(x[0] - __uint_as_float(hi.x << 16), x[1] - __uint_as_float(hi.x & 0xffff0000u));
     lo.y = cvt_pk_bf16(x[2] - __uint_as_float(hi.y << 16), x[3] - __uint_as_float(hi.y & 0xffff0000u));
+}
+
+// An input element's bits as fp32.
+template <int IO>
+__device__ __forceinline__ float in_f32(uint32_t bits) {
+    return IO == kBF16 ? bf16_bits_to_f32(bits) : f16_bits_to_f32(bits);
+}
+
+// Eight fp16 values (one 16-byte piece, element order kept) as two bf16
+// pieces with hi + lo equal to each value exactly: rounding an 11-bit
+// significand to bf16's 8 bits leaves a remainder of at most 4 significant
+// bits, inside bf16's exponent range for every finite fp16 number.
+__device__ __forceinline__ void split_f16x8(const u32x4& raw, u32x4& hi, u32x4& lo) {
+    uint32_t h[4], o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = f16_bits_to_f32(raw[i] & 0xffffu), b = f16_bits_to_f32(raw[i] >> 16);
+        h[i] = cvt_pk_bf16(a, b);
+        o[i] = cvt_pk_bf16(a - __uint_as_float(h[i] << 16), b - __uint_as_float(h[i] & 0xffff0000u));
+    }
+    hi = u32x4{h[0], h[1], h[2], h[3]};
+    lo = u32x4{o[0], o[1], o[2], o[3]};
+}
+__device__ __forceinline__ void split_f16x4(const u32x2& raw, u32x2& hi, u32x2& lo) {
+    const u32x4 r4 = {raw.x, raw.y, 0u, 0u};
+    u32x4 h4, l4;
+    split_f16x8(r4, h4, l4);
+    hi = u32x2{h4.x, h4.y};
+    lo = u32x2{l4.x, l4.y};
 }
 
 __device__ __forceinline__ void split1(float x, uint16_t& hi, uint16_t& lo) {
@@ -146,8 +179,9 @@ __device__ __forceinline__ void forward_quad_row(float (&mine)[16], const float*
 // LDS of the prep kernel.  The chunk's key and query rows (padded rows) are
 // dead once the Gram tiles are formed; the output block (Tb and P in the
 // workspace's fragment order) reuses their space.
+template <int DK>
 struct PrepLds {
-    static constexpr int KS = kDk * 2 + 16;            // K / Q row stride in bytes (padded)
+    static constexpr int KS = DK * 2 + 16;             // K / Q row stride in bytes (padded)
     static constexpr int MS = kC + 1;                  // M row stride in floats
     static constexpr int KR = 0;                       // K rows [64] x KS
     static constexpr int QR = KR + kC * KS;            // Q rows [64] x KS
@@ -160,14 +194,15 @@ struct PrepLds {
     static_assert(4 * kC * kC * 2 <= 2 * kC * KS, "output block fits in the key/query area");
 };
 
-template <int IO>
+template <int IO, int DK>
 __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ g,
     const void* __restrict__ beta, const uint32_t* __restrict__ mask,
     unsigned char* __restrict__ ws, void* __restrict__ k_log, void* __restrict__ g_log,
     uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t nchunks, uint32_t group, int tiled)
 {
-    static_assert(IO == kBF16, "the chunked prefill takes bf16 I/O");
+    static_assert(IO == kBF16 || IO == kF16, "the chunked prefill takes 16-bit I/O");
+    using PrepLds = gdn::PrepLds<DK>;
     extern __shared__ __align__(16) unsigned char lds[];
     constexpr int MS = PrepLds::MS;
     float* gs = reinterpret_cast<float*>(lds + PrepLds::GS);
@@ -184,22 +219,24 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
     const uint32_t t0 = c * kC;
     unsigned char* wsb = ws + (static_cast<size_t>(n) * nchunks + c) * PrefillWs::kBytes;
 
-    // The chunk's key and query rows, 16-byte pieces: thread tid takes piece
-    // tid & 15 of rows (tid >> 4) + 16 j.  Steps past T read step T-1; rows of
-    // inactive steps are stored as zeros (a select, so a NaN there cannot
-    // enter a product).
+    // The chunk's key and query rows, 16-byte pieces: thread tid takes pieces
+    // p = tid + 256 j, piece p % (DK / 8) of row p / (DK / 8).  Steps past T
+    // read step T-1; rows of inactive steps are stored as zeros (a select, so
+    // a NaN there cannot enter a product).
     // Mask words are loaded whether or not there is a mask (from k, whose
     // B*T*Hk*Dk/2 words cover every index, when there is none) and then
     // selected, so the loads are not serialised behind branches.
+    constexpr uint32_t kPieces = DK / 8;               // 16-byte pieces per row
+    constexpr int kPer = kC * kPieces / 256;           // pieces per thread
     {
         const uint32_t* mwords = mask ? mask : static_cast<const uint32_t*>(k);
-        u32x4 kp[4], qp[4];
-        uint32_t mw[4];
-        const uint32_t row = tid >> 4, c16 = tid & 15u;
+        u32x4 kp[kPer], qp[kPer];
+        uint32_t mw[kPer];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t t = t0 + row + 16u * j, tc = t < T ? t : T - 1;
-            const size_t off = ((static_cast<size_t>(b) * T + tc) * Hk + hk) * (kDk * 2) + c16 * 16;
+        for (int j = 0; j < kPer; ++j) {
+            const uint32_t p = tid + 256u * j, row = p / kPieces, pc = p - row * kPieces;
+            const uint32_t t = t0 + row, tc = t < T ? t : T - 1;
+            const size_t off = ((static_cast<size_t>(b) * T + tc) * Hk + hk) * (DK * 2) + pc * 16;
             kp[j] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(k) + off);
             qp[j] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(q) + off);
             const uint32_t m = mwords[static_cast<size_t>(b) * T + tc];
@@ -212,7 +249,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
             const float bl = io_load1<IO>(beta, i);
             const uint32_t mword = mwords[static_cast<size_t>(b) * T + tc];
             const bool act = t < T && (mask ? mword : 1u) > 0u;
-            gs[tid] = act ? bf16_bits_to_f32(graw) : 1.0f;
+            gs[tid] = act ? in_f32<IO>(graw) : 1.0f;
             bs[tid] = act ? bl : 0.0f;
             if (g_log != nullptr && act)                         // tape capture: the gate's bits
                 static_cast<uint16_t*>(g_log)[(static_cast<size_t>(b) * T + t) * Hv + hv] =
@@ -220,15 +257,15 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
         }
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t r = row + 16u * j;
+        for (int j = 0; j < kPer; ++j) {
+            const uint32_t p = tid + 256u * j, r = p / kPieces, pc = p - r * kPieces;
             const bool act = t0 + r < T && mw[j] > 0u;
-            *reinterpret_cast<u32x4*>(lds + PrepLds::KR + r * PrepLds::KS + c16 * 16) = act ? kp[j] : z;
-            *reinterpret_cast<u32x4*>(lds + PrepLds::QR + r * PrepLds::KS + c16 * 16) = act ? qp[j] : z;
+            *reinterpret_cast<u32x4*>(lds + PrepLds::KR + r * PrepLds::KS + pc * 16) = act ? kp[j] : z;
+            *reinterpret_cast<u32x4*>(lds + PrepLds::QR + r * PrepLds::KS + pc * 16) = act ? qp[j] : z;
             if (k_log != nullptr && act)                         // tape capture: key row of this value head
                 *reinterpret_cast<u32x4*>(static_cast<char*>(k_log) +
-                                          ((static_cast<size_t>(b) * T + t0 + r) * Hv + hv) * (kDk * 2) +
-                                          c16 * 16) = kp[j];
+                                          ((static_cast<size_t>(b) * T + t0 + r) * Hv + hv) * (DK * 2) +
+                                          pc * 16) = kp[j];
         }
     }
     __syncthreads();
@@ -254,27 +291,46 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
 
     // Gram tiles G = K K^T and H = Q K^T of row tile w (all four column tiles;
     // above the diagonal the s <= t masks below make A and P exact zeros).
-    // Products of bf16 values are exact in fp32.  32-deep products over key
-    // columns: lane holds x[16 tile + lr][32 m + 8 lg .. +7] as A and B.
+    // Products of bf16 values are exact in fp32 (fp16 inputs: of their hi and
+    // lo parts).  32-deep products over key columns: lane holds
+    // x[16 tile + lr][32 m + 8 lg .. +7] as A and B.
     f32x4v G[4], H[4];
     {
-        u32x4 kw[kDk / 32], qf[kDk / 32];
+        constexpr int NB = DK / 32;
+        u32x4 kw[NB], qf[NB], kwl[NB], qfl[NB];
         const unsigned char* kwr = lds + PrepLds::KR + (16u * w + lr) * PrepLds::KS + lg * 16;
         const unsigned char* qwr = lds + PrepLds::QR + (16u * w + lr) * PrepLds::KS + lg * 16;
 #pragma unroll
-        for (int m = 0; m < kDk / 32; ++m) {
+        for (int m = 0; m < NB; ++m) {
             kw[m] = *reinterpret_cast<const u32x4*>(kwr + m * 64);
             qf[m] = *reinterpret_cast<const u32x4*>(qwr + m * 64);
+            if constexpr (IO == kF16) {
+                split_f16x8(kw[m], kw[m], kwl[m]);
+                split_f16x8(qf[m], qf[m], qfl[m]);
+            }
         }
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const unsigned char* kr = lds + PrepLds::KR + (16u * st + lr) * PrepLds::KS + lg * 16;
             f32x4v g = {0.f, 0.f, 0.f, 0.f}, h = g;
 #pragma unroll
-            for (int m = 0; m < kDk / 32; ++m) {
-                const u32x4 bk = *reinterpret_cast<const u32x4*>(kr + m * 64);
-                g = mfma_bf16_k32(kw[m], bk, g);
-                h = mfma_bf16_k32(qf[m], bk, h);
+            for (int m = 0; m < NB; ++m) {
+                u32x4 bk = *reinterpret_cast<const u32x4*>(kr + m * 64);
+                if constexpr (IO == kBF16) {
+                    g = mfma_bf16_k32(kw[m], bk, g);
+                    h = mfma_bf16_k32(qf[m], bk, h);
+                } else {
+                    u32x4 bkl;
+                    split_f16x8(bk, bk, bkl);
+                    g = mfma_bf16_k32(kw[m], bk, g);
+                    g = mfma_bf16_k32(kw[m], bkl, g);
+                    g = mfma_bf16_k32(kwl[m], bk, g);
+                    g = mfma_bf16_k32(kwl[m], bkl, g);
+                    h = mfma_bf16_k32(qf[m], bk, h);
+                    h = mfma_bf16_k32(qf[m], bkl, h);
+                    h = mfma_bf16_k32(qfl[m], bk, h);
+                    h = mfma_bf16_k32(qfl[m], bkl, h);
+                }
             }
             G[st] = g;
             H[st] = h;
@@ -336,9 +392,11 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
 //
 // One workgroup of eight waves per (b, hv, 16 consecutive value rows).  The
 // state is held transposed in MFMA accumulators: wave w owns the sixteen key
-// columns kcol(w, 0..15), lane l holding S[dv0 + l%16][kcol(w, 4 (l/16) + r)];
-// the hi and lo parts of tiles 2m and 2m+1 side by side are the B operand of
-// the 32-deep product X = K S^T over key columns 32m .. 32m + 31.
+// columns kcol(w, 0..15) (key tile w), lane l holding
+// S[dv0 + l%16][kcol(w, 4 (l/16) + r)]; with 192 key columns waves 4-7 also
+// own key tiles 8-11 (tile w + 4).  The hi and lo parts of tiles 2m and 2m+1
+// side by side are the B operand of the 32-deep product X = K S^T over key
+// columns 32m .. 32m + 31.
 // Waves 0-3 (the K side) take step tile w of the chunk: X_K, R and Delta.
 // Waves 4-7 (the Q side) take step tile w-4: X_Q, and Y of the previous chunk
 // while the K side solves for Delta (Y is not on the state's dependency chain).
@@ -351,15 +409,18 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
 // in the workspace and go straight to registers, two chunks ahead.  Key,
 // query and value rows of inactive steps (masked, or past T) are replaced by
 // zeros.
+template <int IO, int DK>
 struct ScanLds {
+    static constexpr int NB = DK / 32;                 // 32-column key blocks
     static constexpr int KTS = kC + 8;                 // K^T row stride in bf16 (144 bytes, 16-byte aligned)
-    static constexpr int SFR = 0;                      // state fragments [8][64] x 16 B (hi [4], lo [4])
+    static constexpr int SFR = 0;                      // state fragments [2 NB][64] x 16 B (hi [NB], lo [NB])
     static constexpr int BOP = 4 * 64 * 16;            // one step-indexed B operand (see bop_store)
-    static constexpr int RFR = SFR + 8 * 64 * 16;      // R
+    static constexpr int RFR = SFR + 2 * NB * 64 * 16; // R
     static constexpr int DFR = RFR + BOP;              // Delta, two chunks
     static constexpr int DTF = DFR + 2 * BOP;          // rho o Delta
-    static constexpr int KT = DTF + 4 * 64 * 16;       // K^T [dk][t] bf16
-    static constexpr int VR = KT + kDk * KTS * 2;      // v rows [64] x 32 B (bf16, this row block)
+    static constexpr int KT = DTF + 4 * 64 * 16;       // K^T [dk][t] bf16 (of fp16 keys: the hi part)
+    static constexpr int KTL = KT + DK * KTS * 2;      // the lo part of K^T (fp16 keys)
+    static constexpr int VR = KTL + (IO == kF16 ? DK * KTS * 2 : 0);   // v rows [64] x 32 B (this row block)
     static constexpr int GR = VR + kC * 32;            // gamma [64], rho [64] fp32
     static constexpr int AF = GR + 2 * kC * 4;         // active flags [64] u32 (0 or 1)
     static constexpr int OT = AF + kC * 4;             // per wave: its pending output tile [16][16] bf16
@@ -373,19 +434,20 @@ struct ScanStage {
     uint32_t mv;          // threads 32-223: mask word of the v row / flag row (any word without a mask)
 };
 
+template <class L>
 __device__ __forceinline__ void stage_store(const ScanStage& st, bool has_mask, unsigned char* lds, uint32_t T,
                                             uint32_t t0,
                                             uint32_t tid) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     if (tid < 32u) {
-        *reinterpret_cast<u32x4*>(lds + ScanLds::GR + tid * 16) = st.gv;
+        *reinterpret_cast<u32x4*>(lds + L::GR + tid * 16) = st.gv;
     } else if (tid < 160u) {
         const uint32_t p = tid - 32u, vr = p >> 1;
         const bool act = t0 + vr < T && (!has_mask || st.mv > 0u);
-        *reinterpret_cast<u32x4*>(lds + ScanLds::VR + vr * 32 + (p & 1u) * 16) = act ? st.gv : z;
+        *reinterpret_cast<u32x4*>(lds + L::VR + vr * 32 + (p & 1u) * 16) = act ? st.gv : z;
     } else if (tid < 224u) {
         const uint32_t r = tid - 160u;
-        reinterpret_cast<uint32_t*>(lds + ScanLds::AF)[r] = t0 + r < T && (!has_mask || st.mv > 0u) ? 1u : 0u;
+        reinterpret_cast<uint32_t*>(lds + L::AF)[r] = t0 + r < T && (!has_mask || st.mv > 0u) ? 1u : 0u;
     }
 }
 
@@ -421,7 +483,7 @@ __device__ __forceinline__ u32x4 bop_lo(const unsigned char* base, uint32_t kb, 
     return *reinterpret_cast<const u32x4*>(base + 2048 + (kb * 64u + l) * 16u);
 }
 
-template <int IO>
+template <int IO, int DK>
 __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const float* state_in, const uint32_t* __restrict__ mask,
@@ -429,13 +491,17 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     void* __restrict__ delta_log, uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t Dv,
     uint32_t nchunks, uint32_t group, int tiled)
 {
-    static_assert(IO == kBF16, "the chunked prefill takes bf16 I/O");
+    static_assert(IO == kBF16 || IO == kF16, "the chunked prefill takes 16-bit I/O");
+    static_assert(DK == 128 || DK == 192, "key width 128 or 192");
+    using ScanLds = gdn::ScanLds<IO, DK>;
+    constexpr int NB = DK / 32;
     extern __shared__ __align__(16) unsigned char lds[];
     u32x4 (*sfr)[64] = reinterpret_cast<u32x4 (*)[64]>(lds + ScanLds::SFR);
     unsigned char* const rfr = lds + ScanLds::RFR;
     unsigned char* const dfr = lds + ScanLds::DFR;      // chunk c at dfr + (c & 1) * BOP
     unsigned char* const dtf = lds + ScanLds::DTF;
     uint16_t* kt = reinterpret_cast<uint16_t*>(lds + ScanLds::KT);
+    uint16_t* ktl = reinterpret_cast<uint16_t*>(lds + ScanLds::KTL);
     const float* gr = reinterpret_cast<const float*>(lds + ScanLds::GR);
 
     // The wave index is read from lane 0 so that the compiler treats it, and
@@ -452,12 +518,20 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     const uint32_t hk = tiled ? hv % Hk : hv / group;
 
     // This lane's 16-byte state piece: row dv0 + lr, columns kcol(w, 4 lg) .. +3
-    // (the key index is permuted, see kcol).
-    const size_t srow = (static_cast<size_t>(n) * Dv + dv0 + lr) * kDk + kcol(w, 4u * lg);
-    f32x4v acc;
+    // (the key index is permuted, see kcol); with 192 key columns waves 4-7
+    // also hold tile w2 = w + 4.
+    const bool extra = DK == 192 && w >= 4u;
+    const uint32_t w2 = w + 4u;
+    const size_t srow = (static_cast<size_t>(n) * Dv + dv0 + lr) * DK + kcol(w, 4u * lg);
+    const size_t srow2 = (static_cast<size_t>(n) * Dv + dv0 + lr) * DK + kcol(w2, 4u * lg);
+    f32x4v acc, acc2 = {0.f, 0.f, 0.f, 0.f};
     {
         const float4 s4 = *reinterpret_cast<const float4*>(state_in + srow);
         acc = f32x4v{s4.x, s4.y, s4.z, s4.w};
+        if (extra) {
+            const float4 t4 = *reinterpret_cast<const float4*>(state_in + srow2);
+            acc2 = f32x4v{t4.x, t4.y, t4.z, t4.w};
+        }
     }
 
     void* out = qside ? y : delta_log;                  // what this wave writes (delta_log may be NULL)
@@ -465,15 +539,15 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     // This lane's row of the A operand of X (K on the K side, Q on the Q side):
     // step 16 tt + lr, key columns 32 m + 8 lg .. +7 for m = 0..3, i.e. the
     // fragments of key steps 2m and 2m+1, read straight from the input.
-    const char* arow = static_cast<const char*>(qside ? q : k) + (static_cast<size_t>(b) * T * Hk + hk) * (kDk * 2) +
+    const char* arow = static_cast<const char*>(qside ? q : k) + (static_cast<size_t>(b) * T * Hk + hk) * (DK * 2) +
                        lg * 16;
-    const size_t arow_step = static_cast<size_t>(Hk) * kDk * 2;     // bytes per step
+    const size_t arow_step = static_cast<size_t>(Hk) * DK * 2;      // bytes per step
     const char* a_lane = arow + (16u * tt + lr) * arow_step;
     const char* a_last = arow + static_cast<size_t>(T - 1) * arow_step;
-    auto aload = [&](u32x4 (&a)[4], uint32_t t0n) {
+    auto aload = [&](u32x4 (&a)[NB], uint32_t t0n) {
         const char* src = t0n + 16u * tt + lr < T ? a_lane + t0n * arow_step : a_last;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) a[m] = *reinterpret_cast<const u32x4*>(src + m * 64);
+        for (int m = 0; m < NB; ++m) a[m] = *reinterpret_cast<const u32x4*>(src + m * 64);
     };
     // Tb (K side) or P (Q side) fragments of step tile tt: four 16-byte slots
     // per lane (hi, lo), loaded from the workspace one chunk ahead.
@@ -515,7 +589,7 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         st.mv = mwords[in ? t0n + mrow : T - 1];
     };
     ScanStage sta, stb;
-    u32x4 mfa[4], mfb[4], aka[4], akb[4];
+    u32x4 mfa[4], mfb[4], aka[NB], akb[NB];
     {
         const uint32_t c1 = nchunks > 1u ? 1u : 0u;
         sload(sta, 0u);
@@ -537,7 +611,9 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     uint32_t pend_t0 = 0u;
     auto produce = [&](const f32x4v& vals, uint32_t actbits, uint32_t t0p) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ot[(4u * lg + r) * 16 + lr] = static_cast<uint16_t>(f32_to_bf16_bits(vals[r]));
+        for (int r = 0; r < 4; ++r)
+            ot[(4u * lg + r) * 16 + lr] =
+                static_cast<uint16_t>(IO == kBF16 ? f32_to_bf16_bits(vals[r]) : f32_to_f16_bits(vals[r]));
         if (lr == 0u) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) otf[4u * lg + r] = (actbits >> r) & 1u;
@@ -582,21 +658,27 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     // chunks per iteration with the buffers swapped, so that no register still
     // being loaded is copied (a copy would wait for the load) and every load
     // has one to two chunks of compute to arrive in.
-    auto chunk = [&](uint32_t c, ScanStage& st, u32x4 (&mf)[4], u32x4 (&ak)[4])
+    auto chunk = [&](uint32_t c, ScanStage& st, u32x4 (&mf)[4], u32x4 (&ak)[NB])
                      __attribute__((always_inline)) {
         const uint32_t t0 = c * kC;
         // (Past the last chunk the loads repeat it and go unused, so that
         // every iteration issues the same memory operations.)
         const uint32_t c2 = c + 2 < nchunks ? c + 2 : nchunks - 1;
-        stage_store(st, mask != nullptr, lds, T, t0, tid);
+        stage_store<ScanLds>(st, mask != nullptr, lds, T, t0, tid);
         {
             u32x2 hi, lo;
             split4(acc, hi, lo);
-            // hi parts of key steps 2m and 2m+1 side by side in slot m, lo
-            // parts in slot 4 + m: one 16-byte read is then a B operand of
+            // hi parts of key tiles 2m and 2m+1 side by side in slot m, lo
+            // parts in slot NB + m: one 16-byte read is then a B operand of
             // the 32-deep product over key columns 32m .. 32m + 31.
             *reinterpret_cast<u32x2*>(reinterpret_cast<unsigned char*>(&sfr[w >> 1][l]) + (w & 1u) * 8) = hi;
-            *reinterpret_cast<u32x2*>(reinterpret_cast<unsigned char*>(&sfr[4 + (w >> 1)][l]) + (w & 1u) * 8) = lo;
+            *reinterpret_cast<u32x2*>(reinterpret_cast<unsigned char*>(&sfr[NB + (w >> 1)][l]) + (w & 1u) * 8) = lo;
+            if (extra) {
+                split4(acc2, hi, lo);
+                *reinterpret_cast<u32x2*>(reinterpret_cast<unsigned char*>(&sfr[w2 >> 1][l]) + (w2 & 1u) * 8) = hi;
+                *reinterpret_cast<u32x2*>(reinterpret_cast<unsigned char*>(&sfr[NB + (w2 >> 1)][l]) + (w2 & 1u) * 8) =
+                    lo;
+            }
         }
         __syncthreads();
 
@@ -610,18 +692,24 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         // of an inactive step is zero (a select, so a NaN there cannot enter).
         // Lane (lr, lg) holds key columns 32m + 8lg .. +7 of its row for each
         // m: the A operand of the 32-deep product over columns 32m .. 32m + 31.
-        u32x4 a8[4];
+        // fp16 rows: a8 holds the hi and a8l the lo bf16 parts.
+        u32x4 a8[NB], a8l[NB];
         {
             const bool ra = reinterpret_cast<const uint32_t*>(lds + ScanLds::AF)[16u * tt + lr] != 0u;
             const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int m = 0; m < 4; ++m) a8[m] = ra ? ak[m] : z;
+            for (int m = 0; m < NB; ++m) {
+                a8[m] = ra ? ak[m] : z;
+                if constexpr (IO == kF16) split_f16x8(a8[m], a8[m], a8l[m]);
+            }
         }
         f32x4v x = {0.f, 0.f, 0.f, 0.f}, x2 = x;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            x = mfma_bf16_k32(a8[m], sfr[m][l], x);
-            x2 = mfma_bf16_k32(a8[m], sfr[4 + m][l], x2);
+        for (int m = 0; m < NB; ++m) {
+            const u32x4 sh = sfr[m][l], sl = sfr[NB + m][l];
+            x = mfma_bf16_k32(a8[m], sh, x);
+            x2 = mfma_bf16_k32(a8[m], sl, x2);
+            if constexpr (IO == kF16) x2 = mfma_bf16_k32(a8l[m], sh, x2);
         }
         // The previous chunk's outputs and loads for the chunk after next are
         // issued here, behind the first barrier, while the products above run.
@@ -638,19 +726,26 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         if (!qside) {
             // This wave's 16 key rows, transposed into K^T [dk][t] for the state update.
 #pragma unroll
-            for (int ks = 0; ks < kDk / 16; ++ks) {
+            for (int ks = 0; ks < DK / 16; ++ks) {
                 const uint32_t dk = kcol(ks, 4u * lg), t = 16u * tt + lr;
                 const u32x2 a = (ks & 1) ? hi2(a8[ks >> 1]) : lo2(a8[ks >> 1]);
                 kt[(dk + 0) * ScanLds::KTS + t] = static_cast<uint16_t>(a.x);
                 kt[(dk + 1) * ScanLds::KTS + t] = static_cast<uint16_t>(a.x >> 16);
                 kt[(dk + 2) * ScanLds::KTS + t] = static_cast<uint16_t>(a.y);
                 kt[(dk + 3) * ScanLds::KTS + t] = static_cast<uint16_t>(a.y >> 16);
+                if constexpr (IO == kF16) {
+                    const u32x2 al = (ks & 1) ? hi2(a8l[ks >> 1]) : lo2(a8l[ks >> 1]);
+                    ktl[(dk + 0) * ScanLds::KTS + t] = static_cast<uint16_t>(al.x);
+                    ktl[(dk + 1) * ScanLds::KTS + t] = static_cast<uint16_t>(al.x >> 16);
+                    ktl[(dk + 2) * ScanLds::KTS + t] = static_cast<uint16_t>(al.y);
+                    ktl[(dk + 3) * ScanLds::KTS + t] = static_cast<uint16_t>(al.y >> 16);
+                }
             }
             const uint16_t* vr = reinterpret_cast<const uint16_t*>(lds + ScanLds::VR);
             f32x4v R;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                R[r] = bf16_bits_to_f32(vr[(16u * tt + 4u * lg + r) * 16 + lr]) - gam[r] * x[r];
+                R[r] = in_f32<IO>(vr[(16u * tt + 4u * lg + r) * 16 + lr]) - gam[r] * x[r];
             u32x2 hi, lo;
             split4(R, hi, lo);
             bop_store(rfr, tt, lr, lg, hi, lo);
@@ -693,19 +788,35 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         const float gC = gr[kC - 1];
         __syncthreads();
 
-        // S^T <- gamma_63 S^T + K^T (rho o Delta) for this wave's key tile.
-        f32x4v lo_acc = {0.f, 0.f, 0.f, 0.f};
+        // S^T <- gamma_63 S^T + K^T (rho o Delta) for this wave's key tiles.
+        f32x4v lo_acc = {0.f, 0.f, 0.f, 0.f}, lo_acc2 = lo_acc;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] *= gC;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const uint32_t dk = kcol(w, lr);
-            const u32x4 a = *reinterpret_cast<const u32x4*>(&kt[dk * ScanLds::KTS + 32 * kb + 8 * lg]);
-            acc = mfma_bf16_k32(a, bop_hi(dtf, kb, l), acc);
-            lo_acc = mfma_bf16_k32(a, bop_lo(dtf, kb, l), lo_acc);
+        for (int r = 0; r < 4; ++r) {
+            acc[r] *= gC;
+            acc2[r] *= gC;
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] += lo_acc[r];
+        for (int kb = 0; kb < 2; ++kb) {
+            const u32x4 dh = bop_hi(dtf, kb, l), dl = bop_lo(dtf, kb, l);
+            const uint32_t o = kcol(w, lr) * ScanLds::KTS + 32 * kb + 8 * lg;
+            const u32x4 a = *reinterpret_cast<const u32x4*>(&kt[o]);
+            acc = mfma_bf16_k32(a, dh, acc);
+            lo_acc = mfma_bf16_k32(a, dl, lo_acc);
+            if constexpr (IO == kF16) lo_acc = mfma_bf16_k32(*reinterpret_cast<const u32x4*>(&ktl[o]), dh, lo_acc);
+            if (extra) {
+                const uint32_t o2 = kcol(w2, lr) * ScanLds::KTS + 32 * kb + 8 * lg;
+                const u32x4 a2 = *reinterpret_cast<const u32x4*>(&kt[o2]);
+                acc2 = mfma_bf16_k32(a2, dh, acc2);
+                lo_acc2 = mfma_bf16_k32(a2, dl, lo_acc2);
+                if constexpr (IO == kF16)
+                    lo_acc2 = mfma_bf16_k32(*reinterpret_cast<const u32x4*>(&ktl[o2]), dh, lo_acc2);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            acc[r] += lo_acc[r];
+            acc2[r] += lo_acc2[r];
+        }
         mload(mf, c2);                                  // mf's last use was before the third barrier
     };
     uint32_t c = 0;
@@ -723,6 +834,7 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         flush();
     }
     *reinterpret_cast<float4*>(state_out + srow) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    if (extra) *reinterpret_cast<float4*>(state_out + srow2) = make_float4(acc2[0], acc2[1], acc2[2], acc2[3]);
 }
 
 }  // namespace
@@ -772,10 +884,15 @@ hipError_t prefill_scratch(hipStream_t stream, void** out) {
 }
 
 bool prefill_supported(uint32_t Dk, uint32_t Dv, int io) {
-    return io == kBF16 && Dk == static_cast<uint32_t>(kDk) && Dv % kRows == 0;
+    return (io == kBF16 || io == kF16) && (Dk == 128 || Dk == 192) && Dv % kRows == 0;
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+namespace {
+
+template <int IO, int DK>
+hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
+    using PL = PrepLds<DK>;
+    using SL = ScanLds<IO, DK>;
     const uint32_t nchunks = (a.T + kC - 1) / kC;
     const uint32_t group = a.Hv / a.Hk;
     const int tiled = a.map == 1;
@@ -788,23 +905,29 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
     if (bit == 0 || !(lds_set.load(std::memory_order_acquire) & bit)) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gdn_prefill_scan_kernel<kBF16>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, ScanLds::BYTES);
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gdn_prefill_scan_kernel<IO, DK>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, SL::BYTES);
         if (e != hipSuccess) return e;
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gdn_prefill_prep_kernel<kBF16>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, PrepLds::BYTES);
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gdn_prefill_prep_kernel<IO, DK>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, PL::BYTES);
         if (e != hipSuccess) return e;
         lds_set.fetch_or(bit, std::memory_order_release);
     }
-    hipLaunchKernelGGL(gdn_prefill_prep_kernel<kBF16>, dim3(a.B * a.Hv * nchunks), dim3(256), PrepLds::BYTES, stream,
+    hipLaunchKernelGGL((gdn_prefill_prep_kernel<IO, DK>), dim3(a.B * a.Hv * nchunks), dim3(256), PL::BYTES, stream,
                        a.q, a.k, a.g, a.beta, a.mask, ws, a.k_log, a.g_log, a.T, a.Hk, a.Hv, nchunks, group, tiled);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gdn_prefill_scan_kernel<kBF16>, dim3(a.B * a.Hv * (a.Dv / kRows)), dim3(512), ScanLds::BYTES,
-                       stream,
-                       a.q, a.k, a.v, a.state_in, a.mask, ws, a.y, a.state_out, a.delta_log, a.T, a.Hk, a.Hv,
+    hipLaunchKernelGGL((gdn_prefill_scan_kernel<IO, DK>), dim3(a.B * a.Hv * (a.Dv / kRows)), dim3(512), SL::BYTES,
+                       stream, a.q, a.k, a.v, a.state_in, a.mask, ws, a.y, a.state_out, a.delta_log, a.T, a.Hk, a.Hv,
                        a.Dv, nchunks, group, tiled);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+    if (a.io == kBF16) return a.Dk == 128 ? launch_prefill_t<kBF16, 128>(a, stream) : launch_prefill_t<kBF16, 192>(a, stream);
+    return a.Dk == 128 ? launch_prefill_t<kF16, 128>(a, stream) : launch_prefill_t<kF16, 192>(a, stream);
 }
 
 }  // namespace gdn

@@ -213,7 +213,7 @@ CASES = [
     ("pre_null_v", "gdn_prefill", pre(v=None), NULL),
     ("pre_zero_T", "gdn_prefill", pre(T=0), ZERO),
     ("pre_ratio", "gdn_prefill", pre(Hk=3), RATIO),
-    ("pre_f16", "gdn_prefill", pre(io=1), SHAPE),
+    ("pre_dk256", "gdn_prefill", pre(Dk=256), SHAPE),
     ("pre_f32", "gdn_prefill", pre(io=0), SHAPE),
     ("pre_dk64", "gdn_prefill", pre(Dk=64), SHAPE),
     ("pre_dv40", "gdn_prefill", pre(Dv=40), SHAPE),
@@ -253,7 +253,7 @@ CASES = [
     ("repd_null_state_out", "gdn_replay_debug", repd([0, 0, 1, 0], s_out=None), NULL),
     ("prena_bad_dtype", "gdn_prefill_noalloc", prena(io=5), ENUM),
     ("prena_null_q", "gdn_prefill_noalloc", prena(q=None), NULL),
-    ("prena_f16", "gdn_prefill_noalloc", prena(io=1), SHAPE),
+    ("prena_f32", "gdn_prefill_noalloc", prena(io=0), SHAPE),
     ("prena_y_over_v", "gdn_prefill_noalloc", prena(y=P(2, 512)), ALIAS),
     ("prena_k_log_over_q", "gdn_prefill_noalloc", prena(kl=P(0, 16)), ALIAS),
     ("prena_misaligned_g_log", "gdn_prefill_noalloc", prena(gl=P(12, 1)), ALIGN),

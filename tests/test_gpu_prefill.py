@@ -139,10 +139,11 @@ def test_prefill_zero_and_unit_gates():
     _check(inp, "block", "zero and unit gates")
 
 
-def test_prefill_nan_at_inactive_steps_never_reaches_an_output():
+@pytest.mark.parametrize("io,Dk", [("bf16", 128), ("f16", 192)])
+def test_prefill_nan_at_inactive_steps_never_reaches_an_output(io, Dk):
     """Inactive steps are skipped by selection, not by a product with zero:
     NaN in their q, k, v, g and beta cannot reach y, delta or the state."""
-    inp = gi.record_inputs(2, 100, 2, 4, 128, 32, io="bf16", seed=4, mask="bernoulli")
+    inp = gi.record_inputs(2, 100, 2, 4, Dk, 32, io=io, seed=4, mask="bernoulli")
     m = inp["mask"].numpy() > 0
     poisoned = {}
     for name in ("q", "k", "v", "g", "beta"):
@@ -192,37 +193,41 @@ def _bits(t):
 
 
 CAPTURE = [
-    # B, T, Hk, Hv, Dv, map, mask: one step, ragged chunks, several chunks, both maps
-    (1, 1, 1, 2, 16, "block", "ones"),
-    (2, 70, 2, 4, 64, "tiled", "bernoulli"),
-    (1, 129, 1, 3, 32, "block", "trailing"),
-    (3, 64, 2, 2, 16, "tiled", "zeros"),
+    # B, T, Hk, Hv, Dk, Dv, io, map, mask: one step, ragged chunks, several
+    # chunks, both maps, both key widths and both dtypes
+    (1, 1, 1, 2, 128, 16, "bf16", "block", "ones"),
+    (2, 70, 2, 4, 128, 64, "bf16", "tiled", "bernoulli"),
+    (1, 129, 1, 3, 128, 32, "bf16", "block", "trailing"),
+    (3, 64, 2, 2, 128, 16, "bf16", "tiled", "zeros"),
+    (1, 100, 2, 4, 192, 32, "f16", "tiled", "bernoulli"),
+    (2, 65, 4, 4, 192, 128, "bf16", "block", "trailing"),
 ]
 
 
-@pytest.mark.parametrize("case", CAPTURE, ids=lambda c: "B%d_T%d_Hk%d_Hv%d_Dv%d_%s_%s" % c)
+@pytest.mark.parametrize("case", CAPTURE, ids=lambda c: "B%d_T%d_Hk%d_Hv%d_Dk%d_Dv%d_%s_%s_%s" % c)
 def test_prefill_captures_expanded_keys_and_gates(case):
     """k_log holds the keys expanded to value heads and g_log the gates, bit
     for bit, at active steps only; capturing changes no other output, and the
     captured tape replays exactly like one expanded by a separate pass."""
-    B, T, Hk, Hv, Dv, gmap, mask = case
-    inp = gi.record_inputs(B, T, Hk, Hv, 128, Dv, io="bf16", seed=31 + T, mask=mask)
+    B, T, Hk, Hv, Dk, Dv, io, gmap, mask = case
+    inp = gi.record_inputs(B, T, Hk, Hv, Dk, Dv, io=io, seed=31 + T, mask=mask)
     note("prefill with capture %s" % (case,))
     d = to_dev(inp)
-    kl = torch.full((B, T, Hv, 128), K_SENTINEL, dtype=torch.bfloat16, device=dev())
-    gl = torch.full((B, T, Hv), G_SENTINEL, dtype=torch.bfloat16, device=dev())
-    y = torch.full(d["v"].shape, Y_SENTINEL, dtype=torch.bfloat16, device=dev())
-    dl = torch.full(d["v"].shape, D_SENTINEL, dtype=torch.bfloat16, device=dev())
+    dt = d["q"].dtype
+    kl = torch.full((B, T, Hv, Dk), K_SENTINEL, dtype=dt, device=dev())
+    gl = torch.full((B, T, Hv), G_SENTINEL, dtype=dt, device=dev())
+    y = torch.full(d["v"].shape, Y_SENTINEL, dtype=dt, device=dev())
+    dl = torch.full(d["v"].shape, D_SENTINEL, dtype=dt, device=dev())
     y, s, dl = gdn.gdn_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"], d["mask"],
                                gqa_map=gmap, y=y, delta_log=dl, k_log=kl, g_log=gl)
     torch.cuda.synchronize()
     y0, s0, dl0 = _prefill_gpu(inp, gmap)
     assert torch.equal(y, y0) and torch.equal(s, s0) and torch.equal(dl, dl0)
     act = step_mask(inp["mask"], B, T).reshape(B * T)
-    ref_k = oracle.gqa_expand(_bits(inp["k"]).reshape(B * T, Hk, 128), Hv, gmap)
-    got_k = _bits(kl).reshape(B * T, Hv, 128)
+    ref_k = oracle.gqa_expand(_bits(inp["k"]).reshape(B * T, Hk, Dk), Hv, gmap)
+    got_k = _bits(kl).reshape(B * T, Hv, Dk)
     assert np.array_equal(got_k[act], ref_k[act]), "k_log differs from the expanded keys"
-    assert np.all(f64(kl).reshape(B * T, Hv, 128)[~act] == K_SENTINEL), "k_log written at an inactive step"
+    assert np.all(f64(kl).reshape(B * T, Hv, Dk)[~act] == K_SENTINEL), "k_log written at an inactive step"
     got_g, ref_g = _bits(gl).reshape(B * T, Hv), _bits(inp["g"]).reshape(B * T, Hv)
     assert np.array_equal(got_g[act], ref_g[act]), "g_log differs from g"
     assert np.all(f64(gl).reshape(B * T, Hv)[~act] == G_SENTINEL), "g_log written at an inactive step"
@@ -234,3 +239,69 @@ def test_prefill_captures_expanded_keys_and_gates(case):
         torch.cuda.synchronize()
         assert torch.equal(r1, r2), acc
 
+
+# Key width 192 (the record page's shape-cell heads) and fp16 I/O: one step,
+# ragged chunks, several chunks, masks, both maps, Hk < Hv.
+WIDE = [
+    # B, T, Hk, Hv, Dk, Dv, io, mask, map
+    (1, 1, 4, 4, 192, 128, "bf16", "ones", "block"),
+    (1, 200, 4, 4, 192, 128, "bf16", "bernoulli", "block"),
+    (2, 130, 1, 2, 192, 32, "bf16", "trailing", "tiled"),
+    (1, 65, 2, 4, 128, 64, "f16", "ones", "tiled"),
+    (2, 150, 2, 4, 128, 128, "f16", "bernoulli", "block"),
+    (1, 129, 4, 4, 192, 128, "f16", "trailing", "block"),
+    (3, 64, 1, 3, 192, 16, "f16", "none", "tiled"),
+    (1, 100, 1, 1, 192, 1024, "f16", "bernoulli", "block"),
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: "B%d_T%d_Hk%d_Hv%d_Dk%d_Dv%d_%s_%s_%s" % c)
+def test_prefill_wide_keys_and_f16(case):
+    B, T, Hk, Hv, Dk, Dv, io, mask, gmap = case
+    inp = gi.record_inputs(B, T, Hk, Hv, Dk, Dv, io=io, seed=57 + T, mask=mask)
+    _check(inp, gmap, "B%d T%d Dk%d Dv%d %s %s" % (B, T, Dk, Dv, io, mask))
+
+
+def test_prefill_d192_workload_all_heads():
+    """The 4096-step prefill at the Dk=192, Dv=128, Hk=Hv=4 cell at full size,
+    every head against the oracle."""
+    w = gi.WORKLOADS["prefill_d192_128"]
+    inp = gi.workload_inputs("prefill_d192_128", 0)
+    _check(inp, w.gqa_map, "prefill_d192_128 full size")
+
+
+def test_prefill_f16_zero_and_unit_gates():
+    inp = gi.record_inputs(1, 150, 2, 2, 192, 32, io="f16", seed=19, mask="ones")
+    g = inp["g"].clone()
+    beta = inp["beta"].clone()
+    g[0, [0, 63, 64, 120], :] = 0.0
+    g[0, 70:90, 0] = 1.0
+    beta[0, 70:90, 0] = 0.0
+    inp = dict(inp, g=g, beta=beta)
+    _check(inp, "tiled", "fp16 zero and unit gates")
+
+
+def _wide_sweep(n=12, seed=777):
+    """Seeded mixed configurations over both key widths and both dtypes."""
+    r = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        Dk = int(r.choice([128, 192]))
+        io = str(r.choice(["bf16", "f16"]))
+        Dv = int(r.choice([16, 32, 64, 128]))
+        Hk = int(r.integers(1, 4))
+        Hv = Hk * int(r.integers(1, 3))
+        B = int(r.integers(1, 3))
+        T = int(r.choice([1, 17, 64, 65, 129, 200]))
+        while B * Hv * Dv * Dk * T > 12_000_000 and T > 1:
+            T //= 2
+        cases.append((B, T, Hk, Hv, Dk, Dv, io, str(r.choice(["block", "tiled"])),
+                      str(r.choice(["none", "ones", "trailing", "bernoulli"])), seed + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _wide_sweep(), ids=lambda c: "B%d_T%d_Hk%d_Hv%d_Dk%d_Dv%d_%s_%s_%s_s%d" % c)
+def test_prefill_wide_seeded_sweep(case):
+    B, T, Hk, Hv, Dk, Dv, io, gmap, mask, seed = case
+    inp = gi.record_inputs(B, T, Hk, Hv, Dk, Dv, io=io, seed=seed, mask=mask)
+    _check(inp, gmap, "wide sweep %s" % (case,))
