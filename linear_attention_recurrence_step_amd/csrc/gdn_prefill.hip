@@ -118,10 +118,11 @@ __device__ __forceinline__ void split1(float x, uint16_t& hi, uint16_t& lo) {
 
 // Per (b, hv, chunk) block of the workspace, written by prep and read by scan.
 // Tb and P are stored in the A-operand order of the 16 x 16 x 32 matrix
-// instruction: the 32-byte slot ((tt * 2 + kb) * 64 + l) holds, for lane
-// l = 16 lg + lr, the hi and then the lo bf16 parts of
-// M[16 tt + lr][32 kb + 8 lg .. +7], so a wave reads one step tile's
-// operands with four fully coalesced 1 KiB loads.
+// instruction: block (tt * 2 + kb) of 2 KiB holds, for lane l = 16 lg + lr,
+// the hi bf16 parts of M[16 tt + lr][32 kb + 8 lg .. +7] in its 16-byte slot
+// l and the lo parts in slot 64 + l, so a wave reads one step tile's operands
+// with fully coalesced 1 KiB loads (whole cache lines).  Both matrices are
+// zero above the diagonal: blocks kb = 1 of step tiles 0 and 1 are never read.
 struct PrefillWs {
     static constexpr int kMat = kC * kC * 2;             // one 64 x 64 bf16 matrix
     static constexpr int kTb = 0, kP = 2 * kMat;         // Tb, P: hi/lo fragment slots, 16 KiB each
@@ -134,9 +135,9 @@ namespace {
 
 // Byte offset of element [t][s] of a 64 x 64 matrix in the fragment order of
 // PrefillWs (its hi part; the lo part is kFragLo bytes further).
-constexpr uint32_t kFragLo = 16;
+constexpr uint32_t kFragLo = 1024;
 __device__ __forceinline__ uint32_t frag_offset(uint32_t t, uint32_t s) {
-    return (((t >> 4) * 2u + (s >> 5)) * 64u + 16u * ((s & 31u) >> 3) + (t & 15u)) * 32u + (s & 7u) * 2u;
+    return ((t >> 4) * 2u + (s >> 5)) * 2048u + (16u * ((s & 31u) >> 3) + (t & 15u)) * 16u + (s & 7u) * 2u;
 }
 
 // Row I of the forward substitution (I + A) T = identity, then the rows after
@@ -549,16 +550,19 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
 #pragma unroll
         for (int m = 0; m < NB; ++m) a[m] = *reinterpret_cast<const u32x4*>(src + m * 64);
     };
-    // Tb (K side) or P (Q side) fragments of step tile tt: four 16-byte slots
-    // per lane (hi, lo), loaded from the workspace one chunk ahead.
-    // m[2 kb] = hi, m[2 kb + 1] = lo part of step block kb.
-    const size_t mfrag = (qside ? PrefillWs::kP : PrefillWs::kTb) + (static_cast<size_t>(tt) * 2 * 64 + l) * 32;
+    // Tb (K side) or P (Q side) fragments of step tile tt: up to four 16-byte
+    // slots per lane (hi, lo), loaded from the workspace two chunks ahead.
+    // m[2 kb] = hi, m[2 kb + 1] = lo part of step block kb; block 1 only for
+    // step tiles 2 and 3 (it is zero for tiles 0 and 1).
+    const bool upper = tt >= 2u;
+    const size_t mfrag = (qside ? PrefillWs::kP : PrefillWs::kTb) + static_cast<size_t>(tt) * 2 * 2048 + l * 16;
     auto mload = [&](u32x4 (&m)[4], uint32_t cc) {
         const unsigned char* base = wsn + cc * static_cast<size_t>(PrefillWs::kBytes) + mfrag;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            m[2 * kb] = *reinterpret_cast<const u32x4*>(base + kb * 64 * 32);
-            m[2 * kb + 1] = *reinterpret_cast<const u32x4*>(base + kb * 64 * 32 + kFragLo);
+        m[0] = *reinterpret_cast<const u32x4*>(base);
+        m[1] = *reinterpret_cast<const u32x4*>(base + kFragLo);
+        if (upper) {
+            m[2] = *reinterpret_cast<const u32x4*>(base + 2048);
+            m[3] = *reinterpret_cast<const u32x4*>(base + 2048 + kFragLo);
         }
     };
 
@@ -589,7 +593,7 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         st.mv = mwords[in ? t0n + mrow : T - 1];
     };
     ScanStage sta, stb;
-    u32x4 mfa[4], mfb[4], aka[NB], akb[NB];
+    u32x4 mfa[4] = {}, mfb[4] = {}, aka[NB], akb[NB];
     {
         const uint32_t c1 = nchunks > 1u ? 1u : 0u;
         sload(sta, 0u);
@@ -642,6 +646,7 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
         for (int r = 0; r < 4; ++r) Y[r] = gam_prev[r] * xq_prev[r];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            if (kb == 1 && !upper) break;
             const u32x4 dh = bop_hi(dsrc, kb, l), dl = bop_lo(dsrc, kb, l);
             Y = mfma_bf16_k32(p_prev[2 * kb], dh, Y);
             Y2 = mfma_bf16_k32(p_prev[2 * kb], dl, Y2);
@@ -754,10 +759,12 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
 
         if (!qside) {
             // Delta (step tile tt) = Tb R.  Tb is zero above the diagonal, so
-            // the tiles past tt add exact zeros.
+            // the tiles past tt add exact zeros (block 1 is skipped for tiles
+            // 0 and 1).
             f32x4v D = {0.f, 0.f, 0.f, 0.f}, D2 = D;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
+                if (kb == 1 && !upper) break;
                 const u32x4 rh = bop_hi(rfr, kb, l), rl = bop_lo(rfr, kb, l);
                 D = mfma_bf16_k32(mf[2 * kb], rh, D);
                 D2 = mfma_bf16_k32(mf[2 * kb], rl, D2);
@@ -918,8 +925,8 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gdn_prefill_scan_kernel<IO, DK>), dim3(a.B * a.Hv * (a.Dv / kRows)), dim3(512), SL::BYTES,
-                       stream, a.q, a.k, a.v, a.state_in, a.mask, ws, a.y, a.state_out, a.delta_log, a.T, a.Hk, a.Hv,
-                       a.Dv, nchunks, group, tiled);
+                       stream, a.q, a.k, a.v, a.state_in, a.mask, ws, a.y, a.state_out, a.delta_log, a.T, a.Hk,
+                       a.Hv, a.Dv, nchunks, group, tiled);
     return hipGetLastError();
 }
 
