@@ -141,35 +141,37 @@ __device__ __forceinline__ uint32_t frag_offset(uint32_t t, uint32_t s) {
 }
 
 // Row I of the forward substitution (I + A) T = identity, then the rows after
-// it.  Four consecutive lanes share column c of T; lane q of the four keeps
-// col[j] for j = 4m + q in mine[m] and sums the terms of those j, and a quad
-// reduction gives every lane of the four the whole sum.  A is read from LDS
-// in the layout Aq[(i * 4 + q) * kAqRow + m] = A[i, 4m + q], so one 16-byte
-// read covers four of a lane's terms (the same address for every column).
-// Entries of A at and above the diagonal are stored zeros, and mine[] of rows
-// not yet reached is zero, so the sums need no masks.  Row indices are
-// template parameters so that mine[] stays in registers.
-constexpr int kAqRow = 20;       // floats per (row, q): 16 used, padded
+// it, column by column, right-looking.  Four consecutive lanes share column c
+// of T; lane q of the four owns rows i = 4m + q: it keeps their running sums
+// sum[m] = sum_{j < I} A[i, j] T[j, c] and, once row i is reached, T[i, c] in
+// mine[m].  Row I's owner forms T[I, c] = [I == c] - sum, a quad broadcast
+// hands it to the other three lanes, and every lane adds A[i, I] T[I, c] to
+// the sums of its rows.  A is read from LDS in the layout
+// AqT[(j * 4 + q) * kAqRow + m] = A[4m + q, j], so one 16-byte read covers
+// four of a lane's rows (the same address for every column).  A is stored
+// with zeros at and above the diagonal, so the sums of rows at or before I
+// (already used) are the only ones that receive zero terms.  Row indices are
+// template parameters so that the sums stay in registers; the dependency from
+// one row to the next is a subtraction, the broadcast and one multiply-add.
+constexpr int kAqRow = 20;       // floats per (column, q): 16 used, padded
 
 template <int I>
-__device__ __forceinline__ void forward_quad_row(float (&mine)[16], const float* Aq, int c, int q) {
-    constexpr int NM = (I + 3) / 4;                 // m with 4m + q < I for some q
-    const float* row = Aq + (I * 4 + q) * kAqRow;
-    float p0 = 0.0f, p1 = 0.0f;
+__device__ __forceinline__ void forward_right_row(float (&sum)[16], float (&mine)[16], const float* AqT, int c,
+                                                  int q) {
+    constexpr int M0 = I >> 2, Q0 = I & 3;
+    const float own = (I == c ? 1.0f : 0.0f) - sum[M0];            // meaningful on lane Q0 of the quad
+    const float tI = dpp_read<Q0 * 0x55>(own);                      // quad_perm [Q0, Q0, Q0, Q0]
+    mine[M0] = q == Q0 ? tI : mine[M0];
+    const float* col = AqT + (I * 4 + q) * kAqRow;
 #pragma unroll
-    for (int m4 = 0; m4 < (NM + 3) / 4; ++m4) {
-        const float4 a = *reinterpret_cast<const float4*>(row + 4 * m4);
-        if (4 * m4 + 0 < NM) p0 = fmaf(a.x, mine[4 * m4 + 0], p0);
-        if (4 * m4 + 1 < NM) p1 = fmaf(a.y, mine[4 * m4 + 1], p1);
-        if (4 * m4 + 2 < NM) p0 = fmaf(a.z, mine[4 * m4 + 2], p0);
-        if (4 * m4 + 3 < NM) p1 = fmaf(a.w, mine[4 * m4 + 3], p1);
+    for (int m4 = M0 / 4; m4 < 4; ++m4) {
+        const float4 a = *reinterpret_cast<const float4*>(col + 4 * m4);
+        if (4 * m4 + 0 >= M0) sum[4 * m4 + 0] = fmaf(a.x, tI, sum[4 * m4 + 0]);
+        if (4 * m4 + 1 >= M0) sum[4 * m4 + 1] = fmaf(a.y, tI, sum[4 * m4 + 1]);
+        if (4 * m4 + 2 >= M0) sum[4 * m4 + 2] = fmaf(a.z, tI, sum[4 * m4 + 2]);
+        if (4 * m4 + 3 >= M0) sum[4 * m4 + 3] = fmaf(a.w, tI, sum[4 * m4 + 3]);
     }
-    float part = p0 + p1;
-    part += dpp_read<0xb1>(part);      // quad_perm [1,0,3,2]
-    part += dpp_read<0x4e>(part);      // quad_perm [2,3,0,1]: the same bits on all four lanes
-    const float val = (I == c ? 1.0f : 0.0f) - part;
-    mine[I >> 2] = (I & 3) == q ? val : mine[I >> 2];
-    if constexpr (I + 1 < kC) forward_quad_row<I + 1>(mine, Aq, c, q);
+    if constexpr (I + 1 < kC) forward_right_row<I + 1>(sum, mine, AqT, c, q);
 }
 
 // ------------------------------------------------------------------ prep
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
     float* Ml = reinterpret_cast<float*>(lds + PrepLds::ML);
     float* Aq = reinterpret_cast<float*>(lds + PrepLds::AQ);
 
-    const uint32_t tid = threadIdx.x, l = tid & 63u, w = tid >> 6;
+    const uint32_t tid = threadIdx.x, l = tid & 63u, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t lr = l & 15u, lg = l >> 4;
     const uint32_t n = blockIdx.x / nchunks;               // b * Hv + hv
     const uint32_t c = blockIdx.x - n * nchunks;
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
             const int t = 16 * static_cast<int>(w) + 4 * static_cast<int>(lg) + r;
             const int s = 16 * st + static_cast<int>(lr);
             const float m = Ml[t * MS + s];
-            Aq[(t * 4 + (s & 3)) * kAqRow + (s >> 2)] = s < t ? bs[t] * (m * G[st][r]) : 0.0f;
+            Aq[(s * 4 + (t & 3)) * kAqRow + (t >> 2)] = s < t ? bs[t] * (m * G[st][r]) : 0.0f;
             uint16_t hi, lo;
             split1(s <= t ? m * H[st][r] : 0.0f, hi, lo);
             const uint32_t o = frag_offset(static_cast<uint32_t>(t), static_cast<uint32_t>(s));
@@ -362,10 +364,10 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
     // column), then Tb = (I + A)^-1 diag(beta).
     {
         const int col = static_cast<int>(tid >> 2), qq = static_cast<int>(tid & 3u);
-        float mine[16];
+        float mine[16], sum[16];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) mine[m] = 0.0f;
-        forward_quad_row<0>(mine, Aq, col, qq);
+        for (int m = 0; m < 16; ++m) mine[m] = sum[m] = 0.0f;
+        forward_right_row<0>(sum, mine, Aq, col, qq);
         const float bc = bs[col];
         unsigned char* otb = lds + PrepLds::OUT + PrefillWs::kTb;
 #pragma unroll
