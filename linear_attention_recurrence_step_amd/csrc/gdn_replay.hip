@@ -1,5 +1,5 @@
-// gdn_replay: re-fold the accepted prefix of an innovation tape onto a
-// pre-record state snapshot (speculative-decode rollback), gfx950.
+// gdn_replay: the speculative-decode rollback on gfx950 -- from the state saved
+// before the record, apply the accepted positions of the innovation tape.
 //
 // What it computes is the replay kernel (macro `state_replay!`) of the
 // metaltile-std 0.1.0 page src/ffai/gated_delta_replay.rs: per (b, hv, dv) row,

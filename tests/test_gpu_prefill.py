@@ -305,3 +305,29 @@ def test_prefill_wide_seeded_sweep(case):
     B, T, Hk, Hv, Dk, Dv, io, gmap, mask, seed = case
     inp = gi.record_inputs(B, T, Hk, Hv, Dk, Dv, io=io, seed=seed, mask=mask)
     _check(inp, gmap, "wide sweep %s" % (case,))
+
+
+def test_prefill_on_a_side_stream_with_its_own_workspace():
+    """On a stream that is not the current one, with the workspace allocated
+    by the binding: the workspace belongs to that stream, so memory the
+    current stream allocates and writes while the kernels run cannot be it."""
+    inp = gi.record_inputs(2, 300, 2, 4, 128, 64, io="bf16", seed=21, mask="bernoulli")
+    note("prefill on a side stream, binding-allocated workspace")
+    d = to_dev(inp)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    y = torch.full(d["v"].shape, Y_SENTINEL, dtype=torch.bfloat16, device=dev())
+    dl = torch.full(d["v"].shape, D_SENTINEL, dtype=torch.bfloat16, device=dev())
+    y, s, dl = gdn.gdn_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["state_in"], d["mask"],
+                               gqa_map="tiled", y=y, delta_log=dl, stream=side)
+    junk = [torch.full((gdn.gdn_prefill_workspace_size(2, 300, 4) // 4,), float("nan"), device=dev())
+            for _ in range(4)]                      # the current stream's pool, written at once
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    ry, rs, rd = oracle.gdn_record(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                   inp["state_in"], inp["mask"], gqa_map="tiled")
+    act = np.broadcast_to(step_mask(inp["mask"], 2, 300)[:, :, None, None], ry.shape)
+    assert_close(y, ry, torch.bfloat16, "side-stream y", where=act)
+    assert_close(dl, rd, torch.bfloat16, "side-stream delta", where=act)
+    assert_close(s, rs, torch.bfloat16, "side-stream state")
