@@ -62,9 +62,9 @@ RowTiling replay_tiling(const ReplayArgs& a);
 
 hipError_t launch_record(const RecordArgs& a, hipStream_t stream);
 
-// Records of 2..4 steps of bf16 I/O with whole 64-row workgroups (and no
-// forced tiling) run their dense products on the matrix cores
-// (gdn_record_mfma.hip).
+// Records of 2..4 steps of bf16 I/O with Dk in {32, 64, 128, 192} and Dv a
+// multiple of 16 (and no forced tiling) run their dense products on the
+// matrix cores (gdn_record_mfma.hip, one 16-row wave per workgroup).
 bool record_mfma_applies(const RecordArgs& a);
 hipError_t launch_record_mfma(const RecordArgs& a, hipStream_t stream);
 hipError_t launch_replay(const ReplayArgs& a, hipStream_t stream);
