@@ -532,9 +532,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing")
     ap.add_argument("--scrub", choices=("on", "off"), default="on",
-                    help="before every timed step, write and then read back a 1 GiB buffer, so "
-                         "that no input is left in the L2 / 256 MB MALL and no dirty line of the "
-                         "scrub is left to write back during the step")
+                    help="before every timed launch, write and then read back a 1 GiB buffer, so "
+                         "that no input is left in the L2 / 256 MB MALL (not even one an earlier "
+                         "launch of the step read) and no dirty line of the scrub is left to "
+                         "write back during the launch")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="threads of the CPU baseline (default: the affinity mask's cores, at most %d)"
                          % CPU_THREADS_MAX)
@@ -576,27 +577,28 @@ def main():
     scrub_sum = torch.empty((), dtype=torch.float32, device=dev) if scrub else None
 
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
-          for _ in range(args.steps)]
+    # events around every launch: ev[s][i] = (start, end) of launch i of step s
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in launches] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        if scrub:
-            # outside the events: the write evicts the L2 and the MALL, the read
-            # back leaves them holding clean lines of the scrub buffer only
-            scrub_buf.fill_(float(s))
-            torch.sum(scrub_buf, dim=0, out=scrub_sum)
-        ev[s][0].record(stream)
         for i, f in enumerate(launches):
+            if scrub:
+                # outside the events: the write evicts the L2 and the MALL, the
+                # read back leaves them holding clean lines of the scrub buffer only
+                scrub_buf.fill_(float(s * len(launches) + i))
+                torch.sum(scrub_buf, dim=0, out=scrub_sum)
+            ev[s][i][0].record(stream)
             f()
-            ev[s][i + 1].record(stream)
+            ev[s][i][1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     if scrub:
-        # the wall clock includes the scrubs: time the steps by their events instead
-        elapsed = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)) * 1e-3
+        # the wall clock includes the scrubs: a step is the sum of its launches' event intervals
+        elapsed = sum(a.elapsed_time(b) for s in range(args.steps) for a, b in ev[s]) * 1e-3
 
-    samples = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]
+    samples = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
                for i in range(len(launches))]
     per_kernel_ms = [sum(x) / args.steps for x in samples]
 
