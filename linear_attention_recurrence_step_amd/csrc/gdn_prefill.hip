@@ -146,32 +146,41 @@ __device__ __forceinline__ uint32_t frag_offset(uint32_t t, uint32_t s) {
 // sum[m] = sum_{j < I} A[i, j] T[j, c] and, once row i is reached, T[i, c] in
 // mine[m].  Row I's owner forms T[I, c] = [I == c] - sum, a quad broadcast
 // hands it to the other three lanes, and every lane adds A[i, I] T[I, c] to
-// the sums of its rows.  A is read from LDS in the layout
-// AqT[(j * 4 + q) * kAqRow + m] = A[4m + q, j], so one 16-byte read covers
-// four of a lane's rows (the same address for every column).  A is stored
-// with zeros at and above the diagonal, so the sums of rows at or before I
-// (already used) are the only ones that receive zero terms.  Row indices are
-// template parameters so that the sums stay in registers; the dependency from
-// one row to the next is a subtraction, the broadcast and one multiply-add.
-constexpr int kAqRow = 20;       // floats per (column, q): 16 used, padded
+// the sums of its rows.  A is read from LDS in the quad layout (aq_index):
+// the 16 floats A[4m + q, j], m = 0..15, of column j and quad lane q form one
+// 64-byte row, whose four 16-byte groups m/4 = 0..3 are stored at group
+// m/4 ^ (q/2) ^ (j % 4): the four addresses the lanes of a quad read at once
+// (the same for every column) fall on different banks, and so do most of the
+// writes of a wave.  One 16-byte read covers four of a lane's rows.  The lane
+// passes base pointers pe and po for stored groups of even and odd order, so
+// every read address is a constant offset from one of them.  A is
+// stored with zeros at and above the diagonal, so the sums of rows at or
+// before I (already used) are the only ones that receive zero terms.  Row
+// indices are template parameters so that the sums stay in registers; the
+// dependency from one row to the next is a subtraction, the broadcast and one
+// multiply-add.
+__device__ __forceinline__ uint32_t aq_index(uint32_t i, uint32_t j) {      // float index of A[i, j]
+    const uint32_t q = i & 3u, m = i >> 2;
+    return (j * 4u + q) * 16u + ((((m >> 2) ^ (q >> 1) ^ j) & 3u) << 2) + (m & 3u);
+}
 
 template <int I>
-__device__ __forceinline__ void forward_right_row(float (&sum)[16], float (&mine)[16], const float* AqT, int c,
-                                                  int q) {
+__device__ __forceinline__ void forward_right_row(float (&sum)[16], float (&mine)[16], const float* pe,
+                                                  const float* po, int c, int q) {
     constexpr int M0 = I >> 2, Q0 = I & 3;
     const float own = (I == c ? 1.0f : 0.0f) - sum[M0];            // meaningful on lane Q0 of the quad
     const float tI = dpp_read<Q0 * 0x55>(own);                      // quad_perm [Q0, Q0, Q0, Q0]
     mine[M0] = q == Q0 ? tI : mine[M0];
-    const float* col = AqT + (I * 4 + q) * kAqRow;
 #pragma unroll
     for (int m4 = M0 / 4; m4 < 4; ++m4) {
-        const float4 a = *reinterpret_cast<const float4*>(col + 4 * m4);
+        const int v = m4 ^ (I & 3);                                 // stored group, before the lane's q/2
+        const float4 a = *reinterpret_cast<const float4*>((v & 1 ? po : pe) + I * 64 + 4 * v);
         if (4 * m4 + 0 >= M0) sum[4 * m4 + 0] = fmaf(a.x, tI, sum[4 * m4 + 0]);
         if (4 * m4 + 1 >= M0) sum[4 * m4 + 1] = fmaf(a.y, tI, sum[4 * m4 + 1]);
         if (4 * m4 + 2 >= M0) sum[4 * m4 + 2] = fmaf(a.z, tI, sum[4 * m4 + 2]);
         if (4 * m4 + 3 >= M0) sum[4 * m4 + 3] = fmaf(a.w, tI, sum[4 * m4 + 3]);
     }
-    if constexpr (I + 1 < kC) forward_right_row<I + 1>(sum, mine, AqT, c, q);
+    if constexpr (I + 1 < kC) forward_right_row<I + 1>(sum, mine, pe, po, c, q);
 }
 
 // ------------------------------------------------------------------ prep
@@ -179,9 +188,11 @@ __device__ __forceinline__ void forward_right_row(float (&sum)[16], float (&mine
 // One workgroup of four waves per (b, hv, chunk).  Wave w owns row tile w
 // (steps 16w .. 16w+15) of the 64 x 64 matrices.
 //
-// LDS of the prep kernel.  The chunk's key and query rows (padded rows) are
-// dead once the Gram tiles are formed; the output block (Tb and P in the
-// workspace's fragment order) reuses their space.
+// LDS of the prep kernel (52 KiB at Dk = 128: three workgroups per CU).  The
+// chunk's key and query rows (padded rows) are dead once the Gram tiles are
+// formed; the output block (Tb and P in the workspace's fragment order)
+// reuses their space.  M and then A (in the quad layout) share one area: A
+// is held in registers until every wave is done reading M.
 template <int DK>
 struct PrepLds {
     static constexpr int KS = DK * 2 + 16;             // K / Q row stride in bytes (padded)
@@ -190,11 +201,12 @@ struct PrepLds {
     static constexpr int QR = KR + kC * KS;            // Q rows [64] x KS
     static constexpr int OUT = 0;                      // output block, 4 x 8 KiB (aliases K, Q)
     static constexpr int ML = QR + kC * KS;            // M [64][65] fp32
-    static constexpr int AQ = ML + kC * MS * 4;        // A in the quad layout
-    static constexpr int GS = AQ + kC * 4 * kAqRow * 4;   // gates [64] fp32
+    static constexpr int AQ = ML;                      // then A in the quad layout (16 KiB)
+    static constexpr int GS = ML + kC * MS * 4;        // gates [64] fp32
     static constexpr int BS = GS + kC * 4;             // betas [64] fp32
     static constexpr int BYTES = BS + kC * 4;
     static_assert(4 * kC * kC * 2 <= 2 * kC * KS, "output block fits in the key/query area");
+    static_assert(kC * 4 * 16 * 4 <= kC * MS * 4, "A fits where M was");
 };
 
 template <int IO, int DK>
@@ -341,6 +353,8 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
     }
     __syncthreads();       // M is complete; the key and query rows are dead
 
+    // A and P of row tile w; P goes to the output block, A stays in G until
+    // M is dead.
     if (tid < kC) reinterpret_cast<float*>(wsb + PrefillWs::kRho)[tid] = Ml[(kC - 1) * MS + tid];
     unsigned char* op = lds + PrepLds::OUT + PrefillWs::kP;
 #pragma unroll
@@ -350,13 +364,20 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
             const int t = 16 * static_cast<int>(w) + 4 * static_cast<int>(lg) + r;
             const int s = 16 * st + static_cast<int>(lr);
             const float m = Ml[t * MS + s];
-            Aq[(s * 4 + (t & 3)) * kAqRow + (t >> 2)] = s < t ? bs[t] * (m * G[st][r]) : 0.0f;
+            G[st][r] = s < t ? bs[t] * (m * G[st][r]) : 0.0f;
             uint16_t hi, lo;
             split1(s <= t ? m * H[st][r] : 0.0f, hi, lo);
             const uint32_t o = frag_offset(static_cast<uint32_t>(t), static_cast<uint32_t>(s));
             *reinterpret_cast<uint16_t*>(op + o) = hi;
             *reinterpret_cast<uint16_t*>(op + o + kFragLo) = lo;
         }
+    }
+    __syncthreads();       // M is dead
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            Aq[aq_index(16u * w + 4u * lg + r, 16u * st + lr)] = G[st][r];
     }
     __syncthreads();
 
@@ -367,7 +388,8 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
         float mine[16], sum[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) mine[m] = sum[m] = 0.0f;
-        forward_right_row<0>(sum, mine, Aq, col, qq);
+        const int x = qq >> 1;                                       // group order m/4 ^ x
+        forward_right_row<0>(sum, mine, Aq + qq * 16 + 4 * x, Aq + qq * 16 - 4 * x, col, qq);
         const float bc = bs[col];
         unsigned char* otb = lds + PrepLds::OUT + PrefillWs::kTb;
 #pragma unroll
