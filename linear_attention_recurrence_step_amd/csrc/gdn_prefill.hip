@@ -389,7 +389,16 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
 #pragma unroll
         for (int m = 0; m < 16; ++m) mine[m] = sum[m] = 0.0f;
         const int x = qq >> 1;                                       // group order m/4 ^ x
-        forward_right_row<0>(sum, mine, Aq + qq * 16 + 4 * x, Aq + qq * 16 - 4 * x, col, qq);
+        const float* pe = Aq + qq * 16 + 4 * x;
+        const float* po = Aq + qq * 16 - 4 * x;
+        // Wave w holds columns 16w .. 16w+15, and T[i, c] = 0 exactly for
+        // i < c: its rows before 16w add exact zeros and are skipped.
+        switch (w) {
+            case 0: forward_right_row<0>(sum, mine, pe, po, col, qq); break;
+            case 1: forward_right_row<16>(sum, mine, pe, po, col, qq); break;
+            case 2: forward_right_row<32>(sum, mine, pe, po, col, qq); break;
+            default: forward_right_row<48>(sum, mine, pe, po, col, qq); break;
+        }
         const float bc = bs[col];
         unsigned char* otb = lds + PrepLds::OUT + PrefillWs::kTb;
 #pragma unroll
