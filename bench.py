@@ -493,6 +493,32 @@ def copy_bandwidth(dev, launches: int = 20) -> float:
     return 2 * COPY_BYTES * launches / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
+def copy_same_size(dev, nbytes: int, launches: int, scrub_buf, scrub_sum, stream) -> dict:
+    """A plain device copy of nbytes each way (gqa_expand with one head), each
+    launch timed with HIP events after the same cache scrub as the step's
+    launches: the practical ceiling for a kernel that moves that many bytes."""
+    import torch
+    import linear_attention_recurrence_step_amd as gdn
+    k = 1024
+    seq = max(1, nbytes // (4 * k))
+    src = torch.randn(seq, 1, k, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        gdn.gqa_expand(src, 1, "tiled", dst=dst)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for i in range(launches):
+        if scrub_buf is not None:
+            scrub_buf.fill_(float(i))
+            torch.sum(scrub_buf, dim=0, out=scrub_sum)
+        ev[i][0].record(stream)
+        gdn.gqa_expand(src, 1, "tiled", dst=dst)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = _pct([a.elapsed_time(b) for a, b in ev], 50) * 1e3
+    moved = seq * k * 4
+    return {"bytes_each_way": moved, "us": round(us, 2), "GB/s": round(2 * moved / (us * 1e-6) / 1e9, 1)}
+
+
 def reported_hbm_figure():
     """Memory bus width (bits) and clock (kHz) as the HIP runtime reports
     them, and clock x width / 8 in GB/s (None if unavailable).  HBM3E moves
@@ -623,6 +649,12 @@ def main():
                 "traffic": measured_traffic(dk["kernel"], args.workload, dk["name"]),
                 "kernel": dk["name"], "bytes_per_launch": dk["algorithmic_bytes"],
                 "us_per_launch": dk["us"]}
+    if not args.no_peak_probe and not step.prefill_step:
+        # the same bytes moved by a plain copy, timed the same way: the ceiling
+        # at this size (small launches do not reach the large-copy rate)
+        cp = copy_same_size(dev, dk["algorithmic_bytes"] // 2, max(args.steps, 10), scrub_buf, scrub_sum, stream)
+        cp["kernel_frac_of_copy"] = round(dk["GB/s"] / cp["GB/s"], 4)
+        roofline["copy_same_bytes"] = cp
     if step.prefill_step:
         # the long record is a chain of dependent steps, not an HBM stream
         roofline["note"] = ("latency-bound: 64 dependent chunk steps per 16-row block (gdn_prefill)"
