@@ -227,10 +227,17 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
 
     const uint32_t tid = threadIdx.x, l = tid & 63u, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t lr = l & 15u, lg = l >> 4;
-    const uint32_t n = blockIdx.x / nchunks;               // b * Hv + hv
-    const uint32_t c = blockIdx.x - n * nchunks;
-    const uint32_t b = n / Hv, hv = n - b * Hv;
-    const uint32_t hk = tiled ? hv % Hk : hv / group;
+    // Workgroup order: the value heads that share a key head, for one chunk,
+    // are neighbours on one XCD, so the second of them finds that key head's
+    // key and query rows in the XCD's L2.
+    uint32_t li = xcd_contiguous_index(blockIdx.x, gridDim.x);
+    const uint32_t j = li % group;                         // which value head of the key head
+    li /= group;
+    const uint32_t c = li % nchunks;
+    li /= nchunks;
+    const uint32_t hk = li % Hk, b = li / Hk;
+    const uint32_t hv = tiled ? hk + Hk * j : hk * group + j;
+    const uint32_t n = b * Hv + hv;                         // b * Hv + hv
     const uint32_t t0 = c * kC;
     unsigned char* wsb = ws + (static_cast<size_t>(n) * nchunks + c) * PrefillWs::kBytes;
 
