@@ -552,11 +552,17 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     const uint32_t tt = w & 3u;                         // step tile
     const bool qside = w >= 4u;
     const uint32_t slices = Dv / kRows;
-    const uint32_t blk = xcd_contiguous_index(blockIdx.x, gridDim.x);
-    const uint32_t n = blk / slices;                    // b * Hv + hv
-    const uint32_t dv0 = (blk - n * slices) * kRows;
-    const uint32_t b = n / Hv, hv = n - b * Hv;
-    const uint32_t hk = tiled ? hv % Hk : hv / group;
+    // Workgroup order: (b, key head, value head of the key head, row block),
+    // renumbered so each XCD takes a contiguous range: the row blocks of a
+    // head, and the value heads that read one key head's rows, share an L2.
+    uint32_t li = xcd_contiguous_index(blockIdx.x, gridDim.x);
+    const uint32_t dv0 = (li % slices) * kRows;
+    li /= slices;
+    const uint32_t j = li % group;
+    li /= group;
+    const uint32_t hk = li % Hk, b = li / Hk;
+    const uint32_t hv = tiled ? hk + Hk * j : hk * group + j;
+    const uint32_t n = b * Hv + hv;                     // b * Hv + hv
 
     // This lane's 16-byte state piece: row dv0 + lr, columns kcol(w, 4 lg) .. +3
     // (the key index is permuted, see kcol); with 192 key columns waves 4-7
