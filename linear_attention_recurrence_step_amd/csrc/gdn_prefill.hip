@@ -660,10 +660,22 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     bool pend_valid = false;
     uint32_t pend_t0 = 0u;
     auto produce = [&](const f32x4v& vals, uint32_t actbits, uint32_t t0p) {
+        if constexpr (IO == kBF16) {
+            // Round to nearest even with the packed conversion; a NaN is
+            // replaced by the canonical quiet NaN first, so the bits equal
+            // f32_to_bf16_bits' (NaN -> 0x7FC0).
+            f32x4v v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            ot[(4u * lg + r) * 16 + lr] =
-                static_cast<uint16_t>(IO == kBF16 ? f32_to_bf16_bits(vals[r]) : f32_to_f16_bits(vals[r]));
+            for (int r = 0; r < 4; ++r) v[r] = vals[r] != vals[r] ? __uint_as_float(0x7fc00000u) : vals[r];
+            const uint32_t p01 = cvt_pk_bf16(v[0], v[1]), p23 = cvt_pk_bf16(v[2], v[3]);
+            ot[(4u * lg + 0) * 16 + lr] = static_cast<uint16_t>(p01);
+            ot[(4u * lg + 1) * 16 + lr] = static_cast<uint16_t>(p01 >> 16);
+            ot[(4u * lg + 2) * 16 + lr] = static_cast<uint16_t>(p23);
+            ot[(4u * lg + 3) * 16 + lr] = static_cast<uint16_t>(p23 >> 16);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ot[(4u * lg + r) * 16 + lr] = static_cast<uint16_t>(f32_to_f16_bits(vals[r]));
+        }
         if (lr == 0u) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) otf[4u * lg + r] = (actbits >> r) & 1u;
