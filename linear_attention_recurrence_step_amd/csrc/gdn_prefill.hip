@@ -185,28 +185,40 @@ __device__ __forceinline__ void forward_right_row(float (&sum)[16], float (&mine
 
 // ------------------------------------------------------------------ prep
 //
-// One workgroup of four waves per (b, hv, chunk).  Wave w owns row tile w
-// (steps 16w .. 16w+15) of the 64 x 64 matrices.
+// One workgroup of four waves per (b, key head, chunk) and up to kPrepHeads
+// of the value heads that read that key head.  The Gram products G = K K^T
+// and H = Q K^T of a chunk depend on the key head only, so they are formed
+// once from one load of the key and query rows; the gates and betas, M, A,
+// P, (I + A)^-1 and Tb are then taken value head by value head.  Wave w owns
+// row tile w (steps 16w .. 16w+15) of the 64 x 64 matrices.
 //
-// LDS of the prep kernel (52 KiB at Dk = 128: three workgroups per CU).  The
-// chunk's key and query rows (padded rows) are dead once the Gram tiles are
-// formed; the output block (Tb and P in the workspace's fragment order)
-// reuses their space.  M and then A (in the quad layout) share one area: A
-// is held in registers until every wave is done reading M.
+// LDS of the prep kernel (36 KiB at Dk = 128: four workgroups per CU; 44 KiB
+// at Dk = 192: three).  Only the chunk's key rows (padded rows) are staged:
+// each wave loads the 16 query rows of its own row tile straight into the
+// registers of its Gram product.  P (in the workspace's fragment order)
+// takes the key rows' space once the Gram tiles are formed.  M, then A (in
+// the quad layout), then Tb (fragment order) share one area: A is held in
+// registers until every wave is done reading M, and Tb until every wave is
+// done reading A.  A value head's Tb and P leave for the workspace before
+// the next value head's M and P take their places.
+constexpr uint32_t kPrepHeads = 4;     // value heads per prep workgroup, at most
+
 template <int DK>
 struct PrepLds {
-    static constexpr int KS = DK * 2 + 16;             // K / Q row stride in bytes (padded)
+    static constexpr int KS = DK * 2 + 16;             // K row stride in bytes (padded)
     static constexpr int MS = kC + 1;                  // M row stride in floats
     static constexpr int KR = 0;                       // K rows [64] x KS
-    static constexpr int QR = KR + kC * KS;            // Q rows [64] x KS
-    static constexpr int OUT = 0;                      // output block, 4 x 8 KiB (aliases K, Q)
-    static constexpr int ML = QR + kC * KS;            // M [64][65] fp32
+    static constexpr int PO = KR;                      // then P, hi and lo fragments (16 KiB)
+    static constexpr int ML = KR + kC * KS;            // M [64][65] fp32
     static constexpr int AQ = ML;                      // then A in the quad layout (16 KiB)
-    static constexpr int GS = ML + kC * MS * 4;        // gates [64] fp32
-    static constexpr int BS = GS + kC * 4;             // betas [64] fp32
-    static constexpr int BYTES = BS + kC * 4;
-    static_assert(4 * kC * kC * 2 <= 2 * kC * KS, "output block fits in the key/query area");
+    static constexpr int TBO = ML;                     // then Tb, hi and lo fragments (16 KiB)
+    static constexpr int GS = ML + kC * MS * 4;        // gates [kPrepHeads][64] fp32
+    static constexpr int BS = GS + kPrepHeads * kC * 4;   // betas [kPrepHeads][64] fp32
+    static constexpr int BYTES = BS + kPrepHeads * kC * 4;
+    static_assert(PrefillWs::kP - PrefillWs::kTb == 2 * PrefillWs::kMat, "Tb then P in the workspace");
+    static_assert(2 * PrefillWs::kMat <= kC * KS, "P fits where the key rows were");
     static_assert(kC * 4 * 16 * 4 <= kC * MS * 4, "A fits where M was");
+    static_assert(2 * PrefillWs::kMat <= kC * MS * 4, "Tb fits where A was");
 };
 
 template <int IO, int DK>
@@ -214,7 +226,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ g,
     const void* __restrict__ beta, const uint32_t* __restrict__ mask,
     unsigned char* __restrict__ ws, void* __restrict__ k_log, void* __restrict__ g_log,
-    uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t nchunks, uint32_t group, int tiled)
+    uint32_t T, uint32_t Hk, uint32_t Hv, uint32_t nchunks, uint32_t group, uint32_t head_sets, int tiled)
 {
     static_assert(IO == kBF16 || IO == kF16, "the chunked prefill takes 16-bit I/O");
     using PrepLds = gdn::PrepLds<DK>;
@@ -227,32 +239,52 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
 
     const uint32_t tid = threadIdx.x, l = tid & 63u, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t lr = l & 15u, lg = l >> 4;
-    // Workgroup order: the value heads that share a key head, for one chunk,
-    // are neighbours on one XCD, so the second of them finds that key head's
-    // key and query rows in the XCD's L2.
+    // Workgroup order: (b, chunk, key head, set of value heads), the last
+    // fastest, so that the workgroups of one XCD read whole steps' rows of
+    // every key head (contiguous memory).  Set hs takes the value heads
+    // j = kPrepHeads hs .. of the key head (j-th value head: hk + Hk j under
+    // the tiled map, hk group + j under the block map).
     uint32_t li = xcd_contiguous_index(blockIdx.x, gridDim.x);
-    const uint32_t j = li % group;                         // which value head of the key head
-    li /= group;
-    const uint32_t c = li % nchunks;
-    li /= nchunks;
-    const uint32_t hk = li % Hk, b = li / Hk;
-    const uint32_t hv = tiled ? hk + Hk * j : hk * group + j;
-    const uint32_t n = b * Hv + hv;                         // b * Hv + hv
+    const uint32_t hs = li % head_sets;
+    li /= head_sets;
+    const uint32_t hk = li % Hk;
+    li /= Hk;
+    const uint32_t c = li % nchunks, b = li / nchunks;
+    const uint32_t j0 = hs * kPrepHeads;
+    const uint32_t nh = group - j0 < kPrepHeads ? group - j0 : kPrepHeads;   // value heads here
+    auto value_head = [&](uint32_t jj) { return tiled ? hk + Hk * (j0 + jj) : hk * group + j0 + jj; };
     const uint32_t t0 = c * kC;
-    unsigned char* wsb = ws + (static_cast<size_t>(n) * nchunks + c) * PrefillWs::kBytes;
 
-    // The chunk's key and query rows, 16-byte pieces: thread tid takes pieces
-    // p = tid + 256 j, piece p % (DK / 8) of row p / (DK / 8).  Steps past T
-    // read step T-1; rows of inactive steps are stored as zeros (a select, so
+    // The chunk's key rows, 16-byte pieces: thread tid takes pieces
+    // p = tid + 256 j, piece p % (DK / 8) of row p / (DK / 8).  The query rows
+    // of this wave's row tile: lane (lr, lg) takes row 16 w + lr, pieces
+    // 4 m + lg (its A operand of the Gram product below).  Thread tid also
+    // takes the gate and beta of step tid % 64 of value head tid / 64.  Steps
+    // past T read step T-1; rows of inactive steps become zeros (a select, so
     // a NaN there cannot enter a product).
     // Mask words are loaded whether or not there is a mask (from k, whose
     // B*T*Hk*Dk/2 words cover every index, when there is none) and then
     // selected, so the loads are not serialised behind branches.
     constexpr uint32_t kPieces = DK / 8;               // 16-byte pieces per row
     constexpr int kPer = kC * kPieces / 256;           // pieces per thread
+    constexpr int NB = DK / 32;                        // 32-column key blocks
+    static_assert(kPrepHeads * kC == 256, "one gate per thread");
+    const uint32_t* mwords = mask ? mask : static_cast<const uint32_t*>(k);
+    u32x4 qf[NB];                                      // query pieces of row 16 w + lr
     {
-        const uint32_t* mwords = mask ? mask : static_cast<const uint32_t*>(k);
-        u32x4 kp[kPer], qp[kPer];
+        const uint32_t t = t0 + 16u * w + lr, tc = t < T ? t : T - 1;
+        const size_t off = ((static_cast<size_t>(b) * T + tc) * Hk + hk) * (DK * 2) + lg * 16;
+#pragma unroll
+        for (int m = 0; m < NB; ++m)
+            qf[m] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(q) + off + m * 64);
+        const uint32_t mword = mwords[static_cast<size_t>(b) * T + tc];
+        const bool act = t < T && (mask ? mword : 1u) > 0u;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int m = 0; m < NB; ++m) qf[m] = act ? qf[m] : z;
+    }
+    {
+        u32x4 kp[kPer];
         uint32_t mw[kPer];
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
@@ -260,12 +292,14 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
             const uint32_t t = t0 + row, tc = t < T ? t : T - 1;
             const size_t off = ((static_cast<size_t>(b) * T + tc) * Hk + hk) * (DK * 2) + pc * 16;
             kp[j] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(k) + off);
-            qp[j] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(q) + off);
             const uint32_t m = mwords[static_cast<size_t>(b) * T + tc];
             mw[j] = mask ? m : 1u;
         }
-        if (tid < kC) {
-            const uint32_t t = t0 + tid, tc = t < T ? t : T - 1;
+        {
+            const uint32_t jj = tid / kC, ts = tid % kC;
+            const uint32_t jc = jj < nh ? jj : 0u;         // heads past nh load head 0's (unused)
+            const uint32_t hv = value_head(jc);
+            const uint32_t t = t0 + ts, tc = t < T ? t : T - 1;
             const size_t i = (static_cast<size_t>(b) * T + tc) * Hv + hv;
             const uint32_t graw = static_cast<const uint16_t*>(g)[i];
             const float bl = io_load1<IO>(beta, i);
@@ -273,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
             const bool act = t < T && (mask ? mword : 1u) > 0u;
             gs[tid] = act ? in_f32<IO>(graw) : 1.0f;
             bs[tid] = act ? bl : 0.0f;
-            if (g_log != nullptr && act)                         // tape capture: the gate's bits
+            if (g_log != nullptr && act && jj < nh)               // tape capture: the gate's bits
                 static_cast<uint16_t*>(g_log)[(static_cast<size_t>(b) * T + t) * Hv + hv] =
                     static_cast<uint16_t>(graw);
         }
@@ -283,33 +317,15 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
             const uint32_t p = tid + 256u * j, r = p / kPieces, pc = p - r * kPieces;
             const bool act = t0 + r < T && mw[j] > 0u;
             *reinterpret_cast<u32x4*>(lds + PrepLds::KR + r * PrepLds::KS + pc * 16) = act ? kp[j] : z;
-            *reinterpret_cast<u32x4*>(lds + PrepLds::QR + r * PrepLds::KS + pc * 16) = act ? qp[j] : z;
-            if (k_log != nullptr && act)                         // tape capture: key row of this value head
-                *reinterpret_cast<u32x4*>(static_cast<char*>(k_log) +
-                                          ((static_cast<size_t>(b) * T + t0 + r) * Hv + hv) * (DK * 2) +
-                                          pc * 16) = kp[j];
+            if (k_log != nullptr && act)                         // tape capture: the key row of each value head
+                for (uint32_t jj = 0; jj < nh; ++jj)
+                    *reinterpret_cast<u32x4*>(static_cast<char*>(k_log) +
+                                              ((static_cast<size_t>(b) * T + t0 + r) * Hv + value_head(jj)) *
+                                                  (DK * 2) +
+                                              pc * 16) = kp[j];
         }
     }
     __syncthreads();
-
-    // M by running products of the gates (gates held in registers): thread t
-    // walks s = 63 .. 0, multiplying in g_s once s <= t.
-    if (tid < kC) {
-        float gr[kC];
-#pragma unroll
-        for (int s4 = 0; s4 < kC / 4; ++s4) {
-            const float4 v4 = *reinterpret_cast<const float4*>(&gs[4 * s4]);
-            gr[4 * s4] = v4.x; gr[4 * s4 + 1] = v4.y; gr[4 * s4 + 2] = v4.z; gr[4 * s4 + 3] = v4.w;
-        }
-        const int t = static_cast<int>(tid);
-        float p = 1.0f;
-#pragma unroll
-        for (int s = kC - 1; s >= 0; --s) {
-            Ml[t * MS + s] = s <= t ? p : 0.0f;
-            p = s <= t ? p * gr[s] : p;
-        }
-        reinterpret_cast<float*>(wsb + PrefillWs::kGamma)[t] = p;   // gamma_t = g_0 .. g_t
-    }
 
     // Gram tiles G = K K^T and H = Q K^T of row tile w (all four column tiles;
     // above the diagonal the s <= t masks below make A and P exact zeros).
@@ -318,14 +334,11 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
     // x[16 tile + lr][32 m + 8 lg .. +7] as A and B.
     f32x4v G[4], H[4];
     {
-        constexpr int NB = DK / 32;
-        u32x4 kw[NB], qf[NB], kwl[NB], qfl[NB];
+        u32x4 kw[NB], kwl[NB], qfl[NB];
         const unsigned char* kwr = lds + PrepLds::KR + (16u * w + lr) * PrepLds::KS + lg * 16;
-        const unsigned char* qwr = lds + PrepLds::QR + (16u * w + lr) * PrepLds::KS + lg * 16;
 #pragma unroll
         for (int m = 0; m < NB; ++m) {
             kw[m] = *reinterpret_cast<const u32x4*>(kwr + m * 64);
-            qf[m] = *reinterpret_cast<const u32x4*>(qwr + m * 64);
             if constexpr (IO == kF16) {
                 split_f16x8(kw[m], kw[m], kwl[m]);
                 split_f16x8(qf[m], qf[m], qfl[m]);
@@ -334,98 +347,139 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const unsigned char* kr = lds + PrepLds::KR + (16u * st + lr) * PrepLds::KS + lg * 16;
-            f32x4v g = {0.f, 0.f, 0.f, 0.f}, h = g;
+            f32x4v gg = {0.f, 0.f, 0.f, 0.f}, hh = gg;
 #pragma unroll
             for (int m = 0; m < NB; ++m) {
                 u32x4 bk = *reinterpret_cast<const u32x4*>(kr + m * 64);
                 if constexpr (IO == kBF16) {
-                    g = mfma_bf16_k32(kw[m], bk, g);
-                    h = mfma_bf16_k32(qf[m], bk, h);
+                    gg = mfma_bf16_k32(kw[m], bk, gg);
+                    hh = mfma_bf16_k32(qf[m], bk, hh);
                 } else {
                     u32x4 bkl;
                     split_f16x8(bk, bk, bkl);
-                    g = mfma_bf16_k32(kw[m], bk, g);
-                    g = mfma_bf16_k32(kw[m], bkl, g);
-                    g = mfma_bf16_k32(kwl[m], bk, g);
-                    g = mfma_bf16_k32(kwl[m], bkl, g);
-                    h = mfma_bf16_k32(qf[m], bk, h);
-                    h = mfma_bf16_k32(qf[m], bkl, h);
-                    h = mfma_bf16_k32(qfl[m], bk, h);
-                    h = mfma_bf16_k32(qfl[m], bkl, h);
+                    gg = mfma_bf16_k32(kw[m], bk, gg);
+                    gg = mfma_bf16_k32(kw[m], bkl, gg);
+                    gg = mfma_bf16_k32(kwl[m], bk, gg);
+                    gg = mfma_bf16_k32(kwl[m], bkl, gg);
+                    hh = mfma_bf16_k32(qf[m], bk, hh);
+                    hh = mfma_bf16_k32(qf[m], bkl, hh);
+                    hh = mfma_bf16_k32(qfl[m], bk, hh);
+                    hh = mfma_bf16_k32(qfl[m], bkl, hh);
                 }
             }
-            G[st] = g;
-            H[st] = h;
+            G[st] = gg;
+            H[st] = hh;
         }
     }
-    __syncthreads();       // M is complete; the key and query rows are dead
+    __syncthreads();       // the key rows are dead
 
-    // A and P of row tile w; P goes to the output block, A stays in G until
-    // M is dead.
-    if (tid < kC) reinterpret_cast<float*>(wsb + PrefillWs::kRho)[tid] = Ml[(kC - 1) * MS + tid];
-    unsigned char* op = lds + PrepLds::OUT + PrefillWs::kP;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * static_cast<int>(w) + 4 * static_cast<int>(lg) + r;
-            const int s = 16 * st + static_cast<int>(lr);
-            const float m = Ml[t * MS + s];
-            G[st][r] = s < t ? bs[t] * (m * G[st][r]) : 0.0f;
-            uint16_t hi, lo;
-            split1(s <= t ? m * H[st][r] : 0.0f, hi, lo);
-            const uint32_t o = frag_offset(static_cast<uint32_t>(t), static_cast<uint32_t>(s));
-            *reinterpret_cast<uint16_t*>(op + o) = hi;
-            *reinterpret_cast<uint16_t*>(op + o + kFragLo) = lo;
-        }
-    }
-    __syncthreads();       // M is dead
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            Aq[aq_index(16u * w + 4u * lg + r, 16u * st + lr)] = G[st][r];
-    }
-    __syncthreads();
+    for (uint32_t jj = 0; jj < nh; ++jj) {
+        // The thread index passes through an empty asm statement so that the
+        // addresses derived from it are formed per value head, not kept in
+        // registers across the loop.
+        uint32_t tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const uint32_t l = tid & 63u, lr = l & 15u, lg = l >> 4;
+        const uint32_t hv = value_head(jj);
+        const uint32_t n = b * Hv + hv;
+        unsigned char* wsb = ws + (static_cast<size_t>(n) * nchunks + c) * PrefillWs::kBytes;
+        const float* gh = gs + jj * kC;
+        const float* bh = bs + jj * kC;
 
-    // (I + A)^-1 by forward substitution over all four waves (four lanes per
-    // column), then Tb = (I + A)^-1 diag(beta).
-    {
-        const int col = static_cast<int>(tid >> 2), qq = static_cast<int>(tid & 3u);
-        float mine[16], sum[16];
+        // M by running products of the gates (gates held in registers): thread t
+        // walks s = 63 .. 0, multiplying in g_s once s <= t.
+        if (tid < kC) {
+            float gr[kC];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) mine[m] = sum[m] = 0.0f;
-        const int x = qq >> 1;                                       // group order m/4 ^ x
-        const float* pe = Aq + qq * 16 + 4 * x;
-        const float* po = Aq + qq * 16 - 4 * x;
-        // Wave w holds columns 16w .. 16w+15, and T[i, c] = 0 exactly for
-        // i < c: its rows before 16w add exact zeros and are skipped.
-        switch (w) {
-            case 0: forward_right_row<0>(sum, mine, pe, po, col, qq); break;
-            case 1: forward_right_row<16>(sum, mine, pe, po, col, qq); break;
-            case 2: forward_right_row<32>(sum, mine, pe, po, col, qq); break;
-            default: forward_right_row<48>(sum, mine, pe, po, col, qq); break;
-        }
-        const float bc = bs[col];
-        unsigned char* otb = lds + PrepLds::OUT + PrefillWs::kTb;
+            for (int s4 = 0; s4 < kC / 4; ++s4) {
+                const float4 v4 = *reinterpret_cast<const float4*>(&gh[4 * s4]);
+                gr[4 * s4] = v4.x; gr[4 * s4 + 1] = v4.y; gr[4 * s4 + 2] = v4.z; gr[4 * s4 + 3] = v4.w;
+            }
+            const int t = static_cast<int>(tid);
+            float p = 1.0f;
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const int i = 4 * m + qq;
-            uint16_t hi, lo;
-            split1(mine[m] * bc, hi, lo);
-            const uint32_t o = frag_offset(static_cast<uint32_t>(i), static_cast<uint32_t>(col));
-            *reinterpret_cast<uint16_t*>(otb + o) = hi;
-            *reinterpret_cast<uint16_t*>(otb + o + kFragLo) = lo;
+            for (int s = kC - 1; s >= 0; --s) {
+                Ml[t * MS + s] = s <= t ? p : 0.0f;
+                p = s <= t ? p * gr[s] : p;
+            }
+            reinterpret_cast<float*>(wsb + PrefillWs::kGamma)[t] = p;   // gamma_t = g_0 .. g_t
         }
-    }
-    __syncthreads();
+        __syncthreads();   // M is complete
 
-    // The 32 KiB of Tb and P (already in fragment order) to the workspace in
-    // contiguous 16-byte pieces.
+        // A and P of row tile w; P goes to its LDS area, A stays in registers
+        // until M is dead.
+        if (tid < kC) reinterpret_cast<float*>(wsb + PrefillWs::kRho)[tid] = Ml[(kC - 1) * MS + tid];
+        unsigned char* op = lds + PrepLds::PO;
+        f32x4v A[4];
 #pragma unroll
-    for (int j = 0; j < 4 * PrefillWs::kMat / 16 / 256; ++j) {
-        const uint32_t p = tid + 256u * j;
-        *reinterpret_cast<u32x4*>(wsb + p * 16) = *reinterpret_cast<const u32x4*>(lds + PrepLds::OUT + p * 16);
+        for (int st = 0; st < 4; ++st) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * static_cast<int>(w) + 4 * static_cast<int>(lg) + r;
+                const int s = 16 * st + static_cast<int>(lr);
+                const float m = Ml[t * MS + s];
+                A[st][r] = s < t ? bh[t] * (m * G[st][r]) : 0.0f;
+                uint16_t hi, lo;
+                split1(s <= t ? m * H[st][r] : 0.0f, hi, lo);
+                const uint32_t o = frag_offset(static_cast<uint32_t>(t), static_cast<uint32_t>(s));
+                *reinterpret_cast<uint16_t*>(op + o) = hi;
+                *reinterpret_cast<uint16_t*>(op + o + kFragLo) = lo;
+            }
+        }
+        __syncthreads();   // M is dead
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Aq[aq_index(16u * w + 4u * lg + r, 16u * st + lr)] = A[st][r];
+        }
+        __syncthreads();
+
+        // (I + A)^-1 by forward substitution over all four waves (four lanes per
+        // column), then Tb = (I + A)^-1 diag(beta).
+        {
+            const int col = static_cast<int>(tid >> 2), qq = static_cast<int>(tid & 3u);
+            float mine[16], sum[16];
+#pragma unroll
+            for (int m = 0; m < 16; ++m) mine[m] = sum[m] = 0.0f;
+            const int x = qq >> 1;                                       // group order m/4 ^ x
+            const float* pe = Aq + qq * 16 + 4 * x;
+            const float* po = Aq + qq * 16 - 4 * x;
+            // Wave w holds columns 16w .. 16w+15, and T[i, c] = 0 exactly for
+            // i < c: its rows before 16w add exact zeros and are skipped.
+            switch (w) {
+                case 0: forward_right_row<0>(sum, mine, pe, po, col, qq); break;
+                case 1: forward_right_row<16>(sum, mine, pe, po, col, qq); break;
+                case 2: forward_right_row<32>(sum, mine, pe, po, col, qq); break;
+                default: forward_right_row<48>(sum, mine, pe, po, col, qq); break;
+            }
+            const float bc = bh[col];
+            __syncthreads();                                             // every wave is done reading A
+            unsigned char* otb = lds + PrepLds::TBO;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const int i = 4 * m + qq;
+                uint16_t hi, lo;
+                split1(mine[m] * bc, hi, lo);
+                const uint32_t o = frag_offset(static_cast<uint32_t>(i), static_cast<uint32_t>(col));
+                *reinterpret_cast<uint16_t*>(otb + o) = hi;
+                *reinterpret_cast<uint16_t*>(otb + o + kFragLo) = lo;
+            }
+        }
+        __syncthreads();
+
+        // The 32 KiB of Tb and P (already in fragment order) to the workspace in
+        // contiguous 16-byte pieces.
+        constexpr int kOutPer = 2 * PrefillWs::kMat / 16 / 256;          // pieces per thread of each matrix
+#pragma unroll
+        for (int j = 0; j < kOutPer; ++j) {
+            const uint32_t p = tid + 256u * j;
+            *reinterpret_cast<u32x4*>(wsb + PrefillWs::kTb + p * 16) =
+                *reinterpret_cast<const u32x4*>(lds + PrepLds::TBO + p * 16);
+            *reinterpret_cast<u32x4*>(wsb + PrefillWs::kP + p * 16) =
+                *reinterpret_cast<const u32x4*>(lds + PrepLds::PO + p * 16);
+        }
+        if (jj + 1 < nh) __syncthreads();   // the next value head's M and P take these areas
     }
 }
 
@@ -978,8 +1032,10 @@ hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
         if (e != hipSuccess) return e;
         lds_set.fetch_or(bit, std::memory_order_release);
     }
-    hipLaunchKernelGGL((gdn_prefill_prep_kernel<IO, DK>), dim3(a.B * a.Hv * nchunks), dim3(256), PL::BYTES, stream,
-                       a.q, a.k, a.g, a.beta, a.mask, ws, a.k_log, a.g_log, a.T, a.Hk, a.Hv, nchunks, group, tiled);
+    const uint32_t head_sets = (group + kPrepHeads - 1) / kPrepHeads;
+    hipLaunchKernelGGL((gdn_prefill_prep_kernel<IO, DK>), dim3(a.B * a.Hk * nchunks * head_sets), dim3(256), PL::BYTES,
+                       stream, a.q, a.k, a.g, a.beta, a.mask, ws, a.k_log, a.g_log, a.T, a.Hk, a.Hv, nchunks, group,
+                       head_sets, tiled);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gdn_prefill_scan_kernel<IO, DK>), dim3(a.B * a.Hv * (a.Dv / kRows)), dim3(512), SL::BYTES,

@@ -63,6 +63,10 @@ CASES = [
     (2, 256, 2, 6, 64, "none", "tiled"),
     (1, 100, 1, 1, 1024, "bernoulli", "block"),     # the widest head the ABI takes
     (16, 33, 4, 8, 32, "trailing", "tiled"),        # many heads, one ragged chunk each
+    # more value heads per key head than one prep workgroup takes (four):
+    # a full and a partial set of value heads, and two full sets
+    (1, 70, 1, 5, 32, "bernoulli", "block"),
+    (2, 65, 2, 16, 16, "trailing", "tiled"),
 ]
 
 
@@ -201,6 +205,8 @@ CAPTURE = [
     (3, 64, 2, 2, 128, 16, "bf16", "tiled", "zeros"),
     (1, 100, 2, 4, 192, 32, "f16", "tiled", "bernoulli"),
     (2, 65, 4, 4, 192, 128, "bf16", "block", "trailing"),
+    (1, 70, 1, 6, 128, 16, "bf16", "tiled", "bernoulli"),     # two sets of value heads per key head
+    (1, 64, 2, 12, 128, 16, "f16", "block", "ones"),
 ]
 
 
