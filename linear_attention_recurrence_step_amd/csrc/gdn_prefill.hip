@@ -374,9 +374,10 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
     __syncthreads();       // the key rows are dead
 
     for (uint32_t jj = 0; jj < nh; ++jj) {
-        // The thread index passes through an empty asm statement so that the
-        // addresses derived from it are formed per value head, not kept in
-        // registers across the loop.
+        // tid, l, lr and lg shadow the kernel's own on purpose: the thread
+        // index passes through an empty asm statement so that the addresses
+        // derived from it are formed per value head, not kept in registers
+        // across the loop (which pushed the kernel to 196 VGPRs).
         uint32_t tid = threadIdx.x;
         asm volatile("" : "+v"(tid));
         const uint32_t l = tid & 63u, lr = l & 15u, lg = l >> 4;
