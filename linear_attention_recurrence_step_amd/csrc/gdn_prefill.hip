@@ -164,23 +164,46 @@ __device__ __forceinline__ uint32_t aq_index(uint32_t i, uint32_t j) {      // f
     return (j * 4u + q) * 16u + ((((m >> 2) ^ (q >> 1) ^ j) & 3u) << 2) + (m & 3u);
 }
 
+// Row I's reads of A: the groups m4 >= I / 16 of column I (group m4 holds the
+// lane's rows 16 m4 .. 16 m4 + 15, of which only rows after I still take terms).
+template <int I>
+__device__ __forceinline__ void load_a_row(float4 (&a)[4], const float* pe, const float* po) {
+#pragma unroll
+    for (int m4 = (I >> 2) / 4; m4 < 4; ++m4) {
+        const int v = m4 ^ (I & 3);                                 // stored group, before the lane's q/2
+        a[m4] = *reinterpret_cast<const float4*>((v & 1 ? po : pe) + I * 64 + 4 * v);
+    }
+}
+
+// cur holds row I's reads of A; row I + 1's are issued before row I's work,
+// so they are on their way during it.
 template <int I>
 __device__ __forceinline__ void forward_right_row(float (&sum)[16], float (&mine)[16], const float* pe,
-                                                  const float* po, int c, int q) {
+                                                  const float* po, int c, int q, const float4 (&cur)[4]) {
     constexpr int M0 = I >> 2, Q0 = I & 3;
+    float4 nxt[4];
+    if constexpr (I + 1 < kC) load_a_row<I + 1>(nxt, pe, po);
     const float own = (I == c ? 1.0f : 0.0f) - sum[M0];            // meaningful on lane Q0 of the quad
     const float tI = dpp_read<Q0 * 0x55>(own);                      // quad_perm [Q0, Q0, Q0, Q0]
     mine[M0] = q == Q0 ? tI : mine[M0];
 #pragma unroll
     for (int m4 = M0 / 4; m4 < 4; ++m4) {
-        const int v = m4 ^ (I & 3);                                 // stored group, before the lane's q/2
-        const float4 a = *reinterpret_cast<const float4*>((v & 1 ? po : pe) + I * 64 + 4 * v);
+        const float4 a = cur[m4];
         if (4 * m4 + 0 >= M0) sum[4 * m4 + 0] = fmaf(a.x, tI, sum[4 * m4 + 0]);
         if (4 * m4 + 1 >= M0) sum[4 * m4 + 1] = fmaf(a.y, tI, sum[4 * m4 + 1]);
         if (4 * m4 + 2 >= M0) sum[4 * m4 + 2] = fmaf(a.z, tI, sum[4 * m4 + 2]);
         if (4 * m4 + 3 >= M0) sum[4 * m4 + 3] = fmaf(a.w, tI, sum[4 * m4 + 3]);
     }
-    if constexpr (I + 1 < kC) forward_right_row<I + 1>(sum, mine, pe, po, c, q);
+    if constexpr (I + 1 < kC) forward_right_row<I + 1>(sum, mine, pe, po, c, q, nxt);
+}
+
+// The substitution from row I0 on.
+template <int I0>
+__device__ __forceinline__ void forward_right_from(float (&sum)[16], float (&mine)[16], const float* pe,
+                                                   const float* po, int c, int q) {
+    float4 first[4];
+    load_a_row<I0>(first, pe, po);
+    forward_right_row<I0>(sum, mine, pe, po, c, q, first);
 }
 
 // ------------------------------------------------------------------ prep
@@ -387,23 +410,36 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
         const float* gh = gs + jj * kC;
         const float* bh = bs + jj * kC;
 
-        // M by running products of the gates (gates held in registers): thread t
-        // walks s = 63 .. 0, multiplying in g_s once s <= t.
-        if (tid < kC) {
-            float gr[kC];
+        // M[t, s] = g_{s+1} .. g_t (s <= t) by products of the gates, no
+        // division, over all four waves: thread (t = tid / 4, q = tid % 4) takes
+        // columns 16 q .. 16 q + 15 of row t.  It forms the product of its
+        // segment's gates up to t, the quad (the four segments of row t) hands
+        // it the product of the later segments' ones, and it walks its columns
+        // down from there, multiplying in g_s once s <= t.
+        {
+            const int t = static_cast<int>(tid >> 2), q = static_cast<int>(tid & 3u);
+            float gq[16];
 #pragma unroll
-            for (int s4 = 0; s4 < kC / 4; ++s4) {
-                const float4 v4 = *reinterpret_cast<const float4*>(&gh[4 * s4]);
-                gr[4 * s4] = v4.x; gr[4 * s4 + 1] = v4.y; gr[4 * s4 + 2] = v4.z; gr[4 * s4 + 3] = v4.w;
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const float4 v4 = *reinterpret_cast<const float4*>(&gh[16 * q + 4 * i4]);
+                gq[4 * i4] = v4.x; gq[4 * i4 + 1] = v4.y; gq[4 * i4 + 2] = v4.z; gq[4 * i4 + 3] = v4.w;
             }
-            const int t = static_cast<int>(tid);
-            float p = 1.0f;
+            float seg = 1.0f;                                           // g over this segment, up to t
 #pragma unroll
-            for (int s = kC - 1; s >= 0; --s) {
-                Ml[t * MS + s] = s <= t ? p : 0.0f;
-                p = s <= t ? p * gr[s] : p;
+            for (int i = 15; i >= 0; --i) seg = 16 * q + i <= t ? seg * gq[i] : seg;
+            // (The reads run on every lane of the quad, then are selected: a
+            // read from a lane that is switched off would return 0.)
+            const float d1 = dpp_read<0xf9>(seg);                       // quad_perm [1,2,3,3]: segment q + 1
+            const float d2 = dpp_read<0xfe>(seg);                       // quad_perm [2,3,3,3]: segment q + 2
+            const float d3 = dpp_read<0xff>(seg);                       // quad_perm [3,3,3,3]: segment q + 3
+            float r = (q < 3 ? d1 : 1.0f) * (q < 2 ? d2 : 1.0f) * (q < 1 ? d3 : 1.0f);   // later segments, up to t
+            if (q == 0) reinterpret_cast<float*>(wsb + PrefillWs::kGamma)[t] = seg * r;   // gamma_t = g_0 .. g_t
+#pragma unroll
+            for (int i = 15; i >= 0; --i) {
+                const int sc = 16 * q + i;
+                Ml[t * MS + sc] = sc <= t ? r : 0.0f;
+                r = sc <= t ? r * gq[i] : r;
             }
-            reinterpret_cast<float*>(wsb + PrefillWs::kGamma)[t] = p;   // gamma_t = g_0 .. g_t
         }
         __syncthreads();   // M is complete
 
@@ -449,10 +485,10 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
             // Wave w holds columns 16w .. 16w+15, and T[i, c] = 0 exactly for
             // i < c: its rows before 16w add exact zeros and are skipped.
             switch (w) {
-                case 0: forward_right_row<0>(sum, mine, pe, po, col, qq); break;
-                case 1: forward_right_row<16>(sum, mine, pe, po, col, qq); break;
-                case 2: forward_right_row<32>(sum, mine, pe, po, col, qq); break;
-                default: forward_right_row<48>(sum, mine, pe, po, col, qq); break;
+                case 0: forward_right_from<0>(sum, mine, pe, po, col, qq); break;
+                case 1: forward_right_from<16>(sum, mine, pe, po, col, qq); break;
+                case 2: forward_right_from<32>(sum, mine, pe, po, col, qq); break;
+                default: forward_right_from<48>(sum, mine, pe, po, col, qq); break;
             }
             const float bc = bh[col];
             __syncthreads();                                             // every wave is done reading A
