@@ -164,8 +164,9 @@ __device__ __forceinline__ uint32_t aq_index(uint32_t i, uint32_t j) {      // f
     return (j * 4u + q) * 16u + ((((m >> 2) ^ (q >> 1) ^ j) & 3u) << 2) + (m & 3u);
 }
 
-// Row I's reads of A: the groups m4 >= I / 16 of column I (group m4 holds the
-// lane's rows 16 m4 .. 16 m4 + 15, of which only rows after I still take terms).
+// Row I's reads of A: the groups m4 >= I / 16 of column I (group m4 holds A at
+// the lane's four rows among 16 m4 .. 16 m4 + 15; earlier groups' rows are all
+// at or before I and take no more terms).
 template <int I>
 __device__ __forceinline__ void load_a_row(float4 (&a)[4], const float* pe, const float* po) {
 #pragma unroll
