@@ -545,15 +545,20 @@ __global__ __launch_bounds__(256, 2) void gdn_prefill_prep_kernel(
 template <int IO, int DK>
 struct ScanLds {
     static constexpr int NB = DK / 32;                 // 32-column key blocks
-    static constexpr int KTS = kC + 8;                 // K^T row stride in bf16 (144 bytes, 16-byte aligned)
+    // Key rows in LDS: stride 2 DK + 64 bytes (an odd multiple of 64 bytes
+    // modulo 256), and in rows t with t / 8 odd the two 8-byte halves of each
+    // 16-byte piece swapped, so that the transposing reads of half a wave
+    // (four rows of each of two 8-row groups) fall on distinct banks.
+    static constexpr int KRS = DK * 2 + 64;
+    static_assert(KRS % 256 == 64 || KRS % 256 == 192, "key row stride");
     static constexpr int SFR = 0;                      // state fragments [2 NB][64] x 16 B (hi [NB], lo [NB])
     static constexpr int BOP = 4 * 64 * 16;            // one step-indexed B operand (see bop_store)
     static constexpr int RFR = SFR + 2 * NB * 64 * 16; // R
     static constexpr int DFR = RFR + BOP;              // Delta, two chunks
     static constexpr int DTF = DFR + 2 * BOP;          // rho o Delta
-    static constexpr int KT = DTF + 4 * 64 * 16;       // K^T [dk][t] bf16 (of fp16 keys: the hi part)
-    static constexpr int KTL = KT + DK * KTS * 2;      // the lo part of K^T (fp16 keys)
-    static constexpr int VR = KTL + (IO == kF16 ? DK * KTS * 2 : 0);   // v rows [64] x 32 B (this row block)
+    static constexpr int KT = DTF + 4 * 64 * 16;       // K [t][dk] bf16, natural key order (fp16 keys: the hi part)
+    static constexpr int KTL = KT + kC * KRS;          // the lo part of K (fp16 keys)
+    static constexpr int VR = KTL + (IO == kF16 ? kC * KRS : 0);   // v rows [64] x 32 B (this row block)
     static constexpr int GR = VR + kC * 32;            // gamma [64], rho [64] fp32
     static constexpr int AF = GR + 2 * kC * 4;         // active flags [64] u32 (0 or 1)
     static constexpr int OT = AF + kC * 4;             // per wave: its pending output tile [16][16] bf16
@@ -598,6 +603,15 @@ __device__ __forceinline__ uint32_t kcol(uint32_t ks, uint32_t i) {
     return 32u * (ks >> 1) + 8u * (i >> 2) + 4u * (ks & 1u) + (i & 3u);
 }
 
+// Four bf16 values by gfx950's transposing LDS read (ds_read_b64_tr_b16):
+// within each group of 16 lanes, lane j receives element j % 4 of the 8-byte
+// pieces that lanes j / 4 + 4 k (k = 0..3) address, in that order of k.
+typedef short i16x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* p) {
+    typedef __attribute__((address_space(3))) i16x4v lds_i16x4;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
+}
+
 // A [64 steps][16 columns] operand split into hi and lo bf16 parts, written
 // by the wave that holds step tile tt as an accumulator (lane 16 lg + lr:
 // rows 16 tt + 4 lg .. +3 of column lr) and read as the B operand of 32-deep
@@ -633,8 +647,8 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     unsigned char* const rfr = lds + ScanLds::RFR;
     unsigned char* const dfr = lds + ScanLds::DFR;      // chunk c at dfr + (c & 1) * BOP
     unsigned char* const dtf = lds + ScanLds::DTF;
-    uint16_t* kt = reinterpret_cast<uint16_t*>(lds + ScanLds::KT);
-    uint16_t* ktl = reinterpret_cast<uint16_t*>(lds + ScanLds::KTL);
+    unsigned char* const ktb = lds + ScanLds::KT;
+    unsigned char* const ktlb = lds + ScanLds::KTL;
     const float* gr = reinterpret_cast<const float*>(lds + ScanLds::GR);
 
     // The wave index is read from lane 0 so that the compiler treats it, and
@@ -751,6 +765,19 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
     uint32_t* const otf = reinterpret_cast<uint32_t*>(lds + ScanLds::OTF) + w * 16;
     bool pend_valid = false;
     uint32_t pend_t0 = 0u;
+    // The state update's A operand of key tile ks over steps 32 kb .. 32 kb + 31:
+    // lane (lr, lg) gets K[32 kb + 8 lg + j][kcol(ks, lr)], j = 0..7, from two
+    // transposing reads of the row-major keys.  Lane lr addresses row
+    // 32 kb + 8 lg + lr / 4 (then the row 4 below) at the four columns
+    // kcol(ks, 4 (lr % 4) .. + 3), which are consecutive; the read hands lane
+    // lr column kcol(ks, lr) of the four rows its group addressed.
+    auto kt_frag = [&](const unsigned char* base, uint32_t ks, uint32_t kb) {
+        const uint32_t t = 32u * kb + 8u * lg + (lr >> 2);   // t / 8 and (t + 4) / 8 have the parity of lg
+        const uint32_t piece = 4u * (ks >> 1) + (lr & 3u);    // 16-byte piece of columns 8 piece ..
+        const unsigned char* p = base + t * ScanLds::KRS + piece * 16u + (((ks ^ lg) & 1u) * 8u);
+        const u32x2 a = lds_read_tr16(p), b = lds_read_tr16(p + 4u * ScanLds::KRS);
+        return u32x4{a.x, a.y, b.x, b.y};
+    };
     auto produce = [&](const f32x4v& vals, uint32_t actbits, uint32_t t0p) {
         if constexpr (IO == kBF16) {
             // Round to nearest even with the packed conversion; a NaN is
@@ -879,21 +906,18 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
             gam = f32x4v{g4.x, g4.y, g4.z, g4.w};
         }
         if (!qside) {
-            // This wave's 16 key rows, transposed into K^T [dk][t] for the state update.
+            // This wave's 16 key rows into LDS as they are (natural key
+            // order), one 16-byte piece per block; the state update reads them
+            // transposed (kt_frag).
+            const bool swap = (lr & 8u) != 0u;                // row 16 tt + lr in an odd 8-row group
 #pragma unroll
-            for (int ks = 0; ks < DK / 16; ++ks) {
-                const uint32_t dk = kcol(ks, 4u * lg), t = 16u * tt + lr;
-                const u32x2 a = (ks & 1) ? hi2(a8[ks >> 1]) : lo2(a8[ks >> 1]);
-                kt[(dk + 0) * ScanLds::KTS + t] = static_cast<uint16_t>(a.x);
-                kt[(dk + 1) * ScanLds::KTS + t] = static_cast<uint16_t>(a.x >> 16);
-                kt[(dk + 2) * ScanLds::KTS + t] = static_cast<uint16_t>(a.y);
-                kt[(dk + 3) * ScanLds::KTS + t] = static_cast<uint16_t>(a.y >> 16);
+            for (int m = 0; m < NB; ++m) {
+                const uint32_t o = (16u * tt + lr) * ScanLds::KRS + (32u * m + 8u * lg) * 2u;
+                const u32x4 v = a8[m];
+                *reinterpret_cast<u32x4*>(ktb + o) = swap ? u32x4{v.z, v.w, v.x, v.y} : v;
                 if constexpr (IO == kF16) {
-                    const u32x2 al = (ks & 1) ? hi2(a8l[ks >> 1]) : lo2(a8l[ks >> 1]);
-                    ktl[(dk + 0) * ScanLds::KTS + t] = static_cast<uint16_t>(al.x);
-                    ktl[(dk + 1) * ScanLds::KTS + t] = static_cast<uint16_t>(al.x >> 16);
-                    ktl[(dk + 2) * ScanLds::KTS + t] = static_cast<uint16_t>(al.y);
-                    ktl[(dk + 3) * ScanLds::KTS + t] = static_cast<uint16_t>(al.y >> 16);
+                    const u32x4 vl = a8l[m];
+                    *reinterpret_cast<u32x4*>(ktlb + o) = swap ? u32x4{vl.z, vl.w, vl.x, vl.y} : vl;
                 }
             }
             const uint16_t* vr = reinterpret_cast<const uint16_t*>(lds + ScanLds::VR);
@@ -955,18 +979,15 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const u32x4 dh = bop_hi(dtf, kb, l), dl = bop_lo(dtf, kb, l);
-            const uint32_t o = kcol(w, lr) * ScanLds::KTS + 32 * kb + 8 * lg;
-            const u32x4 a = *reinterpret_cast<const u32x4*>(&kt[o]);
+            const u32x4 a = kt_frag(ktb, w, kb);
             acc = mfma_bf16_k32(a, dh, acc);
             lo_acc = mfma_bf16_k32(a, dl, lo_acc);
-            if constexpr (IO == kF16) lo_acc = mfma_bf16_k32(*reinterpret_cast<const u32x4*>(&ktl[o]), dh, lo_acc);
+            if constexpr (IO == kF16) lo_acc = mfma_bf16_k32(kt_frag(ktlb, w, kb), dh, lo_acc);
             if (extra) {
-                const uint32_t o2 = kcol(w2, lr) * ScanLds::KTS + 32 * kb + 8 * lg;
-                const u32x4 a2 = *reinterpret_cast<const u32x4*>(&kt[o2]);
+                const u32x4 a2 = kt_frag(ktb, w2, kb);
                 acc2 = mfma_bf16_k32(a2, dh, acc2);
                 lo_acc2 = mfma_bf16_k32(a2, dl, lo_acc2);
-                if constexpr (IO == kF16)
-                    lo_acc2 = mfma_bf16_k32(*reinterpret_cast<const u32x4*>(&ktl[o2]), dh, lo_acc2);
+                if constexpr (IO == kF16) lo_acc2 = mfma_bf16_k32(kt_frag(ktlb, w2, kb), dh, lo_acc2);
             }
         }
 #pragma unroll
