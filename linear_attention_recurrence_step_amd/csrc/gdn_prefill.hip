@@ -37,8 +37,8 @@
 // (about 16 significant bits).  A product of two split operands takes three
 // MFMAs (hi.hi + hi.lo + lo.hi), a bf16 x split product two; the Gram
 // matrices of fp16 keys and queries take all four.  Accumulation is fp32.  M
-// is formed by running products of the gates (no division), so zero or tiny
-// gates are exact.
+// is formed by products of the gates (no division), so zero or tiny gates are
+// exact.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 
