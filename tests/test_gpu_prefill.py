@@ -67,6 +67,7 @@ CASES = [
     # a full and a partial set of value heads, and two full sets
     (1, 70, 1, 5, 32, "bernoulli", "block"),
     (2, 65, 2, 16, 16, "trailing", "tiled"),
+    (1, 100, 2, 8, 32, "bernoulli", "tiled"),       # exactly one full set of four
 ]
 
 
