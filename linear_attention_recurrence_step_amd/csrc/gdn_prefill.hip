@@ -885,6 +885,13 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
                 if constexpr (IO == kF16) split_f16x8(a8[m], a8[m], a8l[m]);
             }
         }
+        // The previous chunk's outputs and the loads for the chunk after next
+        // are issued here, behind the first barrier and before the products
+        // below, so that the vector-memory path works while the matrix cores
+        // do (issued after the products, they held up R by ~8 µs per launch).
+        flush();
+        sload(st, c2);                                  // st was stored into LDS at the top
+        aload(ak, c2 * kC);                             // ak is free again: its selects are done
         f32x4v x = {0.f, 0.f, 0.f, 0.f}, x2 = x;
 #pragma unroll
         for (int m = 0; m < NB; ++m) {
@@ -893,11 +900,6 @@ __global__ __launch_bounds__(512, 1) void gdn_prefill_scan_kernel(
             x2 = mfma_bf16_k32(a8[m], sl, x2);
             if constexpr (IO == kF16) x2 = mfma_bf16_k32(a8l[m], sh, x2);
         }
-        // The previous chunk's outputs and loads for the chunk after next are
-        // issued here, behind the first barrier, while the products above run.
-        flush();
-        sload(st, c2);                                  // st was stored into LDS at the top
-        aload(ak, c2 * kC);                             // ak is free again: its selects are done
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] += x2[r];
         f32x4v gam;
